@@ -1,0 +1,31 @@
+"""CPU oracle of the W4A4 quantized linear: zigzag permutation, composite SVD.Hadamard block
+rotation, symmetric int4 RTN / per-step / per-token quantization, integer GEMM and dequantization.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package. It shares no code with the GPU library and never imports
+it; the GPU library never imports this package.
+
+Parity unpinned: none of the functions here. Each is pinned by the CPU tests (closed forms,
+library routines, brute force and invariants); see the test module docstrings.
+"""
+from .reference import (  # noqa: F401
+    build,
+    colnorm2,
+    zigzag_perm,
+    block_svd,
+    hadamard,
+    rotation,
+    rotate_rows,
+    pack_weights,
+    weight_rtn,
+    pack_int4,
+    unpack_int4,
+    quantize_act,
+    rotate_quant_act,
+    int_gemm,
+    int_gemm_sampled,
+    dequant,
+    gemm,
+    calibrate_table,
+    linear,
+)

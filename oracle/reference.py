@@ -1,0 +1,376 @@
+"""Python face of the CPU oracle (TEST INFRASTRUCTURE ONLY; see the package docstring).
+
+The arithmetic lives in ``w4a4_oracle.c`` (plain fp64 loops, built with -ffp-contract=off).
+This module adds the steps for which a library routine is the plain definition: the singular
+value decomposition (LAPACK through numpy), the stable sort that orders channels, and the IEEE
+binary16 rounding of outputs (numpy's round-to-nearest-even conversion).
+
+Sources, cited by page title and section:
+ [P1] "Omega-QVLA: Nen VLA W4A4 tren Edge" -- "Y tuong paper: xoay truoc, scale theo step sau"
+      (composite rotation, per-step act_scale_table) and "Build DiT action head pack"
+      (--use-rtn --w-bits 4 --a-bits 4 --num-steps 8 --duquant-block-size 64 --svd-rank 0).
+ [P2] gist.science (pt) "Resumo Tecnico", "Metodologia" 1 (SVD W = U Sigma V^T with R_SVD = U,
+      normalized Hadamard H, R = R_SVD . H, block implementation, zigzag permutation by weight column
+      norms) and 2 (per-step DiT activation scaling from calibration trajectories).
+ [P3] aiexpert.news: a step-count mismatch or a truncated table is a failure mode.
+ [P5] FoldQuantVLA summary, key change 2: dynamic per-token activation quantization.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w4a4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_w4a4_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_i8p = ctypes.POINTER(ctypes.c_int8)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def build() -> str:
+    """Compile the oracle's C core (gcc, -O2 -ffp-contract=off, single-threaded)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-shared", "-fPIC",
+           "-o", _LIB_PATH, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if (not os.path.exists(_LIB_PATH)
+            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.orc_colnorm2.argtypes = [_dp, _i64, _i64, _dp]
+    lib.orc_hadamard.argtypes = [_i64, _dp]
+    lib.orc_rotation.argtypes = [_fp, _i64, _i64, _dp]
+    lib.orc_rotate_rows.argtypes = [_dp, _i64, _i64, _i64, _i64, _i32p, _dp, _dp]
+    lib.orc_weight_rtn.argtypes = [_dp, _i64, _i64, _fp, _i8p]
+    lib.orc_act_quant.argtypes = [_dp, _i64, _i64, ctypes.c_int, ctypes.c_float, _fp, _fp, _i8p, _fp]
+    lib.orc_pack.argtypes = [_i8p, _i64, _i64, _u8p]
+    lib.orc_unpack.argtypes = [_u8p, _i64, _i64, _i8p]
+    lib.orc_int_gemm.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i64p]
+    lib.orc_int_gemm_sampled.argtypes = [_i8p, _i8p, _i64, _i64, _i64p, _i64p, _i64p]
+    lib.orc_dequant.argtypes = [_i64p, _i64, _i64, _fp, ctypes.c_int, _fp, _fp]
+    lib.orc_gelu.argtypes = [_fp, _i64, _dp]
+    for f in ("orc_colnorm2", "orc_hadamard", "orc_rotation", "orc_rotate_rows", "orc_weight_rtn",
+              "orc_act_quant", "orc_pack", "orc_unpack", "orc_int_gemm", "orc_int_gemm_sampled",
+              "orc_dequant", "orc_gelu"):
+        getattr(lib, f).restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, t):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(t)
+
+
+def _f64(a) -> np.ndarray:
+    """Stored fp16/fp32 values widened exactly to fp64."""
+    return np.ascontiguousarray(np.asarray(a).astype(np.float64))
+
+
+def _check_block(K: int, B: int):
+    if B < 1 or (B & (B - 1)) != 0:
+        raise ValueError(f"block size {B} is not a power of two")
+    if K % B != 0:
+        raise ValueError(f"K={K} is not a multiple of the block size {B}")
+
+
+# ----------------------------------------------------------------------------------------------
+# Offline side: zigzag permutation, per-block SVD factor, composite rotation
+# ----------------------------------------------------------------------------------------------
+
+def colnorm2(W) -> np.ndarray:
+    """Squared L2 norm of every input channel (column of W [N, K]), fp64, rows summed in order."""
+    W64 = _f64(W)
+    N, K = W64.shape
+    c2 = np.empty(K, np.float64)
+    _load().orc_colnorm2(_ptr(W64, _dp), N, K, _ptr(c2, _dp))
+    return c2
+
+
+def zigzag_perm(W, B: int) -> np.ndarray:
+    """Zigzag channel permutation [P2 Metodologia 1, "Implementacao em Blocos"; P4 "Implementation
+    par Blocs"]: channels are reordered by weight column norm so that high- and low-norm channels
+    are spread evenly over the rotation blocks.
+
+    Reading taken: rank channels by descending norm (stable, ties to the lower index), then deal the
+    ranks over the nb = K/B blocks like a boustrophedon: ranks [p*nb, (p+1)*nb) form pass p; in an
+    even pass rank p*nb + j goes to block j, in an odd pass to block nb-1-j; inside a block, pass p
+    takes position p. Returns perm int32[K] with perm[b*B + p] = original channel index.
+    """
+    W = np.asarray(W)
+    N, K = W.shape
+    _check_block(K, B)
+    nb = K // B
+    c2 = colnorm2(W)
+    order = np.argsort(-c2, kind="stable")
+    perm = np.empty(K, np.int32)
+    for r in range(K):
+        pss, j = divmod(r, nb)
+        b = j if pss % 2 == 0 else nb - 1 - j
+        perm[b * B + pss] = order[r]
+    return perm
+
+
+def block_svd(W, perm, B: int, return_fp64: bool = False):
+    """Per-block SVD factor [P2 Metodologia 1, "Rotacao SVD": W = U Sigma V^T, R_SVD = U].
+
+    Reading taken: the rotation acts on input channels, so for each block b the factor is the B x B
+    orthogonal matrix of right singular vectors of W_b = W[:, perm[bB:(b+1)B]] (N x B), columns in
+    descending singular value, so that the columns of W_b . U_b have norms sigma_i ("each row's energy
+    controlled by the singular spectrum" in the [in, out] layout the page writes W in). Each column's
+    sign is fixed so that its largest-magnitude entry is positive (first index on ties).
+    Returns U fp32 [nb, B, B] with U[b][i][j] = entry (i, j) of U_b; with return_fp64 also the
+    unrounded fp64 factors and the singular values [nb, B] (zeros padded when N < B).
+    """
+    W64 = _f64(W)
+    N, K = W64.shape
+    _check_block(K, B)
+    nb = K // B
+    perm = np.asarray(perm, np.int64)
+    U64 = np.empty((nb, B, B), np.float64)
+    sig = np.zeros((nb, B), np.float64)
+    for b in range(nb):
+        Wb = W64[:, perm[b * B:(b + 1) * B]]
+        _, s, Vt = np.linalg.svd(Wb, full_matrices=True)
+        V = Vt.T.copy()
+        idx = np.argmax(np.abs(V), axis=0)
+        sgn = np.where(V[idx, np.arange(B)] < 0, -1.0, 1.0)
+        V *= sgn[None, :]
+        U64[b] = V
+        sig[b, :len(s)] = s
+    U32 = U64.astype(np.float32)
+    if return_fp64:
+        return U32, U64, sig
+    return U32
+
+
+def hadamard(B: int) -> np.ndarray:
+    """Normalized natural-order Sylvester Hadamard matrix H_B, fp64 [P2 "Rotacao Hadamard"]."""
+    if B < 1 or (B & (B - 1)) != 0:
+        raise ValueError(f"Hadamard size {B} is not a power of two")
+    H = np.empty((B, B), np.float64)
+    _load().orc_hadamard(B, _ptr(H, _dp))
+    return H
+
+
+def rotation(U, B: int) -> np.ndarray:
+    """Composite rotation R_b = U_b . H_B of every block, fp64 [nb, B, B] [P2: R = R_SVD . H]."""
+    U = np.ascontiguousarray(np.asarray(U, np.float32))
+    nb = U.shape[0]
+    assert U.shape == (nb, B, B)
+    K = nb * B
+    R = np.empty((nb, B, B), np.float64)
+    _load().orc_rotation(_ptr(U, _fp), K, B, _ptr(R, _dp))
+    return R
+
+
+def rotate_rows(A, perm, R, B: int) -> np.ndarray:
+    """A[:, perm] . blockdiag(R_b), fp64, for weights or activations (rows independent)."""
+    A64 = _f64(A)
+    rows, K = A64.shape
+    _check_block(K, B)
+    perm = np.ascontiguousarray(np.asarray(perm, np.int32))
+    R = np.ascontiguousarray(np.asarray(R, np.float64))
+    assert perm.shape == (K,) and R.shape == (K // B, B, B)
+    Y = np.empty((rows, K), np.float64)
+    _load().orc_rotate_rows(_ptr(A64, _dp), rows, K, K, B, _ptr(perm, _i32p), _ptr(R, _dp),
+                            _ptr(Y, _dp))
+    return Y
+
+
+def weight_rtn(Wr) -> tuple[np.ndarray, np.ndarray]:
+    """Per-output-channel symmetric int4 RTN of rotated weights: (s_w fp32 [N], codes int8 [N, K])."""
+    Wr = np.ascontiguousarray(np.asarray(Wr, np.float64))
+    N, K = Wr.shape
+    s_w = np.empty(N, np.float32)
+    p = np.empty((N, K), np.int8)
+    _load().orc_weight_rtn(_ptr(Wr, _dp), N, K, _ptr(s_w, _fp), _ptr(p, _i8p))
+    return s_w, p
+
+
+def pack_int4(q) -> np.ndarray:
+    """Two's-complement nibbles, two per byte, low nibble = even k: uint8 [rows, K/2]."""
+    q = np.ascontiguousarray(np.asarray(q, np.int8))
+    rows, K = q.shape
+    if K % 2:
+        raise ValueError("K must be even to pack two int4 codes per byte")
+    out = np.empty((rows, K // 2), np.uint8)
+    _load().orc_pack(_ptr(q, _i8p), rows, K, _ptr(out, _u8p))
+    return out
+
+
+def unpack_int4(packed, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(np.asarray(packed, np.uint8))
+    rows = packed.shape[0]
+    q = np.empty((rows, K), np.int8)
+    _load().orc_unpack(_ptr(packed, _u8p), rows, K, _ptr(q, _i8p))
+    return q
+
+
+def pack_weights(W, perm, U, B: int, rows=None) -> dict:
+    """Offline weight rotate + per-channel RTN + pack (optionally only the given output rows).
+
+    W' = W[:, perm] . blockdiag(U_b H_B) in fp64; s_w, codes and packed bytes as in ``weight_rtn``.
+    """
+    W = np.asarray(W)
+    if rows is not None:
+        W = W[np.asarray(rows)]
+    K = W.shape[1]
+    R = rotation(U, B)
+    Wr = rotate_rows(W, perm, R, B)
+    s_w, p = weight_rtn(Wr)
+    return {"w_rot": Wr, "w_scale": s_w, "codes": p, "wq": pack_int4(p), "R": R}
+
+
+def quantize_act(Xr, mode: str, table=None, num_steps: int | None = None, step: int | None = None):
+    """Activation int4 quantization of rotated activations Xr (fp64 [M, K]).
+
+    mode "per_step": s = table[step]; a step outside [0, num_steps) or a table shorter than
+      num_steps is an error, never clamped [P3: a step-count mismatch or truncated table is a
+      failure mode]; mode "per_token": s_m from the row absmax.
+    Returns dict(x32, v, codes, scale, xq).
+    """
+    Xr = np.ascontiguousarray(np.asarray(Xr, np.float64))
+    M, K = Xr.shape
+    if mode == "per_step":
+        table = np.asarray(table, np.float32)
+        if num_steps is None:
+            num_steps = len(table)
+        if len(table) < num_steps:
+            raise ValueError("act_scale_table is shorter than the number of steps")
+        if step is None or not (0 <= step < num_steps):
+            raise ValueError(f"step {step} outside [0, {num_steps})")
+        s = float(table[step])
+        if not (s > 0 and np.isfinite(s)):
+            raise ValueError("act_scale_table entry must be positive and finite")
+        imode, ts = 0, s
+    elif mode == "per_token":
+        imode, ts = 1, 1.0
+    else:
+        raise ValueError(mode)
+    x32 = np.empty((M, K), np.float32)
+    v = np.empty((M, K), np.float32)
+    q = np.empty((M, K), np.int8)
+    sc = np.empty(M, np.float32)
+    _load().orc_act_quant(_ptr(Xr, _dp), M, K, imode, ts, _ptr(x32, _fp), _ptr(v, _fp),
+                          _ptr(q, _i8p), _ptr(sc, _fp))
+    return {"x32": x32, "v": v, "codes": q, "scale": sc, "xq": pack_int4(q) if K % 2 == 0 else None}
+
+
+def rotate_quant_act(X, perm, U, B: int, mode: str, table=None, num_steps=None, step=None, R=None):
+    """Runtime activation path: zigzag gather, block rotation, scale, int4 quantize, pack."""
+    if R is None:
+        R = rotation(U, B)
+    Xr = rotate_rows(X, perm, R, B)
+    out = quantize_act(Xr, mode, table, num_steps, step)
+    out["x_rot"] = Xr
+    return out
+
+
+def int_gemm(q, p) -> np.ndarray:
+    """acc = q . p^T in int64 (q [M, K], p [N, K] int8 codes)."""
+    q = np.ascontiguousarray(np.asarray(q, np.int8))
+    p = np.ascontiguousarray(np.asarray(p, np.int8))
+    M, K = q.shape
+    N = p.shape[0]
+    assert p.shape[1] == K
+    acc = np.empty((M, N), np.int64)
+    _load().orc_int_gemm(_ptr(q, _i8p), _ptr(p, _i8p), M, N, K, _ptr(acc, _i64p))
+    return acc
+
+
+def int_gemm_sampled(q, p, mi, ni) -> np.ndarray:
+    q = np.ascontiguousarray(np.asarray(q, np.int8))
+    p = np.ascontiguousarray(np.asarray(p, np.int8))
+    mi = np.ascontiguousarray(np.asarray(mi, np.int64))
+    ni = np.ascontiguousarray(np.asarray(ni, np.int64))
+    K = q.shape[1]
+    acc = np.empty(len(mi), np.int64)
+    _load().orc_int_gemm_sampled(_ptr(q, _i8p), _ptr(p, _i8p), K, len(mi), _ptr(mi, _i64p),
+                                 _ptr(ni, _i64p), _ptr(acc, _i64p))
+    return acc
+
+
+EPI_NONE, EPI_GELU, EPI_RESIDUAL = 0, 1, 2
+
+
+def dequant(acc, x_scale, per_token: bool, w_scale, epilogue: int = EPI_NONE, residual=None):
+    """Y = fp16_rne(fp32(fp32(acc * s_x) * s_w[n])), then the optional epilogue:
+    EPI_GELU: fp16(erf-GELU computed in fp64 of the fp32 dequantized value);
+    EPI_RESIDUAL: fp16(fp32(dequant) + fp32(residual)). Returns (Y fp16, y32 fp32 dequant)."""
+    acc = np.ascontiguousarray(np.asarray(acc, np.int64))
+    M, N = acc.shape
+    if np.any(np.abs(acc) >= 2 ** 31):
+        raise OverflowError("accumulator leaves int32")
+    sx = np.ascontiguousarray(np.asarray(x_scale, np.float32).reshape(-1))
+    sw = np.ascontiguousarray(np.asarray(w_scale, np.float32))
+    y32 = np.empty((M, N), np.float32)
+    _load().orc_dequant(_ptr(acc, _i64p), M, N, _ptr(sx, _fp), 1 if per_token else 0,
+                        _ptr(sw, _fp), _ptr(y32, _fp))
+    if epilogue == EPI_NONE:
+        Y = y32.astype(np.float16)
+    elif epilogue == EPI_GELU:
+        g = np.empty((M, N), np.float64)
+        _load().orc_gelu(_ptr(y32, _fp), M * N, _ptr(g, _dp))
+        Y = g.astype(np.float16)
+    elif epilogue == EPI_RESIDUAL:
+        Y = (y32 + np.asarray(residual, np.float16).astype(np.float32)).astype(np.float16)
+    else:
+        raise ValueError(epilogue)
+    return Y, y32
+
+
+def gemm(xq_codes, x_scale, per_token, w_codes, w_scale, epilogue=EPI_NONE, residual=None):
+    """Integer GEMM of int4 codes followed by dequantization (codes given unpacked, int8)."""
+    acc = int_gemm(xq_codes, w_codes)
+    Y, y32 = dequant(acc, x_scale, per_token, w_scale, epilogue, residual)
+    return {"acc": acc, "Y": Y, "y32": y32}
+
+
+def calibrate_table(X_samples_per_step, perm, U, B: int, R=None) -> np.ndarray:
+    """Per-step act_scale_table from calibration trajectories [P1 "Y tuong paper"; P2 item 2
+    "Calibracao por Passo"]. Reading taken: one scale per (linear, step), the absmax statistic over
+    every calibration sample, token and channel of the rotated activation, stored as a scale:
+    table[t] = fp32(max |fp32(x')| / 7) (1.0f when the max is 0). X_samples_per_step[t] is a list of
+    [M, K] arrays for step t."""
+    if R is None:
+        R = rotation(U, B)
+    T = len(X_samples_per_step)
+    table = np.empty(T, np.float32)
+    for t in range(T):
+        amax = np.float32(0.0)
+        for Xs in X_samples_per_step[t]:
+            x32 = rotate_rows(Xs, perm, R, B).astype(np.float32)
+            amax = max(amax, np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0))
+        table[t] = np.float32(float(amax) / 7.0) if amax > 0 else np.float32(1.0)
+    return table
+
+
+def linear(X, W, B: int, mode: str, table=None, num_steps=None, step=None, perm=None, U=None,
+           epilogue=EPI_NONE, residual=None) -> dict:
+    """The whole W4A4 linear on the CPU: offline (perm, U, pack) then runtime (rotate-quant, GEMM)."""
+    if perm is None:
+        perm = zigzag_perm(W, B)
+    if U is None:
+        U = block_svd(W, perm, B)
+    pw = pack_weights(W, perm, U, B)
+    act = rotate_quant_act(X, perm, U, B, mode, table, num_steps, step, R=pw["R"])
+    g = gemm(act["codes"], act["scale"], mode == "per_token", pw["codes"], pw["w_scale"],
+             epilogue, residual)
+    return {"perm": perm, "U": U, "pack": pw, "act": act, **g}
