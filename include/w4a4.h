@@ -1,0 +1,169 @@
+/*
+ * w4a4.h -- C ABI of libw4a4.so, an MI355X (gfx950) implementation of the W4A4 quantized linear of
+ * Omega-QVLA: zigzag channel permutation, blockwise composite SVD.Hadamard rotation, symmetric int4
+ * activations (per-denoising-step table scale or dynamic per-token scale), int4 RTN weights with a
+ * per-output-channel scale, integer GEMM on int8 MFMA, fp16 output.
+ *
+ * Passages the calls follow (pages cited by title and section):
+ *  - gist.science (pt/fr) summary of arXiv 2605.28803, "Metodologia" / "Methodologie", item 1: the SVD
+ *    W = U Sigma V^T gives R_SVD, a normalized Hadamard H is composed with it, R = R_SVD . H, the
+ *    rotation is applied block by block along the input channels after a zigzag permutation ordered
+ *    by weight column norms, before quantization. Item 2: a per-step activation scale table built
+ *    offline from calibration trajectories and looked up at inference time.
+ *  - vnrobo.com "Omega-QVLA: Nen VLA W4A4 tren Edge", "Y tuong paper" (per-step act_scale_table,
+ *    runtime lookup of the current step's scale) and "Build DiT action head pack" (--use-rtn,
+ *    --w-bits 4, --a-bits 4, --num-steps 8, --duquant-block-size 64).
+ *  - aiexpert.news "Omega-QVLA Reduce el Modelo ... 71%": a step-count mismatch or a truncated table
+ *    is a failure mode, so a step outside the table is an error here, never clamped.
+ *  - radar.vhtltd.com FoldQuantVLA summary, key change 2: dynamic per-token activation quantization.
+ *
+ * Conventions for every call:
+ *  - Every pointer argument is a caller-owned DEVICE pointer (hipMalloc'd or torch CUDA memory)
+ *    unless stated otherwise. The library allocates nothing; scratch memory comes from the `ws`
+ *    argument, sized by the matching *_workspace_bytes() query (ws may be NULL when that is 0).
+ *  - Work is enqueued on `stream` (NULL = the null stream) and the call returns without waiting.
+ *    Arguments are validated on the host before anything is launched; a failing call launches
+ *    nothing and leaves every output untouched. Calls that share a workspace must not overlap.
+ *  - Layouts: X [M][K] and W [N][K] are row-major with row strides ldx / ldw in elements, dtype
+ *    W4A4_F16 (IEEE binary16) or W4A4_F32. perm is int32 [K]: permuted position j takes original
+ *    channel perm[j]; perm == NULL means the identity (the caller already stores channels in
+ *    zigzag order). U is fp32 [K/block][block][block] row-major: entry (i, j) of block b's factor
+ *    U_b is U[(b*block + i)*block + j]; a row vector x_b of block b is rotated as (x_b U_b) H_B, with
+ *    H_B the natural-order Sylvester Hadamard matrix scaled by 1/sqrt(block).
+ *    Packed int4: uint8 [rows][K/2], two's-complement nibbles, low nibble = even k.
+ *    Scales are fp32. Y and residual are IEEE binary16 bit patterns, row-major with strides ldy/ldr.
+ *  - block must be a power of two in [1, 256] dividing K, and K must be even.
+ *  - Return value: W4A4_OK or one of the W4A4_ERR_* codes; w4a4_last_error() then describes the
+ *    failure (thread-local, valid until the next call on the same thread).
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w4a4_status {
+    W4A4_OK = 0,
+    W4A4_ERR_ARG = 1,         /* NULL where a pointer is required, negative size, unknown enum */
+    W4A4_ERR_SHAPE = 2,       /* K odd or not a multiple of block, leading dimension too small */
+    W4A4_ERR_STEP_RANGE = 3,  /* step outside [0, num_steps) */
+    W4A4_ERR_UNSUPPORTED = 4, /* block not a power of two in [1, 256]; size beyond int32 indexing */
+    W4A4_ERR_ALIGN = 5,       /* pointer not aligned as the argument requires */
+    W4A4_ERR_WORKSPACE = 6,   /* ws NULL or smaller than the *_workspace_bytes() figure */
+    W4A4_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+};
+
+enum w4a4_dtype { W4A4_F16 = 0, W4A4_F32 = 1 };
+
+enum w4a4_epilogue {
+    W4A4_EPI_NONE = 0,     /* Y = fp16(dequant) */
+    W4A4_EPI_GELU = 1,     /* Y = fp16(gelu_erf(dequant)), GELU evaluated in fp32 */
+    W4A4_EPI_RESIDUAL = 2  /* Y = fp16(fp32(dequant) + fp32(residual)) */
+};
+
+/* ---------------------------------------------------------------------------------------------
+ * Offline calibration on the device (done once per linear, before packing).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Zigzag permutation [gist.science Metodologia 1, "Implementacao em Blocos"]: rank the input
+ * channels by descending weight column norm (the fp64 sum over rows n = 0..N-1, in that order, of
+ * W[n][k]^2; ties go to the lower channel index), then deal ranks over the nb = K/block blocks like
+ * a boustrophedon: rank r = p*nb + j lands in block j when pass p is even and in block nb-1-j when p
+ * is odd, at position p inside the block. Writes perm[b*block + p] = original channel (int32 [K]).
+ * Bit-exact (integer result of fp64 comparisons). */
+size_t w4a4_zigzag_workspace_bytes(int K);
+int w4a4_zigzag_perm(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                     int32_t *perm, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-block SVD factor [gist.science Metodologia 1, "Rotacao SVD": W = U Sigma V^T, R_SVD]: for each
+ * block b, the right singular vectors of W_b = W[:, perm[b*block .. b*block+block-1]] (N x block),
+ * columns in descending singular value, each column's sign chosen so that its largest-magnitude
+ * entry is positive; computed as the fp64 cyclic-Jacobi eigenbasis of W_b^T W_b and rounded once to
+ * fp32. Writes U fp32 [K/block][block][block]. Singular vectors are unique only up to the sign fixed
+ * here and up to rotations inside repeated singular values (e.g. N < block). block <= 128 here
+ * (W4A4_ERR_UNSUPPORTED above). */
+size_t w4a4_block_svd_workspace_bytes(int N, int K, int block);
+int w4a4_block_svd(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                   const int32_t *perm, float *U, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-step activation scale for one table entry [vnrobo.com "Y tuong paper"; gist.science item 2
+ * "Calibracao por Passo"]: *table_entry = fp32(max |fp32(x')| / 7) over every row of the stacked
+ * calibration activations X [M][K] (several calibration samples of one denoising step stacked along
+ * M), x' being the rotated activation; 1.0f if that max is 0. `rot` is the operand written by
+ * w4a4_pack_weights for this linear. */
+size_t w4a4_calibrate_workspace_bytes(int M, int K, int block);
+int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, float *table_entry,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Offline weight rotate + RTN + pack [gist.science Metodologia 1; vnrobo.com "Build DiT action head
+ * pack": --use-rtn --w-bits 4 --svd-rank 0, i.e. RTN on the whole rotated weight].
+ *
+ * W' = W[:, perm] . blockdiag(R_b), R_b = U_b . H_B, all in fp64 with every dot product summed in
+ * increasing index order without fused multiply-add; s_w[n] = fp32(max_k |W'[n][k]| / 7) (1.0f for a
+ * zero row); codes p = clamp(rint(W' / s_w), -8, 7) (half to even), packed into wq [N][K/2].
+ * Also writes `rot`, the activation-side rotation operand (w4a4_rot_bytes(K, block) bytes, 16-byte
+ * aligned, opaque device layout) that w4a4_rotate_quant_act and w4a4_calibrate_act_scale read.
+ * wq and w_scale are bit-exact functions of (W, perm, U).
+ * ------------------------------------------------------------------------------------------- */
+size_t w4a4_rot_bytes(int K, int block);
+size_t w4a4_pack_workspace_bytes(int N, int K, int block);
+int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                      const int32_t *perm, const float *U, uint8_t *wq, float *w_scale, void *rot,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Runtime activation path: zigzag gather, block rotation x' = X[:, perm] . blockdiag(R_b) computed
+ * on the device in fp32, activation scale, int4 quantization and packing.
+ *  - Per-step mode (act_scale_table != NULL) [vnrobo.com "Y tuong paper"]: s = table[step] for every
+ *    row; step must lie in [0, num_steps) (else W4A4_ERR_STEP_RANGE) and the table must hold at
+ *    least num_steps device floats. x_scale[0] receives s. Entries must be positive and finite; the
+ *    kernel quantizes with 1.0f where one is not, instead of producing NaN codes.
+ *  - Per-token mode (act_scale_table == NULL) [FoldQuantVLA key change 2]: s_m = fp32(max_k |x'_mk|
+ *    / 7) (1.0f for a zero row); x_scale[m] receives s_m for m in [0, M). num_steps/step ignored.
+ *  Codes: r = fp32(1/s), q = clamp(rint(fp32(x' * r)), -8, 7), packed into xq [M][K/2].
+ *  xrot_dbg: NULL in production; otherwise fp32 [M][K] receives x' (test hook).
+ *  M == 0 is a valid empty call.
+ * ------------------------------------------------------------------------------------------- */
+size_t w4a4_act_workspace_bytes(int M, int K, int block, int per_token);
+int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                          const int32_t *perm, const void *rot, const float *act_scale_table,
+                          int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * W4A4 GEMM with fused dequantization [vnrobo.com "Vi sao W4A4 kho hon W4A16?": activations must be
+ * low-bit too for the compute path to be truly low-bit]. acc[m][n] = sum_k q[m][k] p[n][k] is exact
+ * in int32 (int8 MFMA, |acc| <= 64 K, K <= 2^24); Y[m][n] = fp16(fp32(fp32(float(acc) * s_x) *
+ * w_scale[n])) with s_x = x_scale[m] (x_scale_per_token != 0) or x_scale[0], then the epilogue.
+ * xq [M][K/2], wq [N][K/2]; residual [M][N] fp16 (stride ldr) is read only by W4A4_EPI_RESIDUAL.
+ * M == 0 is a valid empty call.
+ * ------------------------------------------------------------------------------------------- */
+size_t w4a4_gemm_workspace_bytes(int M, int N, int K);
+int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, const uint8_t *wq,
+              const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
+              const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Test hook: the raw int32 accumulators acc [M][N] (row-major, dense) of the same integer GEMM. */
+int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Diagnostics (host only).
+ * ------------------------------------------------------------------------------------------- */
+const char *w4a4_last_error(void);
+const char *w4a4_status_string(int status);
+int w4a4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every function that
+include/w4a4.h declares, and rejects bad arguments on the host before anything is launched.
+
+The rejected calls below pass fake, never-dereferenced device addresses: validation returns before
+any HIP call, so these run without a GPU. The step-range rule follows the aiexpert.news page (a step
+count mismatch or truncated act_scale_table is a failure mode, so the library reports it instead of
+clamping the step).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a4_post_quantized_zigzag_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # 256-byte aligned stand-in address
+FAKE_ODD = ctypes.c_void_p(0x10004)  # 4-byte aligned only
+NULL = None
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bd.lib()
+
+
+def test_every_declared_function_is_exported_and_bound(L):
+    names = header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in bd.SIGNATURES, f"{n} missing from the binding"
+    assert set(bd.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(L):
+    assert L.w4a4_abi_version() == 1
+    assert L.w4a4_status_string(3) == b"W4A4_ERR_STEP_RANGE"
+    assert L.w4a4_status_string(99) == b"W4A4_ERR_UNKNOWN"
+
+
+def _rq(L, *, M=16, K=256, ldx=256, block=64, dt=bd.W4A4_F16, X=FAKE, rot=FAKE, table=FAKE,
+        steps=8, step=0, ws=NULL, wsb=0):
+    return L.w4a4_rotate_quant_act(X, dt, M, K, ldx, block, FAKE, rot, table, steps, step, FAKE,
+                                   FAKE, NULL, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("step,steps", [(8, 8), (-1, 8), (100, 8), (0, 0)])
+def test_step_outside_table_is_an_error(L, step, steps):
+    assert _rq(L, step=step, steps=steps) == bd.W4A4_ERR_STEP_RANGE
+    assert b"step" in L.w4a4_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=3), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(block=512), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(block=0), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(K=250, ldx=250, block=1 << 1), bd.W4A4_ERR_SHAPE),   # fine for block 2 ...
+    (dict(K=255, ldx=255, block=1), bd.W4A4_ERR_SHAPE),        # odd K
+    (dict(K=192, ldx=192, block=128), bd.W4A4_ERR_SHAPE),      # K not a multiple of the block
+    (dict(ldx=100), bd.W4A4_ERR_SHAPE),
+    (dict(X=NULL), bd.W4A4_ERR_ARG),
+    (dict(M=-1), bd.W4A4_ERR_ARG),
+    (dict(dt=7), bd.W4A4_ERR_ARG),
+    (dict(rot=FAKE_ODD), bd.W4A4_ERR_ALIGN),
+    (dict(rot=NULL), bd.W4A4_ERR_ARG),
+    (dict(table=NULL), bd.W4A4_ERR_WORKSPACE),                 # per-token needs a workspace
+])
+def test_rotate_quant_rejects(L, kw, code):
+    if kw.get("K") == 250:
+        # K=250 is even and a multiple of block 2, so it is accepted; use M=0 to stay on the host
+        assert _rq(L, M=0, **kw) == bd.W4A4_OK
+        return
+    assert _rq(L, **kw) == code
+    assert L.w4a4_last_error() != b""
+
+
+def test_empty_batch_is_a_valid_call(L):
+    assert _rq(L, M=0) == bd.W4A4_OK
+    assert _rq(L, M=0, table=NULL) == bd.W4A4_OK
+    assert L.w4a4_gemm(NULL, NULL, 0, FAKE, FAKE, 0, 64, 256, NULL, 64, 0, NULL, 0, NULL, 0,
+                       NULL) == bd.W4A4_OK
+    assert L.w4a4_gemm_i32(NULL, FAKE, 0, 64, 256, NULL, NULL, 0, NULL) == bd.W4A4_OK
+
+
+def _gemm(L, *, M=16, N=64, K=256, ldy=64, epi=0, res=NULL, ldr=0, Y=FAKE, ws=NULL, wsb=0):
+    return L.w4a4_gemm(FAKE, FAKE, 1, FAKE, FAKE, M, N, K, Y, ldy, epi, res, ldr, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(epi=5), bd.W4A4_ERR_ARG),
+    (dict(epi=2), bd.W4A4_ERR_ARG),                 # residual epilogue without residual
+    (dict(epi=2, res=FAKE, ldr=10), bd.W4A4_ERR_SHAPE),
+    (dict(ldy=10), bd.W4A4_ERR_SHAPE),
+    (dict(K=255), bd.W4A4_ERR_SHAPE),
+    (dict(N=0), bd.W4A4_ERR_ARG),
+    (dict(Y=NULL), bd.W4A4_ERR_ARG),
+    (dict(Y=ctypes.c_void_p(0x10001)), bd.W4A4_ERR_ALIGN),
+    (dict(K=1 << 25), bd.W4A4_ERR_UNSUPPORTED),
+])
+def test_gemm_rejects(L, kw, code):
+    assert _gemm(L, **kw) == code
+
+
+def test_gemm_split_k_workspace_is_required(L):
+    need = L.w4a4_gemm_workspace_bytes(1024, 2048, 16384)
+    assert need > 0
+    assert _gemm(L, M=1024, N=2048, K=16384, ldy=2048) == bd.W4A4_ERR_WORKSPACE
+    assert _gemm(L, M=1024, N=2048, K=16384, ldy=2048, ws=FAKE, wsb=need - 1) == bd.W4A4_ERR_WORKSPACE
+
+
+def test_pack_and_calibration_reject(L):
+    ws = L.w4a4_pack_workspace_bytes(256, 256, 64)
+    assert ws >= 256 * 64 * 8
+    assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, FAKE,
+                               ws, NULL) == bd.W4A4_ERR_ALIGN
+    assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, ws,
+                               NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               ws - 8, NULL) == bd.W4A4_ERR_WORKSPACE
+    assert L.w4a4_block_svd(FAKE, 0, 64, 512, 512, 256, FAKE, FAKE, FAKE, 1 << 30,
+                            NULL) == bd.W4A4_ERR_UNSUPPORTED
+    assert L.w4a4_zigzag_perm(FAKE, 0, 0, 256, 256, 64, FAKE, FAKE, 1 << 20, NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_calibrate_act_scale(FAKE, 0, 16, 256, 256, 64, FAKE, FAKE, NULL, FAKE, 256,
+                                      NULL) == bd.W4A4_ERR_ARG
+
+
+def test_workspace_and_operand_sizes(L):
+    # the rotation operand holds an fp32 copy and a two-part fp16 split of every R_b
+    assert L.w4a4_rot_bytes(1024, 128) >= 1024 * 128 * (4 + 2 + 2)
+    assert L.w4a4_rot_bytes(1000, 128) == 0
+    assert L.w4a4_act_workspace_bytes(1024, 2048, 128, 0) == 0
+    assert L.w4a4_act_workspace_bytes(1024, 2048, 128, 1) >= 4 * 1024
+    assert L.w4a4_block_svd_workspace_bytes(4096, 1024, 128) >= 1024 * 128 * 8 * 3
+    assert L.w4a4_zigzag_workspace_bytes(16384) >= 16384 * 8

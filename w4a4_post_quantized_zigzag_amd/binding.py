@@ -1,0 +1,201 @@
+"""Thin ctypes binding of libw4a4.so (include/w4a4.h). Argument marshalling only: shapes and
+pointers are taken from torch tensors that live on the GPU, workspaces are torch allocations, and
+every call is enqueued on torch's current stream. All arithmetic runs in the library's HIP kernels;
+there is no fallback: if the library is missing, ``lib()`` raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libw4a4.so")
+
+W4A4_OK, W4A4_ERR_ARG, W4A4_ERR_SHAPE, W4A4_ERR_STEP_RANGE = 0, 1, 2, 3
+W4A4_ERR_UNSUPPORTED, W4A4_ERR_ALIGN, W4A4_ERR_WORKSPACE, W4A4_ERR_HIP = 4, 5, 6, 7
+W4A4_F16, W4A4_F32 = 0, 1
+EPI_NONE, EPI_GELU, EPI_RESIDUAL = 0, 1, 2
+
+_vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/w4a4.h
+SIGNATURES = {
+    "w4a4_zigzag_workspace_bytes": (_sz, [_i]),
+    "w4a4_zigzag_perm": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _sz, _vp]),
+    "w4a4_block_svd_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_block_svd": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _sz, _vp]),
+    "w4a4_calibrate_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_calibrate_act_scale": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "w4a4_rot_bytes": (_sz, [_i, _i]),
+    "w4a4_pack_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_pack_weights": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "w4a4_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "w4a4_rotate_quant_act": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp,
+                                   _vp, _sz, _vp]),
+    "w4a4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz, _vp]),
+    "w4a4_gemm_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "w4a4_last_error": (ctypes.c_char_p, []),
+    "w4a4_status_string": (ctypes.c_char_p, [_i]),
+    "w4a4_abi_version": (_i, []),
+}
+
+_lib = None
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load libw4a4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m w4a4_post_quantized_zigzag_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def check(rc: int):
+    if rc != W4A4_OK:
+        msg = lib().w4a4_last_error().decode()
+        raise W4A4Error(rc, msg)
+
+
+# ---------------------------------------------------------------------------------------------
+# torch-facing helpers (device tensors in, device tensors out)
+# ---------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return W4A4_F16
+    if t.dtype == torch.float32:
+        return W4A4_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ws(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _row_stride(t) -> int:
+    assert t.dim() == 2 and t.stride(1) == 1, "expected a row-major 2-D tensor"
+    return t.stride(0)
+
+
+def zigzag_perm(W, block: int):
+    torch = _torch()
+    N, K = W.shape
+    perm = torch.empty(K, dtype=torch.int32, device=W.device)
+    ws, nb = _ws(lib().w4a4_zigzag_workspace_bytes(K), W.device)
+    check(lib().w4a4_zigzag_perm(_p(W), _dtype_code(W), N, K, _row_stride(W), block, _p(perm),
+                                 _p(ws), nb, _stream()))
+    return perm
+
+
+def block_svd(W, perm, block: int):
+    torch = _torch()
+    N, K = W.shape
+    U = torch.empty((K // block, block, block), dtype=torch.float32, device=W.device)
+    ws, nb = _ws(lib().w4a4_block_svd_workspace_bytes(N, K, block), W.device)
+    check(lib().w4a4_block_svd(_p(W), _dtype_code(W), N, K, _row_stride(W), block, _p(perm), _p(U),
+                               _p(ws), nb, _stream()))
+    return U
+
+
+def pack_weights(W, perm, U, block: int):
+    """Returns (wq uint8 [N, K/2], w_scale fp32 [N], rot uint8 [rot_bytes])."""
+    torch = _torch()
+    N, K = W.shape
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    w_scale = torch.empty(N, dtype=torch.float32, device=W.device)
+    rot = torch.empty(lib().w4a4_rot_bytes(K, block), dtype=torch.uint8, device=W.device)
+    ws, nb = _ws(lib().w4a4_pack_workspace_bytes(N, K, block), W.device)
+    check(lib().w4a4_pack_weights(_p(W), _dtype_code(W), N, K, _row_stride(W), block, _p(perm),
+                                  _p(U), _p(wq), _p(w_scale), _p(rot), _p(ws), nb, _stream()))
+    return wq, w_scale, rot
+
+
+def calibrate_act_scale(X, perm, rot, block: int, out=None):
+    """fp32 scale for one (linear, step) entry from stacked calibration activations X [M, K]."""
+    torch = _torch()
+    M, K = X.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=X.device)
+    ws, nb = _ws(lib().w4a4_calibrate_workspace_bytes(M, K, block), X.device)
+    check(lib().w4a4_calibrate_act_scale(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
+                                         _p(perm), _p(rot), _p(out), _p(ws), nb, _stream()))
+    return out
+
+
+def rotate_quant_act(X, perm, rot, block: int, table=None, num_steps: int = 0, step: int = 0,
+                     xq=None, x_scale=None, xrot_dbg=None, ws=None):
+    torch = _torch()
+    M, K = X.shape
+    per_token = table is None
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(max(M, 1) if per_token else 1, dtype=torch.float32, device=X.device)
+    need = lib().w4a4_act_workspace_bytes(M, K, block, 1 if per_token else 0)
+    if ws is None:
+        ws, nb = _ws(need, X.device)
+    else:
+        nb = ws.numel()
+    check(lib().w4a4_rotate_quant_act(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
+                                      _p(perm), _p(rot), _p(table), num_steps, step, _p(xq),
+                                      _p(x_scale), _p(xrot_dbg), _p(ws), nb, _stream()))
+    return xq, x_scale
+
+
+def gemm(xq, x_scale, per_token: bool, wq, w_scale, K: int, Y=None, epilogue: int = EPI_NONE,
+         residual=None, ws=None):
+    torch = _torch()
+    M, N = xq.shape[0], wq.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=wq.device)
+    need = lib().w4a4_gemm_workspace_bytes(M, N, K)
+    if ws is None:
+        ws, nb = _ws(need, wq.device)
+    else:
+        nb = ws.numel()
+    ldr = _row_stride(residual) if residual is not None else 0
+    check(lib().w4a4_gemm(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale), M, N, K,
+                          _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, _p(ws), nb,
+                          _stream()))
+    return Y
+
+
+def gemm_i32(xq, wq, K: int):
+    torch = _torch()
+    M, N = xq.shape[0], wq.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=wq.device)
+    ws, nb = _ws(lib().w4a4_gemm_workspace_bytes(M, N, K), wq.device)
+    check(lib().w4a4_gemm_i32(_p(xq), _p(wq), M, N, K, _p(acc), _p(ws), nb, _stream()))
+    return acc

@@ -1,0 +1,326 @@
+// C ABI entry points of libw4a4.so: argument validation on the host, workspace carving, launches.
+// Every check runs before anything is enqueued, so a failing call launches nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "w4a4_internal.h"
+
+namespace w4a4 {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int check_launch(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(W4A4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return W4A4_OK;
+}
+
+static int ok()
+{
+    g_err[0] = '\0';
+    return W4A4_OK;
+}
+
+static bool pow2_block(int B) { return B >= 1 && B <= 256 && (B & (B - 1)) == 0; }
+
+static int check_dtype(int dt, const char *name)
+{
+    if (dt != W4A4_F16 && dt != W4A4_F32) return fail(W4A4_ERR_ARG, "%s dtype %d unknown", name, dt);
+    return W4A4_OK;
+}
+
+static size_t dtype_bytes(int dt) { return dt == W4A4_F16 ? 2 : 4; }
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape rules shared by every call that takes K and a block size.
+static int check_kb(int K, int B)
+{
+    if (!pow2_block(B))
+        return fail(W4A4_ERR_UNSUPPORTED, "block %d is not a power of two in [1, 256]", B);
+    if (K <= 0) return fail(W4A4_ERR_ARG, "K = %d must be positive", K);
+    if (K % 2) return fail(W4A4_ERR_SHAPE, "K = %d must be even (two int4 codes per byte)", K);
+    if (K % B) return fail(W4A4_ERR_SHAPE, "K = %d is not a multiple of the block %d", K, B);
+    if (K > (1 << 24)) return fail(W4A4_ERR_UNSUPPORTED, "K = %d above 2^24", K);
+    return W4A4_OK;
+}
+
+static int check_matrix(const void *A, int dt, int rows, int K, int64_t ld, const char *name)
+{
+    int rc = check_dtype(dt, name);
+    if (rc) return rc;
+    if (rows < 0) return fail(W4A4_ERR_ARG, "%s rows = %d negative", name, rows);
+    if (ld < K) return fail(W4A4_ERR_SHAPE, "%s leading dimension %lld < K = %d", name,
+                            (long long)ld, K);
+    if (rows > 0 && !A) return fail(W4A4_ERR_ARG, "%s is NULL", name);
+    if (!aligned(A, dtype_bytes(dt))) return fail(W4A4_ERR_ALIGN, "%s misaligned for its dtype", name);
+    if ((int64_t)rows * ld > ((int64_t)1 << 40))
+        return fail(W4A4_ERR_UNSUPPORTED, "%s larger than 2^40 elements", name);
+    return W4A4_OK;
+}
+
+static int check_ws(const void *ws, size_t have, size_t need)
+{
+    if (need == 0) return W4A4_OK;
+    if (!ws || have < need)
+        return fail(W4A4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, have,
+                    ws ? "" : " (NULL)");
+    if (!aligned(ws, 256)) return fail(W4A4_ERR_ALIGN, "workspace must be 256-byte aligned");
+    return W4A4_OK;
+}
+
+}  // namespace w4a4
+
+using namespace w4a4;
+
+extern "C" {
+
+int w4a4_abi_version(void) { return 1; }
+
+const char *w4a4_last_error(void) { return g_err; }
+
+const char *w4a4_status_string(int status)
+{
+    switch (status) {
+    case W4A4_OK: return "W4A4_OK";
+    case W4A4_ERR_ARG: return "W4A4_ERR_ARG";
+    case W4A4_ERR_SHAPE: return "W4A4_ERR_SHAPE";
+    case W4A4_ERR_STEP_RANGE: return "W4A4_ERR_STEP_RANGE";
+    case W4A4_ERR_UNSUPPORTED: return "W4A4_ERR_UNSUPPORTED";
+    case W4A4_ERR_ALIGN: return "W4A4_ERR_ALIGN";
+    case W4A4_ERR_WORKSPACE: return "W4A4_ERR_WORKSPACE";
+    case W4A4_ERR_HIP: return "W4A4_ERR_HIP";
+    default: return "W4A4_ERR_UNKNOWN";
+    }
+}
+
+// ------------------------------------------------------------------ calibration
+
+size_t w4a4_zigzag_workspace_bytes(int K) { return K > 0 ? zigzag_workspace(K) : 0; }
+
+int w4a4_zigzag_perm(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                     int32_t *perm, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if (N <= 0) return fail(W4A4_ERR_ARG, "N = %d must be positive", N);
+    if ((rc = check_matrix(W, w_dtype, N, K, ldw, "W"))) return rc;
+    if (!perm) return fail(W4A4_ERR_ARG, "perm is NULL");
+    if ((rc = check_ws(ws, ws_bytes, zigzag_workspace(K)))) return rc;
+    if ((rc = launch_zigzag(W, w_dtype, N, K, ldw, block, perm, ws, stream))) return rc;
+    return ok();
+}
+
+size_t w4a4_block_svd_workspace_bytes(int N, int K, int block)
+{
+    if (N <= 0 || K <= 0 || !pow2_block(block) || K % block) return 0;
+    return block_svd_workspace(N, K, block);
+}
+
+int w4a4_block_svd(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                   const int32_t *perm, float *U, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if (block > 128) return fail(W4A4_ERR_UNSUPPORTED, "device SVD supports block <= 128");
+    if (N <= 0) return fail(W4A4_ERR_ARG, "N = %d must be positive", N);
+    if ((rc = check_matrix(W, w_dtype, N, K, ldw, "W"))) return rc;
+    if (!U) return fail(W4A4_ERR_ARG, "U is NULL");
+    if ((rc = check_ws(ws, ws_bytes, block_svd_workspace(N, K, block)))) return rc;
+    if ((rc = launch_block_svd(W, w_dtype, N, K, ldw, block, perm, U, ws, stream))) return rc;
+    return ok();
+}
+
+size_t w4a4_calibrate_workspace_bytes(int M, int K, int block)
+{
+    (void)M; (void)K; (void)block;
+    return 256;
+}
+
+int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, float *table_entry,
+                             void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if ((rc = check_matrix(X, x_dtype, M, K, ldx, "X"))) return rc;
+    if (!rot) return fail(W4A4_ERR_ARG, "rot is NULL");
+    if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
+    if (!table_entry) return fail(W4A4_ERR_ARG, "table_entry is NULL");
+    if ((rc = check_ws(ws, ws_bytes, 256))) return rc;
+    uint32_t *amax = reinterpret_cast<uint32_t *>(ws);
+    if ((rc = launch_fill_u32(amax, 0u, 1, stream))) return rc;
+    if ((rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0,
+                                  ACT_CALIB_MAX, amax, nullptr, nullptr, nullptr, stream)))
+        return rc;
+    if ((rc = launch_scale_from_absmax(amax, table_entry, stream))) return rc;
+    return ok();
+}
+
+// ------------------------------------------------------------------ weight pack
+
+size_t w4a4_rot_bytes(int K, int block)
+{
+    if (K <= 0 || !pow2_block(block) || K % block) return 0;
+    return rot_layout(K, block).total;
+}
+
+size_t w4a4_pack_workspace_bytes(int N, int K, int block)
+{
+    if (N <= 0 || K <= 0 || !pow2_block(block) || K % block) return 0;
+    return align_up((size_t)K * block * sizeof(double), 256) + align_up((size_t)N * 8, 256);
+}
+
+int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                      const int32_t *perm, const float *U, uint8_t *wq, float *w_scale, void *rot,
+                      void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if (N <= 0) return fail(W4A4_ERR_ARG, "N = %d must be positive", N);
+    if ((rc = check_matrix(W, w_dtype, N, K, ldw, "W"))) return rc;
+    if (!U || !wq || !w_scale || !rot) return fail(W4A4_ERR_ARG, "U, wq, w_scale and rot are required");
+    if (!aligned(U, 4) || !aligned(w_scale, 4)) return fail(W4A4_ERR_ALIGN, "U / w_scale misaligned");
+    if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
+    if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_pack_workspace_bytes(N, K, block)))) return rc;
+    double *R64 = reinterpret_cast<double *>(ws);
+    unsigned long long *rowmax = reinterpret_cast<unsigned long long *>(
+        reinterpret_cast<char *>(ws) + align_up((size_t)K * block * sizeof(double), 256));
+    const double hinv = 1.0 / std::sqrt((double)block);
+    if ((rc = launch_rotation(U, K, block, hinv, R64, rot, stream))) return rc;
+    if ((rc = launch_weight_pack(W, w_dtype, N, K, ldw, block, perm, R64, rowmax, wq, w_scale,
+                                 stream)))
+        return rc;
+    return ok();
+}
+
+// ------------------------------------------------------------------ activation path
+
+size_t w4a4_act_workspace_bytes(int M, int K, int block, int per_token)
+{
+    (void)K; (void)block;
+    if (!per_token || M <= 0) return 0;
+    return align_up((size_t)M * sizeof(uint32_t), 256);
+}
+
+int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                          const int32_t *perm, const void *rot, const float *act_scale_table,
+                          int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
+                          void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if ((rc = check_matrix(X, x_dtype, M, K, ldx, "X"))) return rc;
+    if (!rot) return fail(W4A4_ERR_ARG, "rot is NULL");
+    if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
+    if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
+    const bool per_step = act_scale_table != nullptr;
+    if (per_step) {
+        if (num_steps <= 0) return fail(W4A4_ERR_STEP_RANGE, "num_steps = %d must be positive",
+                                        num_steps);
+        if (step < 0 || step >= num_steps)
+            return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
+        if (!aligned(act_scale_table, 4)) return fail(W4A4_ERR_ALIGN, "table misaligned");
+    }
+    if (M > 0 && (!xq || !x_scale)) return fail(W4A4_ERR_ARG, "xq and x_scale are required");
+    if (!aligned(x_scale, 4) || !aligned(xrot_dbg, 4))
+        return fail(W4A4_ERR_ALIGN, "x_scale / xrot_dbg misaligned");
+    const size_t need = w4a4_act_workspace_bytes(M, K, block, !per_step);
+    if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+    if (M == 0) return ok();
+    if (per_step) {
+        rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
+                                 ACT_PER_STEP, nullptr, xq, x_scale, xrot_dbg, stream);
+        if (rc) return rc;
+    } else {
+        uint32_t *rowmax = reinterpret_cast<uint32_t *>(ws);
+        if ((rc = launch_fill_u32(rowmax, 0u, M, stream))) return rc;
+        if ((rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0,
+                                      ACT_TOKEN_MAX, rowmax, nullptr, nullptr, nullptr, stream)))
+            return rc;
+        if ((rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0,
+                                      ACT_TOKEN_QUANT, rowmax, xq, x_scale, xrot_dbg, stream)))
+            return rc;
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------ GEMM
+
+size_t w4a4_gemm_workspace_bytes(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return gemm_workspace(M, N, K);
+}
+
+static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N, int K)
+{
+    if (M < 0 || N <= 0 || K <= 0) return fail(W4A4_ERR_ARG, "bad sizes M=%d N=%d K=%d", M, N, K);
+    if (K % 2) return fail(W4A4_ERR_SHAPE, "K = %d must be even", K);
+    if (K > (1 << 24)) return fail(W4A4_ERR_UNSUPPORTED, "K = %d above 2^24", K);
+    if ((M > 0 && !xq) || !wq) return fail(W4A4_ERR_ARG, "xq / wq is NULL");
+    return W4A4_OK;
+}
+
+int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, const uint8_t *wq,
+              const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
+              const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K))) return rc;
+    if (epilogue != W4A4_EPI_NONE && epilogue != W4A4_EPI_GELU && epilogue != W4A4_EPI_RESIDUAL)
+        return fail(W4A4_ERR_ARG, "unknown epilogue %d", epilogue);
+    if (!w_scale || (M > 0 && (!x_scale || !Y)))
+        return fail(W4A4_ERR_ARG, "x_scale, w_scale and Y are required");
+    if (ldy < N) return fail(W4A4_ERR_SHAPE, "ldy %lld < N = %d", (long long)ldy, N);
+    if (epilogue == W4A4_EPI_RESIDUAL) {
+        if (M > 0 && !residual) return fail(W4A4_ERR_ARG, "residual epilogue without residual");
+        if (ldr < N) return fail(W4A4_ERR_SHAPE, "ldr %lld < N = %d", (long long)ldr, N);
+        if (!aligned(residual, 2)) return fail(W4A4_ERR_ALIGN, "residual misaligned");
+    }
+    if (!aligned(Y, 2) || !aligned(x_scale, 4) || !aligned(w_scale, 4))
+        return fail(W4A4_ERR_ALIGN, "Y / scales misaligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_gemm_workspace_bytes(M, N, K)))) return rc;
+    if (M == 0) return ok();
+    GemmEpilogue epi{};
+    epi.x_scale = x_scale;
+    epi.x_scale_per_token = x_scale_per_token ? 1 : 0;
+    epi.w_scale = w_scale;
+    epi.Y = Y;
+    epi.ldy = ldy;
+    epi.mode = epilogue;
+    epi.residual = residual;
+    epi.ldr = ldr;
+    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream))) return rc;
+    return ok();
+}
+
+int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
+                  void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K))) return rc;
+    if (M > 0 && !acc) return fail(W4A4_ERR_ARG, "acc is NULL");
+    if (!aligned(acc, 4)) return fail(W4A4_ERR_ALIGN, "acc misaligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_gemm_workspace_bytes(M, N, K)))) return rc;
+    if (M == 0) return ok();
+    GemmEpilogue epi{};
+    epi.mode = GEMM_OUT_I32;
+    epi.acc_out = acc;
+    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream))) return rc;
+    return ok();
+}
+
+}  // extern "C"

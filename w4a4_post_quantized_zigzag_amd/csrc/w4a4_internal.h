@@ -1,0 +1,96 @@
+// Internal declarations shared by the translation units of libw4a4.so (not part of the ABI).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "w4a4.h"
+
+namespace w4a4 {
+
+// ---- host-side status handling ---------------------------------------------------------------
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int check_launch(const char *what);  // W4A4_OK, or W4A4_ERR_HIP with the HIP error text
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- device helpers --------------------------------------------------------------------------
+__device__ __forceinline__ float load_as_f32(const void *p, int dtype, int64_t idx)
+{
+    if (dtype == W4A4_F16) return __half2float(reinterpret_cast<const __half *>(p)[idx]);
+    return reinterpret_cast<const float *>(p)[idx];
+}
+
+// fp16 and fp32 values widen to fp64 exactly.
+__device__ __forceinline__ double load_as_f64(const void *p, int dtype, int64_t idx)
+{
+    return (double)load_as_f32(p, dtype, idx);
+}
+
+// Natural-order Sylvester Hadamard sign: (-1)^popcount(l & j).
+__device__ __forceinline__ bool hadamard_negative(int l, int j) { return __popc(l & j) & 1; }
+
+// Layout of the activation rotation operand written by the pack call (all offsets 256-aligned):
+//   [0, r32)          fp32 R_b[i][j] for every block, [nb][B][B] row-major
+//   [r32, r32 + r16)  fp16 high parts of R_b, transposed: hi[b][j][i]
+//   [.., .. + r16)    fp16 low parts scaled by 2^ROT_LO_SHIFT, transposed: lo[b][j][i]
+// with R_b ~= hi + lo * 2^-ROT_LO_SHIFT to about 22 significant bits.
+constexpr int ROT_LO_SHIFT = 12;
+struct RotLayout {
+    size_t r32, r16, total;
+};
+inline RotLayout rot_layout(int K, int B)
+{
+    RotLayout L;
+    L.r32 = align_up((size_t)K * B * sizeof(float), 256);
+    L.r16 = align_up((size_t)K * B * sizeof(uint16_t), 256);
+    L.total = L.r32 + 2 * L.r16;
+    return L;
+}
+
+// ---- launchers (one per kernel family) --------------------------------------------------------
+// offline weight side (k_pack.hip)
+int launch_rotation(const float *U, int K, int B, double hinv, double *R64, void *rot,
+                    hipStream_t s);
+int launch_weight_pack(const void *W, int wdt, int N, int K, int64_t ldw, int B,
+                       const int32_t *perm, const double *R64, unsigned long long *rowmax,
+                       uint8_t *wq, float *w_scale, hipStream_t s);
+
+// activation side (k_act.hip)
+enum ActMode { ACT_PER_STEP = 0, ACT_TOKEN_MAX = 1, ACT_TOKEN_QUANT = 2, ACT_CALIB_MAX = 3 };
+int launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t s);
+int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B,
+                        const int32_t *perm, const void *rot, const float *table, int step,
+                        ActMode mode, uint32_t *rowmax, uint8_t *xq, float *x_scale,
+                        float *xrot_dbg, hipStream_t s);
+int launch_scale_from_absmax(const uint32_t *amax, float *out, hipStream_t s);
+
+// GEMM (k_gemm.hip)
+struct GemmEpilogue {
+    const float *x_scale;
+    int x_scale_per_token;
+    const float *w_scale;
+    uint16_t *Y;
+    int64_t ldy;
+    int mode;  // W4A4_EPI_* or GEMM_OUT_I32
+    const uint16_t *residual;
+    int64_t ldr;
+    int32_t *acc_out;  // GEMM_OUT_I32 destination, dense [M][N]
+};
+constexpr int GEMM_OUT_I32 = 100;
+size_t gemm_workspace(int M, int N, int K);
+int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
+                void *ws, size_t ws_bytes, hipStream_t s);
+
+// calibration (k_calib.hip)
+size_t zigzag_workspace(int K);
+int launch_zigzag(const void *W, int wdt, int N, int K, int64_t ldw, int B, int32_t *perm,
+                  void *ws, hipStream_t s);
+size_t block_svd_workspace(int N, int K, int B);
+int launch_block_svd(const void *W, int wdt, int N, int K, int64_t ldw, int B, const int32_t *perm,
+                     float *U, void *ws, hipStream_t s);
+
+}  // namespace w4a4
