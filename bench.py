@@ -1,0 +1,400 @@
+"""Benchmark of the W4A4 quantized linear on one MI355X.
+
+Default workload: the DiT-action-head MLP up-projection (X fp16 [50, 1024] per denoising step,
+W fp16 [4096, 1024], block-128 rotation, per-step act_scale_table, 8 denoising steps run in order).
+One bench step = the whole runtime path for one batch: for each of the 8 denoising steps, the
+rotate-quantize call (zigzag gather, block rotation, step scale, int4 pack) and the W4A4 GEMM
+(int8 MFMA, fused dequantization, fp16 store). The offline side (device zigzag, block SVD, weight
+rotate + RTN pack, table calibration) runs once before timing and is reported separately.
+
+Timing: inputs and packed weights are resident in HBM; W warmup steps, then K steps replayed from a
+HIP graph of one step, bracketed by synchronizations, timed with HIP events on the launch stream.
+The dominant kernel's average duration is measured separately with HIP events around each of its
+launches on the same stream. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA (POP/s x 1000)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dev(a):
+    return _torch().from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gemm_bytes(M, N, K, per_token):
+    return M * K / 2 + N * K / 2 + 4 * N + 4 * (M if per_token else 1) + 2 * M * N
+
+
+def rq_bytes(M, K, B, xbytes, per_token):
+    return M * K * xbytes + M * K / 2 + 4 * (M if per_token else 1) + 4 * K + 4 * K * B
+
+
+class Linear:
+    """Device state of one W4A4 linear: calibration, packed weights and preallocated buffers."""
+
+    def __init__(self, W, block, bd):
+        torch = _torch()
+        self.bd = bd
+        self.N, self.K = W.shape
+        self.B = block
+        Wd = dev(W)
+        t0 = time.perf_counter()
+        self.perm = bd.zigzag_perm(Wd, block)
+        self.U = bd.block_svd(Wd, self.perm, block)
+        self.wq, self.w_scale, self.rot = bd.pack_weights(Wd, self.perm, self.U, block)
+        torch.cuda.synchronize()
+        self.offline_s = time.perf_counter() - t0
+        del Wd
+        self.table = None
+
+    def buffers(self, M, per_token):
+        torch = _torch()
+        self.xq = torch.empty((M, self.K // 2), dtype=torch.uint8, device="cuda")
+        self.xs = torch.empty(M if per_token else 1, dtype=torch.float32, device="cuda")
+        n = self.bd.lib().w4a4_act_workspace_bytes(M, self.K, self.B, 1 if per_token else 0)
+        self.act_ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        g = self.bd.lib().w4a4_gemm_workspace_bytes(M, self.N, self.K)
+        self.gemm_ws = torch.empty(max(g, 256), dtype=torch.uint8, device="cuda")
+
+    def rq(self, X, step=0, xrot=None):
+        self.bd.rotate_quant_act(X, self.perm, self.rot, self.B, self.table,
+                                 0 if self.table is None else self.table.numel(), step,
+                                 xq=self.xq, x_scale=self.xs, xrot_dbg=xrot, ws=self.act_ws)
+
+    def gemm(self, Y, epilogue=0, residual=None):
+        self.bd.gemm(self.xq, self.xs, self.table is None, self.wq, self.w_scale, self.K, Y=Y,
+                     epilogue=epilogue, residual=residual, ws=self.gemm_ws)
+
+
+def time_graph(fn, steps, warmup):
+    """Capture fn into a HIP graph, replay `warmup` untimed then `steps` timed. Returns ms/step."""
+    torch = _torch()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager run on the side stream before capture (allocator warm-up)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_kernel_calls(calls, reps):
+    """Average duration (ms) of each launch in `calls`, from HIP events recorded around it on the
+    current stream (the stream the library launches on)."""
+    torch = _torch()
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps * len(calls))]
+    i = 0
+    for _ in range(reps):
+        for c in calls:
+            ev[i][0].record()
+            c()
+            ev[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def source_hash(name):
+    with open(os.path.join(ROOT, "w4a4_post_quantized_zigzag_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, workload):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on the current source."""
+    p = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_sha256_16") != source_hash(kernel_file):
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------------------------
+
+def setup_per_step_linear(name, bd, inputs):
+    torch = _torch()
+    d = inputs.linear_inputs(name)
+    lin = Linear(d["W"], d["block"], bd)
+    T = d["steps"]
+    lin.table = torch.empty(T, dtype=torch.float32, device="cuda")
+    for t in range(T):
+        stacked = dev(np.concatenate(d["X_calib"][t], axis=0))
+        bd.calibrate_act_scale(stacked, lin.perm, lin.rot, lin.B, out=lin.table[t:t + 1])
+    M = d["M"]
+    lin.buffers(M, per_token=False)
+    Xs = [dev(x) for x in d["X_steps"]]
+    Ys = [torch.empty((M, lin.N), dtype=torch.float16, device="cuda") for _ in range(T)]
+
+    def step():
+        for t in range(T):
+            lin.rq(Xs[t], t)
+            lin.gemm(Ys[t])
+
+    torch.cuda.synchronize()
+    return d, lin, Xs, Ys, step
+
+
+def setup_per_token_linear(name, bd, inputs):
+    torch = _torch()
+    d = inputs.linear_inputs(name)
+    lin = Linear(d["W"], d["block"], bd)
+    M = d["M"]
+    lin.buffers(M, per_token=True)
+    X = dev(d["X"])
+    Y = torch.empty((M, lin.N), dtype=torch.float16, device="cuda")
+
+    def step():
+        lin.rq(X)
+        lin.gemm(Y)
+
+    torch.cuda.synchronize()
+    return d, lin, [X], [Y], step
+
+
+def setup_stack(bd, inputs, layers=None):
+    """Synthetic action-head stack: per layer QKV -> V slice (identity attention) -> O (+residual)
+    -> up (GELU) -> down (+residual). Per-linear per-step tables are calibrated on the device by
+    running the stack in per-token mode over each step's stacked calibration draws and taking the
+    scale of every linear's rotated input on the way."""
+    torch = _torch()
+    cfg = inputs.STACK
+    Wl = inputs.stack_weights(layers=layers)
+    act = inputs.stack_activations()
+    L, M, h, f, T, B = len(Wl), cfg["M"], cfg["hidden"], cfg["ffn"], cfg["steps"], cfg["block"]
+    t0 = time.perf_counter()
+    lins = [{k: Linear(lw[k], B, bd) for k in ("qkv", "o", "up", "down")} for lw in Wl]
+    offline = time.perf_counter() - t0
+    del Wl
+    for ll in lins:
+        for lin in ll.values():
+            lin.table = torch.empty(T, dtype=torch.float32, device="cuda")
+
+    def empty(shape, dt=torch.float16):
+        return torch.empty(shape, dtype=dt, device="cuda")
+
+    class Bufs:
+        def __init__(self, rows):
+            self.qkv, self.h2, self.g = empty((rows, 3 * h)), empty((rows, h)), empty((rows, f))
+            self.hs = [empty((rows, h)), empty((rows, h))]
+            self.xs = empty(rows, torch.float32)
+            self.xq = {K: empty((rows, K // 2), torch.uint8) for K in (h, f)}
+            self.ws = {K: empty(max(256, bd.lib().w4a4_act_workspace_bytes(rows, K, B, 1)),
+                                torch.uint8) for K in (h, f)}
+            self.gws = {(N, K): empty(max(256, bd.lib().w4a4_gemm_workspace_bytes(rows, N, K)),
+                                      torch.uint8)
+                        for N, K in ((3 * h, h), (h, h), (f, h), (h, f))}
+
+    def linear(lin, X, Y, step, calib, bufs, epi=0, res=None):
+        if calib:
+            bd.calibrate_act_scale(X, lin.perm, lin.rot, B, out=lin.table[step:step + 1])
+        bd.rotate_quant_act(X, lin.perm, lin.rot, B, None if calib else lin.table, T, step,
+                            xq=bufs.xq[lin.K], x_scale=bufs.xs, ws=bufs.ws[lin.K])
+        bd.gemm(bufs.xq[lin.K], bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
+                residual=res, ws=bufs.gws[(lin.N, lin.K)])
+
+    def run_stack(x, step, calib, bufs):
+        cur = x
+        for li, ll in enumerate(lins):
+            nxt = bufs.hs[li % 2]
+            linear(ll["qkv"], cur, bufs.qkv, step, calib, bufs)
+            linear(ll["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
+                   bd.EPI_RESIDUAL, cur)
+            linear(ll["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU)
+            linear(ll["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2)
+            cur = nxt
+        return cur
+
+    t1 = time.perf_counter()
+    cb = Bufs(sum(x.shape[0] for x in act["X_calib"][0]))
+    for t in range(T):
+        run_stack(dev(np.concatenate(act["X_calib"][t], axis=0)), t, True, cb)
+    torch.cuda.synchronize()
+    calib_s = time.perf_counter() - t1
+    del cb
+    torch.cuda.empty_cache()
+    rb = Bufs(M)
+    Xs = [dev(x) for x in act["X_steps"]]
+
+    def step():
+        for t in range(T):
+            run_stack(Xs[t], t, False, rb)
+
+    torch.cuda.synchronize()
+    info = dict(layers=L, M=M, hidden=h, ffn=f, steps=T, offline_s=offline, calib_s=calib_s)
+    return info, lins, Xs, rb, step
+
+
+# ----------------------------------------------------------------------------------------------
+
+def cpu_baseline_per_step(d, budget_s=12.0):
+    """The oracle (single-threaded C, fp64) on the same workload: its own calibration, then the
+    runtime path (rotate-quantize + integer GEMM + dequantization) for as many denoising steps as
+    fit in the budget (at least one). Returns ops/s and a description of the sample."""
+    import oracle
+    W, B = d["W"], d["block"]
+    perm = oracle.zigzag_perm(W, B)
+    U = oracle.block_svd(W, perm, B)
+    pw = oracle.pack_weights(W, perm, U, B)
+    table = oracle.calibrate_table(d["X_calib"], perm, U, B)
+    M, K, N = d["M"], d["K"], d["N"]
+    t0 = time.perf_counter()
+    done = 0
+    outs = []
+    for t, X in enumerate(d["X_steps"]):
+        act = oracle.rotate_quant_act(X, perm, U, B, "per_step", table, d["steps"], t, R=pw["R"])
+        g = oracle.gemm(act["codes"], act["scale"], False, pw["codes"], pw["w_scale"])
+        outs.append(g["Y"])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    ops = done * 2.0 * M * N * K
+    return ops / el, f"{done} of {d['steps']} denoising steps of the same workload (runtime path)", \
+        outs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dit_mlp_up",
+                    choices=["dit_mlp_up", "linear_small", "prefill_proj", "longk_down",
+                             "action_stack"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-supplementary", action="store_true")
+    ap.add_argument("--supp-steps", type=int, default=30)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the W4A4 linear "
+              "shards over tokens with no exchange, so N GPUs would run N copies of this line).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    torch = _torch()
+    from w4a4_post_quantized_zigzag_amd import binding as bd
+    from w4a4_post_quantized_zigzag_amd import inputs
+    bd.lib()
+    torch.cuda.set_device(0)
+
+    result = {"metric": "W4A4 linear TOPS and GB/s (% of int8-MFMA / HBM roofline), 1 MI355X",
+              "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4",
+              "data": "synthetic (seeded draws of the workload's shapes and distributions; "
+                      "random-init weights)"}
+
+    name = args.workload
+    if name in ("dit_mlp_up", "linear_small"):
+        d, lin, Xs, Ys, step = setup_per_step_linear(name, bd, inputs)
+        M, K, N, B, T = d["M"], d["K"], d["N"], d["block"], d["steps"]
+        ms = time_graph(step, args.steps, args.warmup)
+        ops = T * 2.0 * M * N * K
+        xb = 2 if d["xdtype"] == np.float16 else 4
+        bytes_step = T * (gemm_bytes(M, N, K, False) + rq_bytes(M, K, B, xb, False))
+        gemm_ms = time_kernel_calls([lambda t=t: lin.gemm(Ys[t]) for t in range(T)], 50)
+        lin.rq(Xs[0], 0)
+        rq_ms = time_kernel_calls([lambda t=t: lin.rq(Xs[t], t) for t in range(T)], 50)
+        gb = gemm_bytes(M, N, K, False)
+        result.update(value=ops / (ms * 1e-3) / 1e12, ms_per_step=ms,
+                      config={"workload": f"{name}: X fp16 [{M},{K}] x 8 denoising steps in order, "
+                                          f"W fp16 [{N},{K}], block {B}, per-step act_scale_table",
+                              "M": M, "K": K, "N": N, "block": B, "denoising_steps": T,
+                              "scale_mode": "per_step"},
+                      bandwidth_gbps=bytes_step / (ms * 1e-3) / 1e9)
+        result["roofline"] = {"bound": "hbm", "kernel": "k_gemm_w4a4 (BM=64, BN=64)",
+                              "achieved": gb / (gemm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": gb / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                              "traffic": traffic_from_profile("k_gemm.hip", name),
+                              "algorithmic_bytes_per_launch": gb,
+                              "avg_launch_us": gemm_ms * 1e3}
+        result["kernels"] = {"gemm_avg_us": gemm_ms * 1e3, "rotate_quant_avg_us": rq_ms * 1e3,
+                             "rotate_quant_gbps": rq_bytes(M, K, B, xb, False) / (rq_ms * 1e-3) / 1e9}
+        result["offline"] = {"calibrate_and_pack_s": lin.offline_s}
+        if not args.no_cpu_baseline:
+            v, sample, _ = cpu_baseline_per_step(d)
+            result["cpu_baseline"] = {"value": v / 1e12, "unit": "TOPS", "cores": 1,
+                                      "kind": "oracle", "sample": sample}
+    else:
+        raise SystemExit("use --workload dit_mlp_up or linear_small for the headline line; other "
+                         "workloads are reported under 'supplementary'")
+
+    if not args.no_supplementary:
+        result["supplementary"] = supplementary(bd, inputs, args.supp_steps)
+    print(json.dumps(result))
+
+
+def supplementary(bd, inputs, steps):
+    """Shorter runs of the other workloads (large-M per-token linears and the 16-layer stack)."""
+    torch = _torch()
+    out = {}
+    for name in ("prefill_proj", "longk_down"):
+        d, lin, Xs, Ys, step = setup_per_token_linear(name, bd, inputs)
+        M, K, N, B = d["M"], d["K"], d["N"], d["block"]
+        ms = time_graph(step, steps, 5)
+        gemm_ms = time_kernel_calls([lambda: lin.gemm(Ys[0])], 20)
+        rq_ms = time_kernel_calls([lambda: lin.rq(Xs[0])], 20)
+        ops = 2.0 * M * N * K
+        out[name] = {"M": M, "K": K, "N": N, "block": B, "scale_mode": "per_token",
+                     "linear_ms": ms, "linear_tops": ops / (ms * 1e-3) / 1e12,
+                     "gemm_us": gemm_ms * 1e3, "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
+                     "gemm_frac_int8_peak": ops / (gemm_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                     "rotate_quant_us": rq_ms * 1e3,
+                     "rotate_quant_gbps": rq_bytes(M, K, B, 2, True) / (rq_ms * 1e-3) / 1e9,
+                     "rotate_quant_frac_hbm": rq_bytes(M, K, B, 2, True) / (rq_ms * 1e-3) / 1e9
+                     / HBM_PEAK_GBPS,
+                     "calibrate_and_pack_s": lin.offline_s}
+        del lin, Xs, Ys
+        torch.cuda.empty_cache()
+    info, lins, Xs, rb, step = setup_stack(bd, inputs)
+    ms = time_graph(step, max(3, steps // 5), 2)
+    M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]
+    ops = T * L * 2.0 * M * (3 * h * h + h * h + f * h + h * f)
+    out["action_stack"] = {"layers": L, "M": M, "hidden": h, "ffn": f, "steps": T,
+                           "linear_calls": T * L * 4, "ms_per_pass": ms,
+                           "tops": ops / (ms * 1e-3) / 1e12,
+                           "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                           "offline_pack_s": info["offline_s"], "calibration_s": info["calib_s"]}
+    return out
+
+
+if __name__ == "__main__":
+    main()
