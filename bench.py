@@ -110,23 +110,35 @@ def time_graph(fn, steps, warmup):
 
 
 def time_kernel_calls(calls, reps):
-    """Average duration (ms) of each launch in `calls`, from HIP events recorded around it on the
-    current stream (the stream the library launches on)."""
+    """Average duration (ms) of one launch of `calls` (each call enqueues one kernel): a HIP graph
+    holding `reps` back-to-back rounds of the calls is replayed between two HIP events recorded on
+    the launch stream, and the elapsed time is divided by the number of launches. The graph keeps
+    host launch overhead out of the figure; the gap between consecutive graph nodes stays in."""
     torch = _torch()
-    for c in calls:
-        c()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps * len(calls))]
-    i = 0
-    for _ in range(reps):
+
+    def body():
+        for _ in range(reps):
+            for c in calls:
+                c()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
         for c in calls:
-            ev[i][0].record()
             c()
-            ev[i][1].record()
-            i += 1
+    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(calls))
 
 
 def source_hash(name):

@@ -80,6 +80,69 @@ static int check_ws(const void *ws, size_t have, size_t need)
     return W4A4_OK;
 }
 
+// ---- activation path plumbing shared by rotate_quant_act and calibrate_act_scale -------------
+enum ActKind { KIND_STEP = 0, KIND_TOKEN = 1, KIND_CALIB = 2 };
+
+static bool act_on_mfma(int xdt, int B) { return xdt == W4A4_F16 && (B == 64 || B == 128); }
+
+static size_t act_ws_bytes(int M, int K, int B, int kind)
+{
+    size_t n = (kind == KIND_STEP) ? 0 : align_up((size_t)(M > 0 ? M : 1) * sizeof(uint32_t), 256);
+    if (M > 0 && (B == 64 || B == 128) && act_uses_permute_pass(M, K, kind != KIND_STEP))
+        n += act_permute_bytes(M, K);
+    return n;
+}
+
+static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int B,
+                          const int32_t *perm, const void *rot, const float *table, int step,
+                          int kind, uint8_t *xq, float *x_scale, float *xrot, void *ws,
+                          float *calib_out, hipStream_t s)
+{
+    int rc;
+    char *w = reinterpret_cast<char *>(ws);
+    uint32_t *rowmax = reinterpret_cast<uint32_t *>(w);
+    const size_t off = (kind == KIND_STEP) ? 0 : align_up((size_t)M * sizeof(uint32_t), 256);
+    if (kind != KIND_STEP && (rc = launch_fill_u32(rowmax, 0u, kind == KIND_CALIB ? 1 : M, s)))
+        return rc;
+    if (act_on_mfma(xdt, B)) {
+        const uint16_t *xperm = nullptr;
+        if (perm && act_uses_permute_pass(M, K, kind != KIND_STEP)) {
+            uint16_t *xp = reinterpret_cast<uint16_t *>(w + off);
+            if ((rc = launch_permute_rows(X, M, K, ldx, perm, xp, s))) return rc;
+            xperm = xp;
+        }
+        if (kind == KIND_STEP)
+            return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
+                                            nullptr, xq, x_scale, xrot, xperm, s);
+        if (kind == KIND_CALIB) {
+            if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0,
+                                               ACT_CALIB_MAX, rowmax, nullptr, nullptr, nullptr,
+                                               xperm, s)))
+                return rc;
+            return launch_scale_from_absmax(rowmax, calib_out, s);
+        }
+        if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
+                                           rowmax, nullptr, nullptr, nullptr, xperm, s)))
+            return rc;
+        return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
+                                        rowmax, xq, x_scale, xrot, xperm, s);
+    }
+    if (kind == KIND_STEP)
+        return launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
+                                   nullptr, xq, x_scale, xrot, s);
+    if (kind == KIND_CALIB) {
+        if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_CALIB_MAX,
+                                      rowmax, nullptr, nullptr, nullptr, s)))
+            return rc;
+        return launch_scale_from_absmax(rowmax, calib_out, s);
+    }
+    if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
+                                  rowmax, nullptr, nullptr, nullptr, s)))
+        return rc;
+    return launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
+                               rowmax, xq, x_scale, xrot, s);
+}
+
 }  // namespace w4a4
 
 using namespace w4a4;
@@ -144,8 +207,8 @@ int w4a4_block_svd(const void *W, int w_dtype, int N, int K, int64_t ldw, int bl
 
 size_t w4a4_calibrate_workspace_bytes(int M, int K, int block)
 {
-    (void)M; (void)K; (void)block;
-    return 256;
+    if (M < 0 || K <= 0 || !pow2_block(block) || K % block) return 0;
+    return act_ws_bytes(M, K, block, KIND_CALIB);
 }
 
 int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
@@ -158,13 +221,11 @@ int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t l
     if (!rot) return fail(W4A4_ERR_ARG, "rot is NULL");
     if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
     if (!table_entry) return fail(W4A4_ERR_ARG, "table_entry is NULL");
-    if ((rc = check_ws(ws, ws_bytes, 256))) return rc;
-    uint32_t *amax = reinterpret_cast<uint32_t *>(ws);
-    if ((rc = launch_fill_u32(amax, 0u, 1, stream))) return rc;
-    if ((rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0,
-                                  ACT_CALIB_MAX, amax, nullptr, nullptr, nullptr, stream)))
+    if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
+    if ((rc = check_ws(ws, ws_bytes, act_ws_bytes(M, K, block, KIND_CALIB)))) return rc;
+    if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0, KIND_CALIB,
+                             nullptr, nullptr, nullptr, ws, table_entry, stream)))
         return rc;
-    if ((rc = launch_scale_from_absmax(amax, table_entry, stream))) return rc;
     return ok();
 }
 
@@ -210,9 +271,8 @@ int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int
 
 size_t w4a4_act_workspace_bytes(int M, int K, int block, int per_token)
 {
-    (void)K; (void)block;
-    if (!per_token || M <= 0) return 0;
-    return align_up((size_t)M * sizeof(uint32_t), 256);
+    if (M <= 0 || K <= 0 || !pow2_block(block) || K % block) return 0;
+    return act_ws_bytes(M, K, block, per_token ? KIND_TOKEN : KIND_STEP);
 }
 
 int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
@@ -240,20 +300,10 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
     const size_t need = w4a4_act_workspace_bytes(M, K, block, !per_step);
     if ((rc = check_ws(ws, ws_bytes, need))) return rc;
     if (M == 0) return ok();
-    if (per_step) {
-        rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
-                                 ACT_PER_STEP, nullptr, xq, x_scale, xrot_dbg, stream);
-        if (rc) return rc;
-    } else {
-        uint32_t *rowmax = reinterpret_cast<uint32_t *>(ws);
-        if ((rc = launch_fill_u32(rowmax, 0u, M, stream))) return rc;
-        if ((rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0,
-                                      ACT_TOKEN_MAX, rowmax, nullptr, nullptr, nullptr, stream)))
-            return rc;
-        if ((rc = launch_rotate_quant(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0,
-                                      ACT_TOKEN_QUANT, rowmax, xq, x_scale, xrot_dbg, stream)))
-            return rc;
-    }
+    if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
+                             per_step ? KIND_STEP : KIND_TOKEN, xq, x_scale, xrot_dbg, ws, nullptr,
+                             stream)))
+        return rc;
     return ok();
 }
 

@@ -3,22 +3,22 @@
 // scale), optional GELU / residual epilogue and the fp16 store fused into the tile's epilogue.
 //
 // CDNA4 has no int4 matrix instruction and its FP4 format (e2m1) does not hold the uniform int4
-// grid, so nibbles are widened to int8 while being staged into LDS and fed to
-// v_mfma_i32_16x16x64_i8. The widening keeps each nibble in the high half of its byte,
-// (v << 4) & 0xF0F0F0F0 for the even codes and v & 0xF0F0F0F0 for the odd ones, so every int8
-// operand equals 16 * code exactly and the MFMA sums 256 * q * p; an arithmetic shift right by 8
-// recovers the exact integer sum (|sum| <= 64 K, so 256 * 64 K stays below 2^31 for the at most
-// 2^16 k values of one split). Both operands go through the same even/odd reordering of k, so the dot products match.
+// grid, so nibbles are widened to int8 in registers right before v_mfma_i32_16x16x64_i8. The
+// widening keeps each nibble in the high half of its byte, (v << 4) & 0xF0F0F0F0 for the even
+// codes and v & 0xF0F0F0F0 for the odd ones, so every int8 operand equals 16 * code exactly and the
+// MFMA sums 256 * q * p; an arithmetic shift right by 8 recovers the exact integer sum
+// (|sum| <= 64 K, so 256 * 64 K stays below 2^31 for the at most 2^16 k values of one split). Both
+// operands go through the same even/odd reordering of k, so the dot products match.
+#include <cmath>
+
 #include "w4a4_internal.h"
 
 namespace w4a4 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int KS = 64;        // k elements per pipeline step
-constexpr int KSB = KS / 2;   // packed bytes per row per step
-constexpr int LDS_ROW = 80;   // bytes per staged int8 row (64 + 16 pad against bank conflicts)
 constexpr int MAX_K_SPLIT = 1 << 16;  // 256 * 64 * 2^16 = 2^30 fits int32
+constexpr int SMALL_M = 64;           // rows up to which the weight-streaming kernel is used
 
 __device__ __forceinline__ void widen16(const uint4 &p, uint4 &lo, uint4 &hi)
 {
@@ -48,6 +48,22 @@ __device__ __forceinline__ uint4 load_packed16(const uint8_t *__restrict__ base,
     return v;
 }
 
+// Branch-free 16-byte load for the aligned path: out-of-range items read row 0 / byte 0 of the same
+// operand (always in bounds) and report valid = false, so the caller zeroes them when it consumes
+// the data. Keeping the load unconditional lets it stay in flight across the MFMA work.
+__device__ __forceinline__ uint4 load16_clamped(const uint8_t *__restrict__ base, int rows, int row,
+                                                int64_t ld, int kb, int kbend, bool &valid)
+{
+    valid = (row < rows) && (kb < kbend);
+    const int64_t off = valid ? (int64_t)row * ld + kb : 0;
+    return *reinterpret_cast<const uint4 *>(base + off);
+}
+
+__device__ __forceinline__ uint4 zero_unless(const uint4 &v, bool valid)
+{
+    return make_uint4(valid ? v.x : 0u, valid ? v.y : 0u, valid ? v.z : 0u, valid ? v.w : 0u);
+}
+
 __device__ __forceinline__ float gelu_erf(float v)
 {
     return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
@@ -58,29 +74,168 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v)
     return __half_as_ushort(__float2half_rn(v));
 }
 
-// BM x BN output tile, 4 waves as WAVES_M x WAVES_N, each wave (BM/WAVES_M) x (BN/WAVES_N) made of
-// 16x16 MFMA fragments. grid = (N tiles, M tiles, k splits).
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
-__global__ __launch_bounds__(256) void k_gemm_w4a4(const uint8_t *__restrict__ xq,
-                                                   const uint8_t *__restrict__ wq, int M, int N,
-                                                   int K, int k_split, GemmEpilogue epi,
-                                                   int32_t *__restrict__ partial)
+// The dequantization is specified as a chain of fp32 roundings followed by one fp16 rounding.
+// The compiler may otherwise fuse "fp16(a * b)" or "fp16(a * b + c)" into one mixed-precision
+// instruction that rounds once, which differs at fp16 ties; pinning each fp32 intermediate in a
+// register keeps every rounding where it is written.
+__device__ __forceinline__ float fp32_value(float x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Dequantize one accumulator with scales already in registers and store it as fp16.
+__device__ __forceinline__ void store_scaled(const GemmEpilogue &epi, int m, int n, int32_t v,
+                                             float sx, float sw)
 {
 #pragma clang fp contract(off)
-    static_assert(WAVES_M * WAVES_N == 4, "4 waves");
+    float y = fp32_value((float)v * sx);
+    y = fp32_value(y * sw);
+    if (epi.mode == W4A4_EPI_GELU) y = fp32_value(gelu_erf(y));
+    else if (epi.mode == W4A4_EPI_RESIDUAL)
+        y = fp32_value(y + __half2float(__ushort_as_half(epi.residual[(int64_t)m * epi.ldr + n])));
+    epi.Y[(int64_t)m * epi.ldy + n] = f32_to_f16_bits(y);
+}
+
+// Dequantize one accumulator and store it (shared by every GEMM variant).
+__device__ __forceinline__ void store_output(const GemmEpilogue &epi, int m, int n, int N,
+                                             int32_t v)
+{
+#pragma clang fp contract(off)
+    if (epi.mode == GEMM_OUT_I32) {
+        epi.acc_out[(int64_t)m * N + n] = v;
+        return;
+    }
+    const float sx = epi.x_scale_per_token ? epi.x_scale[m] : epi.x_scale[0];
+    store_scaled(epi, m, n, v, sx, epi.w_scale[n]);
+}
+
+// Small-M GEMM (M <= 16 * MF <= 64): the weights are streamed once from HBM, so the kernel is built
+// for memory-level parallelism. A workgroup owns 16 output columns; its 4 waves split K, each wave
+// issuing the loads of a whole chunk of 128-k windows before computing. Each lane loads 16 packed
+// bytes of its operand row per window (lane = row (lane % 16) x k-quarter (lane / 16)) and widens
+// them into the two int8 operands of two v_mfma_i32_16x16x64_i8; both operands use the same
+// widening, so each MFMA pairs identical k. The 4 partial tiles are added exactly in LDS.
+constexpr int SM_CHUNK = 4;  // 128-k windows whose loads are in flight together
+
+template <int MF, bool VEC>
+__global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__ xq,
+                                                     const uint8_t *__restrict__ wq, int M, int N,
+                                                     int K, GemmEpilogue epi)
+{
+    __shared__ int32_t red[4][MF * 16][17];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int ldp = K / 2;
+    const int windows = (ldp + 63) / 64;
+    const int per_wave = (windows + 3) / 4;
+    const int w_begin = wave * per_wave, w_end = min(windows, w_begin + per_wave);
+
+    v4i total[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) total[f] = v4i{0, 0, 0, 0};
+
+    for (int wc = w_begin; wc < w_end; wc += SM_CHUNK) {
+        uint4 bq[SM_CHUNK], aq[SM_CHUNK][MF];
+        bool bv[SM_CHUNK], av[SM_CHUNK][MF];
+#pragma unroll
+        for (int c = 0; c < SM_CHUNK; ++c) {
+            const int kb = (wc + c) * 64 + 16 * g;
+            const int kend = (wc + c < w_end) ? ldp : 0;  // windows past this wave's range read nothing
+            if (VEC) {
+                bq[c] = load16_clamped(wq, N, n0 + r, ldp, kb, kend, bv[c]);
+            } else {
+                bq[c] = load_packed16<false>(wq, N, n0 + r, ldp, kb, kend);
+                bv[c] = true;
+            }
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+                if (VEC) {
+                    aq[c][f] = load16_clamped(xq, M, f * 16 + r, ldp, kb, kend, av[c][f]);
+                } else {
+                    aq[c][f] = load_packed16<false>(xq, M, f * 16 + r, ldp, kb, kend);
+                    av[c][f] = true;
+                }
+            }
+        }
+        v4i acc[MF];
+#pragma unroll
+        for (int f = 0; f < MF; ++f) acc[f] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < SM_CHUNK; ++c) {
+            uint4 b0, b1;
+            widen16(zero_unless(bq[c], bv[c]), b0, b1);
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+                uint4 a0, a1;
+                widen16(zero_unless(aq[c][f], av[c][f]), a0, a1);
+                acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<v4i *>(&a0),
+                                                               *reinterpret_cast<v4i *>(&b0),
+                                                               acc[f], 0, 0, 0);
+                acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<v4i *>(&a1),
+                                                               *reinterpret_cast<v4i *>(&b1),
+                                                               acc[f], 0, 0, 0);
+            }
+        }
+        // fold the chunk (at most 512 k, so 256 * 64 * 512 fits) into the exact running sum
+#pragma unroll
+        for (int f = 0; f < MF; ++f) total[f] += acc[f] >> 8;
+    }
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][f * 16 + 4 * g + i][r] = total[f][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < MF * 16 * 16; e += 256) {
+        const int row = e >> 4, col = e & 15;
+        const int m = row, n = n0 + col;
+        if (m >= M || n >= N) continue;
+        const int32_t v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
+        store_output(epi, m, n, N, v);
+    }
+}
+
+// Large-M GEMM. A BM x BN tile per workgroup of WAVES_M x WAVES_N waves, each wave a
+// (BM/WAVES_M) x (BN/WAVES_N) tile of 16x16 fragments. Operands stay packed in LDS (two stages of
+// 128 k: 64 bytes per row), so LDS traffic per MFMA is half that of staging int8; each wave widens
+// the fragments it reads (3 VALU ops per packed dword), which overlaps with the MFMA pipe.
+// Per stage and wave: FM*FN*2 v_mfma_i32_16x16x64_i8. Global loads of stage s+2 are issued right
+// after the barrier of stage s and stored to LDS after the compute of stage s+1. The 16-byte chunks
+// of a staged row are XOR-swizzled by row so fragment reads and staging writes spread over banks.
+// Tiles are assigned so that the workgroups of one XCD (dispatch id mod 8) share weight tiles.
+constexpr int BG_KS = 128;            // k per stage
+constexpr int BG_ROWB = BG_KS / 2;    // packed bytes per staged row
+
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ ((row >> 1) & 3)) * 16; }
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_big(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
+    int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
+{
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * LDS_ROW];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LDS_ROW];
+    constexpr int A_IT = BM * 4 / NT, B_IT = BN * 4 / NT;  // 16-byte staging items per thread
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * BG_ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BG_ROWB];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // XCD-aware tile order: dispatch id i runs on XCD i % 8; XCD x owns a contiguous range of the
+    // n-major tile order, so tiles sharing weight columns share that XCD's L2.
+    const int T = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int q = T / 8, rm = T % 8, x = id % 8;
+    const int lin = x * q + min(x, rm) + id / 8;
+    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-    const int64_t ldp = K / 2;
-    const int kb_begin = blockIdx.z * (k_split / 2);
-    const int kb_end = min(kb_begin + k_split / 2, (int)ldp);
-    const int steps = (kb_end - kb_begin + KSB - 1) / KSB;
+    const int ldp = K / 2;
+    const int kb_begin = blockIdx.y * (k_split / 2);
+    const int kb_end = min(kb_begin + k_split / 2, ldp);
+    const int stages = (kb_end - kb_begin + BG_ROWB - 1) / BG_ROWB;
 
     v4i acc[FM][FN];
 #pragma unroll
@@ -88,107 +243,359 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(const uint8_t *__restrict__ x
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    // staging assignment: each (row, half) pair is 16 packed bytes
-    constexpr int A_ITEMS = BM * 2, B_ITEMS = BN * 2;
-    constexpr int A_PER = (A_ITEMS + 255) / 256, B_PER = (B_ITEMS + 255) / 256;
-    uint4 ra[A_PER], rb[B_PER];
-
-    auto gload = [&](int step) {
-        const int kb = kb_begin + step * KSB;
+    uint4 ra[A_IT], rb[B_IT];
+    bool va[A_IT], vb[B_IT];
+    auto gload = [&](int st) {
+        const int kb = kb_begin + st * BG_ROWB;
 #pragma unroll
-        for (int t = 0; t < A_PER; ++t) {
-            int item = tid + t * 256;
-            ra[t] = make_uint4(0, 0, 0, 0);
-            if (item < A_ITEMS)
-                ra[t] = load_packed16<VEC>(xq, M, m0 + (item >> 1), ldp, kb + 16 * (item & 1),
-                                           kb_end);
+        for (int t = 0; t < A_IT; ++t) {
+            const int item = tid + t * NT;
+            if (VEC) {
+                ra[t] = load16_clamped(xq, M, m0 + (item >> 2), ldp, kb + 16 * (item & 3), kb_end, va[t]);
+            } else {
+                ra[t] = load_packed16<false>(xq, M, m0 + (item >> 2), ldp, kb + 16 * (item & 3), kb_end);
+                va[t] = true;
+            }
         }
 #pragma unroll
-        for (int t = 0; t < B_PER; ++t) {
-            int item = tid + t * 256;
-            rb[t] = make_uint4(0, 0, 0, 0);
-            if (item < B_ITEMS)
-                rb[t] = load_packed16<VEC>(wq, N, n0 + (item >> 1), ldp, kb + 16 * (item & 1),
-                                           kb_end);
+        for (int t = 0; t < B_IT; ++t) {
+            const int item = tid + t * NT;
+            if (VEC) {
+                rb[t] = load16_clamped(wq, N, n0 + (item >> 2), ldp, kb + 16 * (item & 3), kb_end, vb[t]);
+            } else {
+                rb[t] = load_packed16<false>(wq, N, n0 + (item >> 2), ldp, kb + 16 * (item & 3), kb_end);
+                vb[t] = true;
+            }
         }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int t = 0; t < A_PER; ++t) {
-            int item = tid + t * 256;
-            if (item < A_ITEMS) {
-                uint4 lo, hi;
-                widen16(ra[t], lo, hi);
-                uint8_t *dst = &sA[buf][(item >> 1) * LDS_ROW + 32 * (item & 1)];
-                *reinterpret_cast<uint4 *>(dst) = lo;
-                *reinterpret_cast<uint4 *>(dst + 16) = hi;
-            }
+        for (int t = 0; t < A_IT; ++t) {
+            const int item = tid + t * NT, row = item >> 2;
+            *reinterpret_cast<uint4 *>(&sA[buf][row * BG_ROWB + swz(row, item & 3)]) = zero_unless(ra[t], va[t]);
         }
 #pragma unroll
-        for (int t = 0; t < B_PER; ++t) {
-            int item = tid + t * 256;
-            if (item < B_ITEMS) {
-                uint4 lo, hi;
-                widen16(rb[t], lo, hi);
-                uint8_t *dst = &sB[buf][(item >> 1) * LDS_ROW + 32 * (item & 1)];
-                *reinterpret_cast<uint4 *>(dst) = lo;
-                *reinterpret_cast<uint4 *>(dst + 16) = hi;
-            }
+        for (int t = 0; t < B_IT; ++t) {
+            const int item = tid + t * NT, row = item >> 2;
+            *reinterpret_cast<uint4 *>(&sB[buf][row * BG_ROWB + swz(row, item & 3)]) = zero_unless(rb[t], vb[t]);
         }
     };
 
-    if (steps > 0) {
+    const int fr = lane & 15, fg = lane >> 4;
+    if (stages > 0) {
         gload(0);
         lstore(0);
     }
     __syncthreads();
-    const int frow = lane & 15, fk = (lane >> 4) * 16;
-    for (int st = 0; st < steps; ++st) {
+    if (stages > 1) gload(1);
+    for (int st = 0; st < stages; ++st) {
         const int buf = st & 1;
-        if (st + 1 < steps) gload(st + 1);
-        v4i a[FM], b[FN];
+        v4i b0[FN], b1[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            a[i] = *reinterpret_cast<const v4i *>(&sA[buf][(wm * WTM + i * 16 + frow) * LDS_ROW + fk]);
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * WTN + j * 16 + fr;
+            const uint4 p = *reinterpret_cast<const uint4 *>(&sB[buf][row * BG_ROWB + swz(row, fg)]);
+            uint4 lo, hi;
+            widen16(p, lo, hi);
+            b0[j] = *reinterpret_cast<v4i *>(&lo);
+            b1[j] = *reinterpret_cast<v4i *>(&hi);
+        }
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            b[j] = *reinterpret_cast<const v4i *>(&sB[buf][(wn * WTN + j * 16 + frow) * LDS_ROW + fk]);
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 16 + fr;
+            const uint4 p = *reinterpret_cast<const uint4 *>(&sA[buf][row * BG_ROWB + swz(row, fg)]);
+            uint4 lo, hi;
+            widen16(p, lo, hi);
+            const v4i a0 = *reinterpret_cast<v4i *>(&lo), a1 = *reinterpret_cast<v4i *>(&hi);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        if (st + 1 < steps) lstore(buf ^ 1);
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (st + 1 < stages) lstore(buf ^ 1);
         __syncthreads();
+        if (st + 2 < stages) gload(st + 2);
     }
 
-    // epilogue: fragment (i, j) register r holds row 4*(lane/16) + r, column lane % 16
+    if (partial || epi.mode == GEMM_OUT_I32) {
+        int32_t *dst = partial ? partial + (int64_t)blockIdx.y * M * N : epi.acc_out;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WTN + j * 16 + fr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm * WTM + i * 16 + 4 * fg + r;
+                    if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r] >> 8;
+                }
+            }
+        return;
+    }
+    // scales of this lane's columns and rows, loaded once
+    float wsc[FN], xsc[FM][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) wsc[j] = epi.w_scale[min(n0 + wn * WTN + j * 16 + fr, N - 1)];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            xsc[i][r] = epi.x_scale_per_token
+                            ? epi.x_scale[min(m0 + wm * WTM + i * 16 + 4 * fg + r, M - 1)]
+                            : epi.x_scale[0];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * WTN + j * 16 + (lane & 15);
-            if (n >= N) continue;
+            const int n = n0 + wn * WTN + j * 16 + fr;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + r;
-                if (m >= M) continue;
-                const int32_t v = acc[i][j][r] >> 8;
-                if (partial) {
-                    partial[((int64_t)blockIdx.z * M + m) * N + n] = v;
-                    continue;
+                const int m = m0 + wm * WTM + i * 16 + 4 * fg + r;
+                if (m < M && n < N) store_scaled(epi, m, n, acc[i][j][r] >> 8, xsc[i][r], wsc[j]);
+            }
+        }
+    }
+}
+
+// Pipelined variant of the large-M GEMM for K and the k split multiples of 128 with 16-byte
+// aligned operands. Operand tiles go from global memory straight into a ring of NSTAGE LDS stages
+// with global_load_lds_dwordx4 (no staging registers), so NSTAGE-1 stages of loads are in flight
+// while one stage is multiplied. The workgroup synchronizes with a plain s_barrier after waiting
+// only for the loads of the stage about to be read (s_waitcnt vmcnt), instead of the full drain a
+// fenced barrier implies. Each wave instruction fills 1 KB of LDS (lane L -> bytes 16L..16L+15);
+// a lane picks its global source so that the LDS image is the same XOR-swizzled layout the
+// fragment reads expect. Rows past M / N are clamped to the last row: they only feed outputs that
+// are never stored.
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// One wave-wide 16-byte-per-lane DMA from global memory into LDS at lds_addr + 16 * lane. Written
+// as inline assembly so the compiler does not treat later LDS reads as depending on it (it would
+// drain every outstanding load); the kernel orders it with explicit vmcnt waits and barriers. The
+// instruction writes no VGPR; M0 carries the LDS base (with the one wait state an M0 write needs
+// before an LDS DMA reads it).
+__device__ __forceinline__ void dma_to_lds16(const void *gptr, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t *p)
+{
+    return (uint32_t)(uintptr_t)(const lds_u8_t *)p;
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n)
+{
+    // s_waitcnt with lgkmcnt and expcnt at their no-wait values; n is a small compile-time count
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Epilogue kinds of the pipelined kernel (compile-time, so each variant is straight-line code).
+enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_RESIDUAL,
+       PE_INT32 = 3 };
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
+    int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
+{
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int A_BYTES = BM * BG_ROWB, B_BYTES = BN * BG_ROWB, STAGE = A_BYTES + B_BYTES;
+    constexpr int QA = A_BYTES / 1024 / NW, QB = B_BYTES / 1024 / NW;  // DMA instrs per wave
+    constexpr int L = QA + QB;
+    static_assert(QA * 1024 * NW == A_BYTES && QB * 1024 * NW == B_BYTES, "whole KB per wave");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int T = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int q8 = T / 8, rm = T % 8, x = id % 8;
+    const int lin = x * q8 + min(x, rm) + id / 8;
+    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int ldp = K / 2;
+    const int kb_begin = blockIdx.y * (k_split / 2);
+    const int kb_end = min(kb_begin + k_split / 2, ldp);
+    const int stages = (kb_end - kb_begin) / BG_ROWB;
+
+    // per-lane DMA sources: instruction q of this wave covers staged rows (wave*Q + q)*16 + lane/4,
+    // physical chunk lane%4, which holds logical chunk (lane%4) ^ swizzle(row)
+    const uint8_t *srcA[QA];
+    const uint8_t *srcB[QB];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int row = (wave * QA + q) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 1) & 3);
+        srcA[q] = xq + (int64_t)min(m0 + row, M - 1) * ldp + kb_begin + 16 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int row = (wave * QB + q) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 1) & 3);
+        srcB[q] = wq + (int64_t)min(n0 + row, N - 1) * ldp + kb_begin + 16 * c;
+    }
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = lds_address(smem);
+    auto issue = [&](int st) {
+        const uint32_t base = lds0 + (uint32_t)((st % NSTAGE) * STAGE);
+        const int koff = st * BG_ROWB;
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            dma_to_lds16(srcA[q] + koff, base + (uint32_t)((uwave * QA + q) * 1024));
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+            dma_to_lds16(srcB[q] + koff, base + (uint32_t)(A_BYTES + (uwave * QB + q) * 1024));
+    };
+
+    v4i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+        if (p < stages) issue(p);
+
+    const int fr = lane & 15, fg = lane >> 4;
+    for (int st = 0; st < stages; ++st) {
+        // stages st+1 .. st+NSTAGE-2 may still be in flight; stage st must have landed
+        const int ahead = min(stages - 1 - st, NSTAGE - 2);
+        asm volatile("" ::: "memory");
+        wait_vmcnt(ahead * L);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (st + NSTAGE - 1 < stages) issue(st + NSTAGE - 1);
+        const uint8_t *sA = smem + (st % NSTAGE) * STAGE;
+        const uint8_t *sB = sA + A_BYTES;
+        uint4 pb[FN], pa[FM];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * WTN + j * 16 + fr;
+            pb[j] = *reinterpret_cast<const uint4 *>(&sB[row * BG_ROWB + swz(row, fg)]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 16 + fr;
+            pa[i] = *reinterpret_cast<const uint4 *>(&sA[row * BG_ROWB + swz(row, fg)]);
+        }
+        v4i b0[FN], b1[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            uint4 lo, hi;
+            widen16(pb[j], lo, hi);
+            b0[j] = *reinterpret_cast<v4i *>(&lo);
+            b1[j] = *reinterpret_cast<v4i *>(&hi);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            uint4 lo, hi;
+            widen16(pa[i], lo, hi);
+            const v4i a0 = *reinterpret_cast<v4i *>(&lo), a1 = *reinterpret_cast<v4i *>(&hi);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        // Schedule: all fragment reads first, the B widening and the first A widening, then each
+        // MFMA followed by up to two VALU ops (the next A fragment's widening) so the VALU work
+        // overlaps the matrix pipe instead of running between blocks of MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 12 * FN + 12, 0);
+#pragma unroll
+        for (int t = 0; t < FM * FN * 2; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (t < (FM - 1) * FN * 2) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+    }
+
+    if (PE == PE_INT32) {
+        int32_t *dst = partial ? partial + (int64_t)blockIdx.y * M * N : epi.acc_out;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WTN + j * 16 + fr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm * WTM + i * 16 + 4 * fg + r;
+                    if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r] >> 8;
                 }
-                if (epi.mode == GEMM_OUT_I32) {
-                    epi.acc_out[(int64_t)m * N + n] = v;
-                    continue;
+            }
+        return;
+    } else {
+#pragma clang fp contract(off)
+        // dequantize in registers, stage the fp16 tile in the (now idle) LDS ring, then write whole
+        // 16-byte row chunks. Tile element (row, col) lives at row*BN + 8*((col/8) ^ sw(row)) +
+        // col%8 with sw(row) = (row/4) % 16, which spreads the four rows a fragment store touches
+        // over different banks.
+        static_assert(BM * BN * 2 <= NSTAGE * STAGE, "fp16 tile fits in the LDS ring");
+        static_assert(BN / 8 >= 16, "swizzle needs 16 chunks per row");
+        uint16_t *tile = reinterpret_cast<uint16_t *>(smem);
+        float wsc[FN], xsc[FM][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) wsc[j] = epi.w_scale[min(n0 + wn * WTN + j * 16 + fr, N - 1)];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                xsc[i][r] = epi.x_scale_per_token
+                                ? epi.x_scale[min(m0 + wm * WTM + i * 16 + 4 * fg + r, M - 1)]
+                                : epi.x_scale[0];
+        __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = wn * WTN + j * 16 + fr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = wm * WTM + i * 16 + 4 * fg + r;
+                    float y = fp32_value((float)(acc[i][j][r] >> 8) * xsc[i][r]);
+                    y = fp32_value(y * wsc[j]);
+                    if (PE == PE_GELU) y = fp32_value(gelu_erf(y));
+                    if (PE == PE_RESIDUAL) {
+                        const int m = min(m0 + row, M - 1), n = min(n0 + col, N - 1);
+                        y = fp32_value(y + __half2float(__ushort_as_half(epi.residual[(int64_t)m * epi.ldr + n])));
+                    }
+                    tile[row * BN + (((col >> 3) ^ ((row >> 2) & 15)) << 3) + (col & 7)] =
+                        f32_to_f16_bits(y);
                 }
-                const float sx = epi.x_scale_per_token ? epi.x_scale[m] : epi.x_scale[0];
-                float y = (float)v * sx;
-                y = y * epi.w_scale[n];
-                if (epi.mode == W4A4_EPI_GELU) y = gelu_erf(y);
-                else if (epi.mode == W4A4_EPI_RESIDUAL)
-                    y = y + __half2float(__ushort_as_half(epi.residual[(int64_t)m * epi.ldr + n]));
-                epi.Y[(int64_t)m * epi.ldy + n] = f32_to_f16_bits(y);
+            }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+        for (int e = tid; e < BM * CPR; e += 64 * NW) {
+            const int row = e / CPR, c = e % CPR;
+            const int m = m0 + row, n = n0 + 8 * c;
+            if (m >= M) continue;
+            const uint4 v = *reinterpret_cast<const uint4 *>(&tile[row * BN + ((c ^ ((row >> 2) & 15)) << 3)]);
+            uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
+            if (VEC_OUT && n + 8 <= N) {
+                *reinterpret_cast<uint4 *>(dst) = v;
+            } else {
+                const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y,
+                                       (uint16_t)(v.y >> 16), (uint16_t)v.z, (uint16_t)(v.z >> 16),
+                                       (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+                for (int t = 0; t < 8; ++t)
+                    if (n + t < N) dst[t] = h[t];
             }
         }
     }
@@ -204,47 +611,43 @@ __global__ void k_splitk_epilogue(const int32_t *__restrict__ partial, int split
     const int m = (int)(idx / N), n = (int)(idx % N);
     int32_t v = 0;
     for (int s = 0; s < splits; ++s) v += partial[(int64_t)s * M * N + idx];
-    if (epi.mode == GEMM_OUT_I32) {
-        epi.acc_out[idx] = v;
-        return;
-    }
-    const float sx = epi.x_scale_per_token ? epi.x_scale[m] : epi.x_scale[0];
-    float y = (float)v * sx;
-    y = y * epi.w_scale[n];
-    if (epi.mode == W4A4_EPI_GELU) y = gelu_erf(y);
-    else if (epi.mode == W4A4_EPI_RESIDUAL)
-        y = y + __half2float(__ushort_as_half(epi.residual[(int64_t)m * epi.ldr + n]));
-    epi.Y[(int64_t)m * epi.ldy + n] = f32_to_f16_bits(y);
+    store_output(epi, m, n, N, v);
 }
 
 struct GemmPlan {
+    int kind;  // 0 small-M, 1 = 256x256, 2 = 128x256, 3 = 128x128
     int bm, bn, splits, k_split;
 };
 
+// Pick the tile shape and k split with the smallest estimated time: full rounds of 256 compute
+// units times the per-tile MFMA time (discounted for smaller wave tiles, whose LDS traffic per MFMA
+// is higher), plus the write and read of split-K partials.
 static GemmPlan plan_gemm(int M, int N, int K)
 {
-    GemmPlan p;
-    if (M <= 64) {
-        p.bm = 64;
-        p.bn = 64;
-    } else {
-        p.bm = 128;
-        p.bn = 128;
+    GemmPlan best{0, 0, 16, 1, K};
+    if (M <= SMALL_M) return best;
+    struct Cand { int kind, bm, bn; double eff; };
+    const Cand cands[] = {{1, 256, 256, 1.0}, {2, 128, 256, 0.85}, {3, 128, 128, 0.6}};
+    double best_t = 1e30;
+    for (const Cand &c : cands) {
+        const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        for (int splits = 1; splits <= 16; splits *= 2) {
+            int k_split = ((K + splits - 1) / splits + BG_KS - 1) / BG_KS * BG_KS;
+            if (k_split > MAX_K_SPLIT) continue;
+            const int real_splits = (K + k_split - 1) / k_split;
+            if (real_splits != splits) continue;
+            if (splits > 1 && k_split < 1024) continue;
+            const double rounds = std::ceil(tiles * splits / 256.0);
+            const double t_c = rounds * 2.0 * c.bm * c.bn * k_split / (8192.0 * 2.4e9 * c.eff);
+            const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 4e12 + 3e-6 : 0.0;
+            const double t = t_c + t_r;
+            if (t < best_t * 0.98) {
+                best_t = t;
+                best = GemmPlan{c.kind, c.bm, c.bn, splits, k_split};
+            }
+        }
     }
-    const int64_t tiles = (int64_t)((N + p.bn - 1) / p.bn) * ((M + p.bm - 1) / p.bm);
-    int splits = 1;
-    // long K with too few tiles to fill 256 compute units: split K into exact int32 partials
-    while (tiles * splits < 256 && K / (splits * 2) >= 2048) splits *= 2;
-    int k_split = (K + splits - 1) / splits;
-    k_split = (k_split + KS - 1) / KS * KS;
-    while (k_split > MAX_K_SPLIT) {
-        splits *= 2;
-        k_split = ((K + splits - 1) / splits + KS - 1) / KS * KS;
-    }
-    splits = (K + k_split - 1) / k_split;
-    p.splits = splits;
-    p.k_split = k_split;
-    return p;
+    return best;
 }
 
 size_t gemm_workspace(int M, int N, int K)
@@ -255,15 +658,68 @@ size_t gemm_workspace(int M, int N, int K)
 }
 
 template <int BM, int BN, int WM, int WN>
-static void launch_tile(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq,
-                        int M, int N, int K, int k_split, const GemmEpilogue &epi, int32_t *partial)
+static void launch_big(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq,
+                       int M, int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                       int32_t *partial)
 {
+    const dim3 block(64 * WM * WN);
     if (vec)
-        hipLaunchKernelGGL((k_gemm_w4a4<BM, BN, WM, WN, true>), grid, dim3(256), 0, s, xq, wq, M, N,
-                           K, k_split, epi, partial);
+        hipLaunchKernelGGL((k_gemm_big<BM, BN, WM, WN, true>), grid, block, 0, s, xq, wq, M, N, K,
+                           k_split, tm, tn, epi, partial);
     else
-        hipLaunchKernelGGL((k_gemm_w4a4<BM, BN, WM, WN, false>), grid, dim3(256), 0, s, xq, wq, M,
-                           N, K, k_split, epi, partial);
+        hipLaunchKernelGGL((k_gemm_big<BM, BN, WM, WN, false>), grid, block, 0, s, xq, wq, M, N,
+                           K, k_split, tm, tn, epi, partial);
+}
+
+constexpr int PIPE_STAGES = 4;
+
+template <int BM, int BN, int WM, int WN, int PE, bool VO>
+static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
+                         int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                         int32_t *partial)
+{
+    const size_t lds = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
+    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO>;
+    static bool attr_set = false;  // once per process and instantiation
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return fail(W4A4_ERR_HIP, "gemm LDS request: %s", hipGetErrorString(e));
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO>), grid, dim3(64 * WM * WN),
+                       lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+    return W4A4_OK;
+}
+
+template <int BM, int BN, int WM, int WN>
+static int launch_pipe_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
+                         int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                         int32_t *partial)
+{
+    if (partial || epi.mode == GEMM_OUT_I32)
+        return launch_pipe_e<BM, BN, WM, WN, PE_INT32, false>(grid, s, xq, wq, M, N, K, k_split, tm,
+                                                             tn, epi, partial);
+    const bool vo = (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0);
+#define W4A4_PIPE_E(PEV)                                                                           \
+    return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true>(grid, s, xq, wq, M, N, K, k_split, tm, tn, \
+                                                         epi, partial)                             \
+              : launch_pipe_e<BM, BN, WM, WN, PEV, false>(grid, s, xq, wq, M, N, K, k_split, tm,   \
+                                                          tn, epi, partial);
+    if (epi.mode == W4A4_EPI_GELU) { W4A4_PIPE_E(PE_GELU) }
+    if (epi.mode == W4A4_EPI_RESIDUAL) { W4A4_PIPE_E(PE_RESIDUAL) }
+    W4A4_PIPE_E(PE_NONE)
+#undef W4A4_PIPE_E
+}
+
+static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq,
+                       int M, int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                       int32_t *partial)
+{
+    if (kind == 1)
+        return launch_pipe_t<256, 256, 2, 4>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+    if (kind == 2)
+        return launch_pipe_t<128, 256, 1, 4>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+    return launch_pipe_t<128, 128, 2, 2>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
 }
 
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
@@ -272,6 +728,20 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     if (M == 0) return W4A4_OK;
     GemmPlan p = plan_gemm(M, N, K);
     const bool vec = ((K / 2) % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
+    if (p.kind == 0) {
+        dim3 g((N + 15) / 16);
+        const int mf = (M + 15) / 16;
+#define W4A4_SMALLM(MFV)                                                                           \
+    if (vec) hipLaunchKernelGGL((k_gemm_smallm<MFV, true>), g, dim3(256), 0, s, xq, wq, M, N, K,   \
+                                epi);                                                              \
+    else hipLaunchKernelGGL((k_gemm_smallm<MFV, false>), g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+        if (mf == 1) { W4A4_SMALLM(1) }
+        else if (mf == 2) { W4A4_SMALLM(2) }
+        else if (mf == 3) { W4A4_SMALLM(3) }
+        else { W4A4_SMALLM(4) }
+#undef W4A4_SMALLM
+        return check_launch("gemm small-M");
+    }
     int32_t *partial = nullptr;
     if (p.splits > 1) {
         if (!ws || ws_bytes < gemm_workspace(M, N, K))
@@ -279,11 +749,17 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
                         gemm_workspace(M, N, K));
         partial = reinterpret_cast<int32_t *>(ws);
     }
-    dim3 grid((N + p.bn - 1) / p.bn, (M + p.bm - 1) / p.bm, p.splits);
-    if (p.bm == 64)
-        launch_tile<64, 64, 1, 4>(vec, grid, s, xq, wq, M, N, K, p.k_split, epi, partial);
+    const int tm = (M + p.bm - 1) / p.bm, tn = (N + p.bn - 1) / p.bn;
+    dim3 grid(tm * tn, p.splits);
+    if (vec && K % BG_KS == 0) {
+        int rc = launch_pipe(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
+        if (rc != W4A4_OK) return rc;
+    } else if (p.kind == 1)
+        launch_big<256, 256, 2, 4>(vec, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
+    else if (p.kind == 2)
+        launch_big<128, 256, 1, 4>(vec, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
     else
-        launch_tile<128, 128, 2, 2>(vec, grid, s, xq, wq, M, N, K, p.k_split, epi, partial);
+        launch_big<128, 128, 2, 2>(vec, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
     int rc = check_launch("gemm");
     if (rc != W4A4_OK || p.splits <= 1) return rc;
     const int64_t total = (int64_t)M * N;
