@@ -203,76 +203,35 @@ def setup_per_token_linear(name, bd, inputs):
 
 
 def setup_stack(bd, inputs, layers=None):
-    """Synthetic action-head stack: per layer QKV -> V slice (identity attention) -> O (+residual)
-    -> up (GELU) -> down (+residual). Per-linear per-step tables are calibrated on the device by
-    running the stack in per-token mode over each step's stacked calibration draws and taking the
-    scale of every linear's rotated input on the way."""
+    """Synthetic action-head stack (16 layers of QKV -> V slice -> O + residual -> up + GELU -> down
+    + residual, M = 1600 tokens, 8 denoising steps): device calibration (zigzag, block SVD, pack,
+    per-linear per-step tables from the stacked calibration draws), then one pass = 8 steps x 16
+    layers x 4 W4A4 linears."""
+    from w4a4_post_quantized_zigzag_amd.stack import DeviceStack
     torch = _torch()
     cfg = inputs.STACK
     Wl = inputs.stack_weights(layers=layers)
     act = inputs.stack_activations()
-    L, M, h, f, T, B = len(Wl), cfg["M"], cfg["hidden"], cfg["ffn"], cfg["steps"], cfg["block"]
+    T, B, M = cfg["steps"], cfg["block"], cfg["M"]
     t0 = time.perf_counter()
-    lins = [{k: Linear(lw[k], B, bd) for k in ("qkv", "o", "up", "down")} for lw in Wl]
+    ds = DeviceStack(Wl, B, T)
+    torch.cuda.synchronize()
     offline = time.perf_counter() - t0
     del Wl
-    for ll in lins:
-        for lin in ll.values():
-            lin.table = torch.empty(T, dtype=torch.float32, device="cuda")
-
-    def empty(shape, dt=torch.float16):
-        return torch.empty(shape, dtype=dt, device="cuda")
-
-    class Bufs:
-        def __init__(self, rows):
-            self.qkv, self.h2, self.g = empty((rows, 3 * h)), empty((rows, h)), empty((rows, f))
-            self.hs = [empty((rows, h)), empty((rows, h))]
-            self.xs = empty(rows, torch.float32)
-            self.xq = {K: empty((rows, K // 2), torch.uint8) for K in (h, f)}
-            self.ws = {K: empty(max(256, bd.lib().w4a4_act_workspace_bytes(rows, K, B, 1)),
-                                torch.uint8) for K in (h, f)}
-            self.gws = {(N, K): empty(max(256, bd.lib().w4a4_gemm_workspace_bytes(rows, N, K)),
-                                      torch.uint8)
-                        for N, K in ((3 * h, h), (h, h), (f, h), (h, f))}
-
-    def linear(lin, X, Y, step, calib, bufs, epi=0, res=None):
-        if calib:
-            bd.calibrate_act_scale(X, lin.perm, lin.rot, B, out=lin.table[step:step + 1])
-        bd.rotate_quant_act(X, lin.perm, lin.rot, B, None if calib else lin.table, T, step,
-                            xq=bufs.xq[lin.K], x_scale=bufs.xs, ws=bufs.ws[lin.K])
-        bd.gemm(bufs.xq[lin.K], bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
-                residual=res, ws=bufs.gws[(lin.N, lin.K)])
-
-    def run_stack(x, step, calib, bufs):
-        cur = x
-        for li, ll in enumerate(lins):
-            nxt = bufs.hs[li % 2]
-            linear(ll["qkv"], cur, bufs.qkv, step, calib, bufs)
-            linear(ll["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
-                   bd.EPI_RESIDUAL, cur)
-            linear(ll["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU)
-            linear(ll["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2)
-            cur = nxt
-        return cur
-
     t1 = time.perf_counter()
-    cb = Bufs(sum(x.shape[0] for x in act["X_calib"][0]))
-    for t in range(T):
-        run_stack(dev(np.concatenate(act["X_calib"][t], axis=0)), t, True, cb)
-    torch.cuda.synchronize()
+    ds.calibrate(act["X_calib"])
     calib_s = time.perf_counter() - t1
-    del cb
-    torch.cuda.empty_cache()
-    rb = Bufs(M)
     Xs = [dev(x) for x in act["X_steps"]]
+    ds.bufs(M)
 
     def step():
         for t in range(T):
-            run_stack(Xs[t], t, False, rb)
+            ds.run(Xs[t], t)
 
     torch.cuda.synchronize()
-    info = dict(layers=L, M=M, hidden=h, ffn=f, steps=T, offline_s=offline, calib_s=calib_s)
-    return info, lins, Xs, rb, step
+    info = dict(layers=len(ds.layers), M=M, hidden=ds.h, ffn=ds.f, steps=T, offline_s=offline,
+                calib_s=calib_s)
+    return info, ds, Xs, None, step
 
 
 # ----------------------------------------------------------------------------------------------

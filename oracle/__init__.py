@@ -28,4 +28,8 @@ from .reference import (  # noqa: F401
     gemm,
     calibrate_table,
     linear,
+    stack_prepare,
+    stack_run,
+    stack_calibrate,
+    STACK_LINEARS,
 )

@@ -374,3 +374,74 @@ def linear(X, W, B: int, mode: str, table=None, num_steps=None, step=None, perm=
     g = gemm(act["codes"], act["scale"], mode == "per_token", pw["codes"], pw["w_scale"],
              epilogue, residual)
     return {"perm": perm, "U": U, "pack": pw, "act": act, **g}
+
+
+# ----------------------------------------------------------------------------------------------
+# Synthetic action-head stack (benchmark workload): per layer QKV -> V slice (attention replaced by
+# identity) -> O + residual -> up -> erf-GELU -> down + residual, every linear W4A4. Composed only
+# of the functions above; tokens never mix, so any subset of rows can be run on its own.
+# ----------------------------------------------------------------------------------------------
+
+STACK_LINEARS = ("qkv", "o", "up", "down")
+
+
+def stack_prepare(weights, B: int, calib=None):
+    """Offline side for every linear: zigzag perm, SVD factor (or the given ones) and the pack."""
+    layers = []
+    for li, lw in enumerate(weights):
+        layer = {}
+        for name in STACK_LINEARS:
+            W = lw[name]
+            if calib is None:
+                perm = zigzag_perm(W, B)
+                U = block_svd(W, perm, B)
+            else:
+                perm, U = calib[li][name]
+            layer[name] = {"perm": perm, "U": U, "pack": pack_weights(W, perm, U, B)}
+        layers.append(layer)
+    return layers
+
+
+def _stack_linear(lin, X, B, mode, table, steps, step, epilogue=EPI_NONE, residual=None):
+    act = rotate_quant_act(X, lin["perm"], lin["U"], B, mode, table, steps, step,
+                           R=lin["pack"]["R"])
+    g = gemm(act["codes"], act["scale"], mode == "per_token", lin["pack"]["codes"],
+             lin["pack"]["w_scale"], epilogue, residual)
+    return g["Y"], act
+
+
+def stack_run(layers, X, B: int, mode: str, tables=None, steps=None, step=0, outputs=None,
+              record_tables=None):
+    """One pass of the stack on fp16 X [rows, h]. mode "per_step" uses tables[layer][name][step];
+    mode "per_token" quantizes per token, and with record_tables (a list of per-layer dicts) stores
+    each linear's calibration entry fp32(max |fp32(x')| / 7) (1.0 for a zero max) for `step`.
+    Returns the fp16 output; appends each linear's fp16 output to `outputs` if given."""
+    h = X.shape[1]
+    cur = np.asarray(X, np.float16)
+    for li, layer in enumerate(layers):
+        def lin(name, inp, epi=EPI_NONE, res=None):
+            tab = None if mode == "per_token" else tables[li][name]
+            Y, act = _stack_linear(layer[name], inp, B, mode, tab, steps, step, epi, res)
+            if record_tables is not None:
+                amax = float(np.max(np.abs(act["x32"]))) if act["x32"].size else 0.0
+                record_tables[li][name][step] = np.float32(amax / 7.0) if amax > 0 else 1.0
+            if outputs is not None:
+                outputs.append(Y)
+            return Y
+
+        qkv = lin("qkv", cur)
+        h2 = lin("o", np.ascontiguousarray(qkv[:, 2 * h:3 * h]), EPI_RESIDUAL, cur)
+        g = lin("up", h2, EPI_GELU)
+        cur = lin("down", g, EPI_RESIDUAL, h2)
+    return cur
+
+
+def stack_calibrate(layers, X_calib_per_step, B: int):
+    """Per-linear per-step act_scale_tables: for each step, the stacked calibration draws go through
+    the stack in per-token mode and every linear records the scale of its rotated input."""
+    T = len(X_calib_per_step)
+    tables = [{name: np.ones(T, np.float32) for name in STACK_LINEARS} for _ in layers]
+    for t, draws in enumerate(X_calib_per_step):
+        X = np.concatenate(draws, axis=0)
+        stack_run(layers, X, B, "per_token", steps=T, step=t, record_tables=tables)
+    return tables

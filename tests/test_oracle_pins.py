@@ -414,6 +414,34 @@ def test_rotation_reduces_w4a4_error(name, M, K, N):
     assert e_rot < e_plain
 
 
+def test_stack_wiring_zero_weights_is_identity():
+    # QKV = 0 -> V = 0 -> O(V) = 0 -> h2 = x; up = 0 -> GELU(0) = 0 -> down = 0 -> out = h2 = x
+    h, f, B = 128, 256, 64
+    W = [{"qkv": np.zeros((3 * h, h), np.float16), "o": np.zeros((h, h), np.float16),
+          "up": np.zeros((f, h), np.float16), "down": np.zeros((h, f), np.float16)}
+         for _ in range(2)]
+    layers = oracle.stack_prepare(W, B)
+    X = (_rng(4).standard_normal((9, h)) * 3).astype(np.float16)
+    outs = []
+    Y = oracle.stack_run(layers, X, B, "per_token", outputs=outs)
+    assert np.array_equal(Y, X)
+    assert len(outs) == 8 and not outs[0].any() and np.array_equal(outs[1], X)
+    # calibration of the zero branches records scale 1.0 (all-zero rotated inputs)
+    tables = oracle.stack_calibrate(layers, [[X]], B)
+    assert tables[0]["o"][0] == 1.0 and tables[0]["down"][0] == 1.0 and tables[0]["qkv"][0] > 0
+
+
+def test_stack_rows_are_independent():
+    # tokens never mix: running a subset of rows gives the same rows of the full run
+    h, f, B = 128, 256, 128
+    W = inputs.stack_weights(layers=1, hidden=h, ffn=f, seed=3)
+    layers = oracle.stack_prepare(W, B)
+    X = (_rng(5).standard_normal((12, h))).astype(np.float16)
+    full = oracle.stack_run(layers, X, B, "per_token")
+    part = oracle.stack_run(layers, X[[2, 7, 11]], B, "per_token")
+    assert np.array_equal(full[[2, 7, 11]], part)
+
+
 def test_recipe_constants_from_the_pages():
     with open(os.path.join(GOLDEN, "recipe.json")) as f:
         rc = json.load(f)

@@ -142,13 +142,16 @@ def pack_weights(W, perm, U, block: int):
     return wq, w_scale, rot
 
 
-def calibrate_act_scale(X, perm, rot, block: int, out=None):
+def calibrate_act_scale(X, perm, rot, block: int, out=None, ws=None):
     """fp32 scale for one (linear, step) entry from stacked calibration activations X [M, K]."""
     torch = _torch()
     M, K = X.shape
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=X.device)
-    ws, nb = _ws(lib().w4a4_calibrate_workspace_bytes(M, K, block), X.device)
+    if ws is None:
+        ws, nb = _ws(lib().w4a4_calibrate_workspace_bytes(M, K, block), X.device)
+    else:
+        nb = ws.numel()
     check(lib().w4a4_calibrate_act_scale(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
                                          _p(perm), _p(rot), _p(out), _p(ws), nb, _stream()))
     return out

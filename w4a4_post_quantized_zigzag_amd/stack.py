@@ -1,0 +1,120 @@
+"""Synthetic action-head stack driven through the C ABI: per layer QKV -> V slice (attention
+replaced by identity) -> O with residual -> up with erf-GELU -> down with residual, every linear a
+W4A4 linear with its own zigzag permutation, block SVD factor, packed weights and per-step
+act_scale_table. This module only sequences library calls and owns buffers; all arithmetic runs in
+libw4a4.so.
+
+Per-step tables follow the pages' per-step scaling (vnrobo "Y tuong paper": the runtime looks up the
+current denoising step's scale; gist.science item 2: tables from calibration trajectories): for each
+step, the stack is run in per-token mode over that step's stacked calibration draws, and each
+linear's table entry is the scale of its rotated input on the way.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as bd
+
+LINEARS = ("qkv", "o", "up", "down")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class DeviceLinear:
+    def __init__(self, W, block: int, steps: int, perm=None, U=None):
+        torch = _torch()
+        Wd = W if isinstance(W, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(W)).cuda()
+        self.N, self.K = Wd.shape
+        self.B = block
+        self.perm = bd.zigzag_perm(Wd, block) if perm is None else perm
+        self.U = bd.block_svd(Wd, self.perm, block) if U is None else U
+        self.wq, self.w_scale, self.rot = bd.pack_weights(Wd, self.perm, self.U, block)
+        self.table = torch.empty(steps, dtype=torch.float32, device="cuda")
+        self.steps = steps
+
+
+class _Buffers:
+    def __init__(self, rows: int, h: int, f: int, block: int):
+        torch = _torch()
+        e = lambda shape, dt=torch.float16: torch.empty(shape, dtype=dt, device="cuda")  # noqa: E731
+        self.qkv, self.h2, self.g = e((rows, 3 * h)), e((rows, h)), e((rows, f))
+        self.hs = [e((rows, h)), e((rows, h))]
+        self.xs = e(max(rows, 1), torch.float32)
+        self.xq = {K: e((rows, K // 2), torch.uint8) for K in (h, f)}
+        self.ws = {K: e(max(256, bd.lib().w4a4_act_workspace_bytes(rows, K, block, 1)), torch.uint8)
+                   for K in (h, f)}
+        self.cws = {K: e(max(256, bd.lib().w4a4_calibrate_workspace_bytes(rows, K, block)),
+                         torch.uint8) for K in (h, f)}
+        self.gws = {(N, K): e(max(256, bd.lib().w4a4_gemm_workspace_bytes(rows, N, K)), torch.uint8)
+                    for N, K in ((3 * h, h), (h, h), (f, h), (h, f))}
+
+
+class DeviceStack:
+    """weights: list (one per layer) of dicts qkv [3h,h], o [h,h], up [f,h], down [h,f] (fp16).
+    calib: optional list of per-layer dicts name -> (perm, U) device tensors to use instead of the
+    device calibration kernels."""
+
+    def __init__(self, weights, block: int, steps: int, calib=None):
+        self.block, self.steps = block, steps
+        self.h = weights[0]["o"].shape[0]
+        self.f = weights[0]["up"].shape[0]
+        self.layers = []
+        for li, lw in enumerate(weights):
+            layer = {}
+            for name in LINEARS:
+                pu = calib[li][name] if calib is not None else (None, None)
+                layer[name] = DeviceLinear(lw[name], block, steps, *pu)
+            self.layers.append(layer)
+        self._bufs = {}
+
+    def bufs(self, rows: int) -> _Buffers:
+        if rows not in self._bufs:
+            self._bufs[rows] = _Buffers(rows, self.h, self.f, self.block)
+        return self._bufs[rows]
+
+    def set_tables(self, tables):
+        """tables: list per layer of dict name -> fp32 array [steps]."""
+        torch = _torch()
+        for layer, tl in zip(self.layers, tables):
+            for name in LINEARS:
+                layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
+
+    def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None):
+        if calib:
+            bd.calibrate_act_scale(X, lin.perm, lin.rot, self.block, out=lin.table[step:step + 1],
+                                   ws=bufs.cws[lin.K])
+        bd.rotate_quant_act(X, lin.perm, lin.rot, self.block, None if calib else lin.table,
+                            self.steps, step, xq=bufs.xq[lin.K], x_scale=bufs.xs, ws=bufs.ws[lin.K])
+        bd.gemm(bufs.xq[lin.K], bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
+                residual=res, ws=bufs.gws[(lin.N, lin.K)])
+
+    def run(self, X, step: int, calib: bool = False, outputs=None):
+        """One pass of the stack for denoising step `step` on X fp16 [rows, h] (device). In calib
+        mode the linears quantize per token and record their table entry for `step`. If `outputs`
+        is a list, each linear's output tensor is appended (test hook)."""
+        bufs = self.bufs(X.shape[0])
+        h = self.h
+        cur = X
+        for li, layer in enumerate(self.layers):
+            nxt = bufs.hs[li % 2]
+            self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs)
+            self._linear(layer["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
+                         bd.EPI_RESIDUAL, cur)
+            self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU)
+            self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2)
+            if outputs is not None:
+                outputs.extend([bufs.qkv.clone(), bufs.h2.clone(), bufs.g.clone(), nxt.clone()])
+            cur = nxt
+        return cur
+
+    def calibrate(self, X_calib_per_step):
+        """X_calib_per_step[t]: list of fp16 numpy arrays [rows, h] (calibration draws of step t)."""
+        torch = _torch()
+        for t, draws in enumerate(X_calib_per_step):
+            X = torch.from_numpy(np.ascontiguousarray(np.concatenate(draws, axis=0))).cuda()
+            self.run(X, t, calib=True)
+        torch.cuda.synchronize()
+        self._bufs = {k: v for k, v in self._bufs.items() if k < 4096}
