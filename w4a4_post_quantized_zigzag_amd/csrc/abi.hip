@@ -102,13 +102,18 @@ static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int
     char *w = reinterpret_cast<char *>(ws);
     uint32_t *rowmax = reinterpret_cast<uint32_t *>(w);
     const size_t off = (kind == KIND_STEP) ? 0 : align_up((size_t)M * sizeof(uint32_t), 256);
-    if (kind != KIND_STEP && (rc = launch_fill_u32(rowmax, 0u, kind == KIND_CALIB ? 1 : M, s)))
+    const bool permute_pass = act_on_mfma(xdt, B) && perm && act_uses_permute_pass(M, K, kind != KIND_STEP);
+    // the row maxima start at zero: cleared by the permutation pass when there is one
+    if (kind != KIND_STEP && !permute_pass &&
+        (rc = launch_fill_u32(rowmax, 0u, kind == KIND_CALIB ? 1 : M, s)))
         return rc;
     if (act_on_mfma(xdt, B)) {
         const uint16_t *xperm = nullptr;
-        if (perm && act_uses_permute_pass(M, K, kind != KIND_STEP)) {
+        if (permute_pass) {
             uint16_t *xp = reinterpret_cast<uint16_t *>(w + off);
-            if ((rc = launch_permute_rows(X, M, K, ldx, perm, xp, s))) return rc;
+            if ((rc = launch_permute_rows(X, M, K, ldx, perm, xp,
+                                          kind == KIND_STEP ? nullptr : rowmax, s)))
+                return rc;
             xperm = xp;
         }
         if (kind == KIND_STEP)

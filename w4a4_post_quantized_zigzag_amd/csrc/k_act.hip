@@ -357,15 +357,260 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     }
 }
 
+// ------------------------------------------------------------------ contiguous rows, LDS DMA ring
+//
+// Same arithmetic as k_rq_mfma for rows already in zigzag order (a permuted copy, or the caller's
+// own layout), with the activation tiles streamed by global_load_lds_dwordx4 into a ring of
+// RQ_STAGES LDS tiles so several tiles of loads are in flight while one is multiplied. The ring is
+// synchronized with explicit vmcnt waits and plain s_barrier (a fenced barrier would drain every
+// in-flight tile). Staged rows are XOR-swizzled by 16-byte chunk (chunk ^ (row % chunks_per_row)),
+// which makes the 16 rows a fragment read touches hit 16 different bank groups.
+constexpr int RQ_STAGES = 4;
+constexpr int RQ_RING_MAX_ROWS = 1024;  // rows per workgroup (per-token scales staged in LDS)
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+__device__ __forceinline__ void rq_dma16(const void *gptr, uint32_t lds_addr)
+{
+    // one wave-wide 16-byte-per-lane DMA into LDS at lds_addr + 16 * lane (no VGPR written);
+    // M0 holds the LDS base and needs one wait state before the LDS DMA reads it
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void rq_wait_vmcnt(int n)
+{
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Four rotated values held as acc = 2^12 x' -> four int4 codes packed low nibble first in the low
+// 16 bits (the bits above are garbage). rs = 2^-12 * fp32(1/s), so acc * rs is the fp32 product
+// x' * fp32(1/s) rounded once (both power-of-two scalings are exact for any x' and 1/s that can
+// give a nonzero code). Adding 1.5 * 2^23 rounds that product to an integer, ties to even, and
+// leaves the integer in the low mantissa bits; the clamp to [-8, 7] is applied in that form and
+// the two's-complement nibble is read off the bit pattern.
+__device__ __forceinline__ uint32_t quant_pack4(v4f acc, float rs)
+{
+#pragma clang fp contract(off)
+    constexpr float MAGIC = 12582912.0f;
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float y = acc[i] * rs;
+        float f = y + MAGIC;
+        f = fminf(fmaxf(f, MAGIC - 8.0f), MAGIC + 7.0f);
+        n[i] = __float_as_uint(f);
+    }
+    uint32_t t = (n[0] & 0xFu) | ((n[1] << 4) & ~0xFu);
+    t = (t & 0xFFu) | ((n[2] << 8) & ~0xFFu);
+    return (t & 0xFFFu) | ((n[3] << 12) & ~0xFFFu);
+}
+
+template <int MODE, int B, bool DBG>
+__global__ __launch_bounds__(256) void k_rq_ring(
+    const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const _Float16 *__restrict__ rhi,
+    const _Float16 *__restrict__ rlo, const float *__restrict__ table, int step,
+    uint32_t *__restrict__ rowmax, uint8_t *__restrict__ xq, float *__restrict__ x_scale,
+    float *__restrict__ xrot_dbg, int rows_per_wg, int row_groups)
+{
+#pragma clang fp contract(off)
+    constexpr int KK = B / 32, JW = B / 4, JF = JW / 16, MF = MT / 16;
+    constexpr float LO = 1.0f / (1 << ROT_LO_SHIFT);
+    constexpr int NXCD = 8;
+    constexpr int ROWB = B * 2;                   // bytes per staged row
+    constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+    constexpr int TILE = MT * ROWB;               // bytes per tile
+    constexpr int QPW = TILE / 1024 / 4;          // DMA instructions per wave per tile
+    constexpr int RPI = 1024 / ROWB;              // rows per DMA instruction
+    constexpr int OB = B / 2;                     // packed output bytes per row of one block
+    constexpr int OCH = MT * OB / 16;             // 16-byte output chunks per tile
+    extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+    __shared__ float smax[4][MT];
+    __shared__ __attribute__((aligned(16))) uint8_t sq[MT * OB];
+    __shared__ float srcp[MODE == ACT_TOKEN_QUANT ? RQ_RING_MAX_ROWS : 1];
+
+    // Workgroup -> (block b, row group). Workgroups are dealt round-robin to the 8 XCDs, each with
+    // its own L2; when the block count allows, all row groups of a block go to one XCD, one after
+    // another, so that block's R_b fragments come into that L2 once and are hit by the rest.
+    const int nb = K / B, wg = blockIdx.x;
+    int b, rgi;
+    if (nb % NXCD == 0) {
+        const int x = wg % NXCD, i = wg / NXCD;
+        b = NXCD * (i / row_groups) + x;
+        rgi = i % row_groups;
+    } else {
+        b = wg / row_groups;
+        rgi = wg % row_groups;
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int jbase = wave * JW;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int row_begin = rgi * rows_per_wg;
+    const int row_end = min(M, row_begin + rows_per_wg);
+    const int ntiles = (row_end - row_begin + MT - 1) / MT;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(const lds_u8_t *)ring;
+
+    // DMA sources of this lane: instruction q covers tile rows (wave*QPW + q)*RPI + lane/CPR,
+    // physical chunk lane % CPR holding logical chunk (lane % CPR) ^ (row % CPR)
+    auto issue = [&](int t) {
+        const uint32_t base = ring0 + (uint32_t)((t % RQ_STAGES) * TILE);
+        const int m0 = row_begin + t * MT;
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) {
+            const int row = (uwave * QPW + q) * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ (row % CPR);
+            const int m = min(m0 + row, row_end - 1);
+            rq_dma16(X + (int64_t)m * ldx + b * B + 8 * c, base + (uint32_t)((uwave * QPW + q) * 1024));
+        }
+    };
+
+    // the first tiles' loads go out before the set-up loads below, so the two latencies overlap
+#pragma unroll
+    for (int p = 0; p < RQ_STAGES - 1; ++p)
+        if (p < ntiles) issue(p);
+
+    // per-token reciprocal scales (times 2^-12) of this workgroup's rows, staged in LDS: a global
+    // load inside the tile loop would make the compiler wait for every DMA issued before it
+    if (MODE == ACT_TOKEN_QUANT) {
+        for (int i = tid; i < row_end - row_begin; i += 256) {
+            const float s = scale_from_absmax(__uint_as_float(rowmax[row_begin + i]));
+            srcp[i] = (float)(1.0 / (double)s) * LO;
+            if (b == 0) x_scale[row_begin + i] = s;
+        }
+    }
+    // R_b^T fragments of this wave's output channels; the high part is scaled by 2^12 (exact, as
+    // |R| <= 1) so that x.hi and x.lo accumulate in one fp32 accumulator at the same scale
+    v8h ahi[JF][KK], alo[JF][KK];
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int64_t off = ((int64_t)b * B + jbase + 16 * jf + r) * B + 32 * kk + 8 * g;
+            ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off) * (_Float16)(1 << ROT_LO_SHIFT);
+            alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
+        }
+    float rs_step = 0.0f;
+    if (MODE == ACT_PER_STEP) {
+        const float s = step_scale(table, step);
+        rs_step = (float)(1.0 / (double)s) * LO;
+        if (blockIdx.x == 0 && b == 0 && tid == 0) x_scale[0] = s;
+    }
+    if (MODE == ACT_TOKEN_QUANT) __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int ahead = min(ntiles - 1 - t, RQ_STAGES - 2);
+        asm volatile("" ::: "memory");
+        rq_wait_vmcnt(ahead * QPW);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + RQ_STAGES - 1 < ntiles) issue(t + RQ_STAGES - 1);
+        const uint8_t *tile = ring + (t % RQ_STAGES) * TILE;
+        const int m0 = row_begin + t * MT;
+
+        // acc[mf][jf] = 2^12 x' for tokens mf*16 + (lane % 16), channels jbase + 16 jf + 4 (lane / 16)
+        // + 0..3; consecutive MFMAs go to different accumulators
+        v4f acc[MF][JF];
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+            for (int jf = 0; jf < JF; ++jf) acc[mf][jf] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            v8h xb[MF];
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+                const int row = mf * 16 + r;
+                const int c = (4 * kk + g) ^ (row % CPR);
+                xb[mf] = *reinterpret_cast<const v8h *>(&tile[row * ROWB + 16 * c]);
+            }
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int jf = 0; jf < JF; ++jf)
+                    acc[mf][jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jf][kk], xb[mf], acc[mf][jf], 0, 0, 0);
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int jf = 0; jf < JF; ++jf)
+                    acc[mf][jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jf][kk], xb[mf], acc[mf][jf], 0, 0, 0);
+        }
+
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+            const int row = mf * 16 + r;
+            const int m = m0 + row;
+            if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
+                float a = 0.0f;
+#pragma unroll
+                for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(acc[mf][jf][i]));
+                a = fmaxf(a, __shfl_xor(a, 16));
+                a = fmaxf(a, __shfl_xor(a, 32));
+                if (g == 0) smax[wave][row] = (m < row_end) ? a * LO : 0.0f;
+                continue;
+            }
+            const int jl = jbase + 4 * g;  // first of this lane's 4 channels within the block
+            if (DBG && m < row_end) {
+#pragma unroll
+                for (int jf = 0; jf < JF; ++jf)
+                    *reinterpret_cast<float4 *>(&xrot_dbg[(int64_t)m * K + b * B + jl + 16 * jf]) =
+                        make_float4(acc[mf][jf][0] * LO, acc[mf][jf][1] * LO, acc[mf][jf][2] * LO,
+                                    acc[mf][jf][3] * LO);
+            }
+            const float rs = (MODE == ACT_TOKEN_QUANT) ? srcp[min(m, row_end - 1) - row_begin] : rs_step;
+#pragma unroll
+            for (int jf = 0; jf < JF; ++jf)
+                *reinterpret_cast<uint16_t *>(&sq[row * OB + (jl + 16 * jf) / 2]) =
+                    (uint16_t)quant_pack4(acc[mf][jf], rs);
+        }
+        // Tile epilogue after every wave's LDS writes (lgkmcnt(0) + plain barrier; the next write
+        // to smax / sq comes after the next tile's barrier, by which time these reads are consumed)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
+            if (tid < MT) {
+                const float a = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+                if (MODE == ACT_TOKEN_MAX) {
+                    if (m0 + tid < row_end) atomicMax(&rowmax[m0 + tid], __float_as_uint(a));
+                } else {
+                    float u = a;
+                    for (int off = 32; off > 0; off >>= 1) u = fmaxf(u, __shfl_xor(u, off));
+                    if (tid == 0) atomicMax(&rowmax[0], __float_as_uint(u));
+                }
+            }
+        } else if (tid < OCH) {
+            // packed codes of the tile: one 16-byte store per thread (OB / 16 chunks per row)
+            const int row = tid / (OB / 16), ch = tid % (OB / 16);
+            if (m0 + row < row_end)
+                *reinterpret_cast<uint4 *>(&xq[(int64_t)(m0 + row) * (K / 2) + b * OB + 16 * ch]) =
+                    *reinterpret_cast<const uint4 *>(&sq[row * OB + 16 * ch]);
+        }
+    }
+}
+
 // Zigzag gather of whole rows: Xp[m][j] = X[m][perm[j]] (fp16), one workgroup per row, the source
-// row staged in LDS with 16-byte loads and the permuted row written with 16-byte stores.
+// row staged in LDS with 16-byte loads and the permuted row written with 16-byte stores. The
+// workgroup of row m also clears zero_row[m] (the per-token maxima the next pass accumulates), when
+// given, which saves a separate fill launch.
 template <bool VEC>
 __global__ __launch_bounds__(256) void k_permute_rows(const uint16_t *__restrict__ X, int64_t ldx,
                                                       int K, const int32_t *__restrict__ perm,
-                                                      uint16_t *__restrict__ Xp)
+                                                      uint16_t *__restrict__ Xp,
+                                                      uint32_t *__restrict__ zero_row)
 {
     extern __shared__ uint16_t srow[];
     const int m = blockIdx.x, tid = threadIdx.x;
+    if (zero_row && tid == 0) zero_row[m] = 0u;
     const uint16_t *xr = X + (int64_t)m * ldx;
     uint16_t *out = Xp + (int64_t)m * K;
     if (VEC) {
@@ -393,12 +638,14 @@ __global__ __launch_bounds__(256) void k_permute_rows(const uint16_t *__restrict
 
 bool act_uses_permute_pass(int M, int K, int per_token)
 {
-    (void)M;
-    // long rows make the in-kernel 2-byte gather touch a new cache line per element; a separate
-    // coalesced permutation pass (its output stays in the 256 MB last-level cache) is then cheaper,
-    // and per-token mode reads the permuted rows twice. The pass stages a whole row in LDS.
+    // The in-kernel gather issues one 2-byte load per element, each from a different cache line of
+    // a long row; a coalesced permutation pass (its output stays in the 256 MB last-level cache)
+    // followed by 16-byte DMA tile loads wins once the batch is a few MB, and earlier in per-token
+    // mode, which reads the rows twice (and where the pass also clears the row maxima). The pass
+    // stages a whole row in LDS.
     if (K > 65536) return false;
-    return K > 4096 || (per_token && K > 2048);
+    const int64_t elems = (int64_t)M * K;
+    return per_token ? (K >= 2048 || elems >= (1 << 20)) : (elems >= (1 << 22));
 }
 
 size_t act_permute_bytes(int M, int K) { return align_up((size_t)M * K * sizeof(uint16_t), 256); }
@@ -430,6 +677,41 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
     const bool rows_aligned = ((uintptr_t)src % 16 == 0) && (ld % 8 == 0);
     const bool gather = ((perm != nullptr) && (xperm == nullptr)) || !rows_aligned;
     if (xperm) perm = nullptr;
+    if (!gather && ((uintptr_t)xq % 16 == 0)) {
+        // rows in zigzag order: LDS DMA ring (rows per workgroup capped by the staged scales)
+        const int rpw_r = min(rpw, RQ_RING_MAX_ROWS);
+        const int groups = (M + rpw_r - 1) / rpw_r;
+        dim3 grid_r(groups * nb);
+        const size_t lds = (size_t)RQ_STAGES * MT * B * sizeof(uint16_t);
+#define W4A4_RING(MODEV, BV, DV)                                                                   \
+    do {                                                                                           \
+        static bool attr_set = false;                                                              \
+        if (!attr_set) {                                                                           \
+            hipError_t e = hipFuncSetAttribute((const void *)k_rq_ring<MODEV, BV, DV>,             \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+            if (e != hipSuccess)                                                                   \
+                return fail(W4A4_ERR_HIP, "rotate-quantize LDS request: %s", hipGetErrorString(e)); \
+            attr_set = true;                                                                       \
+        }                                                                                          \
+        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV>), grid_r, dim3(256), lds, s, src, ld, M, K,   \
+                           rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r, groups);   \
+    } while (0)
+#define W4A4_RING_B(MODEV)                                                                         \
+    if (B == 128) W4A4_RING(MODEV, 128, false); else W4A4_RING(MODEV, 64, false);
+#define W4A4_RING_BD(MODEV)                                                                        \
+    if (xrot_dbg) { if (B == 128) W4A4_RING(MODEV, 128, true); else W4A4_RING(MODEV, 64, true); }  \
+    else { W4A4_RING_B(MODEV) }
+        switch (mode) {
+        case ACT_PER_STEP: W4A4_RING_BD(ACT_PER_STEP) break;
+        case ACT_TOKEN_MAX: W4A4_RING_B(ACT_TOKEN_MAX) break;
+        case ACT_TOKEN_QUANT: W4A4_RING_BD(ACT_TOKEN_QUANT) break;
+        case ACT_CALIB_MAX: W4A4_RING_B(ACT_CALIB_MAX) break;
+        }
+#undef W4A4_RING_BD
+#undef W4A4_RING_B
+#undef W4A4_RING
+        return check_launch("rotate-quantize (ring)");
+    }
 #define W4A4_RQ(MODEV, BV, GV)                                                                     \
     hipLaunchKernelGGL((k_rq_mfma<MODEV, BV, GV>), grid, dim3(256), 0, s, src, ld, M, K, perm, rhi, \
                        rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw)
@@ -448,7 +730,7 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
 }
 
 int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t *perm, uint16_t *xp,
-                        hipStream_t s)
+                        uint32_t *zero_row, hipStream_t s)
 {
     if (M == 0) return W4A4_OK;
     const size_t lds = (size_t)K * sizeof(uint16_t);
@@ -460,8 +742,12 @@ int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t 
         if (e != hipSuccess) return fail(W4A4_ERR_HIP, "permute LDS request: %s", hipGetErrorString(e));
     }
     const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
-    if (vec) hipLaunchKernelGGL(k_permute_rows<true>, dim3(M), dim3(256), lds, s, x, ldx, K, perm, xp);
-    else hipLaunchKernelGGL(k_permute_rows<false>, dim3(M), dim3(256), lds, s, x, ldx, K, perm, xp);
+    if (vec)
+        hipLaunchKernelGGL(k_permute_rows<true>, dim3(M), dim3(256), lds, s, x, ldx, K, perm, xp,
+                           zero_row);
+    else
+        hipLaunchKernelGGL(k_permute_rows<false>, dim3(M), dim3(256), lds, s, x, ldx, K, perm, xp,
+                           zero_row);
     return check_launch("permute rows");
 }
 

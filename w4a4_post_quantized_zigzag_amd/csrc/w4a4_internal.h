@@ -68,11 +68,11 @@ int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B
                         float *xrot_dbg, hipStream_t s);
 int launch_scale_from_absmax(const uint32_t *amax, float *out, hipStream_t s);
 // fp16 activations with block 64 or 128: MFMA rotation; xperm (optional) holds rows already in
-// zigzag order, written by launch_permute_rows.
+// zigzag order, written by launch_permute_rows (which also clears zero_row[0..M) when given).
 bool act_uses_permute_pass(int M, int K, int per_token);
 size_t act_permute_bytes(int M, int K);
 int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t *perm, uint16_t *xp,
-                        hipStream_t s);
+                        uint32_t *zero_row, hipStream_t s);
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
