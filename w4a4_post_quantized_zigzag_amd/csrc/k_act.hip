@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const int64_t off = ((int64_t)b * B + jbase + 16 * jf + r) * B + 32 * kk + 8 * g;
+            const int64_t off = rot16_fragment(b, jbase / 16 + jf, kk, lane, B);
             ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off);
             alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
         }
@@ -367,6 +367,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
 // which makes the 16 rows a fragment read touches hit 16 different bank groups.
 constexpr int RQ_STAGES = 4;
 constexpr int RQ_RING_MAX_ROWS = 1024;  // rows per workgroup (per-token scales staged in LDS)
+constexpr int RQ_SMALL_M = 256;         // batches up to this many tokens use k_rq_small
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 __device__ __forceinline__ void rq_dma16(const void *gptr, uint32_t lds_addr)
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
     for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const int64_t off = ((int64_t)b * B + jbase + 16 * jf + r) * B + 32 * kk + 8 * g;
+            const int64_t off = rot16_fragment(b, jbase / 16 + jf, kk, lane, B);
             ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off) * (_Float16)(1 << ROT_LO_SHIFT);
             alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
         }
@@ -598,6 +599,135 @@ __global__ __launch_bounds__(256) void k_rq_ring(
     }
 }
 
+// ------------------------------------------------------------------ few tokens
+//
+// With at most RQ_SMALL_M tokens there are too few row tiles to amortize a block's R_b fragments,
+// and the launch is latency-bound; the grid is spread as wide as the work allows instead: one
+// workgroup per (16-token slice, block), each wave holding the fragments of a quarter of the
+// block's output channels. The slice's inputs X[m][perm[b*B + i]] are gathered with 2-byte loads
+// (no permuted copy, no alignment needed; copying whole rows to LDS first moves more bytes per CU
+// and measured slower) and staged in LDS as the MFMA B operand.
+template <int MODE, int B, bool DBG>
+__global__ __launch_bounds__(256) void k_rq_small(
+    const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const int32_t *__restrict__ perm,
+    const _Float16 *__restrict__ rhi, const _Float16 *__restrict__ rlo,
+    const float *__restrict__ table, int step, uint32_t *__restrict__ rowmax,
+    uint8_t *__restrict__ xq, float *__restrict__ x_scale, float *__restrict__ xrot_dbg)
+{
+#pragma clang fp contract(off)
+    constexpr int KK = B / 32, JW = B / 4, JF = JW / 16;
+    constexpr int LDSR = B + 8;         // halves per staged row (16-byte pad)
+    constexpr int RSTEP = 256 / B;      // rows gathered per pass of the workgroup
+    constexpr int PER = 16 / RSTEP;     // gathered elements per thread
+    constexpr float LO = 1.0f / (1 << ROT_LO_SHIFT);
+    __shared__ __attribute__((aligned(16))) uint16_t sx[16 * LDSR];
+    __shared__ float smax[4][16];
+
+    // workgroup -> (16-token slice, block); with 8 | nb the slices of a block share an XCD (and
+    // its L2, where the block's fragments are then fetched once)
+    const int nb = K / B, ns = gridDim.x / nb, wg = blockIdx.x;
+    int b, si;
+    if (nb % 8 == 0) {
+        const int i = wg / 8;
+        b = 8 * (i / ns) + wg % 8;
+        si = i % ns;
+    } else {
+        b = wg / ns;
+        si = wg % ns;
+    }
+    const int m0 = si * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int jbase = wave * JW;
+
+    // gather: thread -> input column tid % B of the block, rows tid / B + RSTEP * i (clamped)
+    const int gc = tid % B, gr0 = tid / B;
+    const int64_t src_col = perm ? (int64_t)perm[b * B + gc] : (int64_t)b * B + gc;
+    uint16_t xv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int m = min(m0 + gr0 + RSTEP * i, M - 1);
+        xv[i] = X[(int64_t)m * ldx + src_col];
+    }
+    v8h ahi[JF][KK], alo[JF][KK];
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int64_t off = rot16_fragment(b, jbase / 16 + jf, kk, lane, B);
+            ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off) * (_Float16)(1 << ROT_LO_SHIFT);
+            alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
+        }
+    float rs = 0.0f;
+    if (MODE == ACT_PER_STEP) {
+        const float s = step_scale(table, step);
+        rs = (float)(1.0 / (double)s) * LO;
+        if (si == 0 && b == 0 && tid == 0) x_scale[0] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int rr = gr0 + RSTEP * i;
+        sx[rr * LDSR + gc] = (m0 + rr < M) ? xv[i] : (uint16_t)0;
+    }
+    __syncthreads();
+
+    // acc[jf] = 2^12 x' for token m0 + (lane % 16), channels jbase + 16 jf + 4 (lane / 16) + 0..3
+    v4f acc[JF];
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf) acc[jf] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const v8h xb = *reinterpret_cast<const v8h *>(&sx[r * LDSR + 32 * kk + 8 * g]);
+#pragma unroll
+        for (int jf = 0; jf < JF; ++jf)
+            acc[jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jf][kk], xb, acc[jf], 0, 0, 0);
+#pragma unroll
+        for (int jf = 0; jf < JF; ++jf)
+            acc[jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jf][kk], xb, acc[jf], 0, 0, 0);
+    }
+
+    const int m = m0 + r;
+    if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
+        float a = 0.0f;
+#pragma unroll
+        for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(acc[jf][i]));
+        a = fmaxf(a, __shfl_xor(a, 16));
+        a = fmaxf(a, __shfl_xor(a, 32));
+        if (g == 0) smax[wave][r] = (m < M) ? a * LO : 0.0f;
+        __syncthreads();
+        if (tid < 16) {
+            float u = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+            if (MODE == ACT_TOKEN_MAX) {
+                if (m0 + tid < M) atomicMax(&rowmax[m0 + tid], __float_as_uint(u));
+            } else {
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) u = fmaxf(u, __shfl_xor(u, off));
+                if (tid == 0) atomicMax(&rowmax[0], __float_as_uint(u));
+            }
+        }
+        return;
+    }
+    if (m >= M) return;
+    const int jl = jbase + 4 * g;
+    if (DBG) {
+#pragma unroll
+        for (int jf = 0; jf < JF; ++jf)
+            *reinterpret_cast<float4 *>(&xrot_dbg[(int64_t)m * K + b * B + jl + 16 * jf]) =
+                make_float4(acc[jf][0] * LO, acc[jf][1] * LO, acc[jf][2] * LO, acc[jf][3] * LO);
+    }
+    if (MODE == ACT_TOKEN_QUANT) {
+        const float s = scale_from_absmax(__uint_as_float(rowmax[m]));
+        rs = (float)(1.0 / (double)s) * LO;
+        if (b == 0 && wave == 0 && g == 0) x_scale[m] = s;
+    }
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf)
+        *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * (K / 2) + (b * B + jl + 16 * jf) / 2]) =
+            (uint16_t)quant_pack4(acc[jf], rs);
+}
+
 // Zigzag gather of whole rows: Xp[m][j] = X[m][perm[j]] (fp16), one workgroup per row, the source
 // row staged in LDS with 16-byte loads and the permuted row written with 16-byte stores. The
 // workgroup of row m also clears zero_row[m] (the per-token maxima the next pass accumulates), when
@@ -643,7 +773,7 @@ bool act_uses_permute_pass(int M, int K, int per_token)
     // followed by 16-byte DMA tile loads wins once the batch is a few MB, and earlier in per-token
     // mode, which reads the rows twice (and where the pass also clears the row maxima). The pass
     // stages a whole row in LDS.
-    if (K > 65536) return false;
+    if (K > 65536 || M <= RQ_SMALL_M) return false;  // few tokens: gathered in the kernel
     const int64_t elems = (int64_t)M * K;
     return per_token ? (K >= 2048 || elems >= (1 << 20)) : (elems >= (1 << 22));
 }
@@ -669,6 +799,28 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
     const _Float16 *rhi = reinterpret_cast<const _Float16 *>(base + L.r32);
     const _Float16 *rlo = reinterpret_cast<const _Float16 *>(base + L.r32 + L.r16);
     const int nb = K / B;
+    if (M <= RQ_SMALL_M && !xperm) {
+        dim3 grid_s(((M + 15) / 16) * nb);
+        const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
+#define W4A4_SMALL(MODEV, BV, DV)                                                                  \
+    hipLaunchKernelGGL((k_rq_small<MODEV, BV, DV>), grid_s, dim3(256), 0, s, x, ldx, M, K, perm,   \
+                       rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg)
+#define W4A4_SMALL_B(MODEV)                                                                        \
+    if (B == 128) W4A4_SMALL(MODEV, 128, false); else W4A4_SMALL(MODEV, 64, false);
+#define W4A4_SMALL_BD(MODEV)                                                                       \
+    if (xrot_dbg) { if (B == 128) W4A4_SMALL(MODEV, 128, true); else W4A4_SMALL(MODEV, 64, true); } \
+    else { W4A4_SMALL_B(MODEV) }
+        switch (mode) {
+        case ACT_PER_STEP: W4A4_SMALL_BD(ACT_PER_STEP) break;
+        case ACT_TOKEN_MAX: W4A4_SMALL_B(ACT_TOKEN_MAX) break;
+        case ACT_TOKEN_QUANT: W4A4_SMALL_BD(ACT_TOKEN_QUANT) break;
+        case ACT_CALIB_MAX: W4A4_SMALL_B(ACT_CALIB_MAX) break;
+        }
+#undef W4A4_SMALL_BD
+#undef W4A4_SMALL_B
+#undef W4A4_SMALL
+        return check_launch("rotate-quantize (few tokens)");
+    }
     const int rpw = rq_rows_per_wg(M, nb);
     dim3 grid((M + rpw - 1) / rpw, nb);
     const uint16_t *src = xperm ? xperm : reinterpret_cast<const uint16_t *>(X);

@@ -12,7 +12,7 @@
 namespace w4a4 {
 
 // One thread per (b, i, j): R64[b][i][j] = sum_l U_b[i][l] * H[l][j], l increasing; also the fp32
-// copy and the fp16 high/low split (transposed) consumed by the activation kernels.
+// copy and the fp16 high/low split (MFMA operand order) consumed by the activation kernels.
 __global__ void k_rotation(const float *__restrict__ U, int K, int B, double hinv,
                            double *__restrict__ R64, float *__restrict__ r32,
                            __half *__restrict__ rhi, __half *__restrict__ rlo)
@@ -38,7 +38,7 @@ __global__ void k_rotation(const float *__restrict__ U, int K, int B, double hin
     __half hi = __float2half_rn((float)s);
     double rem = s - (double)__half2float(hi);
     __half lo = __float2half_rn((float)(rem * (double)(1 << ROT_LO_SHIFT)));
-    const int64_t t = ((int64_t)b * B + j) * B + i;  // transposed [b][j][i]
+    const int64_t t = rot16_index(b, i, j, B);
     rhi[t] = hi;
     rlo[t] = lo;
 }

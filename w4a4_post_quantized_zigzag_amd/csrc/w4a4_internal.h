@@ -35,13 +35,29 @@ __device__ __forceinline__ bool hadamard_negative(int l, int j) { return __popc(
 
 // Layout of the activation rotation operand written by the pack call (all offsets 256-aligned):
 //   [0, r32)          fp32 R_b[i][j] for every block, [nb][B][B] row-major
-//   [r32, r32 + r16)  fp16 high parts of R_b, transposed: hi[b][j][i]
-//   [.., .. + r16)    fp16 low parts scaled by 2^ROT_LO_SHIFT, transposed: lo[b][j][i]
+//   [r32, r32 + r16)  fp16 high parts of R_b, in MFMA operand order (rot16_index)
+//   [.., .. + r16)    fp16 low parts scaled by 2^ROT_LO_SHIFT, same order
 // with R_b ~= hi + lo * 2^-ROT_LO_SHIFT to about 22 significant bits.
 constexpr int ROT_LO_SHIFT = 12;
 struct RotLayout {
     size_t r32, r16, total;
 };
+// Position of R_b[i][j]'s fp16 part. For B a multiple of 32 the parts are stored as the A operand
+// of v_mfma_f32_16x16x32_f16 with R_b^T as the matrix: per block b, 16-channel group j / 16 and
+// 32-input chunk i / 32, one contiguous 1 KB run in which lane l = (j % 16) + 16 ((i % 32) / 8)
+// holds inputs 32 (i / 32) + 8 (l / 16) + 0..7 of channel j, so a wave loads a fragment with one
+// fully used 16-byte-per-lane load. Other block sizes use the plain transpose [b][j][i].
+__host__ __device__ inline int64_t rot16_index(int b, int i, int j, int B)
+{
+    if (B % 32 != 0) return ((int64_t)b * B + j) * B + i;
+    const int64_t run = ((int64_t)b * (B / 16) + j / 16) * (B / 32) + i / 32;
+    return (run * 64 + (j % 16) + 16 * ((i % 32) / 8)) * 8 + (i % 8);
+}
+// Element offset of the fragment (16-channel group jt, chunk kk) of block b for lane `lane`.
+__host__ __device__ inline int64_t rot16_fragment(int b, int jt, int kk, int lane, int B)
+{
+    return ((((int64_t)b * (B / 16) + jt) * (B / 32) + kk) * 64 + lane) * 8;
+}
 inline RotLayout rot_layout(int K, int B)
 {
     RotLayout L;
