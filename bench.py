@@ -274,7 +274,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-supplementary", action="store_true")
     ap.add_argument("--supp-steps", type=int, default=30)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of known size (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the W4A4 linear "
               "shards over tokens with no exchange, so N GPUs would run N copies of this line).",
@@ -311,7 +317,9 @@ def main():
                               "M": M, "K": K, "N": N, "block": B, "denoising_steps": T,
                               "scale_mode": "per_step"},
                       bandwidth_gbps=bytes_step / (ms * 1e-3) / 1e9)
-        result["roofline"] = {"bound": "hbm", "kernel": "k_gemm_w4a4 (BM=64, BN=64)",
+        result["roofline"] = {"bound": "hbm",
+                              "kernel": "k_gemm_smallm<4> (16 output columns per workgroup, "
+                                        "K split over its 4 waves)",
                               "achieved": gb / (gemm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": gb / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                               "traffic": traffic_from_profile("k_gemm.hip", name),
@@ -331,6 +339,23 @@ def main():
     if not args.no_supplementary:
         result["supplementary"] = supplementary(bd, inputs, args.supp_steps)
     print(json.dumps(result))
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(reps=3):
+    """A plain copy of COPY_BYTES (larger than the 256 MB last-level cache, so it streams from and
+    to HBM), `reps` times: under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE per dispatch give the
+    factor from those counters to bytes."""
+    torch = _torch()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}))
 
 
 def supplementary(bd, inputs, steps):

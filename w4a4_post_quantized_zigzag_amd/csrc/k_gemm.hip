@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
                                                      const uint8_t *__restrict__ wq, int M, int N,
                                                      int K, GemmEpilogue epi)
 {
+#pragma clang fp contract(off)
     __shared__ int32_t red[4][MF * 16][17];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -132,29 +133,48 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
     const int per_wave = (windows + 3) / 4;
     const int w_begin = wave * per_wave, w_end = min(windows, w_begin + per_wave);
 
+    // Epilogue operands are fetched first, so their latency hides under the operand loads. The
+    // epilogue thread owns column n0 + (tid % 16) and rows tid / 16 + 16 f.
+    const int ecol = threadIdx.x & 15, erow = threadIdx.x >> 4;
+    const bool scaled = epi.mode != GEMM_OUT_I32;
+    float e_sw = 0.0f, e_sx[MF];
+    uint16_t e_res[MF];
+    if (scaled) {
+        e_sw = epi.w_scale[min(n0 + ecol, N - 1)];
+#pragma unroll
+        for (int f = 0; f < MF; ++f) {
+            const int m = min(erow + 16 * f, M - 1);
+            e_sx[f] = epi.x_scale_per_token ? epi.x_scale[m] : epi.x_scale[0];
+            e_res[f] = (epi.mode == W4A4_EPI_RESIDUAL)
+                           ? epi.residual[(int64_t)m * epi.ldr + min(n0 + ecol, N - 1)]
+                           : (uint16_t)0;
+        }
+    }
+
     v4i total[MF];
 #pragma unroll
     for (int f = 0; f < MF; ++f) total[f] = v4i{0, 0, 0, 0};
 
     for (int wc = w_begin; wc < w_end; wc += SM_CHUNK) {
+        const int nc = min(SM_CHUNK, w_end - wc);  // live windows of this chunk (wave-uniform)
         uint4 bq[SM_CHUNK], aq[SM_CHUNK][MF];
         bool bv[SM_CHUNK], av[SM_CHUNK][MF];
 #pragma unroll
         for (int c = 0; c < SM_CHUNK; ++c) {
+            if (c >= nc) continue;
             const int kb = (wc + c) * 64 + 16 * g;
-            const int kend = (wc + c < w_end) ? ldp : 0;  // windows past this wave's range read nothing
             if (VEC) {
-                bq[c] = load16_clamped(wq, N, n0 + r, ldp, kb, kend, bv[c]);
+                bq[c] = load16_clamped(wq, N, n0 + r, ldp, kb, ldp, bv[c]);
             } else {
-                bq[c] = load_packed16<false>(wq, N, n0 + r, ldp, kb, kend);
+                bq[c] = load_packed16<false>(wq, N, n0 + r, ldp, kb, ldp);
                 bv[c] = true;
             }
 #pragma unroll
             for (int f = 0; f < MF; ++f) {
                 if (VEC) {
-                    aq[c][f] = load16_clamped(xq, M, f * 16 + r, ldp, kb, kend, av[c][f]);
+                    aq[c][f] = load16_clamped(xq, M, f * 16 + r, ldp, kb, ldp, av[c][f]);
                 } else {
-                    aq[c][f] = load_packed16<false>(xq, M, f * 16 + r, ldp, kb, kend);
+                    aq[c][f] = load_packed16<false>(xq, M, f * 16 + r, ldp, kb, ldp);
                     av[c][f] = true;
                 }
             }
@@ -164,6 +184,7 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
         for (int f = 0; f < MF; ++f) acc[f] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < SM_CHUNK; ++c) {
+            if (c >= nc) continue;
             uint4 b0, b1;
             widen16(zero_unless(bq[c], bv[c]), b0, b1);
 #pragma unroll
@@ -187,12 +208,21 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[wave][f * 16 + 4 * g + i][r] = total[f][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < MF * 16 * 16; e += 256) {
-        const int row = e >> 4, col = e & 15;
-        const int m = row, n = n0 + col;
+    const int n = n0 + ecol;
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+        const int m = erow + 16 * f;
         if (m >= M || n >= N) continue;
-        const int32_t v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
-        store_output(epi, m, n, N, v);
+        const int32_t v = red[0][m][ecol] + red[1][m][ecol] + red[2][m][ecol] + red[3][m][ecol];
+        if (!scaled) {
+            epi.acc_out[(int64_t)m * N + n] = v;
+            continue;
+        }
+        float y = fp32_value((float)v * e_sx[f]);
+        y = fp32_value(y * e_sw);
+        if (epi.mode == W4A4_EPI_GELU) y = fp32_value(gelu_erf(y));
+        else if (epi.mode == W4A4_EPI_RESIDUAL) y = fp32_value(y + __half2float(__ushort_as_half(e_res[f])));
+        epi.Y[(int64_t)m * epi.ldy + n] = f32_to_f16_bits(y);
     }
 }
 
