@@ -341,6 +341,59 @@ def main():
     print(json.dumps(result))
 
 
+COLD_BYTES = 512 << 20  # distinct operand copies cycled per round: twice the 256 MB last-level cache
+
+
+def cold_hbm(bd, inputs):
+    """HBM-bound kernels on cold operands: each timed launch reads a different copy of its large
+    operand, and the copies add up to COLD_BYTES, so by the time a copy comes round again the
+    last-level cache has been flushed by the others.
+    - small-M GEMM sweep, M in {16, 50, 64} with N = K = 16384 (128 MB of packed weights per copy),
+      where the weight stream is long enough for its bandwidth to be measurable;
+    - rotate-quantize of the prefill and long-K workloads (per-token, zigzag order), cycling copies
+      of X (4 MB and 32 MB)."""
+    torch = _torch()
+    out = {"note": "cold: operands cycled over distinct copies totalling 512 MB",
+           "small_m_gemm": [], "rotate_quant": []}
+    N = K = 16384
+    g = torch.Generator(device="cuda").manual_seed(7)
+    wbytes = N * K // 2
+    copies = max(2, COLD_BYTES // wbytes)
+    wqs = [torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+           for _ in range(copies)]
+    w_scale = torch.rand(N, generator=g, device="cuda") * 1e-2
+    for M in (16, 50, 64):
+        xq = torch.randint(0, 256, (M, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+        xs = torch.ones(1, device="cuda")
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ws = torch.empty(max(256, bd.lib().w4a4_gemm_workspace_bytes(M, N, K)), dtype=torch.uint8,
+                         device="cuda")
+        ms = time_kernel_calls([lambda w=w: bd.gemm(xq, xs, False, w, w_scale, K, Y=Y, ws=ws)
+                                for w in wqs], 10)
+        gbps = gemm_bytes(M, N, K, False) / (ms * 1e-3) / 1e9
+        out["small_m_gemm"].append({"M": M, "N": N, "K": K, "weight_copies": copies,
+                                    "gemm_us": ms * 1e3, "gbps": gbps,
+                                    "frac_hbm": gbps / HBM_PEAK_GBPS,
+                                    "tops": 2.0 * M * N * K / (ms * 1e-3) / 1e12})
+    del wqs
+    torch.cuda.empty_cache()
+    for name in ("prefill_proj", "longk_down"):
+        d = inputs.linear_inputs(name, M=1)  # weights only; X copies are drawn on the device
+        M, K = inputs.LINEAR_WORKLOADS[name]["M"], d["K"]
+        lin = Linear(d["W"], d["block"], bd)
+        lin.buffers(M, per_token=True)
+        xcopies = max(2, COLD_BYTES // (M * K * 2))
+        Xs = [torch.randn((M, K), generator=g, device="cuda").half() for _ in range(xcopies)]
+        ms = time_kernel_calls([lambda X=X: lin.rq(X) for X in Xs], 4)
+        gbps = rq_bytes(M, K, d["block"], 2, True) / (ms * 1e-3) / 1e9
+        out["rotate_quant"].append({"workload": name, "M": M, "K": K, "x_copies": xcopies,
+                                    "scale_mode": "per_token", "rq_us": ms * 1e3, "gbps": gbps,
+                                    "frac_hbm": gbps / HBM_PEAK_GBPS})
+        del Xs, lin
+        torch.cuda.empty_cache()
+    return out
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -380,6 +433,7 @@ def supplementary(bd, inputs, steps):
                      "calibrate_and_pack_s": lin.offline_s}
         del lin, Xs, Ys
         torch.cuda.empty_cache()
+    out["cold_hbm"] = cold_hbm(bd, inputs)
     info, lins, Xs, rb, step = setup_stack(bd, inputs)
     ms = time_graph(step, max(3, steps // 5), 2)
     M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]

@@ -111,7 +111,8 @@ int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t l
  * zero row); codes p = clamp(rint(W' / s_w), -8, 7) (half to even), packed into wq [N][K/2].
  * Also writes `rot`, the activation-side rotation operand (w4a4_rot_bytes(K, block) bytes, 16-byte
  * aligned, opaque device layout) that w4a4_rotate_quant_act and w4a4_calibrate_act_scale read.
- * wq and w_scale are bit-exact functions of (W, perm, U).
+ * wq and w_scale are bit-exact functions of (W, perm, U). U == NULL stands for U_b = I (R_b = H_B,
+ * the Hadamard-only mode of w4a4_rotate_quant_act_hadamard).
  * ------------------------------------------------------------------------------------------- */
 size_t w4a4_rot_bytes(int K, int block);
 size_t w4a4_pack_workspace_bytes(int N, int K, int block);
@@ -137,6 +138,20 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
                           const int32_t *perm, const void *rot, const float *act_scale_table,
                           int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Hadamard-only rotation mode: the same runtime call for R_b = H_B (U_b = I), the block Hadamard
+ * transform on its own [FoldQuantVLA summary, key change 2: block Hadamard transform with dynamic
+ * per-token quantization; gist.science Metodologia 1 names the Hadamard factor of the composite
+ * rotation]. Weights for this mode are packed by w4a4_pack_weights with U == NULL. No rotation
+ * operand and no workspace: each row is staged on chip and transformed with fp64 butterflies, so x'
+ * is the fp32 rounding of a value within a few fp64 ulps of X[:, perm] . blockdiag(H_B). Scales and
+ * codes follow w4a4_rotate_quant_act (per-step with act_scale_table, per-token without). block must
+ * be 64 or 128 and K at most 65536 (fp16 X) or 32768 (fp32 X), else W4A4_ERR_UNSUPPORTED; xq must
+ * be 16-byte aligned (W4A4_ERR_ALIGN). */
+int w4a4_rotate_quant_act_hadamard(const void *X, int x_dtype, int M, int K, int64_t ldx,
+                                   int block, const int32_t *perm, const float *act_scale_table,
+                                   int num_steps, int step, uint8_t *xq, float *x_scale,
+                                   float *xrot_dbg, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * W4A4 GEMM with fused dequantization [vnrobo.com "Vi sao W4A4 kho hon W4A16?": activations must be

@@ -84,6 +84,36 @@ def test_rotate_quant_rejects(L, kw, code):
     assert L.w4a4_last_error() != b""
 
 
+def _rqh(L, *, M=16, K=256, ldx=256, block=64, dt=bd.W4A4_F16, X=FAKE, table=FAKE, steps=8,
+         step=0, xq=FAKE):
+    return L.w4a4_rotate_quant_act_hadamard(X, dt, M, K, ldx, block, FAKE, table, steps, step, xq,
+                                            FAKE, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=32), bd.W4A4_ERR_UNSUPPORTED),            # the butterfly kernel takes 64 or 128
+    (dict(block=256, K=512, ldx=512), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(K=1 << 17, ldx=1 << 17), bd.W4A4_ERR_UNSUPPORTED),  # row longer than the LDS stage
+    (dict(K=1 << 16, ldx=1 << 16, dt=bd.W4A4_F32), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(step=8), bd.W4A4_ERR_STEP_RANGE),
+    (dict(steps=0), bd.W4A4_ERR_STEP_RANGE),
+    (dict(xq=ctypes.c_void_p(0x10004)), bd.W4A4_ERR_ALIGN),
+    (dict(xq=NULL), bd.W4A4_ERR_ARG),
+    (dict(K=192, ldx=192, block=128), bd.W4A4_ERR_SHAPE),
+    (dict(ldx=100), bd.W4A4_ERR_SHAPE),
+])
+def test_rotate_quant_hadamard_rejects(L, kw, code):
+    assert _rqh(L, **kw) == code
+    assert L.w4a4_last_error() != b""
+
+
+def test_hadamard_empty_batch_and_limits(L):
+    assert _rqh(L, M=0) == bd.W4A4_OK
+    assert _rqh(L, M=0, table=NULL) == bd.W4A4_OK
+    assert _rqh(L, M=0, K=1 << 16, ldx=1 << 16) == bd.W4A4_OK            # 128 KB fp16 row
+    assert _rqh(L, M=0, K=1 << 15, ldx=1 << 15, dt=bd.W4A4_F32) == bd.W4A4_OK
+
+
 def test_empty_batch_is_a_valid_call(L):
     assert _rq(L, M=0) == bd.W4A4_OK
     assert _rq(L, M=0, table=NULL) == bd.W4A4_OK
@@ -123,7 +153,8 @@ def test_pack_and_calibration_reject(L):
     assert ws >= 256 * 64 * 8
     assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, FAKE,
                                ws, NULL) == bd.W4A4_ERR_ALIGN
-    assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, ws,
+    # U may be NULL (U_b = I), the outputs may not
+    assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, NULL, NULL, FAKE, FAKE, FAKE, ws,
                                NULL) == bd.W4A4_ERR_ARG
     assert L.w4a4_pack_weights(FAKE, 0, 256, 256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                ws - 8, NULL) == bd.W4A4_ERR_WORKSPACE

@@ -31,6 +31,8 @@ SIGNATURES = {
     "w4a4_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4a4_rotate_quant_act": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "w4a4_rotate_quant_act_hadamard": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _i, _i, _vp, _vp,
+                                            _vp, _vp]),
     "w4a4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
     "w4a4_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz, _vp]),
     "w4a4_gemm_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -130,7 +132,7 @@ def block_svd(W, perm, block: int):
 
 
 def pack_weights(W, perm, U, block: int):
-    """Returns (wq uint8 [N, K/2], w_scale fp32 [N], rot uint8 [rot_bytes])."""
+    """Returns (wq uint8 [N, K/2], w_scale fp32 [N], rot uint8 [rot_bytes]). U None: U_b = I."""
     torch = _torch()
     N, K = W.shape
     wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
@@ -174,6 +176,22 @@ def rotate_quant_act(X, perm, rot, block: int, table=None, num_steps: int = 0, s
     check(lib().w4a4_rotate_quant_act(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
                                       _p(perm), _p(rot), _p(table), num_steps, step, _p(xq),
                                       _p(x_scale), _p(xrot_dbg), _p(ws), nb, _stream()))
+    return xq, x_scale
+
+
+def rotate_quant_act_hadamard(X, perm, block: int, table=None, num_steps: int = 0, step: int = 0,
+                              xq=None, x_scale=None, xrot_dbg=None):
+    """Hadamard-only rotation mode (R_b = H_B); per-token scales when table is None."""
+    torch = _torch()
+    M, K = X.shape
+    per_token = table is None
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(max(M, 1) if per_token else 1, dtype=torch.float32, device=X.device)
+    check(lib().w4a4_rotate_quant_act_hadamard(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
+                                               _p(perm), _p(table), num_steps, step, _p(xq),
+                                               _p(x_scale), _p(xrot_dbg), _stream()))
     return xq, x_scale
 
 

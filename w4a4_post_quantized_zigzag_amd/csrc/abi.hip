@@ -256,7 +256,7 @@ int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int
     if ((rc = check_kb(K, block))) return rc;
     if (N <= 0) return fail(W4A4_ERR_ARG, "N = %d must be positive", N);
     if ((rc = check_matrix(W, w_dtype, N, K, ldw, "W"))) return rc;
-    if (!U || !wq || !w_scale || !rot) return fail(W4A4_ERR_ARG, "U, wq, w_scale and rot are required");
+    if (!wq || !w_scale || !rot) return fail(W4A4_ERR_ARG, "wq, w_scale and rot are required");
     if (!aligned(U, 4) || !aligned(w_scale, 4)) return fail(W4A4_ERR_ALIGN, "U / w_scale misaligned");
     if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
     if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
@@ -308,6 +308,40 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
     if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
                              per_step ? KIND_STEP : KIND_TOKEN, xq, x_scale, xrot_dbg, ws, nullptr,
                              stream)))
+        return rc;
+    return ok();
+}
+
+int w4a4_rotate_quant_act_hadamard(const void *X, int x_dtype, int M, int K, int64_t ldx,
+                                   int block, const int32_t *perm, const float *act_scale_table,
+                                   int num_steps, int step, uint8_t *xq, float *x_scale,
+                                   float *xrot_dbg, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if (block != 64 && block != 128)
+        return fail(W4A4_ERR_UNSUPPORTED, "Hadamard-only rotation supports block 64 or 128, not %d",
+                    block);
+    if ((rc = check_matrix(X, x_dtype, M, K, ldx, "X"))) return rc;
+    if (hadamard_lds_bytes(1, K, block, x_dtype, nullptr) > 128 * 1024)
+        return fail(W4A4_ERR_UNSUPPORTED, "K = %d too long for the staged-row Hadamard kernel "
+                    "(at most 65536 fp16 or 32768 fp32 values per row)", K);
+    if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
+    const bool per_step = act_scale_table != nullptr;
+    if (per_step) {
+        if (num_steps <= 0) return fail(W4A4_ERR_STEP_RANGE, "num_steps = %d must be positive",
+                                        num_steps);
+        if (step < 0 || step >= num_steps)
+            return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
+        if (!aligned(act_scale_table, 4)) return fail(W4A4_ERR_ALIGN, "table misaligned");
+    }
+    if (M > 0 && (!xq || !x_scale)) return fail(W4A4_ERR_ARG, "xq and x_scale are required");
+    if (!aligned(xq, 16)) return fail(W4A4_ERR_ALIGN, "xq must be 16-byte aligned");
+    if (!aligned(x_scale, 4) || !aligned(xrot_dbg, 4))
+        return fail(W4A4_ERR_ALIGN, "x_scale / xrot_dbg misaligned");
+    if (M == 0) return ok();
+    if ((rc = launch_rotate_quant_hadamard(X, x_dtype, M, K, ldx, block, perm, act_scale_table, step,
+                                           xq, x_scale, xrot_dbg, stream)))
         return rc;
     return ok();
 }

@@ -5,6 +5,8 @@
 // scale (vnrobo.com "Y tuong paper": the runtime only looks up the step's scale) or a dynamic
 // per-token scale (FoldQuantVLA summary, key change 2). The decision q = rint(x' * fp32(1/s)) is
 // taken in fp32.
+#include <cmath>
+
 #include "w4a4_internal.h"
 
 namespace w4a4 {
@@ -726,6 +728,232 @@ __global__ __launch_bounds__(256) void k_rq_small(
     for (int jf = 0; jf < JF; ++jf)
         *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * (K / 2) + (b * B + jl + 16 * jf) / 2]) =
             (uint16_t)quant_pack4(acc[jf], rs);
+}
+
+// ------------------------------------------------------------------ Hadamard-only rotation
+//
+// The rotation with U_b = I, R_b = H_B: the plain block Walsh-Hadamard transform (the
+// FoldQuantVLA summary's block Hadamard, the DuQuant-style rotation without the SVD factor). No
+// rotation operand is read, so a workgroup stages whole rows of X in LDS with coalesced loads,
+// gathers each block's zigzag inputs from LDS and applies the transform as log2(B) butterfly stages
+// in fp64: a quad of 4 lanes per (row, block) unit with B / 4 values each, the low index bits inside
+// a lane and the two high bits across the quad (exchanged with quad-permute DPP moves, plain VALU
+// work), scaled once by fp64(1/sqrt(B)). Each value is the fp32 rounding of an fp64 result a few
+// ulps from the exact x'. The oracle rounds the same real number, so the two agree unless x' lies
+// within ~2^-45 (relative) of an fp32 rounding boundary, or the block's signed sum cancels to a
+// value comparable to the oracle's own fp64 rounding.
+// Per-token mode takes the row maximum in the same workgroup, with no second pass over HBM: the
+// first sweep keeps HD_KEEP rounds of results in registers, and the second recomputes any further
+// rounds from LDS.
+constexpr int HD_UNITS = 64;  // (row, block) units per round of the workgroup: 64 quads
+constexpr int HD_KEEP = 2;
+constexpr int HD_MAX_LDS = 128 * 1024;  // staged rows; the entry point rejects larger K
+
+__device__ __forceinline__ double hd_load(const uint16_t *p, int i)
+{
+    return (double)__half2float(__ushort_as_half(p[i]));
+}
+__device__ __forceinline__ double hd_load(const float *p, int i) { return (double)p[i]; }
+
+// x from the lane of this quad selected by the quad-permute control CTRL (both 32-bit halves)
+template <int CTRL>
+__device__ __forceinline__ double quad_dpp(double x)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm(1, 0, 3, 2)
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm(2, 3, 0, 1)
+
+template <int MODE, int B, typename XT, bool DBG>
+__global__ __launch_bounds__(256) void k_rq_hadamard(
+    const XT *__restrict__ X, int64_t ldx, int M, int K, int rows_per_wg, int vec_load, double hinv,
+    const int32_t *__restrict__ perm, const float *__restrict__ table, int step,
+    uint8_t *__restrict__ xq, float *__restrict__ x_scale, float *__restrict__ xrot_dbg)
+{
+#pragma clang fp contract(off)
+    constexpr int EPT = B / 4;  // values per lane
+    extern __shared__ __attribute__((aligned(16))) unsigned char hd_smem[];
+    XT *srow = reinterpret_cast<XT *>(hd_smem);
+    __shared__ uint32_t smax[HD_UNITS];
+    const int tid = threadIdx.x, t4 = tid & 3, slot = tid >> 2;
+    const int row0 = blockIdx.x * rows_per_wg;
+    const int nrows = min(rows_per_wg, M - row0);
+    const int nb = K / B;
+    const int units = nrows * nb;
+
+    if (vec_load) {
+        constexpr int VE = 16 / sizeof(XT);
+        const int cpr = K / VE;
+        for (int c = tid; c < nrows * cpr; c += 256) {
+            const int rr = c / cpr, cc = c % cpr;
+            *reinterpret_cast<uint4 *>(&srow[(int64_t)rr * K + VE * cc]) =
+                *reinterpret_cast<const uint4 *>(&X[(int64_t)(row0 + rr) * ldx + VE * cc]);
+        }
+    } else {
+        for (int c = tid; c < nrows * K; c += 256) {
+            const int rr = c / K, cc = c % K;
+            srow[(int64_t)rr * K + cc] = X[(int64_t)(row0 + rr) * ldx + cc];
+        }
+    }
+    if (tid < HD_UNITS) smax[tid] = 0u;
+    __syncthreads();
+
+    // the lane's EPT values of unit u (row u / nb, block u % nb): inputs EPT * t4 + e of the block
+    auto transform = [&](int u, float (&out)[EPT]) {
+        const int rr = u / nb, b = u % nb;
+        const XT *xr = srow + (int64_t)rr * K;
+        double v[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int j = b * B + EPT * t4 + e;
+            v[e] = hd_load(xr, perm ? perm[j] : j);
+        }
+#pragma unroll
+        for (int d = 1; d < EPT; d <<= 1)
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (!(e & d)) {
+                    const double a = v[e], c = v[e + d];
+                    v[e] = a + c;
+                    v[e + d] = a - c;
+                }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const double p = quad_dpp<DPP_QUAD_XOR1>(v[e]);
+            v[e] = (t4 & 1) ? p - v[e] : v[e] + p;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const double p = quad_dpp<DPP_QUAD_XOR2>(v[e]);
+            v[e] = (t4 & 2) ? p - v[e] : v[e] + p;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) out[e] = (float)(v[e] * hinv);
+    };
+    // quantize the unit with r = fp32(1/s) and store its EPT codes (EPT / 2 contiguous bytes)
+    auto emit = [&](int u, const float (&x)[EPT], float r) {
+        const int m = row0 + u / nb, col = (u % nb) * B + EPT * t4;
+        if (DBG) {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) xrot_dbg[(int64_t)m * K + col + e] = x[e];
+        }
+        uint32_t w[EPT / 8];
+#pragma unroll
+        for (int k = 0; k < EPT / 8; ++k) {
+            uint32_t t = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t |= (uint32_t)(quant_code(x[8 * k + e], r) & 0xF) << (4 * e);
+            w[k] = t;
+        }
+        uint8_t *dst = xq + (int64_t)m * (K / 2) + col / 2;
+        if (EPT == 32) *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1 % (EPT / 8)], w[2 % (EPT / 8)], w[3 % (EPT / 8)]);
+        else *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1 % (EPT / 8)]);
+    };
+
+    if (MODE == ACT_PER_STEP) {
+        const float s = step_scale(table, step);
+        const float r = (float)(1.0 / (double)s);
+        if (blockIdx.x == 0 && tid == 0) x_scale[0] = s;
+        for (int u = slot; u < units; u += HD_UNITS) {
+            float x[EPT];
+            transform(u, x);
+            emit(u, x, r);
+        }
+        return;
+    }
+
+    // per token: row maxima first (kept results for the first HD_KEEP rounds), then quantize
+    float keep[HD_KEEP][EPT];
+    auto row_max = [&](int u, const float (&x)[EPT]) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) a = fmaxf(a, fabsf(x[e]));
+        a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), DPP_QUAD_XOR1, 0xF, 0xF, false)));
+        a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), DPP_QUAD_XOR2, 0xF, 0xF, false)));
+        if (t4 == 0) atomicMax(&smax[u / nb], __float_as_uint(a));
+    };
+#pragma unroll
+    for (int k = 0; k < HD_KEEP; ++k) {
+        const int u = slot + k * HD_UNITS;
+        if (u < units) {
+            transform(u, keep[k]);
+            row_max(u, keep[k]);
+        }
+    }
+    for (int u = slot + HD_KEEP * HD_UNITS; u < units; u += HD_UNITS) {
+        float x[EPT];
+        transform(u, x);
+        row_max(u, x);
+    }
+    __syncthreads();
+    auto finish = [&](int u, const float (&x)[EPT]) {
+        const int rr = u / nb;
+        const float s = scale_from_absmax(__uint_as_float(smax[rr]));
+        if (u % nb == 0 && t4 == 0) x_scale[row0 + rr] = s;
+        emit(u, x, (float)(1.0 / (double)s));
+    };
+#pragma unroll
+    for (int k = 0; k < HD_KEEP; ++k) {
+        const int u = slot + k * HD_UNITS;
+        if (u < units) finish(u, keep[k]);
+    }
+    for (int u = slot + HD_KEEP * HD_UNITS; u < units; u += HD_UNITS) {
+        float x[EPT];
+        transform(u, x);
+        finish(u, x);
+    }
+}
+
+size_t hadamard_lds_bytes(int M, int K, int B, int x_dtype, int *rows_per_wg)
+{
+    const int nb = K / B;
+    int r = max(1, min(HD_UNITS / nb, M / 256));
+    if (rows_per_wg) *rows_per_wg = r;
+    return (size_t)r * K * (x_dtype == W4A4_F16 ? 2 : 4);
+}
+
+int launch_rotate_quant_hadamard(const void *X, int x_dtype, int M, int K, int64_t ldx, int B,
+                                 const int32_t *perm, const float *table, int step, uint8_t *xq,
+                                 float *x_scale, float *xrot_dbg, hipStream_t s)
+{
+    if (M == 0) return W4A4_OK;
+    int rpw = 1;
+    const size_t lds = hadamard_lds_bytes(M, K, B, x_dtype, &rpw);
+    const int esz = x_dtype == W4A4_F16 ? 2 : 4;
+    const int vec = ((uintptr_t)X % 16 == 0) && ((ldx * esz) % 16 == 0) && ((K * esz) % 16 == 0);
+    const double hinv = 1.0 / std::sqrt((double)B);
+    dim3 grid((M + rpw - 1) / rpw);
+    const bool per_step = table != nullptr;
+#define W4A4_HD_LAUNCH(MODEV, BV, XTV, DV)                                                         \
+    do {                                                                                           \
+        static bool attr_set = false;                                                              \
+        if (lds > 64 * 1024 && !attr_set) {                                                        \
+            hipError_t e = hipFuncSetAttribute((const void *)k_rq_hadamard<MODEV, BV, XTV, DV>,    \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,         \
+                                               HD_MAX_LDS);                                        \
+            if (e != hipSuccess)                                                                   \
+                return fail(W4A4_ERR_HIP, "Hadamard rotate LDS request: %s", hipGetErrorString(e)); \
+            attr_set = true;                                                                       \
+        }                                                                                          \
+        hipLaunchKernelGGL((k_rq_hadamard<MODEV, BV, XTV, DV>), grid, dim3(256), lds, s,           \
+                           reinterpret_cast<const XTV *>(X), ldx, M, K, rpw, vec, hinv, perm,      \
+                           table, step, xq, x_scale, xrot_dbg);                                    \
+    } while (0)
+#define W4A4_HD_D(MODEV, BV, XTV)                                                                  \
+    if (xrot_dbg) W4A4_HD_LAUNCH(MODEV, BV, XTV, true); else W4A4_HD_LAUNCH(MODEV, BV, XTV, false);
+#define W4A4_HD_X(MODEV, BV)                                                                       \
+    if (x_dtype == W4A4_F16) { W4A4_HD_D(MODEV, BV, uint16_t) } else { W4A4_HD_D(MODEV, BV, float) }
+#define W4A4_HD_B(MODEV)                                                                           \
+    if (B == 128) { W4A4_HD_X(MODEV, 128) } else { W4A4_HD_X(MODEV, 64) }
+    if (per_step) { W4A4_HD_B(ACT_PER_STEP) } else { W4A4_HD_B(ACT_TOKEN_QUANT) }
+#undef W4A4_HD_B
+#undef W4A4_HD_X
+#undef W4A4_HD_D
+#undef W4A4_HD_LAUNCH
+    return check_launch("rotate-quantize (Hadamard)");
 }
 
 // Zigzag gather of whole rows: Xp[m][j] = X[m][perm[j]] (fp16), one workgroup per row, the source

@@ -11,8 +11,9 @@
 
 namespace w4a4 {
 
-// One thread per (b, i, j): R64[b][i][j] = sum_l U_b[i][l] * H[l][j], l increasing; also the fp32
-// copy and the fp16 high/low split (MFMA operand order) consumed by the activation kernels.
+// One thread per (b, i, j): R64[b][i][j] = sum_l U_b[i][l] * H[l][j], l increasing (U == NULL
+// stands for U_b = I, giving R_b = H exactly); also the fp32 copy and the fp16 high/low split (MFMA
+// operand order) consumed by the activation kernels.
 __global__ void k_rotation(const float *__restrict__ U, int K, int B, double hinv,
                            double *__restrict__ R64, float *__restrict__ r32,
                            __half *__restrict__ rhi, __half *__restrict__ rlo)
@@ -25,12 +26,16 @@ __global__ void k_rotation(const float *__restrict__ U, int K, int B, double hin
     const int64_t bi = idx / B;  // b * B + i
     const int b = (int)(bi / B);
     const int i = (int)(bi % B);
-    const float *u = U + bi * B;
     double s = 0.0;
-    for (int l = 0; l < B; ++l) {
-        double h = hadamard_negative(l, j) ? -hinv : hinv;
-        double p = (double)u[l] * h;
-        s = s + p;
+    if (U) {
+        const float *u = U + bi * B;
+        for (int l = 0; l < B; ++l) {
+            double h = hadamard_negative(l, j) ? -hinv : hinv;
+            double p = (double)u[l] * h;
+            s = s + p;
+        }
+    } else {
+        s = hadamard_negative(i, j) ? -hinv : hinv;
     }
     R64[idx] = s;
     r32[idx] = (float)s;

@@ -89,6 +89,12 @@ bool act_uses_permute_pass(int M, int K, int per_token);
 size_t act_permute_bytes(int M, int K);
 int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t *perm, uint16_t *xp,
                         uint32_t *zero_row, hipStream_t s);
+// Hadamard-only rotation (U_b = I), B in {64, 128}: LDS bytes of the staged rows (and the rows per
+// workgroup), and the single-kernel rotate-quantize (table == NULL selects per-token scales).
+size_t hadamard_lds_bytes(int M, int K, int B, int x_dtype, int *rows_per_wg);
+int launch_rotate_quant_hadamard(const void *X, int x_dtype, int M, int K, int64_t ldx, int B,
+                                 const int32_t *perm, const float *table, int step, uint8_t *xq,
+                                 float *x_scale, float *xrot_dbg, hipStream_t s);
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
