@@ -1,5 +1,6 @@
 """CPU oracle of the W4A4 quantized linear: zigzag permutation, composite SVD.Hadamard block
-rotation, symmetric int4 RTN / per-step / per-token quantization, integer GEMM and dequantization.
+rotation, symmetric int4 RTN / per-step / per-token quantization, integer GEMM and dequantization;
+the same steps on the int8 grid for the W8A8 linears (``bits=8``).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
 of ``bench.py`` may import this package. It shares no code with the GPU library and never imports
@@ -20,6 +21,8 @@ from .reference import (  # noqa: F401
     weight_rtn,
     pack_int4,
     unpack_int4,
+    pack_codes,
+    BITS_QMAX,
     quantize_act,
     rotate_quant_act,
     int_gemm,

@@ -59,6 +59,9 @@ def _load():
     lib.orc_rotate_rows.argtypes = [_dp, _i64, _i64, _i64, _i64, _i32p, _dp, _dp]
     lib.orc_weight_rtn.argtypes = [_dp, _i64, _i64, _fp, _i8p]
     lib.orc_act_quant.argtypes = [_dp, _i64, _i64, ctypes.c_int, ctypes.c_float, _fp, _fp, _i8p, _fp]
+    lib.orc_weight_rtn_q.argtypes = [_dp, _i64, _i64, ctypes.c_int, _fp, _i8p]
+    lib.orc_act_quant_q.argtypes = [_dp, _i64, _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, _fp,
+                                    _fp, _i8p, _fp]
     lib.orc_pack.argtypes = [_i8p, _i64, _i64, _u8p]
     lib.orc_unpack.argtypes = [_u8p, _i64, _i64, _i8p]
     lib.orc_int_gemm.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i64p]
@@ -67,7 +70,7 @@ def _load():
     lib.orc_gelu.argtypes = [_fp, _i64, _dp]
     for f in ("orc_colnorm2", "orc_hadamard", "orc_rotation", "orc_rotate_rows", "orc_weight_rtn",
               "orc_act_quant", "orc_pack", "orc_unpack", "orc_int_gemm", "orc_int_gemm_sampled",
-              "orc_dequant", "orc_gelu"):
+              "orc_dequant", "orc_gelu", "orc_weight_rtn_q", "orc_act_quant_q"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -194,14 +197,36 @@ def rotate_rows(A, perm, R, B: int) -> np.ndarray:
     return Y
 
 
-def weight_rtn(Wr) -> tuple[np.ndarray, np.ndarray]:
-    """Per-output-channel symmetric int4 RTN of rotated weights: (s_w fp32 [N], codes int8 [N, K])."""
+BITS_QMAX = {4: 7, 8: 127}  # symmetric grids [-(qmax + 1), qmax]
+
+
+def _qmax(bits: int) -> int:
+    if bits not in BITS_QMAX:
+        raise ValueError(f"bits must be 4 or 8, not {bits}")
+    return BITS_QMAX[bits]
+
+
+def weight_rtn(Wr, bits: int = 4) -> tuple[np.ndarray, np.ndarray]:
+    """Per-output-channel symmetric RTN of rotated weights: (s_w fp32 [N], codes int8 [N, K]).
+    bits 4 is the W4A4 grid; bits 8 the W8A8 grid of the FoldQuantVLA summary (key change 5)."""
     Wr = np.ascontiguousarray(np.asarray(Wr, np.float64))
     N, K = Wr.shape
     s_w = np.empty(N, np.float32)
     p = np.empty((N, K), np.int8)
-    _load().orc_weight_rtn(_ptr(Wr, _dp), N, K, _ptr(s_w, _fp), _ptr(p, _i8p))
+    if bits == 4:
+        _load().orc_weight_rtn(_ptr(Wr, _dp), N, K, _ptr(s_w, _fp), _ptr(p, _i8p))
+    else:
+        _load().orc_weight_rtn_q(_ptr(Wr, _dp), N, K, _qmax(bits), _ptr(s_w, _fp), _ptr(p, _i8p))
     return s_w, p
+
+
+def pack_codes(q, bits: int) -> np.ndarray:
+    """Device byte layout of codes: int4 nibble pairs (uint8 [rows, K/2]) or int8 bytes
+    (uint8 [rows, K], two's complement)."""
+    if bits == 4:
+        return pack_int4(q)
+    _qmax(bits)
+    return np.ascontiguousarray(np.asarray(q, np.int8)).view(np.uint8)
 
 
 def pack_int4(q) -> np.ndarray:
@@ -223,7 +248,7 @@ def unpack_int4(packed, K: int) -> np.ndarray:
     return q
 
 
-def pack_weights(W, perm, U, B: int, rows=None) -> dict:
+def pack_weights(W, perm, U, B: int, rows=None, bits: int = 4) -> dict:
     """Offline weight rotate + per-channel RTN + pack (optionally only the given output rows).
 
     W' = W[:, perm] . blockdiag(U_b H_B) in fp64; s_w, codes and packed bytes as in ``weight_rtn``.
@@ -234,12 +259,13 @@ def pack_weights(W, perm, U, B: int, rows=None) -> dict:
     K = W.shape[1]
     R = rotation(U, B)
     Wr = rotate_rows(W, perm, R, B)
-    s_w, p = weight_rtn(Wr)
-    return {"w_rot": Wr, "w_scale": s_w, "codes": p, "wq": pack_int4(p), "R": R}
+    s_w, p = weight_rtn(Wr, bits)
+    return {"w_rot": Wr, "w_scale": s_w, "codes": p, "wq": pack_codes(p, bits), "R": R}
 
 
-def quantize_act(Xr, mode: str, table=None, num_steps: int | None = None, step: int | None = None):
-    """Activation int4 quantization of rotated activations Xr (fp64 [M, K]).
+def quantize_act(Xr, mode: str, table=None, num_steps: int | None = None, step: int | None = None,
+                 bits: int = 4):
+    """Activation quantization (int4, or int8 with bits=8) of rotated activations Xr (fp64 [M, K]).
 
     mode "per_step": s = table[step]; a step outside [0, num_steps) or a table shorter than
       num_steps is an error, never clamped [P3: a step-count mismatch or truncated table is a
@@ -268,17 +294,23 @@ def quantize_act(Xr, mode: str, table=None, num_steps: int | None = None, step: 
     v = np.empty((M, K), np.float32)
     q = np.empty((M, K), np.int8)
     sc = np.empty(M, np.float32)
-    _load().orc_act_quant(_ptr(Xr, _dp), M, K, imode, ts, _ptr(x32, _fp), _ptr(v, _fp),
-                          _ptr(q, _i8p), _ptr(sc, _fp))
-    return {"x32": x32, "v": v, "codes": q, "scale": sc, "xq": pack_int4(q) if K % 2 == 0 else None}
+    if bits == 4:
+        _load().orc_act_quant(_ptr(Xr, _dp), M, K, imode, ts, _ptr(x32, _fp), _ptr(v, _fp),
+                              _ptr(q, _i8p), _ptr(sc, _fp))
+    else:
+        _load().orc_act_quant_q(_ptr(Xr, _dp), M, K, imode, ts, _qmax(bits), _ptr(x32, _fp),
+                                _ptr(v, _fp), _ptr(q, _i8p), _ptr(sc, _fp))
+    xq = pack_codes(q, bits) if (bits == 8 or K % 2 == 0) else None
+    return {"x32": x32, "v": v, "codes": q, "scale": sc, "xq": xq}
 
 
-def rotate_quant_act(X, perm, U, B: int, mode: str, table=None, num_steps=None, step=None, R=None):
-    """Runtime activation path: zigzag gather, block rotation, scale, int4 quantize, pack."""
+def rotate_quant_act(X, perm, U, B: int, mode: str, table=None, num_steps=None, step=None, R=None,
+                     bits: int = 4):
+    """Runtime activation path: zigzag gather, block rotation, scale, quantize (int4 or int8), pack."""
     if R is None:
         R = rotation(U, B)
     Xr = rotate_rows(X, perm, R, B)
-    out = quantize_act(Xr, mode, table, num_steps, step)
+    out = quantize_act(Xr, mode, table, num_steps, step, bits)
     out["x_rot"] = Xr
     return out
 
@@ -343,12 +375,13 @@ def gemm(xq_codes, x_scale, per_token, w_codes, w_scale, epilogue=EPI_NONE, resi
     return {"acc": acc, "Y": Y, "y32": y32}
 
 
-def calibrate_table(X_samples_per_step, perm, U, B: int, R=None) -> np.ndarray:
+def calibrate_table(X_samples_per_step, perm, U, B: int, R=None, bits: int = 4) -> np.ndarray:
     """Per-step act_scale_table from calibration trajectories [P1 "Y tuong paper"; P2 item 2
     "Calibracao por Passo"]. Reading taken: one scale per (linear, step), the absmax statistic over
     every calibration sample, token and channel of the rotated activation, stored as a scale:
-    table[t] = fp32(max |fp32(x')| / 7) (1.0f when the max is 0). X_samples_per_step[t] is a list of
-    [M, K] arrays for step t."""
+    table[t] = fp32(max |fp32(x')| / 7) (1.0f when the max is 0), with 127 in place of 7 for int8
+    activations. X_samples_per_step[t] is a list of [M, K] arrays for step t."""
+    qmax = float(_qmax(bits))
     if R is None:
         R = rotation(U, B)
     T = len(X_samples_per_step)
@@ -358,19 +391,20 @@ def calibrate_table(X_samples_per_step, perm, U, B: int, R=None) -> np.ndarray:
         for Xs in X_samples_per_step[t]:
             x32 = rotate_rows(Xs, perm, R, B).astype(np.float32)
             amax = max(amax, np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0))
-        table[t] = np.float32(float(amax) / 7.0) if amax > 0 else np.float32(1.0)
+        table[t] = np.float32(float(amax) / qmax) if amax > 0 else np.float32(1.0)
     return table
 
 
 def linear(X, W, B: int, mode: str, table=None, num_steps=None, step=None, perm=None, U=None,
-           epilogue=EPI_NONE, residual=None) -> dict:
-    """The whole W4A4 linear on the CPU: offline (perm, U, pack) then runtime (rotate-quant, GEMM)."""
+           epilogue=EPI_NONE, residual=None, bits: int = 4) -> dict:
+    """The whole quantized linear on the CPU (W4A4, or W8A8 with bits=8): offline (perm, U, pack)
+    then runtime (rotate-quant, GEMM)."""
     if perm is None:
         perm = zigzag_perm(W, B)
     if U is None:
         U = block_svd(W, perm, B)
-    pw = pack_weights(W, perm, U, B)
-    act = rotate_quant_act(X, perm, U, B, mode, table, num_steps, step, R=pw["R"])
+    pw = pack_weights(W, perm, U, B, bits=bits)
+    act = rotate_quant_act(X, perm, U, B, mode, table, num_steps, step, R=pw["R"], bits=bits)
     g = gemm(act["codes"], act["scale"], mode == "per_token", pw["codes"], pw["w_scale"],
              epilogue, residual)
     return {"perm": perm, "U": U, "pack": pw, "act": act, **g}

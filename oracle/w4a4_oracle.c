@@ -110,6 +110,60 @@ static int8_t orc_clamp_code(double v)
     return (int8_t)v;
 }
 
+/* The same symmetric grid at another width: codes in [-(qmax + 1), qmax], qmax = 2^(bits-1) - 1
+ * (7 for int4; 127 for the int8 codes of the W8A8 linears that the FoldQuantVLA summary keeps for
+ * the attention-output and FFN-down projections, key change 5). */
+static int8_t orc_clamp_q(double v, int qmax)
+{
+    if (v < -(double)qmax - 1.0) return (int8_t)(-qmax - 1);
+    if (v > (double)qmax) return (int8_t)qmax;
+    return (int8_t)v;
+}
+
+/* Per-output-channel symmetric RTN at width qmax: s_w[n] = fp32(max_k |W'[n][k]| / qmax) (1.0f for a
+ * zero row), p = clamp(rint(W' / s_w), -(qmax + 1), qmax), in fp64. */
+void orc_weight_rtn_q(const double *Wr, int64_t N, int64_t K, int qmax, float *s_w, int8_t *p)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        const double *w = Wr + n * K;
+        double m = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = fabs(w[k]);
+            if (a > m) m = a;
+        }
+        float s = (m > 0.0) ? (float)(m / (double)qmax) : 1.0f;
+        s_w[n] = s;
+        for (int64_t k = 0; k < K; ++k) p[n * K + k] = orc_clamp_q(rint(w[k] / (double)s), qmax);
+    }
+}
+
+/* Activation quantization at width qmax, as orc_act_quant with 7 replaced by qmax:
+ * per-token s_m = fp32(max_k |x32[m][k]| / qmax); q = clamp(rint(fp32(x32 * r)), -(qmax + 1), qmax). */
+void orc_act_quant_q(const double *Xr, int64_t rows, int64_t K, int mode, float table_scale,
+                     int qmax, float *x32, float *v, int8_t *q, float *scale)
+{
+    for (int64_t m = 0; m < rows; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float x = (float)Xr[m * K + k];
+            x32[m * K + k] = x;
+            float a = fabsf(x);
+            if (a > amax) amax = a;
+        }
+        float s;
+        if (mode == 0) s = table_scale;
+        else s = (amax > 0.0f) ? (float)((double)amax / (double)qmax) : 1.0f;
+        scale[m] = s;
+        float r = (float)(1.0 / (double)s);
+        for (int64_t k = 0; k < K; ++k) {
+            float y = x32[m * K + k] * r;
+            v[m * K + k] = y;
+            float t = rintf(y);
+            q[m * K + k] = orc_clamp_q((double)t, qmax);
+        }
+    }
+}
+
 /* Per-output-channel symmetric 4-bit round-to-nearest of the rotated weights
  * [P1 "Build DiT action head pack": --use-rtn --w-bits 4]:
  * s_w[n] = fp32(max_k |W'[n][k]| / 7) (divided in fp64, then rounded once to fp32), 1.0f for an
