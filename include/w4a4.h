@@ -171,6 +171,38 @@ int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * W8A8 linears [radar.vhtltd.com FoldQuantVLA summary, key change 5: the attention-output and FFN
+ * down projections kept at W8A8 raise the real-robot success rate at about 1 ms of latency]: the
+ * same rotation, scales and calls on the symmetric int8 grid. Codes are int8, one per byte, two's
+ * complement, stored [rows][K]; 7 becomes 127 in every scale (s_w[n] = fp32(max |W'| / 127),
+ * per-token s_m = fp32(max |x'| / 127), calibrated table entries fp32(max |x'| / 127)) and codes are
+ * clamp(rint(.), -128, 127). The rotation operand `rot` is the one w4a4_pack_weights_w8 writes (the
+ * same layout as w4a4_pack_weights), and the activation workspace is w4a4_act_workspace_bytes /
+ * w4a4_calibrate_workspace_bytes. Alignment: int8 wq 2 bytes, int8 xq 4 bytes (W4A4_ERR_ALIGN).
+ * GEMM: acc = sum_k q p is exact in int32 for K <= 2^16 (W4A4_ERR_UNSUPPORTED above); K must be a
+ * multiple of 64 (W4A4_ERR_SHAPE) and xq, wq 16-byte aligned (W4A4_ERR_ALIGN); the dequantization
+ * and epilogues are those of w4a4_gemm.
+ * ------------------------------------------------------------------------------------------- */
+int w4a4_pack_weights_w8(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                         const int32_t *perm, const float *U, uint8_t *wq, float *w_scale,
+                         void *rot, void *ws, size_t ws_bytes, hipStream_t stream);
+int w4a4_calibrate_act_scale_a8(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                                const int32_t *perm, const void *rot, float *table_entry,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+int w4a4_rotate_quant_act_a8(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, const float *act_scale_table,
+                             int num_steps, int step, uint8_t *xq, float *x_scale,
+                             float *xrot_dbg, void *ws, size_t ws_bytes, hipStream_t stream);
+size_t w4a4_gemm_w8a8_workspace_bytes(int M, int N, int K);
+int w4a4_gemm_w8a8(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
+                   const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
+                   int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+/* Test hook: int32 accumulators of the int8 GEMM. */
+int w4a4_gemm_w8a8_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Diagnostics (host only).
  * ------------------------------------------------------------------------------------------- */
 const char *w4a4_last_error(void);

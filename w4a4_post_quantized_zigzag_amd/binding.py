@@ -36,6 +36,15 @@ SIGNATURES = {
     "w4a4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
     "w4a4_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz, _vp]),
     "w4a4_gemm_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "w4a4_pack_weights_w8": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                  _vp]),
+    "w4a4_calibrate_act_scale_a8": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "w4a4_rotate_quant_act_a8": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                                      _vp, _vp, _sz, _vp]),
+    "w4a4_gemm_w8a8_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_gemm_w8a8": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz,
+                            _vp]),
+    "w4a4_gemm_w8a8_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_status_string": (ctypes.c_char_p, [_i]),
     "w4a4_abi_version": (_i, []),
@@ -131,41 +140,51 @@ def block_svd(W, perm, block: int):
     return U
 
 
-def pack_weights(W, perm, U, block: int):
-    """Returns (wq uint8 [N, K/2], w_scale fp32 [N], rot uint8 [rot_bytes]). U None: U_b = I."""
+def _code_cols(K: int, bits: int) -> int:
+    if bits not in (4, 8):
+        raise ValueError(f"bits must be 4 or 8, not {bits}")
+    return K // 2 if bits == 4 else K
+
+
+def pack_weights(W, perm, U, block: int, bits: int = 4):
+    """Returns (wq uint8 [N, K/2] (int4) or [N, K] (int8), w_scale fp32 [N], rot uint8 [rot_bytes]).
+    U None: U_b = I."""
     torch = _torch()
     N, K = W.shape
-    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    wq = torch.empty((N, _code_cols(K, bits)), dtype=torch.uint8, device=W.device)
     w_scale = torch.empty(N, dtype=torch.float32, device=W.device)
     rot = torch.empty(lib().w4a4_rot_bytes(K, block), dtype=torch.uint8, device=W.device)
     ws, nb = _ws(lib().w4a4_pack_workspace_bytes(N, K, block), W.device)
-    check(lib().w4a4_pack_weights(_p(W), _dtype_code(W), N, K, _row_stride(W), block, _p(perm),
-                                  _p(U), _p(wq), _p(w_scale), _p(rot), _p(ws), nb, _stream()))
+    fn = lib().w4a4_pack_weights if bits == 4 else lib().w4a4_pack_weights_w8
+    check(fn(_p(W), _dtype_code(W), N, K, _row_stride(W), block, _p(perm), _p(U), _p(wq),
+             _p(w_scale), _p(rot), _p(ws), nb, _stream()))
     return wq, w_scale, rot
 
 
-def calibrate_act_scale(X, perm, rot, block: int, out=None, ws=None):
+def calibrate_act_scale(X, perm, rot, block: int, out=None, ws=None, bits: int = 4):
     """fp32 scale for one (linear, step) entry from stacked calibration activations X [M, K]."""
     torch = _torch()
     M, K = X.shape
+    _code_cols(K, bits)
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=X.device)
     if ws is None:
         ws, nb = _ws(lib().w4a4_calibrate_workspace_bytes(M, K, block), X.device)
     else:
         nb = ws.numel()
-    check(lib().w4a4_calibrate_act_scale(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
-                                         _p(perm), _p(rot), _p(out), _p(ws), nb, _stream()))
+    fn = lib().w4a4_calibrate_act_scale if bits == 4 else lib().w4a4_calibrate_act_scale_a8
+    check(fn(_p(X), _dtype_code(X), M, K, _row_stride(X), block, _p(perm), _p(rot), _p(out), _p(ws),
+             nb, _stream()))
     return out
 
 
 def rotate_quant_act(X, perm, rot, block: int, table=None, num_steps: int = 0, step: int = 0,
-                     xq=None, x_scale=None, xrot_dbg=None, ws=None):
+                     xq=None, x_scale=None, xrot_dbg=None, ws=None, bits: int = 4):
     torch = _torch()
     M, K = X.shape
     per_token = table is None
     if xq is None:
-        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+        xq = torch.empty((M, _code_cols(K, bits)), dtype=torch.uint8, device=X.device)
     if x_scale is None:
         x_scale = torch.empty(max(M, 1) if per_token else 1, dtype=torch.float32, device=X.device)
     need = lib().w4a4_act_workspace_bytes(M, K, block, 1 if per_token else 0)
@@ -173,9 +192,9 @@ def rotate_quant_act(X, perm, rot, block: int, table=None, num_steps: int = 0, s
         ws, nb = _ws(need, X.device)
     else:
         nb = ws.numel()
-    check(lib().w4a4_rotate_quant_act(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
-                                      _p(perm), _p(rot), _p(table), num_steps, step, _p(xq),
-                                      _p(x_scale), _p(xrot_dbg), _p(ws), nb, _stream()))
+    fn = lib().w4a4_rotate_quant_act if bits == 4 else lib().w4a4_rotate_quant_act_a8
+    check(fn(_p(X), _dtype_code(X), M, K, _row_stride(X), block, _p(perm), _p(rot), _p(table),
+             num_steps, step, _p(xq), _p(x_scale), _p(xrot_dbg), _p(ws), nb, _stream()))
     return xq, x_scale
 
 
@@ -196,27 +215,33 @@ def rotate_quant_act_hadamard(X, perm, block: int, table=None, num_steps: int = 
 
 
 def gemm(xq, x_scale, per_token: bool, wq, w_scale, K: int, Y=None, epilogue: int = EPI_NONE,
-         residual=None, ws=None):
+         residual=None, ws=None, bits: int = 4):
+    """W4A4 GEMM (bits 4, packed int4 operands) or W8A8 GEMM (bits 8, int8 operands)."""
     torch = _torch()
     M, N = xq.shape[0], wq.shape[0]
+    _code_cols(K, bits)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=wq.device)
-    need = lib().w4a4_gemm_workspace_bytes(M, N, K)
+    wsb = lib().w4a4_gemm_workspace_bytes if bits == 4 else lib().w4a4_gemm_w8a8_workspace_bytes
+    need = wsb(M, N, K)
     if ws is None:
         ws, nb = _ws(need, wq.device)
     else:
         nb = ws.numel()
     ldr = _row_stride(residual) if residual is not None else 0
-    check(lib().w4a4_gemm(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale), M, N, K,
-                          _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, _p(ws), nb,
-                          _stream()))
+    fn = lib().w4a4_gemm if bits == 4 else lib().w4a4_gemm_w8a8
+    check(fn(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale), M, N, K, _p(Y),
+             _row_stride(Y), epilogue, _p(residual), ldr, _p(ws), nb, _stream()))
     return Y
 
 
-def gemm_i32(xq, wq, K: int):
+def gemm_i32(xq, wq, K: int, bits: int = 4):
     torch = _torch()
     M, N = xq.shape[0], wq.shape[0]
+    _code_cols(K, bits)
     acc = torch.empty((M, N), dtype=torch.int32, device=wq.device)
-    ws, nb = _ws(lib().w4a4_gemm_workspace_bytes(M, N, K), wq.device)
-    check(lib().w4a4_gemm_i32(_p(xq), _p(wq), M, N, K, _p(acc), _p(ws), nb, _stream()))
+    wsb = lib().w4a4_gemm_workspace_bytes if bits == 4 else lib().w4a4_gemm_w8a8_workspace_bytes
+    ws, nb = _ws(wsb(M, N, K), wq.device)
+    fn = lib().w4a4_gemm_i32 if bits == 4 else lib().w4a4_gemm_w8a8_i32
+    check(fn(_p(xq), _p(wq), M, N, K, _p(acc), _p(ws), nb, _stream()))
     return acc

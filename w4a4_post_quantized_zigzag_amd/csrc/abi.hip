@@ -96,7 +96,7 @@ static size_t act_ws_bytes(int M, int K, int B, int kind)
 static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int B,
                           const int32_t *perm, const void *rot, const float *table, int step,
                           int kind, uint8_t *xq, float *x_scale, float *xrot, void *ws,
-                          float *calib_out, hipStream_t s)
+                          float *calib_out, hipStream_t s, bool q8 = false)
 {
     int rc;
     char *w = reinterpret_cast<char *>(ws);
@@ -118,34 +118,34 @@ static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int
         }
         if (kind == KIND_STEP)
             return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
-                                            nullptr, xq, x_scale, xrot, xperm, s);
+                                            nullptr, xq, x_scale, xrot, xperm, q8, s);
         if (kind == KIND_CALIB) {
             if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0,
                                                ACT_CALIB_MAX, rowmax, nullptr, nullptr, nullptr,
-                                               xperm, s)))
+                                               xperm, false, s)))
                 return rc;
-            return launch_scale_from_absmax(rowmax, calib_out, s);
+            return launch_scale_from_absmax(rowmax, calib_out, q8, s);
         }
         if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
-                                           rowmax, nullptr, nullptr, nullptr, xperm, s)))
+                                           rowmax, nullptr, nullptr, nullptr, xperm, false, s)))
             return rc;
         return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
-                                        rowmax, xq, x_scale, xrot, xperm, s);
+                                        rowmax, xq, x_scale, xrot, xperm, q8, s);
     }
     if (kind == KIND_STEP)
         return launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
-                                   nullptr, xq, x_scale, xrot, s);
+                                   nullptr, xq, x_scale, xrot, q8, s);
     if (kind == KIND_CALIB) {
         if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_CALIB_MAX,
-                                      rowmax, nullptr, nullptr, nullptr, s)))
+                                      rowmax, nullptr, nullptr, nullptr, false, s)))
             return rc;
-        return launch_scale_from_absmax(rowmax, calib_out, s);
+        return launch_scale_from_absmax(rowmax, calib_out, q8, s);
     }
     if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
-                                  rowmax, nullptr, nullptr, nullptr, s)))
+                                  rowmax, nullptr, nullptr, nullptr, false, s)))
         return rc;
     return launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
-                               rowmax, xq, x_scale, xrot, s);
+                               rowmax, xq, x_scale, xrot, q8, s);
 }
 
 }  // namespace w4a4
@@ -216,9 +216,9 @@ size_t w4a4_calibrate_workspace_bytes(int M, int K, int block)
     return act_ws_bytes(M, K, block, KIND_CALIB);
 }
 
-int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
-                             const int32_t *perm, const void *rot, float *table_entry,
-                             void *ws, size_t ws_bytes, hipStream_t stream)
+static int calibrate_entry(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                           const int32_t *perm, const void *rot, float *table_entry, void *ws,
+                           size_t ws_bytes, hipStream_t stream, bool q8)
 {
     int rc;
     if ((rc = check_kb(K, block))) return rc;
@@ -229,9 +229,25 @@ int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t l
     if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
     if ((rc = check_ws(ws, ws_bytes, act_ws_bytes(M, K, block, KIND_CALIB)))) return rc;
     if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0, KIND_CALIB,
-                             nullptr, nullptr, nullptr, ws, table_entry, stream)))
+                             nullptr, nullptr, nullptr, ws, table_entry, stream, q8)))
         return rc;
     return ok();
+}
+
+int w4a4_calibrate_act_scale(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, float *table_entry,
+                             void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return calibrate_entry(X, x_dtype, M, K, ldx, block, perm, rot, table_entry, ws, ws_bytes,
+                           stream, false);
+}
+
+int w4a4_calibrate_act_scale_a8(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                                const int32_t *perm, const void *rot, float *table_entry,
+                                void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return calibrate_entry(X, x_dtype, M, K, ldx, block, perm, rot, table_entry, ws, ws_bytes,
+                           stream, true);
 }
 
 // ------------------------------------------------------------------ weight pack
@@ -248,9 +264,9 @@ size_t w4a4_pack_workspace_bytes(int N, int K, int block)
     return align_up((size_t)K * block * sizeof(double), 256) + align_up((size_t)N * 8, 256);
 }
 
-int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+static int pack_entry(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
                       const int32_t *perm, const float *U, uint8_t *wq, float *w_scale, void *rot,
-                      void *ws, size_t ws_bytes, hipStream_t stream)
+                      void *ws, size_t ws_bytes, hipStream_t stream, int bits)
 {
     int rc;
     if ((rc = check_kb(K, block))) return rc;
@@ -266,10 +282,27 @@ int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int
         reinterpret_cast<char *>(ws) + align_up((size_t)K * block * sizeof(double), 256));
     const double hinv = 1.0 / std::sqrt((double)block);
     if ((rc = launch_rotation(U, K, block, hinv, R64, rot, stream))) return rc;
-    if ((rc = launch_weight_pack(W, w_dtype, N, K, ldw, block, perm, R64, rowmax, wq, w_scale,
+    if (bits == 8 && !aligned(wq, 2)) return fail(W4A4_ERR_ALIGN, "int8 wq must be 2-byte aligned");
+    if ((rc = launch_weight_pack(W, w_dtype, N, K, ldw, block, perm, R64, rowmax, wq, w_scale, bits,
                                  stream)))
         return rc;
     return ok();
+}
+
+int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                      const int32_t *perm, const float *U, uint8_t *wq, float *w_scale, void *rot,
+                      void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return pack_entry(W, w_dtype, N, K, ldw, block, perm, U, wq, w_scale, rot, ws, ws_bytes, stream,
+                      4);
+}
+
+int w4a4_pack_weights_w8(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                         const int32_t *perm, const float *U, uint8_t *wq, float *w_scale,
+                         void *rot, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return pack_entry(W, w_dtype, N, K, ldw, block, perm, U, wq, w_scale, rot, ws, ws_bytes, stream,
+                      8);
 }
 
 // ------------------------------------------------------------------ activation path
@@ -280,10 +313,10 @@ size_t w4a4_act_workspace_bytes(int M, int K, int block, int per_token)
     return act_ws_bytes(M, K, block, per_token ? KIND_TOKEN : KIND_STEP);
 }
 
-int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
-                          const int32_t *perm, const void *rot, const float *act_scale_table,
-                          int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                          void *ws, size_t ws_bytes, hipStream_t stream)
+static int rq_entry(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                    const int32_t *perm, const void *rot, const float *act_scale_table,
+                    int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
+                    void *ws, size_t ws_bytes, hipStream_t stream, bool q8)
 {
     int rc;
     if ((rc = check_kb(K, block))) return rc;
@@ -305,11 +338,30 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
     const size_t need = w4a4_act_workspace_bytes(M, K, block, !per_step);
     if ((rc = check_ws(ws, ws_bytes, need))) return rc;
     if (M == 0) return ok();
+    if (q8 && !aligned(xq, 4)) return fail(W4A4_ERR_ALIGN, "int8 xq must be 4-byte aligned");
     if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
                              per_step ? KIND_STEP : KIND_TOKEN, xq, x_scale, xrot_dbg, ws, nullptr,
-                             stream)))
+                             stream, q8)))
         return rc;
     return ok();
+}
+
+int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                          const int32_t *perm, const void *rot, const float *act_scale_table,
+                          int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
+                          void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return rq_entry(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, num_steps, step, xq,
+                    x_scale, xrot_dbg, ws, ws_bytes, stream, false);
+}
+
+int w4a4_rotate_quant_act_a8(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, const float *act_scale_table,
+                             int num_steps, int step, uint8_t *xq, float *x_scale,
+                             float *xrot_dbg, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return rq_entry(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, num_steps, step, xq,
+                    x_scale, xrot_dbg, ws, ws_bytes, stream, true);
 }
 
 int w4a4_rotate_quant_act_hadamard(const void *X, int x_dtype, int M, int K, int64_t ldx,
@@ -351,24 +403,43 @@ int w4a4_rotate_quant_act_hadamard(const void *X, int x_dtype, int M, int K, int
 size_t w4a4_gemm_workspace_bytes(int M, int N, int K)
 {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return gemm_workspace(M, N, K);
+    return gemm_workspace(M, N, K, false);
 }
 
-static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N, int K)
+size_t w4a4_gemm_w8a8_workspace_bytes(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return gemm_workspace(M, N, K, true);
+}
+
+}  // extern "C"
+
+namespace w4a4 {
+
+static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, bool q8)
 {
     if (M < 0 || N <= 0 || K <= 0) return fail(W4A4_ERR_ARG, "bad sizes M=%d N=%d K=%d", M, N, K);
-    if (K % 2) return fail(W4A4_ERR_SHAPE, "K = %d must be even", K);
-    if (K > (1 << 24)) return fail(W4A4_ERR_UNSUPPORTED, "K = %d above 2^24", K);
     if ((M > 0 && !xq) || !wq) return fail(W4A4_ERR_ARG, "xq / wq is NULL");
+    if (!q8) {
+        if (K % 2) return fail(W4A4_ERR_SHAPE, "K = %d must be even", K);
+        if (K > (1 << 24)) return fail(W4A4_ERR_UNSUPPORTED, "K = %d above 2^24", K);
+        return W4A4_OK;
+    }
+    if (K % 64) return fail(W4A4_ERR_SHAPE, "int8 GEMM needs K a multiple of 64, not %d", K);
+    if (K > (1 << 16))
+        return fail(W4A4_ERR_UNSUPPORTED, "int8 GEMM K = %d above 2^16 (int32 sums)", K);
+    if (!aligned(xq, 16) || !aligned(wq, 16))
+        return fail(W4A4_ERR_ALIGN, "int8 operands must be 16-byte aligned");
     return W4A4_OK;
 }
 
-int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, const uint8_t *wq,
-              const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
-              const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream)
+static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
+                      const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
+                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
+                      size_t ws_bytes, hipStream_t stream, bool q8)
 {
     int rc;
-    if ((rc = check_gemm_common(xq, wq, M, N, K))) return rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K, q8))) return rc;
     if (epilogue != W4A4_EPI_NONE && epilogue != W4A4_EPI_GELU && epilogue != W4A4_EPI_RESIDUAL)
         return fail(W4A4_ERR_ARG, "unknown epilogue %d", epilogue);
     if (!w_scale || (M > 0 && (!x_scale || !Y)))
@@ -381,7 +452,7 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
     }
     if (!aligned(Y, 2) || !aligned(x_scale, 4) || !aligned(w_scale, 4))
         return fail(W4A4_ERR_ALIGN, "Y / scales misaligned");
-    if ((rc = check_ws(ws, ws_bytes, w4a4_gemm_workspace_bytes(M, N, K)))) return rc;
+    if ((rc = check_ws(ws, ws_bytes, M > 0 ? gemm_workspace(M, N, K, q8) : 0))) return rc;
     if (M == 0) return ok();
     GemmEpilogue epi{};
     epi.x_scale = x_scale;
@@ -392,24 +463,57 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
     epi.mode = epilogue;
     epi.residual = residual;
     epi.ldr = ldr;
-    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream))) return rc;
+    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8))) return rc;
     return ok();
+}
+
+static int gemm_i32_entry(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
+                          void *ws, size_t ws_bytes, hipStream_t stream, bool q8)
+{
+    int rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K, q8))) return rc;
+    if (M > 0 && !acc) return fail(W4A4_ERR_ARG, "acc is NULL");
+    if (!aligned(acc, 4)) return fail(W4A4_ERR_ALIGN, "acc misaligned");
+    if ((rc = check_ws(ws, ws_bytes, M > 0 ? gemm_workspace(M, N, K, q8) : 0))) return rc;
+    if (M == 0) return ok();
+    GemmEpilogue epi{};
+    epi.mode = GEMM_OUT_I32;
+    epi.acc_out = acc;
+    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8))) return rc;
+    return ok();
+}
+
+}  // namespace w4a4
+
+extern "C" {
+
+int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, const uint8_t *wq,
+              const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
+              const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
+                      residual, ldr, ws, ws_bytes, stream, false);
 }
 
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
                   void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    int rc;
-    if ((rc = check_gemm_common(xq, wq, M, N, K))) return rc;
-    if (M > 0 && !acc) return fail(W4A4_ERR_ARG, "acc is NULL");
-    if (!aligned(acc, 4)) return fail(W4A4_ERR_ALIGN, "acc misaligned");
-    if ((rc = check_ws(ws, ws_bytes, w4a4_gemm_workspace_bytes(M, N, K)))) return rc;
-    if (M == 0) return ok();
-    GemmEpilogue epi{};
-    epi.mode = GEMM_OUT_I32;
-    epi.acc_out = acc;
-    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream))) return rc;
-    return ok();
+    return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, false);
+}
+
+int w4a4_gemm_w8a8(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
+                   const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
+                   int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
+                   size_t ws_bytes, hipStream_t stream)
+{
+    return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
+                      residual, ldr, ws, ws_bytes, stream, true);
+}
+
+int w4a4_gemm_w8a8_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
+                       void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

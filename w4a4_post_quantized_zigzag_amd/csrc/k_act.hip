@@ -31,27 +31,32 @@ __device__ __forceinline__ float step_scale(const float *table, int step)
     return (s > 0.0f && s <= 3.402823466e38f) ? s : 1.0f;
 }
 
-// fp32(max / 7) divided in fp64 (exactly the fp32 quotient, the double rounding being innocuous
-// for an fp32 dividend); 1.0f for a zero max.
-__device__ __forceinline__ float scale_from_absmax(float amax)
+// fp32(max / qmax) divided in fp64 (exactly the fp32 quotient, the double rounding being innocuous
+// for an fp32 dividend); 1.0f for a zero max. qmax = 7 for int4 codes, 127 for the int8 codes of
+// the W8A8 linears (Q8).
+template <bool Q8>
+__device__ __forceinline__ float scale_from_absmax_q(float amax)
 {
-    return amax > 0.0f ? (float)((double)amax / 7.0) : 1.0f;
+    return amax > 0.0f ? (float)((double)amax / (Q8 ? 127.0 : 7.0)) : 1.0f;
 }
+__device__ __forceinline__ float scale_from_absmax(float amax) { return scale_from_absmax_q<false>(amax); }
 
-__device__ __forceinline__ int quant_code(float x, float r)
+template <bool Q8>
+__device__ __forceinline__ int quant_code_q(float x, float r)
 {
     float y = x * r;
     float t = rintf(y);
-    t = fminf(fmaxf(t, -8.0f), 7.0f);
+    t = fminf(fmaxf(t, Q8 ? -128.0f : -8.0f), Q8 ? 127.0f : 7.0f);
     return (int)t;
 }
+__device__ __forceinline__ int quant_code(float x, float r) { return quant_code_q<false>(x, r); }
 
 // Workgroup = RQ_ROWS rows x one chunk of up to 256 positions (whole blocks); 128 threads, each
 // owning two adjacent positions (one output byte).
 constexpr int RQ_ROWS = 8;
 constexpr int RQ_CHUNK = 256;
 
-template <int MODE>
+template <int MODE, bool Q8>
 __global__ __launch_bounds__(128) void k_rotate_quant_valu(
     const void *__restrict__ X, int xdt, int M, int K, int64_t ldx, int B,
     const int32_t *__restrict__ perm, const float *__restrict__ R32, const float *__restrict__ table,
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(128) void k_rotate_quant_valu(
         if (m >= M) continue;
         float s;
         if (MODE == ACT_PER_STEP) s = step_scale(table, step);
-        else s = scale_from_absmax(__uint_as_float(rowmax[m]));
+        else s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[m]));
         if (blockIdx.y == 0 && tid == 0) {
             if (MODE == ACT_PER_STEP) {
                 if (blockIdx.x == 0 && r == 0) x_scale[0] = s;
@@ -142,39 +147,39 @@ __global__ __launch_bounds__(128) void k_rotate_quant_valu(
         }
         if (!active) continue;
         const float rcp = (float)(1.0 / (double)s);
-        const int q0 = quant_code(acc[r][0], rcp);
-        const int q1 = quant_code(acc[r][1], rcp);
-        xq[(int64_t)m * (K / 2) + kp / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+        const int q0 = quant_code_q<Q8>(acc[r][0], rcp);
+        const int q1 = quant_code_q<Q8>(acc[r][1], rcp);
+        if (Q8)
+            *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * K + kp]) =
+                (uint16_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8));
+        else
+            xq[(int64_t)m * (K / 2) + kp / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
     }
 }
 
 int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B,
                         const int32_t *perm, const void *rot, const float *table, int step,
                         ActMode mode, uint32_t *rowmax, uint8_t *xq, float *x_scale,
-                        float *xrot_dbg, hipStream_t s)
+                        float *xrot_dbg, bool q8, hipStream_t s)
 {
     if (M == 0) return W4A4_OK;
     const float *R32 = reinterpret_cast<const float *>(rot);
     dim3 grid((M + RQ_ROWS - 1) / RQ_ROWS, (K + RQ_CHUNK - 1) / RQ_CHUNK);
     dim3 block(RQ_CHUNK / 2);
+#define W4A4_VALU(MODEV, QV)                                                                       \
+    hipLaunchKernelGGL((k_rotate_quant_valu<MODEV, QV>), grid, block, 0, s, X, xdt, M, K, ldx, B,  \
+                       perm, R32, table, step, rowmax, xq, x_scale, xrot_dbg)
     switch (mode) {
     case ACT_PER_STEP:
-        hipLaunchKernelGGL(k_rotate_quant_valu<ACT_PER_STEP>, grid, block, 0, s, X, xdt, M, K, ldx,
-                           B, perm, R32, table, step, rowmax, xq, x_scale, xrot_dbg);
+        if (q8) W4A4_VALU(ACT_PER_STEP, true); else W4A4_VALU(ACT_PER_STEP, false);
         break;
-    case ACT_TOKEN_MAX:
-        hipLaunchKernelGGL(k_rotate_quant_valu<ACT_TOKEN_MAX>, grid, block, 0, s, X, xdt, M, K, ldx,
-                           B, perm, R32, table, step, rowmax, xq, x_scale, xrot_dbg);
-        break;
+    case ACT_TOKEN_MAX: W4A4_VALU(ACT_TOKEN_MAX, false); break;
     case ACT_TOKEN_QUANT:
-        hipLaunchKernelGGL(k_rotate_quant_valu<ACT_TOKEN_QUANT>, grid, block, 0, s, X, xdt, M, K,
-                           ldx, B, perm, R32, table, step, rowmax, xq, x_scale, xrot_dbg);
+        if (q8) W4A4_VALU(ACT_TOKEN_QUANT, true); else W4A4_VALU(ACT_TOKEN_QUANT, false);
         break;
-    case ACT_CALIB_MAX:
-        hipLaunchKernelGGL(k_rotate_quant_valu<ACT_CALIB_MAX>, grid, block, 0, s, X, xdt, M, K, ldx,
-                           B, perm, R32, table, step, rowmax, xq, x_scale, xrot_dbg);
-        break;
+    case ACT_CALIB_MAX: W4A4_VALU(ACT_CALIB_MAX, false); break;
     }
+#undef W4A4_VALU
     return check_launch("rotate-quantize");
 }
 
@@ -192,7 +197,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int MT = 64;  // token rows per tile
 
-template <int MODE, int B, bool GATHER>
+template <int MODE, int B, bool GATHER, bool Q8>
 __global__ __launch_bounds__(256) void k_rq_mfma(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const int32_t *__restrict__ perm,
     const _Float16 *__restrict__ rhi, const _Float16 *__restrict__ rlo,
@@ -328,14 +333,20 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
             }
             float rcp = rcp_step;
             if (MODE == ACT_TOKEN_QUANT) {
-                const float s = scale_from_absmax(__uint_as_float(rowmax[m]));
+                const float s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[m]));
                 rcp = (float)(1.0 / (double)s);
                 if (b == 0 && wave == 0 && g == 0) x_scale[m] = s;
             }
 #pragma unroll
             for (int jf = 0; jf < JF; ++jf) {
-                const int q0 = quant_code(v[jf][0], rcp), q1 = quant_code(v[jf][1], rcp);
-                const int q2 = quant_code(v[jf][2], rcp), q3 = quant_code(v[jf][3], rcp);
+                const int q0 = quant_code_q<Q8>(v[jf][0], rcp), q1 = quant_code_q<Q8>(v[jf][1], rcp);
+                const int q2 = quant_code_q<Q8>(v[jf][2], rcp), q3 = quant_code_q<Q8>(v[jf][3], rcp);
+                if (Q8) {
+                    *reinterpret_cast<uint32_t *>(&xq[(int64_t)m * K + jcol + 16 * jf]) =
+                        (uint32_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) |
+                                   ((uint32_t)(q3 & 0xFF) << 24));
+                    continue;
+                }
                 const uint16_t packed = (uint16_t)((q0 & 0xF) | ((q1 & 0xF) << 4) |
                                                    ((q2 & 0xF) << 8) | ((q3 & 0xF) << 12));
                 *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * (K / 2) + (jcol + 16 * jf) / 2]) = packed;
@@ -401,24 +412,29 @@ __device__ __forceinline__ void rq_wait_vmcnt(int n)
 // give a nonzero code). Adding 1.5 * 2^23 rounds that product to an integer, ties to even, and
 // leaves the integer in the low mantissa bits; the clamp to [-8, 7] is applied in that form and
 // the two's-complement nibble is read off the bit pattern.
+// Q8: int8 codes, clamp to [-128, 127] and one byte per code (four bytes returned).
+template <bool Q8 = false>
 __device__ __forceinline__ uint32_t quant_pack4(v4f acc, float rs)
 {
 #pragma clang fp contract(off)
     constexpr float MAGIC = 12582912.0f;
+    constexpr float LOQ = Q8 ? -128.0f : -8.0f, HIQ = Q8 ? 127.0f : 7.0f;
     uint32_t n[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float y = acc[i] * rs;
         float f = y + MAGIC;
-        f = fminf(fmaxf(f, MAGIC - 8.0f), MAGIC + 7.0f);
+        f = fminf(fmaxf(f, MAGIC + LOQ), MAGIC + HIQ);
         n[i] = __float_as_uint(f);
     }
+    if (Q8)
+        return (n[0] & 0xFFu) | ((n[1] & 0xFFu) << 8) | ((n[2] & 0xFFu) << 16) | (n[3] << 24);
     uint32_t t = (n[0] & 0xFu) | ((n[1] << 4) & ~0xFu);
     t = (t & 0xFFu) | ((n[2] << 8) & ~0xFFu);
     return (t & 0xFFFu) | ((n[3] << 12) & ~0xFFFu);
 }
 
-template <int MODE, int B, bool DBG>
+template <int MODE, int B, bool DBG, bool Q8>
 __global__ __launch_bounds__(256) void k_rq_ring(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const _Float16 *__restrict__ rhi,
     const _Float16 *__restrict__ rlo, const float *__restrict__ table, int step,
@@ -434,8 +450,9 @@ __global__ __launch_bounds__(256) void k_rq_ring(
     constexpr int TILE = MT * ROWB;               // bytes per tile
     constexpr int QPW = TILE / 1024 / 4;          // DMA instructions per wave per tile
     constexpr int RPI = 1024 / ROWB;              // rows per DMA instruction
-    constexpr int OB = B / 2;                     // packed output bytes per row of one block
+    constexpr int OB = Q8 ? B : B / 2;            // output code bytes per row of one block
     constexpr int OCH = MT * OB / 16;             // 16-byte output chunks per tile
+    const int64_t ldq = Q8 ? K : K / 2;           // output row stride in bytes
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
     __shared__ float smax[4][MT];
     __shared__ __attribute__((aligned(16))) uint8_t sq[MT * OB];
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
     // load inside the tile loop would make the compiler wait for every DMA issued before it
     if (MODE == ACT_TOKEN_QUANT) {
         for (int i = tid; i < row_end - row_begin; i += 256) {
-            const float s = scale_from_absmax(__uint_as_float(rowmax[row_begin + i]));
+            const float s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[row_begin + i]));
             srcp[i] = (float)(1.0 / (double)s) * LO;
             if (b == 0) x_scale[row_begin + i] = s;
         }
@@ -573,9 +590,14 @@ __global__ __launch_bounds__(256) void k_rq_ring(
             }
             const float rs = (MODE == ACT_TOKEN_QUANT) ? srcp[min(m, row_end - 1) - row_begin] : rs_step;
 #pragma unroll
-            for (int jf = 0; jf < JF; ++jf)
-                *reinterpret_cast<uint16_t *>(&sq[row * OB + (jl + 16 * jf) / 2]) =
-                    (uint16_t)quant_pack4(acc[mf][jf], rs);
+            for (int jf = 0; jf < JF; ++jf) {
+                if (Q8)
+                    *reinterpret_cast<uint32_t *>(&sq[row * OB + jl + 16 * jf]) =
+                        quant_pack4<true>(acc[mf][jf], rs);
+                else
+                    *reinterpret_cast<uint16_t *>(&sq[row * OB + (jl + 16 * jf) / 2]) =
+                        (uint16_t)quant_pack4(acc[mf][jf], rs);
+            }
         }
         // Tile epilogue after every wave's LDS writes (lgkmcnt(0) + plain barrier; the next write
         // to smax / sq comes after the next tile's barrier, by which time these reads are consumed)
@@ -591,12 +613,14 @@ __global__ __launch_bounds__(256) void k_rq_ring(
                     if (tid == 0) atomicMax(&rowmax[0], __float_as_uint(u));
                 }
             }
-        } else if (tid < OCH) {
-            // packed codes of the tile: one 16-byte store per thread (OB / 16 chunks per row)
-            const int row = tid / (OB / 16), ch = tid % (OB / 16);
-            if (m0 + row < row_end)
-                *reinterpret_cast<uint4 *>(&xq[(int64_t)(m0 + row) * (K / 2) + b * OB + 16 * ch]) =
-                    *reinterpret_cast<const uint4 *>(&sq[row * OB + 16 * ch]);
+        } else {
+            // codes of the tile: 16-byte stores (OB / 16 chunks per row)
+            for (int e = tid; e < OCH; e += 256) {
+                const int row = e / (OB / 16), ch = e % (OB / 16);
+                if (m0 + row < row_end)
+                    *reinterpret_cast<uint4 *>(&xq[(int64_t)(m0 + row) * ldq + b * OB + 16 * ch]) =
+                        *reinterpret_cast<const uint4 *>(&sq[row * OB + 16 * ch]);
+            }
         }
     }
 }
@@ -609,7 +633,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
 // block's output channels. The slice's inputs X[m][perm[b*B + i]] are gathered with 2-byte loads
 // (no permuted copy, no alignment needed; copying whole rows to LDS first moves more bytes per CU
 // and measured slower) and staged in LDS as the MFMA B operand.
-template <int MODE, int B, bool DBG>
+template <int MODE, int B, bool DBG, bool Q8>
 __global__ __launch_bounds__(256) void k_rq_small(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const int32_t *__restrict__ perm,
     const _Float16 *__restrict__ rhi, const _Float16 *__restrict__ rlo,
@@ -720,14 +744,19 @@ __global__ __launch_bounds__(256) void k_rq_small(
                 make_float4(acc[jf][0] * LO, acc[jf][1] * LO, acc[jf][2] * LO, acc[jf][3] * LO);
     }
     if (MODE == ACT_TOKEN_QUANT) {
-        const float s = scale_from_absmax(__uint_as_float(rowmax[m]));
+        const float s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[m]));
         rs = (float)(1.0 / (double)s) * LO;
         if (b == 0 && wave == 0 && g == 0) x_scale[m] = s;
     }
 #pragma unroll
-    for (int jf = 0; jf < JF; ++jf)
-        *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * (K / 2) + (b * B + jl + 16 * jf) / 2]) =
-            (uint16_t)quant_pack4(acc[jf], rs);
+    for (int jf = 0; jf < JF; ++jf) {
+        if (Q8)
+            *reinterpret_cast<uint32_t *>(&xq[(int64_t)m * K + b * B + jl + 16 * jf]) =
+                quant_pack4<true>(acc[jf], rs);
+        else
+            *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * (K / 2) + (b * B + jl + 16 * jf) / 2]) =
+                (uint16_t)quant_pack4(acc[jf], rs);
+    }
 }
 
 // ------------------------------------------------------------------ Hadamard-only rotation
@@ -1019,7 +1048,7 @@ static int rq_rows_per_wg(int M, int nb)
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                             const uint16_t *xperm, hipStream_t s)
+                             const uint16_t *xperm, bool q8, hipStream_t s)
 {
     if (M == 0) return W4A4_OK;
     RotLayout L = rot_layout(K, B);
@@ -1027,24 +1056,26 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
     const _Float16 *rhi = reinterpret_cast<const _Float16 *>(base + L.r32);
     const _Float16 *rlo = reinterpret_cast<const _Float16 *>(base + L.r32 + L.r16);
     const int nb = K / B;
+    // Every family below is instantiated for both code widths in the quantizing modes (per-step,
+    // per-token second pass) and for int4 only in the max-only passes, which write no codes.
     if (M <= RQ_SMALL_M && !xperm) {
         dim3 grid_s(((M + 15) / 16) * nb);
         const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
-#define W4A4_SMALL(MODEV, BV, DV)                                                                  \
-    hipLaunchKernelGGL((k_rq_small<MODEV, BV, DV>), grid_s, dim3(256), 0, s, x, ldx, M, K, perm,   \
-                       rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg)
-#define W4A4_SMALL_B(MODEV)                                                                        \
-    if (B == 128) W4A4_SMALL(MODEV, 128, false); else W4A4_SMALL(MODEV, 64, false);
-#define W4A4_SMALL_BD(MODEV)                                                                       \
-    if (xrot_dbg) { if (B == 128) W4A4_SMALL(MODEV, 128, true); else W4A4_SMALL(MODEV, 64, true); } \
-    else { W4A4_SMALL_B(MODEV) }
+#define W4A4_SMALL(MODEV, BV, DV, QV)                                                              \
+    hipLaunchKernelGGL((k_rq_small<MODEV, BV, DV, QV>), grid_s, dim3(256), 0, s, x, ldx, M, K,     \
+                       perm, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg)
+#define W4A4_SMALL_B(MODEV, DV, QV)                                                                \
+    if (B == 128) W4A4_SMALL(MODEV, 128, DV, QV); else W4A4_SMALL(MODEV, 64, DV, QV);
+#define W4A4_SMALL_Q(MODEV)                                                                        \
+    if (xrot_dbg) { if (q8) { W4A4_SMALL_B(MODEV, true, true) } else { W4A4_SMALL_B(MODEV, true, false) } } \
+    else { if (q8) { W4A4_SMALL_B(MODEV, false, true) } else { W4A4_SMALL_B(MODEV, false, false) } }
         switch (mode) {
-        case ACT_PER_STEP: W4A4_SMALL_BD(ACT_PER_STEP) break;
-        case ACT_TOKEN_MAX: W4A4_SMALL_B(ACT_TOKEN_MAX) break;
-        case ACT_TOKEN_QUANT: W4A4_SMALL_BD(ACT_TOKEN_QUANT) break;
-        case ACT_CALIB_MAX: W4A4_SMALL_B(ACT_CALIB_MAX) break;
+        case ACT_PER_STEP: W4A4_SMALL_Q(ACT_PER_STEP) break;
+        case ACT_TOKEN_MAX: W4A4_SMALL_B(ACT_TOKEN_MAX, false, false) break;
+        case ACT_TOKEN_QUANT: W4A4_SMALL_Q(ACT_TOKEN_QUANT) break;
+        case ACT_CALIB_MAX: W4A4_SMALL_B(ACT_CALIB_MAX, false, false) break;
         }
-#undef W4A4_SMALL_BD
+#undef W4A4_SMALL_Q
 #undef W4A4_SMALL_B
 #undef W4A4_SMALL
         return check_launch("rotate-quantize (few tokens)");
@@ -1063,47 +1094,50 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         const int groups = (M + rpw_r - 1) / rpw_r;
         dim3 grid_r(groups * nb);
         const size_t lds = (size_t)RQ_STAGES * MT * B * sizeof(uint16_t);
-#define W4A4_RING(MODEV, BV, DV)                                                                   \
+#define W4A4_RING(MODEV, BV, DV, QV)                                                               \
     do {                                                                                           \
         static bool attr_set = false;                                                              \
         if (!attr_set) {                                                                           \
-            hipError_t e = hipFuncSetAttribute((const void *)k_rq_ring<MODEV, BV, DV>,             \
+            hipError_t e = hipFuncSetAttribute((const void *)k_rq_ring<MODEV, BV, DV, QV>,         \
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
             if (e != hipSuccess)                                                                   \
                 return fail(W4A4_ERR_HIP, "rotate-quantize LDS request: %s", hipGetErrorString(e)); \
             attr_set = true;                                                                       \
         }                                                                                          \
-        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV>), grid_r, dim3(256), lds, s, src, ld, M, K,   \
-                           rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r, groups);   \
+        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV>), grid_r, dim3(256), lds, s, src, ld, M,  \
+                           K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r, groups); \
     } while (0)
-#define W4A4_RING_B(MODEV)                                                                         \
-    if (B == 128) W4A4_RING(MODEV, 128, false); else W4A4_RING(MODEV, 64, false);
-#define W4A4_RING_BD(MODEV)                                                                        \
-    if (xrot_dbg) { if (B == 128) W4A4_RING(MODEV, 128, true); else W4A4_RING(MODEV, 64, true); }  \
-    else { W4A4_RING_B(MODEV) }
+#define W4A4_RING_B(MODEV, DV, QV)                                                                 \
+    if (B == 128) W4A4_RING(MODEV, 128, DV, QV); else W4A4_RING(MODEV, 64, DV, QV);
+#define W4A4_RING_Q(MODEV)                                                                         \
+    if (xrot_dbg) { if (q8) { W4A4_RING_B(MODEV, true, true) } else { W4A4_RING_B(MODEV, true, false) } } \
+    else { if (q8) { W4A4_RING_B(MODEV, false, true) } else { W4A4_RING_B(MODEV, false, false) } }
         switch (mode) {
-        case ACT_PER_STEP: W4A4_RING_BD(ACT_PER_STEP) break;
-        case ACT_TOKEN_MAX: W4A4_RING_B(ACT_TOKEN_MAX) break;
-        case ACT_TOKEN_QUANT: W4A4_RING_BD(ACT_TOKEN_QUANT) break;
-        case ACT_CALIB_MAX: W4A4_RING_B(ACT_CALIB_MAX) break;
+        case ACT_PER_STEP: W4A4_RING_Q(ACT_PER_STEP) break;
+        case ACT_TOKEN_MAX: W4A4_RING_B(ACT_TOKEN_MAX, false, false) break;
+        case ACT_TOKEN_QUANT: W4A4_RING_Q(ACT_TOKEN_QUANT) break;
+        case ACT_CALIB_MAX: W4A4_RING_B(ACT_CALIB_MAX, false, false) break;
         }
-#undef W4A4_RING_BD
+#undef W4A4_RING_Q
 #undef W4A4_RING_B
 #undef W4A4_RING
         return check_launch("rotate-quantize (ring)");
     }
-#define W4A4_RQ(MODEV, BV, GV)                                                                     \
-    hipLaunchKernelGGL((k_rq_mfma<MODEV, BV, GV>), grid, dim3(256), 0, s, src, ld, M, K, perm, rhi, \
-                       rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw)
-#define W4A4_RQ_B(MODEV)                                                                           \
-    if (B == 128) { if (gather) W4A4_RQ(MODEV, 128, true); else W4A4_RQ(MODEV, 128, false); }      \
-    else { if (gather) W4A4_RQ(MODEV, 64, true); else W4A4_RQ(MODEV, 64, false); }
+#define W4A4_RQ(MODEV, BV, GV, QV)                                                                 \
+    hipLaunchKernelGGL((k_rq_mfma<MODEV, BV, GV, QV>), grid, dim3(256), 0, s, src, ld, M, K, perm, \
+                       rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw)
+#define W4A4_RQ_B(MODEV, QV)                                                                       \
+    if (B == 128) { if (gather) W4A4_RQ(MODEV, 128, true, QV); else W4A4_RQ(MODEV, 128, false, QV); } \
+    else { if (gather) W4A4_RQ(MODEV, 64, true, QV); else W4A4_RQ(MODEV, 64, false, QV); }
+#define W4A4_RQ_Q(MODEV)                                                                           \
+    if (q8) { W4A4_RQ_B(MODEV, true) } else { W4A4_RQ_B(MODEV, false) }
     switch (mode) {
-    case ACT_PER_STEP: W4A4_RQ_B(ACT_PER_STEP) break;
-    case ACT_TOKEN_MAX: W4A4_RQ_B(ACT_TOKEN_MAX) break;
-    case ACT_TOKEN_QUANT: W4A4_RQ_B(ACT_TOKEN_QUANT) break;
-    case ACT_CALIB_MAX: W4A4_RQ_B(ACT_CALIB_MAX) break;
+    case ACT_PER_STEP: W4A4_RQ_Q(ACT_PER_STEP) break;
+    case ACT_TOKEN_MAX: W4A4_RQ_B(ACT_TOKEN_MAX, false) break;
+    case ACT_TOKEN_QUANT: W4A4_RQ_Q(ACT_TOKEN_QUANT) break;
+    case ACT_CALIB_MAX: W4A4_RQ_B(ACT_CALIB_MAX, false) break;
     }
+#undef W4A4_RQ_Q
 #undef W4A4_RQ_B
 #undef W4A4_RQ
     return check_launch("rotate-quantize (mfma)");
@@ -1131,14 +1165,15 @@ int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t 
     return check_launch("permute rows");
 }
 
-__global__ void k_scale_from_absmax(const uint32_t *amax, float *out)
+__global__ void k_scale_from_absmax(const uint32_t *amax, float *out, int q8)
 {
-    out[0] = scale_from_absmax(__uint_as_float(amax[0]));
+    out[0] = q8 ? scale_from_absmax_q<true>(__uint_as_float(amax[0]))
+                : scale_from_absmax(__uint_as_float(amax[0]));
 }
 
-int launch_scale_from_absmax(const uint32_t *amax, float *out, hipStream_t s)
+int launch_scale_from_absmax(const uint32_t *amax, float *out, bool q8, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_scale_from_absmax, dim3(1), dim3(1), 0, s, amax, out);
+    hipLaunchKernelGGL(k_scale_from_absmax, dim3(1), dim3(1), 0, s, amax, out, q8 ? 1 : 0);
     return check_launch("scale from absmax");
 }
 

@@ -116,9 +116,11 @@ __device__ __forceinline__ void store_output(const GemmEpilogue &epi, int m, int
 // bytes of its operand row per window (lane = row (lane % 16) x k-quarter (lane / 16)) and widens
 // them into the two int8 operands of two v_mfma_i32_16x16x64_i8; both operands use the same
 // widening, so each MFMA pairs identical k. The 4 partial tiles are added exactly in LDS.
-constexpr int SM_CHUNK = 4;  // 128-k windows whose loads are in flight together
+// Q8: int8 operands (W8A8), one code per byte: a 64-byte window is 64 k and its 16 bytes per lane
+// are already the MFMA operand, so there is one MFMA per window and no scaling by 256.
+constexpr int SM_CHUNK = 4;  // 64-byte windows whose loads are in flight together
 
-template <int MF, bool VEC>
+template <int MF, bool VEC, bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__ xq,
                                                      const uint8_t *__restrict__ wq, int M, int N,
                                                      int K, GemmEpilogue epi)
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16;
-    const int ldp = K / 2;
+    const int ldp = Q8 ? K : K / 2;  // bytes per operand row
     const int windows = (ldp + 63) / 64;
     const int per_wave = (windows + 3) / 4;
     const int w_begin = wave * per_wave, w_end = min(windows, w_begin + per_wave);
@@ -185,6 +187,17 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
 #pragma unroll
         for (int c = 0; c < SM_CHUNK; ++c) {
             if (c >= nc) continue;
+            if (Q8) {
+                uint4 b = zero_unless(bq[c], bv[c]);
+#pragma unroll
+                for (int f = 0; f < MF; ++f) {
+                    uint4 a = zero_unless(aq[c][f], av[c][f]);
+                    acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<v4i *>(&a),
+                                                                   *reinterpret_cast<v4i *>(&b),
+                                                                   acc[f], 0, 0, 0);
+                }
+                continue;
+            }
             uint4 b0, b1;
             widen16(zero_unless(bq[c], bv[c]), b0, b1);
 #pragma unroll
@@ -199,9 +212,10 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
                                                                acc[f], 0, 0, 0);
             }
         }
-        // fold the chunk (at most 512 k, so 256 * 64 * 512 fits) into the exact running sum
+        // fold the chunk (at most 512 k, so 256 * 64 * 512 fits) into the exact running sum;
+        // int8 sums are exact as they stand
 #pragma unroll
-        for (int f = 0; f < MF; ++f) total[f] += acc[f] >> 8;
+        for (int f = 0; f < MF; ++f) total[f] += Q8 ? acc[f] : (acc[f] >> 8);
     }
 #pragma unroll
     for (int f = 0; f < MF; ++f)
@@ -437,7 +451,10 @@ __device__ __forceinline__ void wait_vmcnt(int n)
 enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_RESIDUAL,
        PE_INT32 = 3 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT>
+// Q8: int8 operands (W8A8): a staged 64-byte row is 64 k, each fragment read is already an MFMA
+// operand (one v_mfma_i32_16x16x64_i8 per fragment pair and stage, no widening) and the sums are
+// not scaled by 256.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT, bool Q8>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
     int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
@@ -448,21 +465,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     constexpr int A_BYTES = BM * BG_ROWB, B_BYTES = BN * BG_ROWB, STAGE = A_BYTES + B_BYTES;
     constexpr int QA = A_BYTES / 1024 / NW, QB = B_BYTES / 1024 / NW;  // DMA instrs per wave
     constexpr int L = QA + QB;
+    constexpr int SHIFT = Q8 ? 0 : 8;  // int4 operands enter the MFMA as 16 * code
     static_assert(QA * 1024 * NW == A_BYTES && QB * 1024 * NW == B_BYTES, "whole KB per wave");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int T = tiles_m * tiles_n;
     const int id = blockIdx.x;
-    const int q8 = T / 8, rm = T % 8, x = id % 8;
-    const int lin = x * q8 + min(x, rm) + id / 8;
+    const int per_x = T / 8, rm = T % 8, x = id % 8;
+    const int lin = x * per_x + min(x, rm) + id / 8;
     const int tn = lin / tiles_m, tm = lin % tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int ldp = K / 2;
-    const int kb_begin = blockIdx.y * (k_split / 2);
-    const int kb_end = min(kb_begin + k_split / 2, ldp);
+    const int ldp = Q8 ? K : K / 2;  // bytes per operand row
+    const int split_bytes = Q8 ? k_split : k_split / 2;
+    const int kb_begin = blockIdx.y * split_bytes;
+    const int kb_end = min(kb_begin + split_bytes, ldp);
     const int stages = (kb_end - kb_begin) / BG_ROWB;
 
     // per-lane DMA sources: instruction q of this wave covers staged rows (wave*Q + q)*16 + lane/4,
@@ -526,6 +545,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
             const int row = wm * WTM + i * 16 + fr;
             pa[i] = *reinterpret_cast<const uint4 *>(&sA[row * BG_ROWB + swz(row, fg)]);
         }
+        if (Q8) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        *reinterpret_cast<const v4i *>(&pa[i]), *reinterpret_cast<const v4i *>(&pb[j]),
+                        acc[i][j], 0, 0, 0);
+            continue;
+        }
         v4i b0[FN], b1[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -567,7 +596,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = m0 + wm * WTM + i * 16 + 4 * fg + r;
-                    if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r] >> 8;
+                    if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r] >> SHIFT;
                 }
             }
         return;
@@ -599,7 +628,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = wm * WTM + i * 16 + 4 * fg + r;
-                    float y = fp32_value((float)(acc[i][j][r] >> 8) * xsc[i][r]);
+                    float y = fp32_value((float)(acc[i][j][r] >> SHIFT) * xsc[i][r]);
                     y = fp32_value(y * wsc[j]);
                     if (PE == PE_GELU) y = fp32_value(gelu_erf(y));
                     if (PE == PE_RESIDUAL) {
@@ -651,8 +680,9 @@ struct GemmPlan {
 
 // Pick the tile shape and k split with the smallest estimated time: full rounds of 256 compute
 // units times the per-tile MFMA time (discounted for smaller wave tiles, whose LDS traffic per MFMA
-// is higher), plus the write and read of split-K partials.
-static GemmPlan plan_gemm(int M, int N, int K)
+// is higher), plus the write and read of split-K partials. kg is the k granularity of a stage (128
+// for packed int4, 64 for int8 operands).
+static GemmPlan plan_gemm(int M, int N, int K, int kg)
 {
     GemmPlan best{0, 0, 16, 1, K};
     if (M <= SMALL_M) return best;
@@ -662,7 +692,7 @@ static GemmPlan plan_gemm(int M, int N, int K)
     for (const Cand &c : cands) {
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         for (int splits = 1; splits <= 16; splits *= 2) {
-            int k_split = ((K + splits - 1) / splits + BG_KS - 1) / BG_KS * BG_KS;
+            int k_split = ((K + splits - 1) / splits + kg - 1) / kg * kg;
             if (k_split > MAX_K_SPLIT) continue;
             const int real_splits = (K + k_split - 1) / k_split;
             if (real_splits != splits) continue;
@@ -680,9 +710,9 @@ static GemmPlan plan_gemm(int M, int N, int K)
     return best;
 }
 
-size_t gemm_workspace(int M, int N, int K)
+size_t gemm_workspace(int M, int N, int K, bool q8)
 {
-    GemmPlan p = plan_gemm(M, N, K);
+    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS);
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t);
 }
@@ -703,86 +733,98 @@ static void launch_big(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, co
 
 constexpr int PIPE_STAGES = 4;
 
-template <int BM, int BN, int WM, int WN, int PE, bool VO>
+template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8>
 static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
     const size_t lds = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
-    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO>;
+    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8>;
     static bool attr_set = false;  // once per process and instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(W4A4_ERR_HIP, "gemm LDS request: %s", hipGetErrorString(e));
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO>), grid, dim3(64 * WM * WN),
-                       lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8>), grid,
+                       dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
     return W4A4_OK;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool Q8>
 static int launch_pipe_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
     if (partial || epi.mode == GEMM_OUT_I32)
-        return launch_pipe_e<BM, BN, WM, WN, PE_INT32, false>(grid, s, xq, wq, M, N, K, k_split, tm,
-                                                             tn, epi, partial);
+        return launch_pipe_e<BM, BN, WM, WN, PE_INT32, false, Q8>(grid, s, xq, wq, M, N, K, k_split,
+                                                                 tm, tn, epi, partial);
     const bool vo = (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0);
 #define W4A4_PIPE_E(PEV)                                                                           \
-    return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true>(grid, s, xq, wq, M, N, K, k_split, tm, tn, \
-                                                         epi, partial)                             \
-              : launch_pipe_e<BM, BN, WM, WN, PEV, false>(grid, s, xq, wq, M, N, K, k_split, tm,   \
-                                                          tn, epi, partial);
+    return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, \
+                                                             tn, epi, partial)                     \
+              : launch_pipe_e<BM, BN, WM, WN, PEV, false, Q8>(grid, s, xq, wq, M, N, K, k_split,   \
+                                                              tm, tn, epi, partial);
     if (epi.mode == W4A4_EPI_GELU) { W4A4_PIPE_E(PE_GELU) }
     if (epi.mode == W4A4_EPI_RESIDUAL) { W4A4_PIPE_E(PE_RESIDUAL) }
     W4A4_PIPE_E(PE_NONE)
 #undef W4A4_PIPE_E
 }
 
+template <bool Q8>
 static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq,
                        int M, int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                        int32_t *partial)
 {
     if (kind == 1)
-        return launch_pipe_t<256, 256, 2, 4>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+        return launch_pipe_t<256, 256, 2, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
+                                                 partial);
     if (kind == 2)
-        return launch_pipe_t<128, 256, 1, 4>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
-    return launch_pipe_t<128, 128, 2, 2>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+        return launch_pipe_t<128, 256, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
+                                                 partial);
+    return launch_pipe_t<128, 128, 2, 2, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
 }
 
+// q8: int8 operands [rows][K] (W8A8); the caller guarantees K % 64 == 0 and 16-byte aligned
+// operands for them.
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
-                void *ws, size_t ws_bytes, hipStream_t s)
+                void *ws, size_t ws_bytes, hipStream_t s, bool q8)
 {
     if (M == 0) return W4A4_OK;
-    GemmPlan p = plan_gemm(M, N, K);
-    const bool vec = ((K / 2) % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
+    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS);
+    const int row_bytes = q8 ? K : K / 2;
+    const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     if (p.kind == 0) {
         dim3 g((N + 15) / 16);
         const int mf = (M + 15) / 16;
-#define W4A4_SMALLM(MFV)                                                                           \
-    if (vec) hipLaunchKernelGGL((k_gemm_smallm<MFV, true>), g, dim3(256), 0, s, xq, wq, M, N, K,   \
+#define W4A4_SMALLM_Q(MFV, QV)                                                                     \
+    if (vec) hipLaunchKernelGGL((k_gemm_smallm<MFV, true, QV>), g, dim3(256), 0, s, xq, wq, M, N, K, \
                                 epi);                                                              \
-    else hipLaunchKernelGGL((k_gemm_smallm<MFV, false>), g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+    else hipLaunchKernelGGL((k_gemm_smallm<MFV, false, QV>), g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+#define W4A4_SMALLM(MFV)                                                                           \
+    if (q8) { W4A4_SMALLM_Q(MFV, true) } else { W4A4_SMALLM_Q(MFV, false) }
         if (mf == 1) { W4A4_SMALLM(1) }
         else if (mf == 2) { W4A4_SMALLM(2) }
         else if (mf == 3) { W4A4_SMALLM(3) }
         else { W4A4_SMALLM(4) }
 #undef W4A4_SMALLM
+#undef W4A4_SMALLM_Q
         return check_launch("gemm small-M");
     }
     int32_t *partial = nullptr;
     if (p.splits > 1) {
-        if (!ws || ws_bytes < gemm_workspace(M, N, K))
-            return fail(W4A4_ERR_WORKSPACE, "gemm needs %zu workspace bytes",
-                        gemm_workspace(M, N, K));
+        const size_t need = gemm_workspace(M, N, K, q8);
+        if (!ws || ws_bytes < need)
+            return fail(W4A4_ERR_WORKSPACE, "gemm needs %zu workspace bytes", need);
         partial = reinterpret_cast<int32_t *>(ws);
     }
     const int tm = (M + p.bm - 1) / p.bm, tn = (N + p.bn - 1) / p.bn;
     dim3 grid(tm * tn, p.splits);
-    if (vec && K % BG_KS == 0) {
-        int rc = launch_pipe(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
+    if (q8) {
+        int rc = launch_pipe<true>(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
+        if (rc != W4A4_OK) return rc;
+    } else if (vec && K % BG_KS == 0) {
+        int rc = launch_pipe<false>(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
         if (rc != W4A4_OK) return rc;
     } else if (p.kind == 1)
         launch_big<256, 256, 2, 4>(vec, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(128) void k_weight_pack(const void *__restrict__ W,
                                                      const double *__restrict__ R64,
                                                      unsigned long long *__restrict__ rowmax,
                                                      uint8_t *__restrict__ wq,
-                                                     float *__restrict__ w_scale)
+                                                     float *__restrict__ w_scale, int qmax)
 {
 #pragma clang fp contract(off)
     __shared__ double sW[WP_ROWS][WP_CHUNK];
@@ -152,31 +152,36 @@ __global__ __launch_bounds__(128) void k_weight_pack(const void *__restrict__ W,
             const int n = n0 + r;
             if (n >= N) continue;
             const double m = __longlong_as_double((long long)rowmax[n]);
-            const float s = (m > 0.0) ? (float)(m / 7.0) : 1.0f;
+            const float s = (m > 0.0) ? (float)(m / (double)qmax) : 1.0f;
             if (blockIdx.y == 0 && tid == 0) w_scale[n] = s;
             if (!active) continue;
             int q[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 double v = rint(acc[r][h] / (double)s);
-                v = fmin(fmax(v, -8.0), 7.0);
+                v = fmin(fmax(v, -(double)qmax - 1.0), (double)qmax);
                 q[h] = (int)v;
             }
-            wq[(int64_t)n * (K / 2) + kp / 2] = (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+            if (qmax == 7)
+                wq[(int64_t)n * (K / 2) + kp / 2] = (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+            else
+                *reinterpret_cast<uint16_t *>(&wq[(int64_t)n * K + kp]) =
+                    (uint16_t)((q[0] & 0xFF) | ((q[1] & 0xFF) << 8));
         }
     }
 }
 
 int launch_weight_pack(const void *W, int wdt, int N, int K, int64_t ldw, int B,
                        const int32_t *perm, const double *R64, unsigned long long *rowmax,
-                       uint8_t *wq, float *w_scale, hipStream_t s)
+                       uint8_t *wq, float *w_scale, int bits, hipStream_t s)
 {
+    const int qmax = bits == 8 ? 127 : 7;
     hipLaunchKernelGGL(k_fill_u64, dim3((N + 255) / 256), dim3(256), 0, s, rowmax, (int64_t)N);
     dim3 grid((N + WP_ROWS - 1) / WP_ROWS, (K + WP_CHUNK - 1) / WP_CHUNK);
     hipLaunchKernelGGL(k_weight_pack<0>, grid, dim3(WP_CHUNK / 2), 0, s, W, wdt, N, K, ldw, B,
-                       perm, R64, rowmax, wq, w_scale);
+                       perm, R64, rowmax, wq, w_scale, qmax);
     hipLaunchKernelGGL(k_weight_pack<1>, grid, dim3(WP_CHUNK / 2), 0, s, W, wdt, N, K, ldw, B,
-                       perm, R64, rowmax, wq, w_scale);
+                       perm, R64, rowmax, wq, w_scale, qmax);
     return check_launch("weight pack");
 }
 

@@ -73,7 +73,7 @@ int launch_rotation(const float *U, int K, int B, double hinv, double *R64, void
                     hipStream_t s);
 int launch_weight_pack(const void *W, int wdt, int N, int K, int64_t ldw, int B,
                        const int32_t *perm, const double *R64, unsigned long long *rowmax,
-                       uint8_t *wq, float *w_scale, hipStream_t s);
+                       uint8_t *wq, float *w_scale, int bits, hipStream_t s);
 
 // activation side (k_act.hip)
 enum ActMode { ACT_PER_STEP = 0, ACT_TOKEN_MAX = 1, ACT_TOKEN_QUANT = 2, ACT_CALIB_MAX = 3 };
@@ -81,8 +81,9 @@ int launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t s);
 int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B,
                         const int32_t *perm, const void *rot, const float *table, int step,
                         ActMode mode, uint32_t *rowmax, uint8_t *xq, float *x_scale,
-                        float *xrot_dbg, hipStream_t s);
-int launch_scale_from_absmax(const uint32_t *amax, float *out, hipStream_t s);
+                        float *xrot_dbg, bool q8, hipStream_t s);
+// q8 (here and below): int8 codes [M][K] with scales max / 127 instead of packed int4 and max / 7
+int launch_scale_from_absmax(const uint32_t *amax, float *out, bool q8, hipStream_t s);
 // fp16 activations with block 64 or 128: MFMA rotation; xperm (optional) holds rows already in
 // zigzag order, written by launch_permute_rows (which also clears zero_row[0..M) when given).
 bool act_uses_permute_pass(int M, int K, int per_token);
@@ -98,7 +99,7 @@ int launch_rotate_quant_hadamard(const void *X, int x_dtype, int M, int K, int64
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                             const uint16_t *xperm, hipStream_t s);
+                             const uint16_t *xperm, bool q8, hipStream_t s);
 
 // GEMM (k_gemm.hip)
 struct GemmEpilogue {
@@ -113,9 +114,10 @@ struct GemmEpilogue {
     int32_t *acc_out;  // GEMM_OUT_I32 destination, dense [M][N]
 };
 constexpr int GEMM_OUT_I32 = 100;
-size_t gemm_workspace(int M, int N, int K);
+// q8: int8 operands [rows][K] (W8A8) instead of packed int4 [rows][K/2]
+size_t gemm_workspace(int M, int N, int K, bool q8);
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
-                void *ws, size_t ws_bytes, hipStream_t s);
+                void *ws, size_t ws_bytes, hipStream_t s, bool q8);
 
 // calibration (k_calib.hip)
 size_t zigzag_workspace(int K);
