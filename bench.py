@@ -202,11 +202,11 @@ def setup_per_token_linear(name, bd, inputs):
     return d, lin, [X], [Y], step
 
 
-def setup_stack(bd, inputs, layers=None):
+def setup_stack(bd, inputs, layers=None, w8=()):
     """Synthetic action-head stack (16 layers of QKV -> V slice -> O + residual -> up + GELU -> down
     + residual, M = 1600 tokens, 8 denoising steps): device calibration (zigzag, block SVD, pack,
     per-linear per-step tables from the stacked calibration draws), then one pass = 8 steps x 16
-    layers x 4 W4A4 linears."""
+    layers x 4 linears (W4A4, or W8A8 for the names in w8)."""
     from w4a4_post_quantized_zigzag_amd.stack import DeviceStack
     torch = _torch()
     cfg = inputs.STACK
@@ -214,7 +214,7 @@ def setup_stack(bd, inputs, layers=None):
     act = inputs.stack_activations()
     T, B, M = cfg["steps"], cfg["block"], cfg["M"]
     t0 = time.perf_counter()
-    ds = DeviceStack(Wl, B, T)
+    ds = DeviceStack(Wl, B, T, w8=w8)
     torch.cuda.synchronize()
     offline = time.perf_counter() - t0
     del Wl
@@ -434,15 +434,18 @@ def supplementary(bd, inputs, steps):
         del lin, Xs, Ys
         torch.cuda.empty_cache()
     out["cold_hbm"] = cold_hbm(bd, inputs)
-    info, lins, Xs, rb, step = setup_stack(bd, inputs)
-    ms = time_graph(step, max(3, steps // 5), 2)
-    M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]
-    ops = T * L * 2.0 * M * (3 * h * h + h * h + f * h + h * f)
-    out["action_stack"] = {"layers": L, "M": M, "hidden": h, "ffn": f, "steps": T,
-                           "linear_calls": T * L * 4, "ms_per_pass": ms,
-                           "tops": ops / (ms * 1e-3) / 1e12,
-                           "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
-                           "offline_pack_s": info["offline_s"], "calibration_s": info["calib_s"]}
+    for name, w8 in (("action_stack", ()), ("action_stack_mixed", ("o", "down"))):
+        info, lins, Xs, rb, step = setup_stack(bd, inputs, w8=w8)
+        ms = time_graph(step, max(3, steps // 5), 2)
+        M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]
+        ops = T * L * 2.0 * M * (3 * h * h + h * h + f * h + h * f)
+        out[name] = {"layers": L, "M": M, "hidden": h, "ffn": f, "steps": T,
+                     "w8a8_linears": list(w8), "linear_calls": T * L * 4, "ms_per_pass": ms,
+                     "tops": ops / (ms * 1e-3) / 1e12,
+                     "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                     "offline_pack_s": info["offline_s"], "calibration_s": info["calib_s"]}
+        del lins, Xs, step
+        torch.cuda.empty_cache()
     return out
 
 

@@ -419,8 +419,10 @@ def linear(X, W, B: int, mode: str, table=None, num_steps=None, step=None, perm=
 STACK_LINEARS = ("qkv", "o", "up", "down")
 
 
-def stack_prepare(weights, B: int, calib=None):
-    """Offline side for every linear: zigzag perm, SVD factor (or the given ones) and the pack."""
+def stack_prepare(weights, B: int, calib=None, w8=()):
+    """Offline side for every linear: zigzag perm, SVD factor (or the given ones) and the pack.
+    Linears named in w8 (e.g. ("o", "down"), the FoldQuantVLA summary's W8A8 attention-output and
+    FFN-down projections) use the int8 grid, the others int4."""
     layers = []
     for li, lw in enumerate(weights):
         layer = {}
@@ -431,14 +433,16 @@ def stack_prepare(weights, B: int, calib=None):
                 U = block_svd(W, perm, B)
             else:
                 perm, U = calib[li][name]
-            layer[name] = {"perm": perm, "U": U, "pack": pack_weights(W, perm, U, B)}
+            bits = 8 if name in w8 else 4
+            layer[name] = {"perm": perm, "U": U, "bits": bits,
+                           "pack": pack_weights(W, perm, U, B, bits=bits)}
         layers.append(layer)
     return layers
 
 
 def _stack_linear(lin, X, B, mode, table, steps, step, epilogue=EPI_NONE, residual=None):
     act = rotate_quant_act(X, lin["perm"], lin["U"], B, mode, table, steps, step,
-                           R=lin["pack"]["R"])
+                           R=lin["pack"]["R"], bits=lin.get("bits", 4))
     g = gemm(act["codes"], act["scale"], mode == "per_token", lin["pack"]["codes"],
              lin["pack"]["w_scale"], epilogue, residual)
     return g["Y"], act
@@ -448,8 +452,9 @@ def stack_run(layers, X, B: int, mode: str, tables=None, steps=None, step=0, out
               record_tables=None):
     """One pass of the stack on fp16 X [rows, h]. mode "per_step" uses tables[layer][name][step];
     mode "per_token" quantizes per token, and with record_tables (a list of per-layer dicts) stores
-    each linear's calibration entry fp32(max |fp32(x')| / 7) (1.0 for a zero max) for `step`.
-    Returns the fp16 output; appends each linear's fp16 output to `outputs` if given."""
+    each linear's calibration entry fp32(max |fp32(x')| / 7) (1.0 for a zero max; 127 in place of 7
+    for an int8 linear) for `step`. Returns the fp16 output; appends each linear's fp16 output to
+    `outputs` if given."""
     h = X.shape[1]
     cur = np.asarray(X, np.float16)
     for li, layer in enumerate(layers):
@@ -458,7 +463,8 @@ def stack_run(layers, X, B: int, mode: str, tables=None, steps=None, step=0, out
             Y, act = _stack_linear(layer[name], inp, B, mode, tab, steps, step, epi, res)
             if record_tables is not None:
                 amax = float(np.max(np.abs(act["x32"]))) if act["x32"].size else 0.0
-                record_tables[li][name][step] = np.float32(amax / 7.0) if amax > 0 else 1.0
+                qmax = float(_qmax(layer[name].get("bits", 4)))
+                record_tables[li][name][step] = np.float32(amax / qmax) if amax > 0 else 1.0
             if outputs is not None:
                 outputs.append(Y)
             return Y

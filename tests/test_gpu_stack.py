@@ -79,3 +79,30 @@ def test_stack_full_width_sampled_rows():
     rows = np.array([0, 1, 7, 399, 800, 1234, 1598, 1599])
     yo = oracle.stack_run(layers, X[rows], B, "per_step", tables, T, 0)
     check_y_tolerance(yd[rows], yo)
+
+
+def test_stack_mixed_w8a8():
+    # attention-output and FFN-down at W8A8 (int8 grid), QKV and up at W4A4
+    L, h, f, M, T = 2, 256, 1024, 100, 2
+    w8 = ("o", "down")
+    W = inputs.stack_weights(layers=L, hidden=h, ffn=f, seed=21)
+    A = inputs.stack_activations(M=M, hidden=h, steps=T, calib=2, seed=21)
+    layers = oracle.stack_prepare(W, B, w8=w8)
+    tables = oracle.stack_calibrate(layers, A["X_calib"], B)
+    ds = DeviceStack(W, B, T, calib=_device_calib(layers), w8=w8)
+    assert [ds.layers[0][n].bits for n in LINEARS] == [4, 8, 4, 8]
+    for li in range(L):
+        for n in LINEARS:
+            assert np.array_equal(host(ds.layers[li][n].wq), layers[li][n]["pack"]["wq"])
+    ds.set_tables(tables)
+    for t in range(T):
+        outs_o, outs_d = [], []
+        oracle.stack_run(layers, A["X_steps"][t], B, "per_step", tables, T, t, outputs=outs_o)
+        ds.run(dev(A["X_steps"][t]), t, outputs=outs_d)
+        for yd, yo in zip(outs_d, outs_o):
+            check_y_tolerance(host(yd), yo)
+    # device calibration of the mixed stack records max/127 for the int8 linears
+    ds2 = DeviceStack(W, B, T, calib=_device_calib(layers), w8=w8)
+    ds2.calibrate(A["X_calib"])
+    got = host(ds2.layers[0]["o"].table)
+    assert np.allclose(got, tables[0]["o"], rtol=2e-3, atol=0)

@@ -459,3 +459,30 @@ def test_recipe_constants_from_the_pages():
     W = _rng(0).standard_normal((B, 2 * B))
     assert sorted(oracle.zigzag_perm(W, B).tolist()) == list(range(2 * B))
     assert rc["svd_rank"] == 0 and rc["use_rtn"] and rc["w_bits"] == 4
+
+
+def test_mixed_stack_w8a8_linears():
+    # FoldQuantVLA summary: attention-output and FFN-down at W8A8, the rest W4A4. Layer 0's QKV is
+    # W4A4 in both configurations, so the O projection sees the same input; its table entry is the
+    # same max over 127 instead of 7, and its output lands much closer to the exact product.
+    h, f, B = 128, 512, 64
+    W = inputs.stack_weights(layers=1, hidden=h, ffn=f, seed=8)
+    X = (_rng(9).standard_normal((24, h))).astype(np.float16)
+    l4 = oracle.stack_prepare(W, B)
+    l8 = oracle.stack_prepare(W, B, w8=("o", "down"))
+    assert [l8[0][n]["bits"] for n in ("qkv", "o", "up", "down")] == [4, 8, 4, 8]
+    assert l8[0]["o"]["pack"]["wq"].shape == (h, h) and l4[0]["o"]["pack"]["wq"].shape == (h, h // 2)
+    t4 = oracle.stack_calibrate(l4, [[X]], B)
+    t8 = oracle.stack_calibrate(l8, [[X]], B)
+    assert t8[0]["qkv"][0] == t4[0]["qkv"][0]
+    for a, b in ((t4[0]["o"][0], t8[0]["o"][0]),):
+        assert abs(float(a) * 7.0 - float(b) * 127.0) <= 2 ** -22 * float(a) * 7.0
+    o4, o8 = [], []
+    oracle.stack_run(l4, X, B, "per_token", outputs=o4)
+    oracle.stack_run(l8, X, B, "per_token", outputs=o8)
+    assert np.array_equal(o4[0], o8[0])
+    V = o4[0][:, 2 * h:3 * h].astype(np.float64)
+    exact = V @ W[0]["o"].astype(np.float64).T + X.astype(np.float64)
+    e4 = np.linalg.norm(o4[1] - exact) / np.linalg.norm(exact - X)
+    e8 = np.linalg.norm(o8[1] - exact) / np.linalg.norm(exact - X)
+    assert e8 < e4 / 4

@@ -1,8 +1,9 @@
 """Synthetic action-head stack driven through the C ABI: per layer QKV -> V slice (attention
 replaced by identity) -> O with residual -> up with erf-GELU -> down with residual, every linear a
-W4A4 linear with its own zigzag permutation, block SVD factor, packed weights and per-step
-act_scale_table. This module only sequences library calls and owns buffers; all arithmetic runs in
-libw4a4.so.
+W4A4 linear (or, for the linears named in w8, a W8A8 linear: the FoldQuantVLA summary's mixed
+configuration keeps the attention-output and FFN-down projections at W8A8) with its own zigzag
+permutation, block SVD factor, packed weights and per-step act_scale_table. This module only
+sequences library calls and owns buffers; all arithmetic runs in libw4a4.so.
 
 Per-step tables follow the pages' per-step scaling (vnrobo "Y tuong paper": the runtime looks up the
 current denoising step's scale; gist.science item 2: tables from calibration trajectories): for each
@@ -24,14 +25,15 @@ def _torch():
 
 
 class DeviceLinear:
-    def __init__(self, W, block: int, steps: int, perm=None, U=None):
+    def __init__(self, W, block: int, steps: int, perm=None, U=None, bits: int = 4):
         torch = _torch()
         Wd = W if isinstance(W, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(W)).cuda()
         self.N, self.K = Wd.shape
         self.B = block
         self.perm = bd.zigzag_perm(Wd, block) if perm is None else perm
         self.U = bd.block_svd(Wd, self.perm, block) if U is None else U
-        self.wq, self.w_scale, self.rot = bd.pack_weights(Wd, self.perm, self.U, block)
+        self.bits = bits
+        self.wq, self.w_scale, self.rot = bd.pack_weights(Wd, self.perm, self.U, block, bits=bits)
         self.table = torch.empty(steps, dtype=torch.float32, device="cuda")
         self.steps = steps
 
@@ -43,21 +45,24 @@ class _Buffers:
         self.qkv, self.h2, self.g = e((rows, 3 * h)), e((rows, h)), e((rows, f))
         self.hs = [e((rows, h)), e((rows, h))]
         self.xs = e(max(rows, 1), torch.float32)
-        self.xq = {K: e((rows, K // 2), torch.uint8) for K in (h, f)}
+        self.xq = {(K, b): e((rows, K // 2 if b == 4 else K), torch.uint8)
+                   for K in (h, f) for b in (4, 8)}
         self.ws = {K: e(max(256, bd.lib().w4a4_act_workspace_bytes(rows, K, block, 1)), torch.uint8)
                    for K in (h, f)}
         self.cws = {K: e(max(256, bd.lib().w4a4_calibrate_workspace_bytes(rows, K, block)),
                          torch.uint8) for K in (h, f)}
-        self.gws = {(N, K): e(max(256, bd.lib().w4a4_gemm_workspace_bytes(rows, N, K)), torch.uint8)
-                    for N, K in ((3 * h, h), (h, h), (f, h), (h, f))}
+        self.gws = {(N, K, b): e(max(256, (bd.lib().w4a4_gemm_workspace_bytes if b == 4 else
+                                           bd.lib().w4a4_gemm_w8a8_workspace_bytes)(rows, N, K)),
+                                 torch.uint8)
+                    for N, K in ((3 * h, h), (h, h), (f, h), (h, f)) for b in (4, 8)}
 
 
 class DeviceStack:
     """weights: list (one per layer) of dicts qkv [3h,h], o [h,h], up [f,h], down [h,f] (fp16).
     calib: optional list of per-layer dicts name -> (perm, U) device tensors to use instead of the
-    device calibration kernels."""
+    device calibration kernels. w8: names of the linears run as W8A8 (e.g. ("o", "down"))."""
 
-    def __init__(self, weights, block: int, steps: int, calib=None):
+    def __init__(self, weights, block: int, steps: int, calib=None, w8=()):
         self.block, self.steps = block, steps
         self.h = weights[0]["o"].shape[0]
         self.f = weights[0]["up"].shape[0]
@@ -66,7 +71,8 @@ class DeviceStack:
             layer = {}
             for name in LINEARS:
                 pu = calib[li][name] if calib is not None else (None, None)
-                layer[name] = DeviceLinear(lw[name], block, steps, *pu)
+                layer[name] = DeviceLinear(lw[name], block, steps, *pu,
+                                           bits=8 if name in w8 else 4)
             self.layers.append(layer)
         self._bufs = {}
 
@@ -83,13 +89,15 @@ class DeviceStack:
                 layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
 
     def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None):
+        b = lin.bits
         if calib:
             bd.calibrate_act_scale(X, lin.perm, lin.rot, self.block, out=lin.table[step:step + 1],
-                                   ws=bufs.cws[lin.K])
+                                   ws=bufs.cws[lin.K], bits=b)
+        xq = bufs.xq[(lin.K, b)]
         bd.rotate_quant_act(X, lin.perm, lin.rot, self.block, None if calib else lin.table,
-                            self.steps, step, xq=bufs.xq[lin.K], x_scale=bufs.xs, ws=bufs.ws[lin.K])
-        bd.gemm(bufs.xq[lin.K], bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
-                residual=res, ws=bufs.gws[(lin.N, lin.K)])
+                            self.steps, step, xq=xq, x_scale=bufs.xs, ws=bufs.ws[lin.K], bits=b)
+        bd.gemm(xq, bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
+                ws=bufs.gws[(lin.N, lin.K, b)], bits=b)
 
     def run(self, X, step: int, calib: bool = False, outputs=None):
         """One pass of the stack for denoising step `step` on X fp16 [rows, h] (device). In calib
