@@ -64,14 +64,43 @@ __device__ __forceinline__ uint4 zero_unless(const uint4 &v, bool valid)
     return make_uint4(valid ? v.x : 0u, valid ? v.y : 0u, valid ? v.z : 0u, valid ? v.w : 0u);
 }
 
+// erf-GELU, v * Phi(v), in fp32 with one branch-free path: for w = min(|v|, 6),
+// Phi(-w) = exp(-w^2/2) * g(w) where g(w) = 0.5 erfc(w / sqrt 2) exp(w^2 / 2) is a degree-7
+// polynomial in t = 1 / (1 + 0.3 w) (relative least-squares fit on [0, 6], relative error 1.6e-7;
+// fit_gelu_tail.py beside this file regenerates the coefficients), and Phi(v) = 1 - Phi(-w) for
+// v >= 0. Beyond |v| = 6 the tail is below 1e-9 and leaves GELU unchanged at fp16 resolution. The
+// result is within about 1e-6 relative of the exact value, so after the fp16 rounding it equals
+// the correctly rounded GELU or its neighbour; it costs two transcendental and about 15 other VALU
+// operations, several times less than a library erf with range branches.
 __device__ __forceinline__ float gelu_erf(float v)
 {
-    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    const float w = fminf(fabsf(v), 6.0f);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3f, w, 1.0f));
+    float p = 0.0311708786f;
+    p = fmaf(p, t, -0.220824048f);
+    p = fmaf(p, t, 0.48928532f);
+    p = fmaf(p, t, -0.294268399f);
+    p = fmaf(p, t, 0.306398928f);
+    p = fmaf(p, t, 0.0590155609f);
+    p = fmaf(p, t, 0.129963309f);
+    p = fmaf(p, t, -0.000741627882f);
+    const float e = __builtin_amdgcn_exp2f((v * v) * -0.721347520444482f);  // exp(-v^2/2)
+    const float tail = p * e;                                               // Phi(-|v|)
+    return v * (v >= 0.0f ? 1.0f - tail : tail);
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v)
 {
     return __half_as_ushort(__float2half_rn(v));
+}
+
+// Two fp32 values rounded to fp16 (to nearest even, v_cvt_pk_f16_f32), packed low value first.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi)
+{
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t h = __builtin_convertvector(f2_t{lo, hi}, h2_t);
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // The dequantization is specified as a chain of fp32 roundings followed by one fp16 rounding.
@@ -551,7 +580,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        *reinterpret_cast<const v4i *>(&pa[i]), *reinterpret_cast<const v4i *>(&pb[j]),
+                        *reinterpret_cast<const v4i *>(&pb[j]), *reinterpret_cast<const v4i *>(&pa[i]),
                         acc[i][j], 0, 0, 0);
             continue;
         }
@@ -570,8 +599,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
             const v4i a0 = *reinterpret_cast<v4i *>(&lo), a1 = *reinterpret_cast<v4i *>(&hi);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0[j], a0, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1[j], a1, acc[i][j], 0, 0, 0);
             }
         }
         // Schedule: all fragment reads first, the B widening and the first A widening, then each
@@ -586,75 +615,93 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         }
     }
 
+    // The weight fragment is the MFMA's A operand and the activation fragment its B operand, so
+    // the accumulator of fragment (i, j) holds, in lane (fr, fg), output row
+    // m = m0 + wm * WTM + 16 i + fr and the four consecutive output columns
+    // n = n0 + wn * WTN + 16 j + 4 fg + 0..3: each lane dequantizes and stores 8 contiguous bytes.
+    const int mrow = m0 + wm * WTM + fr, ncol = n0 + wn * WTN + 4 * fg;
     if (PE == PE_INT32) {
         int32_t *dst = partial ? partial + (int64_t)blockIdx.y * M * N : epi.acc_out;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * WTN + j * 16 + fr;
+                const int m = mrow + i * 16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + wm * WTM + i * 16 + 4 * fg + r;
+                    const int n = ncol + j * 16 + r;
                     if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r] >> SHIFT;
                 }
             }
         return;
     } else {
 #pragma clang fp contract(off)
-        // dequantize in registers, stage the fp16 tile in the (now idle) LDS ring, then write whole
-        // 16-byte row chunks. Tile element (row, col) lives at row*BN + 8*((col/8) ^ sw(row)) +
-        // col%8 with sw(row) = (row/4) % 16, which spreads the four rows a fragment store touches
-        // over different banks.
-        static_assert(BM * BN * 2 <= NSTAGE * STAGE, "fp16 tile fits in the LDS ring");
-        static_assert(BN / 8 >= 16, "swizzle needs 16 chunks per row");
-        uint16_t *tile = reinterpret_cast<uint16_t *>(smem);
-        float wsc[FN], xsc[FM][4];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) wsc[j] = epi.w_scale[min(n0 + wn * WTN + j * 16 + fr, N - 1)];
+        // VEC_OUT: Y, the residual and the weight scales are read or written 4 columns at a time
+        // (the host checks their alignment and row strides); columns past N take the element path.
+        float xsc[FM];
+        float wsc[FN][4];
+        uint32_t rsd[FM][FN][2];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
+            xsc[i] = epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                xsc[i][r] = epi.x_scale_per_token
-                                ? epi.x_scale[min(m0 + wm * WTM + i * 16 + 4 * fg + r, M - 1)]
-                                : epi.x_scale[0];
-        __syncthreads();  // every wave is done reading the ring
+        for (int j = 0; j < FN; ++j) {
+            const int n = ncol + j * 16;
+            if (VEC_OUT && n + 3 < N) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
+                wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
+            } else {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+                for (int r = 0; r < 4; ++r) wsc[j][r] = epi.w_scale[min(n + r, N - 1)];
+            }
+        }
+        // residual values: prefetched 4 at a time on the vector path, read one by one otherwise
+        auto residual4 = [&](int m, int n, uint32_t (&h)[2]) {
+            const uint16_t *src = epi.residual + (int64_t)min(m, M - 1) * epi.ldr;
+            if (VEC_OUT && n + 3 < N) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src + n);
+                h[0] = v.x; h[1] = v.y;
+            } else {
+                uint32_t e[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e[r] = src[min(n + r, N - 1)];
+                h[0] = e[0] | (e[1] << 16); h[1] = e[2] | (e[3] << 16);
+            }
+        };
+        if (PE == PE_RESIDUAL && VEC_OUT) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) residual4(mrow + i * 16, ncol + j * 16, rsd[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = mrow + i * 16;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int col = wn * WTN + j * 16 + fr;
+                const int n = ncol + j * 16;
+                float y[4];
+                if (PE == PE_RESIDUAL && !VEC_OUT) residual4(m, n, rsd[i][j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = wm * WTM + i * 16 + 4 * fg + r;
-                    float y = fp32_value((float)(acc[i][j][r] >> SHIFT) * xsc[i][r]);
-                    y = fp32_value(y * wsc[j]);
-                    if (PE == PE_GELU) y = fp32_value(gelu_erf(y));
+                    y[r] = fp32_value((float)(acc[i][j][r] >> SHIFT) * xsc[i]);
+                    y[r] = fp32_value(y[r] * wsc[j][r]);
+                    if (PE == PE_GELU) y[r] = fp32_value(gelu_erf(y[r]));
                     if (PE == PE_RESIDUAL) {
-                        const int m = min(m0 + row, M - 1), n = min(n0 + col, N - 1);
-                        y = fp32_value(y + __half2float(__ushort_as_half(epi.residual[(int64_t)m * epi.ldr + n])));
+                        const uint32_t hv = rsd[i][j][r >> 1] >> (16 * (r & 1));
+                        y[r] = fp32_value(y[r] + __half2float(__ushort_as_half((uint16_t)hv)));
                     }
-                    tile[row * BN + (((col >> 3) ^ ((row >> 2) & 15)) << 3) + (col & 7)] =
-                        f32_to_f16_bits(y);
                 }
-            }
-        __syncthreads();
-        constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-        for (int e = tid; e < BM * CPR; e += 64 * NW) {
-            const int row = e / CPR, c = e % CPR;
-            const int m = m0 + row, n = n0 + 8 * c;
-            if (m >= M) continue;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&tile[row * BN + ((c ^ ((row >> 2) & 15)) << 3)]);
-            uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
-            if (VEC_OUT && n + 8 <= N) {
-                *reinterpret_cast<uint4 *>(dst) = v;
-            } else {
-                const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y,
-                                       (uint16_t)(v.y >> 16), (uint16_t)v.z, (uint16_t)(v.z >> 16),
-                                       (uint16_t)v.w, (uint16_t)(v.w >> 16)};
-                for (int t = 0; t < 8; ++t)
-                    if (n + t < N) dst[t] = h[t];
+                if (m >= M) continue;
+                uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
+                if (VEC_OUT && n + 3 < N) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(f32x2_to_f16x2(y[0], y[1]),
+                                                                 f32x2_to_f16x2(y[2], y[3]));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) dst[r] = f32_to_f16_bits(y[r]);
+                }
             }
         }
     }
@@ -759,7 +806,11 @@ static int launch_pipe_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
     if (partial || epi.mode == GEMM_OUT_I32)
         return launch_pipe_e<BM, BN, WM, WN, PE_INT32, false, Q8>(grid, s, xq, wq, M, N, K, k_split,
                                                                  tm, tn, epi, partial);
-    const bool vo = (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0);
+    // 4-column groups: 8-byte Y / residual accesses and 16-byte weight-scale loads
+    const bool vo = (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+                    ((uintptr_t)epi.w_scale % 16 == 0) &&
+                    (epi.mode != W4A4_EPI_RESIDUAL ||
+                     (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
 #define W4A4_PIPE_E(PEV)                                                                           \
     return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, \
                                                              tn, epi, partial)                     \
