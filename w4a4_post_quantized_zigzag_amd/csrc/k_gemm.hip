@@ -622,15 +622,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const int mrow = m0 + wm * WTM + fr, ncol = n0 + wn * WTN + 4 * fg;
     if (PE == PE_INT32) {
         int32_t *dst = partial ? partial + (int64_t)blockIdx.y * M * N : epi.acc_out;
+        // four consecutive columns per lane: one 16-byte store when the rows allow it
+        const bool vec4 = (N % 4 == 0) && ((uintptr_t)dst % 16 == 0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int m = mrow + i * 16;
+                const int m = mrow + i * 16, n = ncol + j * 16;
+                if (m >= M) continue;
+                if (vec4 && n + 3 < N) {
+                    *reinterpret_cast<int4 *>(&dst[(int64_t)m * N + n]) =
+                        make_int4(acc[i][j][0] >> SHIFT, acc[i][j][1] >> SHIFT,
+                                  acc[i][j][2] >> SHIFT, acc[i][j][3] >> SHIFT);
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = ncol + j * 16 + r;
-                    if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r] >> SHIFT;
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) dst[(int64_t)m * N + n + r] = acc[i][j][r] >> SHIFT;
                 }
             }
         return;
@@ -718,6 +725,49 @@ __global__ void k_splitk_epilogue(const int32_t *__restrict__ partial, int split
     int32_t v = 0;
     for (int s = 0; s < splits; ++s) v += partial[(int64_t)s * M * N + idx];
     store_output(epi, m, n, N, v);
+}
+
+// Same reduction four columns at a time (N % 4 == 0, 16-byte aligned partials, and 8-byte fp16
+// rows / 16-byte weight scales, checked by the host): vector loads of the partials and the
+// epilogue operands, one 8-byte store per thread.
+__global__ void k_splitk_epilogue4(const int32_t *__restrict__ partial, int splits, int M, int N,
+                                   GemmEpilogue epi)
+{
+#pragma clang fp contract(off)
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t MN = (int64_t)M * N;
+    if (g >= MN / 4) return;
+    const int64_t idx = g * 4;
+    const int m = (int)(idx / N), n = (int)(idx % N);
+    int4 v = *reinterpret_cast<const int4 *>(partial + idx);
+    for (int sp = 1; sp < splits; ++sp) {
+        const int4 t = *reinterpret_cast<const int4 *>(partial + sp * MN + idx);
+        v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+    }
+    if (epi.mode == GEMM_OUT_I32) {
+        *reinterpret_cast<int4 *>(epi.acc_out + idx) = v;
+        return;
+    }
+    const float sx = epi.x_scale_per_token ? epi.x_scale[m] : epi.x_scale[0];
+    const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
+    const int32_t a[4] = {v.x, v.y, v.z, v.w};
+    const float ws[4] = {w4.x, w4.y, w4.z, w4.w};
+    uint32_t rh[2] = {0u, 0u};
+    if (epi.mode == W4A4_EPI_RESIDUAL) {
+        const uint2 r = *reinterpret_cast<const uint2 *>(epi.residual + (int64_t)m * epi.ldr + n);
+        rh[0] = r.x; rh[1] = r.y;
+    }
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        y[r] = fp32_value((float)a[r] * sx);
+        y[r] = fp32_value(y[r] * ws[r]);
+        if (epi.mode == W4A4_EPI_GELU) y[r] = fp32_value(gelu_erf(y[r]));
+        else if (epi.mode == W4A4_EPI_RESIDUAL)
+            y[r] = fp32_value(y[r] + __half2float(__ushort_as_half((uint16_t)(rh[r >> 1] >> (16 * (r & 1))))));
+    }
+    *reinterpret_cast<uint2 *>(epi.Y + (int64_t)m * epi.ldy + n) =
+        make_uint2(f32x2_to_f16x2(y[0], y[1]), f32x2_to_f16x2(y[2], y[3]));
 }
 
 struct GemmPlan {
@@ -886,8 +936,18 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     int rc = check_launch("gemm");
     if (rc != W4A4_OK || p.splits <= 1) return rc;
     const int64_t total = (int64_t)M * N;
-    hipLaunchKernelGGL(k_splitk_epilogue, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       partial, p.splits, M, N, epi);
+    const bool out_vec = (epi.mode == GEMM_OUT_I32)
+                             ? ((uintptr_t)epi.acc_out % 16 == 0)
+                             : ((epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+                                ((uintptr_t)epi.w_scale % 16 == 0) &&
+                                (epi.mode != W4A4_EPI_RESIDUAL ||
+                                 (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0)));
+    if (N % 4 == 0 && (uintptr_t)partial % 16 == 0 && out_vec)
+        hipLaunchKernelGGL(k_splitk_epilogue4, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256),
+                           0, s, partial, p.splits, M, N, epi);
+    else
+        hipLaunchKernelGGL(k_splitk_epilogue, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                           s, partial, p.splits, M, N, epi);
     return check_launch("gemm split-k epilogue");
 }
 
