@@ -68,9 +68,13 @@ def _load():
     lib.orc_int_gemm_sampled.argtypes = [_i8p, _i8p, _i64, _i64, _i64p, _i64p, _i64p]
     lib.orc_dequant.argtypes = [_i64p, _i64, _i64, _fp, ctypes.c_int, _fp, _fp]
     lib.orc_gelu.argtypes = [_fp, _i64, _dp]
+    lib.orc_act_quant_grouped.argtypes = [_dp, _i64, _i64, _i64, _fp, _fp, _fp, _i8p]
+    lib.orc_int_gemm_grouped.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i64, _i64p]
+    lib.orc_dequant_grouped.argtypes = [_i64p, _i64, _i64, _i64, _fp, _fp, _fp]
     for f in ("orc_colnorm2", "orc_hadamard", "orc_rotation", "orc_rotate_rows", "orc_weight_rtn",
               "orc_act_quant", "orc_pack", "orc_unpack", "orc_int_gemm", "orc_int_gemm_sampled",
-              "orc_dequant", "orc_gelu", "orc_weight_rtn_q", "orc_act_quant_q"):
+              "orc_dequant", "orc_gelu", "orc_weight_rtn_q", "orc_act_quant_q",
+              "orc_act_quant_grouped", "orc_int_gemm_grouped", "orc_dequant_grouped"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -355,6 +359,12 @@ def dequant(acc, x_scale, per_token: bool, w_scale, epilogue: int = EPI_NONE, re
     y32 = np.empty((M, N), np.float32)
     _load().orc_dequant(_ptr(acc, _i64p), M, N, _ptr(sx, _fp), 1 if per_token else 0,
                         _ptr(sw, _fp), _ptr(y32, _fp))
+    return _epilogue(y32, epilogue, residual), y32
+
+
+def _epilogue(y32, epilogue, residual):
+    """fp16 output of the fp32 dequantized values, after the optional GELU or residual add."""
+    M, N = y32.shape
     if epilogue == EPI_NONE:
         Y = y32.astype(np.float16)
     elif epilogue == EPI_GELU:
@@ -365,7 +375,7 @@ def dequant(acc, x_scale, per_token: bool, w_scale, epilogue: int = EPI_NONE, re
         Y = (y32 + np.asarray(residual, np.float16).astype(np.float32)).astype(np.float16)
     else:
         raise ValueError(epilogue)
-    return Y, y32
+    return Y
 
 
 def gemm(xq_codes, x_scale, per_token, w_codes, w_scale, epilogue=EPI_NONE, residual=None):
@@ -395,15 +405,116 @@ def calibrate_table(X_samples_per_step, perm, U, B: int, R=None, bits: int = 4) 
     return table
 
 
+# ----------------------------------------------------------------------------------------------
+# Group-wise (per rotation block) per-step activation scales: the integer-GEMM form of the pages'
+# per-channel act_scale_table [P1 "Y tuong paper": the table is per layer, per step, per channel;
+# P2 item 2 "Calibracao por Passo"]. One scale per (linear, step, rotation block): the integer GEMM
+# keeps one int32 partial per block and folds it in with that block's scale.
+# ----------------------------------------------------------------------------------------------
+
+def quantize_act_grouped(Xr, B: int, table, num_steps=None, step=None) -> dict:
+    """Int4 quantization of rotated activations Xr (fp64 [M, K]) with the scales of row `step` of a
+    [num_steps, K/B] table: position k uses s = table[step][k // B]. Same step-range rules as the
+    per-step mode. Returns dict(x32, v, codes, scale (the K/B scales used), xq)."""
+    Xr = np.ascontiguousarray(np.asarray(Xr, np.float64))
+    M, K = Xr.shape
+    _check_block(K, B)
+    table = np.asarray(table, np.float32)
+    if table.ndim != 2 or table.shape[1] != K // B:
+        raise ValueError("grouped act_scale_table must be [num_steps, K / block]")
+    if num_steps is None:
+        num_steps = table.shape[0]
+    if table.shape[0] < num_steps:
+        raise ValueError("act_scale_table is shorter than the number of steps")
+    if step is None or not (0 <= step < num_steps):
+        raise ValueError(f"step {step} outside [0, {num_steps})")
+    sg = np.ascontiguousarray(table[step])
+    if not np.all((sg > 0) & np.isfinite(sg)):
+        raise ValueError("act_scale_table entries must be positive and finite")
+    x32 = np.empty((M, K), np.float32)
+    v = np.empty((M, K), np.float32)
+    q = np.empty((M, K), np.int8)
+    _load().orc_act_quant_grouped(_ptr(Xr, _dp), M, K, B, _ptr(sg, _fp), _ptr(x32, _fp),
+                                  _ptr(v, _fp), _ptr(q, _i8p))
+    xq = pack_int4(q) if K % 2 == 0 else None
+    return {"x32": x32, "v": v, "codes": q, "scale": sg.copy(), "xq": xq}
+
+
+def int_gemm_grouped(q, p, B: int) -> np.ndarray:
+    """acc[g] = q[:, block g] . p[:, block g]^T in int64 ([K/B, M, N])."""
+    q = np.ascontiguousarray(np.asarray(q, np.int8))
+    p = np.ascontiguousarray(np.asarray(p, np.int8))
+    M, K = q.shape
+    N = p.shape[0]
+    assert p.shape[1] == K and K % B == 0
+    acc = np.empty((K // B, M, N), np.int64)
+    _load().orc_int_gemm_grouped(_ptr(q, _i8p), _ptr(p, _i8p), M, N, K, B, _ptr(acc, _i64p))
+    return acc
+
+
+def dequant_grouped(acc_g, x_scales, w_scale, epilogue: int = EPI_NONE, residual=None):
+    """y = fma chain over blocks in order (y = fmaf(acc_g, s_g, y) from y = 0), then
+    fp32(y * s_w[n]), then the epilogue as in dequant. Returns (Y fp16, y32)."""
+    acc_g = np.ascontiguousarray(np.asarray(acc_g, np.int64))
+    nb, M, N = acc_g.shape
+    if np.any(np.abs(acc_g.sum(axis=0)) >= 2 ** 31):
+        raise OverflowError("accumulator leaves int32")
+    sg = np.ascontiguousarray(np.asarray(x_scales, np.float32).reshape(-1))
+    assert sg.shape[0] == nb
+    sw = np.ascontiguousarray(np.asarray(w_scale, np.float32))
+    y32 = np.empty((M, N), np.float32)
+    _load().orc_dequant_grouped(_ptr(acc_g, _i64p), nb, M, N, _ptr(sg, _fp), _ptr(sw, _fp),
+                                _ptr(y32, _fp))
+    return _epilogue(y32, epilogue, residual), y32
+
+
+def gemm_grouped(xq_codes, x_scales, w_codes, w_scale, B: int, epilogue=EPI_NONE, residual=None):
+    """Group-wise integer GEMM (int4 codes given unpacked) and dequantization."""
+    acc_g = int_gemm_grouped(xq_codes, w_codes, B)
+    Y, y32 = dequant_grouped(acc_g, x_scales, w_scale, epilogue, residual)
+    return {"acc_g": acc_g, "acc": acc_g.sum(axis=0), "Y": Y, "y32": y32}
+
+
+def calibrate_table_grouped(X_samples_per_step, perm, U, B: int, R=None) -> np.ndarray:
+    """[T, K/B] table: table[t][g] = fp32(max |fp32(x')| over every calibration sample and token of
+    step t and the channels of rotation block g, / 7) (1.0f for a zero max), the per-step
+    statistic of calibrate_table taken per block."""
+    if R is None:
+        R = rotation(U, B)
+    T = len(X_samples_per_step)
+    K = np.asarray(X_samples_per_step[0][0]).shape[1]
+    nb = K // B
+    table = np.empty((T, nb), np.float32)
+    for t in range(T):
+        amax = np.zeros(nb, np.float32)
+        for Xs in X_samples_per_step[t]:
+            x32 = rotate_rows(Xs, perm, R, B).astype(np.float32)
+            if x32.size:
+                amax = np.maximum(amax, np.abs(x32).reshape(-1, nb, B).max(axis=(0, 2)))
+        for g in range(nb):
+            table[t, g] = np.float32(float(amax[g]) / 7.0) if amax[g] > 0 else np.float32(1.0)
+    return table
+
+
 def linear(X, W, B: int, mode: str, table=None, num_steps=None, step=None, perm=None, U=None,
            epilogue=EPI_NONE, residual=None, bits: int = 4) -> dict:
     """The whole quantized linear on the CPU (W4A4, or W8A8 with bits=8): offline (perm, U, pack)
-    then runtime (rotate-quant, GEMM)."""
+    then runtime (rotate-quant, GEMM). mode "per_block" takes a [num_steps, K/B] table of
+    group-wise scales (int4 only)."""
     if perm is None:
         perm = zigzag_perm(W, B)
     if U is None:
         U = block_svd(W, perm, B)
     pw = pack_weights(W, perm, U, B, bits=bits)
+    if mode == "per_block":
+        if bits != 4:
+            raise ValueError("group-wise scales are defined for int4 activations")
+        Xr = rotate_rows(X, perm, pw["R"], B)
+        act = quantize_act_grouped(Xr, B, table, num_steps, step)
+        act["x_rot"] = Xr
+        g = gemm_grouped(act["codes"], act["scale"], pw["codes"], pw["w_scale"], B, epilogue,
+                         residual)
+        return {"perm": perm, "U": U, "pack": pw, "act": act, **g}
     act = rotate_quant_act(X, perm, U, B, mode, table, num_steps, step, R=pw["R"], bits=bits)
     g = gemm(act["codes"], act["scale"], mode == "per_token", pw["codes"], pw["w_scale"],
              epilogue, residual)

@@ -215,6 +215,53 @@ void orc_act_quant(const double *Xr, int64_t rows, int64_t K, int mode, float ta
     }
 }
 
+/* Group-wise per-step activation quantization (one scale per rotation block, the integer-GEMM
+ * form of a per-channel act_scale_table): position k uses s[k / B];
+ * q = clamp(rint(fp32(x32 * fp32(1 / s_g))), -8, 7), every step as in orc_act_quant. */
+void orc_act_quant_grouped(const double *Xr, int64_t rows, int64_t K, int64_t B, const float *s,
+                           float *x32, float *v, int8_t *q)
+{
+    for (int64_t m = 0; m < rows; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float x = (float)Xr[m * K + k];
+            x32[m * K + k] = x;
+            float r = (float)(1.0 / (double)s[k / B]);
+            float y = x * r;
+            v[m * K + k] = y;
+            q[m * K + k] = orc_clamp_code((double)rintf(y));
+        }
+}
+
+/* Integer GEMM split by rotation block: acc[g][m][n] = sum over k in block g of q[m][k] p[n][k],
+ * in int64, k increasing. */
+void orc_int_gemm_grouped(const int8_t *q, const int8_t *p, int64_t M, int64_t N, int64_t K,
+                          int64_t B, int64_t *acc)
+{
+    int64_t nb = K / B;
+    for (int64_t g = 0; g < nb; ++g)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t t = 0;
+                for (int64_t k = g * B; k < (g + 1) * B; ++k)
+                    t += (int64_t)q[m * K + k] * (int64_t)p[n * K + k];
+                acc[(g * M + m) * N + n] = t;
+            }
+}
+
+/* Group-wise dequantization: y = 0, then for g = 0, 1, ..., nb - 1: y = fmaf((float)acc_g, s_g, y)
+ * (one correctly rounded fused multiply-add per block, in block order), then y = fp32(y * s_w[n]). */
+void orc_dequant_grouped(const int64_t *acc, int64_t nb, int64_t M, int64_t N, const float *sg,
+                         const float *sw, float *y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float t = 0.0f;
+            for (int64_t g = 0; g < nb; ++g)
+                t = fmaf((float)acc[(g * M + m) * N + n], sg[g], t);
+            y[m * N + n] = t * sw[n];
+        }
+}
+
 /* Two's-complement nibble packing, two codes per byte, low nibble = even k. */
 void orc_pack(const int8_t *q, int64_t rows, int64_t K, uint8_t *out)
 {
