@@ -185,6 +185,56 @@ def setup_per_step_linear(name, bd, inputs):
     return d, lin, Xs, Ys, step
 
 
+def grouped_scales(bd, inputs, steps):
+    """Group-wise (per rotation block) per-step scales on the DiT MLP up-projection: device
+    calibration of the [8, K/128] table, then the same 8-step pass as the headline with the
+    group-wise rotate-quantize and GEMM; plus the group-wise GEMM alone on a stack-shaped
+    projection (M = 1600) against the single-scale GEMM of the same shape."""
+    torch = _torch()
+    d = inputs.linear_inputs("dit_mlp_up")
+    lin = Linear(d["W"], d["block"], bd)
+    T, M, K, N, B = d["steps"], d["M"], d["K"], d["N"], d["block"]
+    nb = K // B
+    table = torch.empty((T, nb), dtype=torch.float32, device="cuda")
+    for t in range(T):
+        stacked = dev(np.concatenate(d["X_calib"][t], axis=0))
+        bd.calibrate_act_scale_grouped(stacked, lin.perm, lin.rot, B, out=table[t])
+    lin.buffers(M, per_token=False)
+    xs = torch.empty(nb, dtype=torch.float32, device="cuda")
+    Xs = [dev(x) for x in d["X_steps"]]
+    Ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(T)]
+
+    def step():
+        for t in range(T):
+            bd.rotate_quant_act_grouped(Xs[t], lin.perm, lin.rot, B, table, T, t, xq=lin.xq,
+                                        x_scale=xs, ws=lin.act_ws)
+            bd.gemm_grouped(lin.xq, xs, lin.wq, lin.w_scale, K, B, Y=Ys[t])
+
+    ms = time_graph(step, steps, 5)
+    gemm_ms = time_kernel_calls([lambda t=t: bd.gemm_grouped(lin.xq, xs, lin.wq, lin.w_scale, K, B,
+                                                             Y=Ys[t]) for t in range(T)], 50)
+    out = {"dit_mlp_up": {"M": M, "K": K, "N": N, "block": B, "denoising_steps": T,
+                          "ms_per_step": ms, "tops": T * 2.0 * M * N * K / (ms * 1e-3) / 1e12,
+                          "gemm_us": gemm_ms * 1e3}}
+    del lin, Xs, Ys
+    g = torch.Generator(device="cuda").manual_seed(3)
+    M2, N2, K2 = 1600, 3072, 1024
+    xq = torch.randint(0, 256, (M2, K2 // 2), generator=g, dtype=torch.uint8, device="cuda")
+    wq = torch.randint(0, 256, (N2, K2 // 2), generator=g, dtype=torch.uint8, device="cuda")
+    sx = torch.rand(K2 // B, generator=g, device="cuda") * 1e-2 + 1e-3
+    sw = torch.rand(N2, generator=g, device="cuda") * 1e-2 + 1e-3
+    Y = torch.empty((M2, N2), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(256, bd.lib().w4a4_gemm_workspace_bytes(M2, N2, K2)), dtype=torch.uint8,
+                     device="cuda")
+    tg = time_kernel_calls([lambda: bd.gemm_grouped(xq, sx, wq, sw, K2, B, Y=Y)], 20)
+    tp = time_kernel_calls([lambda: bd.gemm(xq, sx[:1], False, wq, sw, K2, Y=Y, ws=ws)], 20)
+    ops = 2.0 * M2 * N2 * K2
+    out["gemm_1600x3072x1024"] = {"grouped_us": tg * 1e3, "grouped_tops": ops / (tg * 1e-3) / 1e12,
+                                  "single_scale_us": tp * 1e3,
+                                  "single_scale_tops": ops / (tp * 1e-3) / 1e12}
+    return out
+
+
 def setup_per_token_linear(name, bd, inputs):
     torch = _torch()
     d = inputs.linear_inputs(name)
@@ -434,6 +484,7 @@ def supplementary(bd, inputs, steps):
         del lin, Xs, Ys
         torch.cuda.empty_cache()
     out["cold_hbm"] = cold_hbm(bd, inputs)
+    out["group_wise_scales"] = grouped_scales(bd, inputs, max(20, steps))
     for name, w8 in (("action_stack", ()), ("action_stack_mixed", ("o", "down"))):
         info, lins, Xs, rb, step = setup_stack(bd, inputs, w8=w8)
         ms = time_graph(step, max(3, steps // 5), 2)

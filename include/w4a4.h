@@ -203,6 +203,37 @@ int w4a4_gemm_w8a8_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Group-wise per-step activation scales [vnrobo.com "Y tuong paper": the act_scale_table is per
+ * layer, per step and per channel; gist.science item 2 "Calibracao por Passo"]: the integer-GEMM
+ * form of a channel-varying table keeps one scale per (step, rotation block), and the GEMM folds
+ * each block's exact int32 partial in with that block's scale. int4 codes, fp16 activations and
+ * block 128 only (else W4A4_ERR_UNSUPPORTED); same weights, perm and `rot` as the per-step mode.
+ *  - Calibration: table_row[g] = fp32(max |fp32(x')| / 7) over every row of X and the channels of
+ *    block g (1.0f for a zero max), g in [0, K/128). Workspace: w4a4_calibrate_workspace_bytes.
+ *  - Rotate-quantize: act_scale_table is [num_steps][K/128] device floats; position k of step
+ *    `step` is quantized with s = table[step][k / 128] (r = fp32(1/s), q = clamp(rint(fp32(x' *
+ *    r)), -8, 7)); x_scale[g] receives the K/128 scales used. Step range and entry rules as in the
+ *    per-step mode. Workspace: w4a4_act_workspace_bytes(M, K, block, 0).
+ *  - GEMM: acc_g[m][n] = sum over k in block g of q p (exact), y = 0 then y = fmaf(float(acc_g),
+ *    x_scales[g], y) for g = 0, 1, ... in order (one correctly rounded fused multiply-add per
+ *    block), then Y = fp16(fp32(y * w_scale[n])) with the epilogues of w4a4_gemm. xq and wq must
+ *    be 16-byte aligned (W4A4_ERR_ALIGN); no workspace.
+ * ------------------------------------------------------------------------------------------- */
+int w4a4_calibrate_act_scale_grouped(const void *X, int x_dtype, int M, int K, int64_t ldx,
+                                     int block, const int32_t *perm, const void *rot,
+                                     float *table_row, void *ws, size_t ws_bytes,
+                                     hipStream_t stream);
+int w4a4_rotate_quant_act_grouped(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                                  const int32_t *perm, const void *rot,
+                                  const float *act_scale_table, int num_steps, int step,
+                                  uint8_t *xq, float *x_scale, float *xrot_dbg, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
+int w4a4_gemm_grouped(const uint8_t *xq, const float *x_scales, const uint8_t *wq,
+                      const float *w_scale, int M, int N, int K, int block, uint16_t *Y,
+                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr,
+                      hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Diagnostics (host only).
  * ------------------------------------------------------------------------------------------- */
 const char *w4a4_last_error(void);

@@ -76,8 +76,12 @@ def compare_codes(q_dev, q_orc, v_orc, x_orc, eps, scale_dev, scale_orc, per_tok
     diff = q_dev != q_orc
     if not diff.any():
         return 0
-    s_orc = np.asarray(scale_orc, np.float64).reshape(-1, 1)
-    s_dev = np.asarray(scale_dev, np.float64).reshape(-1, 1)
+    # scales: one per row (per-step broadcast or per-token), or a 2-D array broadcastable to the
+    # codes (one scale per column group)
+    s_orc = np.asarray(scale_orc, np.float64)
+    s_dev = np.asarray(scale_dev, np.float64)
+    s_orc = s_orc if s_orc.ndim == 2 else s_orc.reshape(-1, 1)
+    s_dev = s_dev if s_dev.ndim == 2 else s_dev.reshape(-1, 1)
     r = 1.0 / s_orc
     srel = np.abs(s_dev - s_orc) / s_orc + 2.0 ** -22
     tau = eps * r + np.abs(v_orc) * srel + 1e-6

@@ -173,3 +173,55 @@ def test_workspace_and_operand_sizes(L):
     assert L.w4a4_act_workspace_bytes(1024, 2048, 128, 1) >= 4 * 1024
     assert L.w4a4_block_svd_workspace_bytes(4096, 1024, 128) >= 1024 * 128 * 8 * 3
     assert L.w4a4_zigzag_workspace_bytes(16384) >= 16384 * 8
+
+
+# ---- group-wise scales: host-side validation (nothing is launched on these paths)
+
+def _rqg(L, *, M=16, K=256, ldx=256, block=128, dt=bd.W4A4_F16, table=FAKE, steps=8, step=3,
+         xq=FAKE, ws=NULL, wsb=0):
+    return L.w4a4_rotate_quant_act_grouped(FAKE, dt, M, K, ldx, block, FAKE, FAKE, table, steps,
+                                           step, xq, FAKE, NULL, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=64), bd.W4A4_ERR_UNSUPPORTED),           # GEMM folds one 128-k block per stage
+    (dict(dt=bd.W4A4_F32), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(step=8), bd.W4A4_ERR_STEP_RANGE),
+    (dict(step=-1), bd.W4A4_ERR_STEP_RANGE),
+    (dict(steps=0), bd.W4A4_ERR_STEP_RANGE),
+    (dict(table=NULL), bd.W4A4_ERR_ARG),                  # no per-token form of group-wise scales
+    (dict(xq=NULL), bd.W4A4_ERR_ARG),
+    (dict(K=192, ldx=192), bd.W4A4_ERR_SHAPE),
+])
+def test_rotate_quant_grouped_rejects(L, kw, code):
+    assert _rqg(L, **kw) == code
+    assert L.w4a4_last_error() != b""
+
+
+def _gg(L, *, M=16, N=64, K=256, block=128, xq=FAKE, wq=FAKE, epi=0, res=NULL, ldr=0, ldy=64):
+    return L.w4a4_gemm_grouped(xq, FAKE, wq, FAKE, M, N, K, block, FAKE, ldy, epi, res, ldr, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=64), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(K=320), bd.W4A4_ERR_SHAPE),
+    (dict(xq=ctypes.c_void_p(0x10008)), bd.W4A4_ERR_ALIGN),
+    (dict(wq=ctypes.c_void_p(0x10004)), bd.W4A4_ERR_ALIGN),
+    (dict(ldy=32), bd.W4A4_ERR_SHAPE),
+    (dict(epi=2), bd.W4A4_ERR_ARG),                       # residual epilogue without residual
+    (dict(epi=7), bd.W4A4_ERR_ARG),
+    (dict(N=0), bd.W4A4_ERR_ARG),
+])
+def test_gemm_grouped_rejects(L, kw, code):
+    assert _gg(L, **kw) == code
+
+
+def test_grouped_empty_batch_and_calibration_checks(L):
+    assert _rqg(L, M=0) == bd.W4A4_OK
+    assert _gg(L, M=0, xq=NULL) == bd.W4A4_OK
+    assert L.w4a4_calibrate_act_scale_grouped(FAKE, bd.W4A4_F16, 16, 256, 256, 64, FAKE, FAKE, FAKE,
+                                              NULL, 0, NULL) == bd.W4A4_ERR_UNSUPPORTED
+    assert L.w4a4_calibrate_act_scale_grouped(FAKE, bd.W4A4_F16, 16, 256, 256, 128, FAKE, FAKE, NULL,
+                                              NULL, 0, NULL) == bd.W4A4_ERR_ARG
+    # the calibration workspace holds one maximum per rotation block even for few rows
+    assert L.w4a4_calibrate_workspace_bytes(2, 128 * 512, 128) >= 512 * 4

@@ -45,6 +45,11 @@ SIGNATURES = {
     "w4a4_gemm_w8a8": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz,
                             _vp]),
     "w4a4_gemm_w8a8_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "w4a4_calibrate_act_scale_grouped": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _sz,
+                                              _vp]),
+    "w4a4_rotate_quant_act_grouped": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                                           _vp, _vp, _sz, _vp]),
+    "w4a4_gemm_grouped": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_status_string": (ctypes.c_char_p, [_i]),
     "w4a4_abi_version": (_i, []),
@@ -245,3 +250,50 @@ def gemm_i32(xq, wq, K: int, bits: int = 4):
     fn = lib().w4a4_gemm_i32 if bits == 4 else lib().w4a4_gemm_w8a8_i32
     check(fn(_p(xq), _p(wq), M, N, K, _p(acc), _p(ws), nb, _stream()))
     return acc
+
+
+def calibrate_act_scale_grouped(X, perm, rot, block: int, out=None, ws=None):
+    """Group-wise calibration: K / block fp32 scales (one per rotation block) for one step."""
+    torch = _torch()
+    M, K = X.shape
+    if out is None:
+        out = torch.empty(K // block, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws, nb = _ws(lib().w4a4_calibrate_workspace_bytes(M, K, block), X.device)
+    else:
+        nb = ws.numel()
+    check(lib().w4a4_calibrate_act_scale_grouped(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
+                                                 _p(perm), _p(rot), _p(out), _p(ws), nb, _stream()))
+    return out
+
+
+def rotate_quant_act_grouped(X, perm, rot, block: int, table, num_steps: int, step: int, xq=None,
+                             x_scale=None, xrot_dbg=None, ws=None):
+    """Rotate-quantize with group-wise scales: table [num_steps, K / block]."""
+    torch = _torch()
+    M, K = X.shape
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(K // block, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws, nb = _ws(lib().w4a4_act_workspace_bytes(M, K, block, 0), X.device)
+    else:
+        nb = ws.numel()
+    check(lib().w4a4_rotate_quant_act_grouped(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
+                                              _p(perm), _p(rot), _p(table), num_steps, step, _p(xq),
+                                              _p(x_scale), _p(xrot_dbg), _p(ws), nb, _stream()))
+    return xq, x_scale
+
+
+def gemm_grouped(xq, x_scales, wq, w_scale, K: int, block: int, Y=None, epilogue: int = EPI_NONE,
+                 residual=None):
+    """W4A4 GEMM with group-wise activation scales x_scales [K / block]."""
+    torch = _torch()
+    M, N = xq.shape[0], wq.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=wq.device)
+    ldr = _row_stride(residual) if residual is not None else 0
+    check(lib().w4a4_gemm_grouped(_p(xq), _p(x_scales), _p(wq), _p(w_scale), M, N, K, block, _p(Y),
+                                  _row_stride(Y), epilogue, _p(residual), ldr, _stream()))
+    return Y

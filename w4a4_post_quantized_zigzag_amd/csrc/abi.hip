@@ -87,7 +87,9 @@ static bool act_on_mfma(int xdt, int B) { return xdt == W4A4_F16 && (B == 64 || 
 
 static size_t act_ws_bytes(int M, int K, int B, int kind)
 {
-    size_t n = (kind == KIND_STEP) ? 0 : align_up((size_t)(M > 0 ? M : 1) * sizeof(uint32_t), 256);
+    // maxima: one per row (per-token), one per rotation block (calibration, grouped or not)
+    const int nmax = (kind == KIND_CALIB) ? max(max(M, 1), K / B) : max(M, 1);
+    size_t n = (kind == KIND_STEP) ? 0 : align_up((size_t)nmax * sizeof(uint32_t), 256);
     if (M > 0 && (B == 64 || B == 128) && act_uses_permute_pass(M, K, kind != KIND_STEP))
         n += act_permute_bytes(M, K);
     return n;
@@ -96,17 +98,26 @@ static size_t act_ws_bytes(int M, int K, int B, int kind)
 static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int B,
                           const int32_t *perm, const void *rot, const float *table, int step,
                           int kind, uint8_t *xq, float *x_scale, float *xrot, void *ws,
-                          float *calib_out, hipStream_t s, bool q8 = false)
+                          float *calib_out, hipStream_t s, bool q8 = false, bool grouped = false)
 {
     int rc;
     char *w = reinterpret_cast<char *>(ws);
     uint32_t *rowmax = reinterpret_cast<uint32_t *>(w);
-    const size_t off = (kind == KIND_STEP) ? 0 : align_up((size_t)M * sizeof(uint32_t), 256);
+    const int nb = K / B;
+    const int nmax = (kind == KIND_CALIB) ? max(max(M, 1), nb) : max(M, 1);
+    const size_t off = (kind == KIND_STEP) ? 0 : align_up((size_t)nmax * sizeof(uint32_t), 256);
     const bool permute_pass = act_on_mfma(xdt, B) && perm && act_uses_permute_pass(M, K, kind != KIND_STEP);
-    // the row maxima start at zero: cleared by the permutation pass when there is one
-    if (kind != KIND_STEP && !permute_pass &&
-        (rc = launch_fill_u32(rowmax, 0u, kind == KIND_CALIB ? 1 : M, s)))
+    // the maxima start at zero: cleared by the permutation pass (its first M entries) when there
+    // is one; group-wise scales (grouped) index the table row and the maxima by rotation block
+    const int nclear = (kind == KIND_CALIB) ? (grouped ? nb : 1) : M;
+    if (kind != KIND_STEP && (!permute_pass || nclear > M) &&
+        (rc = launch_fill_u32(rowmax, 0u, nclear, s)))
         return rc;
+    const int gstride = grouped ? 1 : 0;
+    if (grouped && kind == KIND_STEP) {
+        table += (size_t)step * nb;
+        step = 0;
+    }
     if (act_on_mfma(xdt, B)) {
         const uint16_t *xperm = nullptr;
         if (permute_pass) {
@@ -118,13 +129,13 @@ static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int
         }
         if (kind == KIND_STEP)
             return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
-                                            nullptr, xq, x_scale, xrot, xperm, q8, s);
+                                            nullptr, xq, x_scale, xrot, xperm, q8, s, gstride);
         if (kind == KIND_CALIB) {
             if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0,
                                                ACT_CALIB_MAX, rowmax, nullptr, nullptr, nullptr,
-                                               xperm, false, s)))
+                                               xperm, false, s, gstride)))
                 return rc;
-            return launch_scale_from_absmax(rowmax, calib_out, q8, s);
+            return launch_scale_from_absmax(rowmax, calib_out, q8, s, grouped ? nb : 1);
         }
         if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
                                            rowmax, nullptr, nullptr, nullptr, xperm, false, s)))
@@ -514,6 +525,102 @@ int w4a4_gemm_w8a8_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K
                        void *ws, size_t ws_bytes, hipStream_t stream)
 {
     return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, true);
+}
+
+// ------------------------------------------------------------------ group-wise scales
+
+static int check_grouped(int x_dtype, int block)
+{
+    if (block != 128)
+        return fail(W4A4_ERR_UNSUPPORTED, "group-wise scales need block 128 (got %d)", block);
+    if (x_dtype != W4A4_F16)
+        return fail(W4A4_ERR_UNSUPPORTED, "group-wise scales need fp16 activations");
+    return W4A4_OK;
+}
+
+int w4a4_calibrate_act_scale_grouped(const void *X, int x_dtype, int M, int K, int64_t ldx,
+                                     int block, const int32_t *perm, const void *rot,
+                                     float *table_row, void *ws, size_t ws_bytes,
+                                     hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if ((rc = check_grouped(x_dtype, block))) return rc;
+    if ((rc = check_matrix(X, x_dtype, M, K, ldx, "X"))) return rc;
+    if (!rot) return fail(W4A4_ERR_ARG, "rot is NULL");
+    if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
+    if (!table_row) return fail(W4A4_ERR_ARG, "table_row is NULL");
+    if (!aligned(perm, 4) || !aligned(table_row, 4)) return fail(W4A4_ERR_ALIGN, "perm / table_row misaligned");
+    if ((rc = check_ws(ws, ws_bytes, act_ws_bytes(M, K, block, KIND_CALIB)))) return rc;
+    if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, nullptr, 0, KIND_CALIB,
+                             nullptr, nullptr, nullptr, ws, table_row, stream, false, true)))
+        return rc;
+    return ok();
+}
+
+int w4a4_rotate_quant_act_grouped(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                                  const int32_t *perm, const void *rot,
+                                  const float *act_scale_table, int num_steps, int step,
+                                  uint8_t *xq, float *x_scale, float *xrot_dbg, void *ws,
+                                  size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if ((rc = check_grouped(x_dtype, block))) return rc;
+    if ((rc = check_matrix(X, x_dtype, M, K, ldx, "X"))) return rc;
+    if (!rot) return fail(W4A4_ERR_ARG, "rot is NULL");
+    if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
+    if (!aligned(perm, 4)) return fail(W4A4_ERR_ALIGN, "perm misaligned");
+    if (!act_scale_table) return fail(W4A4_ERR_ARG, "group-wise scales need the table");
+    if (num_steps <= 0) return fail(W4A4_ERR_STEP_RANGE, "num_steps = %d must be positive", num_steps);
+    if (step < 0 || step >= num_steps)
+        return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
+    if (!aligned(act_scale_table, 4)) return fail(W4A4_ERR_ALIGN, "table misaligned");
+    if (M > 0 && (!xq || !x_scale)) return fail(W4A4_ERR_ARG, "xq and x_scale are required");
+    if (!aligned(x_scale, 4) || !aligned(xrot_dbg, 4))
+        return fail(W4A4_ERR_ALIGN, "x_scale / xrot_dbg misaligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_act_workspace_bytes(M, K, block, 0)))) return rc;
+    if (M == 0) return ok();
+    if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
+                             KIND_STEP, xq, x_scale, xrot_dbg, ws, nullptr, stream, false, true)))
+        return rc;
+    return ok();
+}
+
+int w4a4_gemm_grouped(const uint8_t *xq, const float *x_scales, const uint8_t *wq,
+                      const float *w_scale, int M, int N, int K, int block, uint16_t *Y,
+                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr,
+                      hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K, false))) return rc;
+    if (block != 128)
+        return fail(W4A4_ERR_UNSUPPORTED, "group-wise scales need block 128 (got %d)", block);
+    if (K % block) return fail(W4A4_ERR_SHAPE, "K = %d not a multiple of block %d", K, block);
+    if (epilogue != W4A4_EPI_NONE && epilogue != W4A4_EPI_GELU && epilogue != W4A4_EPI_RESIDUAL)
+        return fail(W4A4_ERR_ARG, "unknown epilogue %d", epilogue);
+    if (!wq || !w_scale || !x_scales || (M > 0 && (!xq || !Y)))
+        return fail(W4A4_ERR_ARG, "NULL operand");
+    if (ldy < N) return fail(W4A4_ERR_SHAPE, "ldy = %lld < N = %d", (long long)ldy, N);
+    if (epilogue == W4A4_EPI_RESIDUAL && (!residual || ldr < N))
+        return fail(W4A4_ERR_ARG, "residual epilogue needs residual with ldr >= N");
+    if (!aligned(xq, 16) || !aligned(wq, 16))
+        return fail(W4A4_ERR_ALIGN, "group-wise GEMM needs 16-byte aligned xq and wq");
+    if (!aligned(x_scales, 4) || !aligned(w_scale, 4) || !aligned(Y, 2) || !aligned(residual, 2))
+        return fail(W4A4_ERR_ALIGN, "scales / Y / residual misaligned");
+    if (M == 0) return ok();
+    GemmEpilogue epi{};
+    epi.x_scale = x_scales;
+    epi.x_scale_per_token = 0;
+    epi.w_scale = w_scale;
+    epi.Y = Y;
+    epi.ldy = ldy;
+    epi.mode = epilogue;
+    epi.residual = residual;
+    epi.ldr = ldr;
+    epi.acc_out = nullptr;
+    rc = launch_gemm_grouped(xq, wq, M, N, K, epi, stream);
+    return rc ? rc : ok();
 }
 
 }  // extern "C"

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     const _Float16 *__restrict__ rhi, const _Float16 *__restrict__ rlo,
     const float *__restrict__ table, int step, uint32_t *__restrict__ rowmax,
     uint8_t *__restrict__ xq, float *__restrict__ x_scale, float *__restrict__ xrot_dbg,
-    int rows_per_wg)
+    int rows_per_wg, int gstride)
 {
 #pragma clang fp contract(off)
     constexpr int KK = B / 32;       // 32-wide k steps
@@ -230,9 +230,9 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
 
     float s_step = 1.0f, rcp_step = 1.0f;
     if (MODE == ACT_PER_STEP) {
-        s_step = step_scale(table, step);
+        s_step = step_scale(table, step + b * gstride);
         rcp_step = (float)(1.0 / (double)s_step);
-        if (blockIdx.x == 0 && b == 0 && tid == 0) x_scale[0] = s_step;
+        if (blockIdx.x == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s_step;
     }
 
     const int row_begin = blockIdx.x * rows_per_wg;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
                     // one atomic per tile: reduce the tile's rows within wave 0
                     float t = a;
                     for (int off = 32; off > 0; off >>= 1) t = fmaxf(t, __shfl_xor(t, off));
-                    if (tid == 0) atomicMax(&rowmax[0], __float_as_uint(t));
+                    if (tid == 0) atomicMax(&rowmax[b * gstride], __float_as_uint(t));
                 }
             }
         }
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const _Float16 *__restrict__ rhi,
     const _Float16 *__restrict__ rlo, const float *__restrict__ table, int step,
     uint32_t *__restrict__ rowmax, uint8_t *__restrict__ xq, float *__restrict__ x_scale,
-    float *__restrict__ xrot_dbg, int rows_per_wg, int row_groups)
+    float *__restrict__ xrot_dbg, int rows_per_wg, int row_groups, int gstride)
 {
 #pragma clang fp contract(off)
     constexpr int KK = B / 32, JW = B / 4, JF = JW / 16, MF = MT / 16;
@@ -521,9 +521,9 @@ __global__ __launch_bounds__(256) void k_rq_ring(
         }
     float rs_step = 0.0f;
     if (MODE == ACT_PER_STEP) {
-        const float s = step_scale(table, step);
+        const float s = step_scale(table, step + b * gstride);
         rs_step = (float)(1.0 / (double)s) * LO;
-        if (blockIdx.x == 0 && b == 0 && tid == 0) x_scale[0] = s;
+        if (rgi == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s;
     }
     if (MODE == ACT_TOKEN_QUANT) __syncthreads();
 
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
                 } else {
                     float u = a;
                     for (int off = 32; off > 0; off >>= 1) u = fmaxf(u, __shfl_xor(u, off));
-                    if (tid == 0) atomicMax(&rowmax[0], __float_as_uint(u));
+                    if (tid == 0) atomicMax(&rowmax[b * gstride], __float_as_uint(u));
                 }
             }
         } else {
@@ -638,7 +638,8 @@ __global__ __launch_bounds__(256) void k_rq_small(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const int32_t *__restrict__ perm,
     const _Float16 *__restrict__ rhi, const _Float16 *__restrict__ rlo,
     const float *__restrict__ table, int step, uint32_t *__restrict__ rowmax,
-    uint8_t *__restrict__ xq, float *__restrict__ x_scale, float *__restrict__ xrot_dbg)
+    uint8_t *__restrict__ xq, float *__restrict__ x_scale, float *__restrict__ xrot_dbg,
+    int gstride)
 {
 #pragma clang fp contract(off)
     constexpr int KK = B / 32, JW = B / 4, JF = JW / 16;
@@ -686,9 +687,9 @@ __global__ __launch_bounds__(256) void k_rq_small(
         }
     float rs = 0.0f;
     if (MODE == ACT_PER_STEP) {
-        const float s = step_scale(table, step);
+        const float s = step_scale(table, step + b * gstride);
         rs = (float)(1.0 / (double)s) * LO;
-        if (si == 0 && b == 0 && tid == 0) x_scale[0] = s;
+        if (si == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -730,7 +731,7 @@ __global__ __launch_bounds__(256) void k_rq_small(
             } else {
 #pragma unroll
                 for (int off = 8; off > 0; off >>= 1) u = fmaxf(u, __shfl_xor(u, off));
-                if (tid == 0) atomicMax(&rowmax[0], __float_as_uint(u));
+                if (tid == 0) atomicMax(&rowmax[b * gstride], __float_as_uint(u));
             }
         }
         return;
@@ -1048,7 +1049,7 @@ static int rq_rows_per_wg(int M, int nb)
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                             const uint16_t *xperm, bool q8, hipStream_t s)
+                             const uint16_t *xperm, bool q8, hipStream_t s, int gstride)
 {
     if (M == 0) return W4A4_OK;
     RotLayout L = rot_layout(K, B);
@@ -1063,7 +1064,7 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
 #define W4A4_SMALL(MODEV, BV, DV, QV)                                                              \
     hipLaunchKernelGGL((k_rq_small<MODEV, BV, DV, QV>), grid_s, dim3(256), 0, s, x, ldx, M, K,     \
-                       perm, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg)
+                       perm, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, gstride)
 #define W4A4_SMALL_B(MODEV, DV, QV)                                                                \
     if (B == 128) W4A4_SMALL(MODEV, 128, DV, QV); else W4A4_SMALL(MODEV, 64, DV, QV);
 #define W4A4_SMALL_Q(MODEV)                                                                        \
@@ -1105,7 +1106,8 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
             attr_set = true;                                                                       \
         }                                                                                          \
         hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV>), grid_r, dim3(256), lds, s, src, ld, M,  \
-                           K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r, groups); \
+                           K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r, groups, \
+                           gstride);                                                               \
     } while (0)
 #define W4A4_RING_B(MODEV, DV, QV)                                                                 \
     if (B == 128) W4A4_RING(MODEV, 128, DV, QV); else W4A4_RING(MODEV, 64, DV, QV);
@@ -1125,7 +1127,7 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
     }
 #define W4A4_RQ(MODEV, BV, GV, QV)                                                                 \
     hipLaunchKernelGGL((k_rq_mfma<MODEV, BV, GV, QV>), grid, dim3(256), 0, s, src, ld, M, K, perm, \
-                       rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw)
+                       rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw, gstride)
 #define W4A4_RQ_B(MODEV, QV)                                                                       \
     if (B == 128) { if (gather) W4A4_RQ(MODEV, 128, true, QV); else W4A4_RQ(MODEV, 128, false, QV); } \
     else { if (gather) W4A4_RQ(MODEV, 64, true, QV); else W4A4_RQ(MODEV, 64, false, QV); }
@@ -1165,15 +1167,19 @@ int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t 
     return check_launch("permute rows");
 }
 
-__global__ void k_scale_from_absmax(const uint32_t *amax, float *out, int q8)
+// count scales (one per calibration group: the whole linear, or each rotation block)
+__global__ void k_scale_from_absmax(const uint32_t *amax, float *out, int q8, int count)
 {
-    out[0] = q8 ? scale_from_absmax_q<true>(__uint_as_float(amax[0]))
-                : scale_from_absmax(__uint_as_float(amax[0]));
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    out[i] = q8 ? scale_from_absmax_q<true>(__uint_as_float(amax[i]))
+                : scale_from_absmax(__uint_as_float(amax[i]));
 }
 
-int launch_scale_from_absmax(const uint32_t *amax, float *out, bool q8, hipStream_t s)
+int launch_scale_from_absmax(const uint32_t *amax, float *out, bool q8, hipStream_t s, int count)
 {
-    hipLaunchKernelGGL(k_scale_from_absmax, dim3(1), dim3(1), 0, s, amax, out, q8 ? 1 : 0);
+    hipLaunchKernelGGL(k_scale_from_absmax, dim3((count + 255) / 256), dim3(256), 0, s, amax, out,
+                       q8 ? 1 : 0, count);
     return check_launch("scale from absmax");
 }
 

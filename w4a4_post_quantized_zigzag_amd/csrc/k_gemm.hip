@@ -431,6 +431,86 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_big(
     }
 }
 
+// Group-wise small-M GEMM (M <= 16 * MF): one 128-k rotation block per window. The 4 waves take
+// the blocks of a group of 4 * SMG_G in turn (wave w: blocks c0 + 4 i + w), each leaving the exact
+// int32 partial tile of its block in LDS; then every thread folds the partials of its outputs into
+// fp32 in block order with one fused multiply-add per block, y = fma(float(acc_g), s_g, y), and
+// the epilogue scales by the weight scale. Operands must be 16-byte aligned with K % 128 == 0.
+constexpr int SMG_G = 2;  // blocks per wave per group
+
+template <int MF>
+__global__ __launch_bounds__(256) void k_gemm_smallm_g(const uint8_t *__restrict__ xq,
+                                                       const uint8_t *__restrict__ wq, int M,
+                                                       int N, int K, GemmEpilogue epi)
+{
+#pragma clang fp contract(off)
+    __shared__ int32_t part[4 * SMG_G][MF * 16][17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int ldp = K / 2, nb = K / 128;
+    const int ecol = tid & 15, erow = tid >> 4;
+    const int en = min(n0 + ecol, N - 1);
+    const float e_sw = epi.w_scale[en];
+    uint16_t e_res[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+        e_res[f] = (epi.mode == W4A4_EPI_RESIDUAL)
+                       ? epi.residual[(int64_t)min(erow + 16 * f, M - 1) * epi.ldr + en]
+                       : (uint16_t)0;
+    float y[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) y[f] = 0.0f;
+
+    for (int c0 = 0; c0 < nb; c0 += 4 * SMG_G) {
+        uint4 bq[SMG_G], aq[SMG_G][MF];
+        bool bv[SMG_G], av[SMG_G][MF];
+#pragma unroll
+        for (int i = 0; i < SMG_G; ++i) {
+            const int blk = c0 + 4 * i + wave;
+            const int kb = min(blk, nb - 1) * 64 + 16 * g;
+            bq[i] = load16_clamped(wq, N, n0 + r, ldp, kb, ldp, bv[i]);
+#pragma unroll
+            for (int f = 0; f < MF; ++f) aq[i][f] = load16_clamped(xq, M, f * 16 + r, ldp, kb, ldp, av[i][f]);
+        }
+#pragma unroll
+        for (int i = 0; i < SMG_G; ++i) {
+            if (c0 + 4 * i + wave >= nb) continue;
+            uint4 b0, b1;
+            widen16(zero_unless(bq[i], bv[i]), b0, b1);
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+                uint4 a0, a1;
+                widen16(zero_unless(aq[i][f], av[i][f]), a0, a1);
+                v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<v4i *>(&a0),
+                                                                *reinterpret_cast<v4i *>(&b0),
+                                                                v4i{0, 0, 0, 0}, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<v4i *>(&a1),
+                                                           *reinterpret_cast<v4i *>(&b1), acc, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) part[4 * i + wave][f * 16 + 4 * g + t][r] = acc[t] >> 8;
+            }
+        }
+        __syncthreads();
+        for (int j = 0; j < 4 * SMG_G && c0 + j < nb; ++j) {
+            const float sg = epi.x_scale[c0 + j];
+#pragma unroll
+            for (int f = 0; f < MF; ++f) y[f] = fmaf((float)part[j][erow + 16 * f][ecol], sg, y[f]);
+        }
+        __syncthreads();
+    }
+    const int n = n0 + ecol;
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+        const int m = erow + 16 * f;
+        if (m >= M || n >= N) continue;
+        float t = fp32_value(y[f] * e_sw);
+        if (epi.mode == W4A4_EPI_GELU) t = fp32_value(gelu_erf(t));
+        else if (epi.mode == W4A4_EPI_RESIDUAL) t = fp32_value(t + __half2float(__ushort_as_half(e_res[f])));
+        epi.Y[(int64_t)m * epi.ldy + n] = f32_to_f16_bits(t);
+    }
+}
+
 // Pipelined variant of the large-M GEMM for K and the k split multiples of 128 with 16-byte
 // aligned operands. Operand tiles go from global memory straight into a ring of NSTAGE LDS stages
 // with global_load_lds_dwordx4 (no staging registers), so NSTAGE-1 stages of loads are in flight
@@ -483,7 +563,8 @@ enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_
 // Q8: int8 operands (W8A8): a staged 64-byte row is 64 k, each fragment read is already an MFMA
 // operand (one v_mfma_i32_16x16x64_i8 per fragment pair and stage, no widening) and the sums are
 // not scaled by 256.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT, bool Q8>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT, bool Q8,
+          bool GS = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
     int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
@@ -547,6 +628,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    // GS (group-wise scales): a stage is one 128-k rotation block; its exact partial is folded into
+    // yf with one fused multiply-add by the block's scale (epi.x_scale[block]), in block order
+    float yf[GS ? FM : 1][GS ? FN : 1][4];
+    if (GS) {
+#pragma unroll
+        for (int i = 0; i < (GS ? FM : 1); ++i)
+#pragma unroll
+            for (int j = 0; j < (GS ? FN : 1); ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yf[i][j][r] = 0.0f;
+    }
 
 #pragma unroll
     for (int p = 0; p < NSTAGE - 1; ++p)
@@ -599,9 +691,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
             const v4i a0 = *reinterpret_cast<v4i *>(&lo), a1 = *reinterpret_cast<v4i *>(&hi);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0[j], a0, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0[j], a0, GS ? v4i{0, 0, 0, 0} : acc[i][j], 0, 0, 0);
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1[j], a1, acc[i][j], 0, 0, 0);
             }
+        }
+        if (GS) {
+            const float sg = epi.x_scale[st];
+#pragma unroll
+            for (int i = 0; i < (GS ? FM : 1); ++i)
+#pragma unroll
+                for (int j = 0; j < (GS ? FN : 1); ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        yf[i][j][r] = fmaf((float)(acc[i][j][r] >> 8), sg, yf[i][j][r]);
         }
         // Schedule: all fragment reads first, the B widening and the first A widening, then each
         // MFMA followed by up to two VALU ops (the next A fragment's widening) so the VALU work
@@ -650,7 +752,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         uint32_t rsd[FM][FN][2];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            xsc[i] = epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
+            xsc[i] = GS ? 0.0f
+                        : epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = ncol + j * 16;
@@ -691,8 +794,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                 if (PE == PE_RESIDUAL && !VEC_OUT) residual4(m, n, rsd[i][j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    y[r] = fp32_value((float)(acc[i][j][r] >> SHIFT) * xsc[i]);
-                    y[r] = fp32_value(y[r] * wsc[j][r]);
+                    if (GS) {
+                        y[r] = fp32_value(yf[GS ? i : 0][GS ? j : 0][r] * wsc[j][r]);
+                    } else {
+                        y[r] = fp32_value((float)(acc[i][j][r] >> SHIFT) * xsc[i]);
+                        y[r] = fp32_value(y[r] * wsc[j][r]);
+                    }
                     if (PE == PE_GELU) y[r] = fp32_value(gelu_erf(y[r]));
                     if (PE == PE_RESIDUAL) {
                         const uint32_t hv = rsd[i][j][r >> 1] >> (16 * (r & 1));
@@ -830,30 +937,30 @@ static void launch_big(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, co
 
 constexpr int PIPE_STAGES = 4;
 
-template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8>
+template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = false>
 static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
     const size_t lds = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
-    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8>;
+    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>;
     static bool attr_set = false;  // once per process and instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(W4A4_ERR_HIP, "gemm LDS request: %s", hipGetErrorString(e));
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8>), grid,
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>), grid,
                        dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
     return W4A4_OK;
 }
 
-template <int BM, int BN, int WM, int WN, bool Q8>
+template <int BM, int BN, int WM, int WN, bool Q8, bool GS = false>
 static int launch_pipe_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
-    if (partial || epi.mode == GEMM_OUT_I32)
+    if (!GS && (partial || epi.mode == GEMM_OUT_I32))
         return launch_pipe_e<BM, BN, WM, WN, PE_INT32, false, Q8>(grid, s, xq, wq, M, N, K, k_split,
                                                                  tm, tn, epi, partial);
     // 4-column groups: 8-byte Y / residual accesses and 16-byte weight-scale loads
@@ -862,10 +969,10 @@ static int launch_pipe_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
                     (epi.mode != W4A4_EPI_RESIDUAL ||
                      (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
 #define W4A4_PIPE_E(PEV)                                                                           \
-    return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, \
-                                                             tn, epi, partial)                     \
-              : launch_pipe_e<BM, BN, WM, WN, PEV, false, Q8>(grid, s, xq, wq, M, N, K, k_split,   \
-                                                              tm, tn, epi, partial);
+    return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true, Q8, GS>(grid, s, xq, wq, M, N, K, k_split, \
+                                                                 tm, tn, epi, partial)             \
+              : launch_pipe_e<BM, BN, WM, WN, PEV, false, Q8, GS>(grid, s, xq, wq, M, N, K,        \
+                                                                  k_split, tm, tn, epi, partial);
     if (epi.mode == W4A4_EPI_GELU) { W4A4_PIPE_E(PE_GELU) }
     if (epi.mode == W4A4_EPI_RESIDUAL) { W4A4_PIPE_E(PE_RESIDUAL) }
     W4A4_PIPE_E(PE_NONE)
@@ -884,6 +991,39 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
         return launch_pipe_t<128, 256, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
                                                  partial);
     return launch_pipe_t<128, 128, 2, 2, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+}
+
+// Group-wise GEMM (per rotation block activation scales in epi.x_scale[K / 128]): the grouped
+// small-M kernel for M <= 64, else the pipelined kernel with GS (one block per stage, no K split,
+// the 128-row tiles whose registers hold the fp32 accumulators). The caller guarantees
+// K % 128 == 0 and 16-byte aligned operands.
+int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int K,
+                        const GemmEpilogue &epi, hipStream_t s)
+{
+    if (M == 0) return W4A4_OK;
+    if (M <= SMALL_M) {
+        dim3 g((N + 15) / 16);
+        const int mf = (M + 15) / 16;
+        if (mf == 1) hipLaunchKernelGGL(k_gemm_smallm_g<1>, g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+        else if (mf == 2) hipLaunchKernelGGL(k_gemm_smallm_g<2>, g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+        else if (mf == 3) hipLaunchKernelGGL(k_gemm_smallm_g<3>, g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+        else hipLaunchKernelGGL(k_gemm_smallm_g<4>, g, dim3(256), 0, s, xq, wq, M, N, K, epi);
+        return check_launch("gemm grouped small-M");
+    }
+    // 128 x 256 tiles unless 128 x 128 tiles take fewer rounds of 256 compute units at their
+    // (lower) per-tile efficiency
+    const int tm = (M + 127) / 128, tn2 = (N + 255) / 256, tn3 = (N + 127) / 128;
+    const double t2 = std::ceil(tm * (double)tn2 / 256.0) * 2.0 / 0.85;
+    const double t3 = std::ceil(tm * (double)tn3 / 256.0) * 1.0 / 0.6;
+    int rc;
+    if (t2 <= t3)
+        rc = launch_pipe_t<128, 256, 1, 4, false, true>(dim3(tm * tn2, 1), s, xq, wq, M, N, K, K, tm,
+                                                        tn2, epi, nullptr);
+    else
+        rc = launch_pipe_t<128, 128, 2, 2, false, true>(dim3(tm * tn3, 1), s, xq, wq, M, N, K, K, tm,
+                                                        tn3, epi, nullptr);
+    if (rc != W4A4_OK) return rc;
+    return check_launch("gemm grouped");
 }
 
 // q8: int8 operands [rows][K] (W8A8); the caller guarantees K % 64 == 0 and 16-byte aligned

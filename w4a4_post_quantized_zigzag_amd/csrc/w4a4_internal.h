@@ -83,7 +83,8 @@ int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B
                         ActMode mode, uint32_t *rowmax, uint8_t *xq, float *x_scale,
                         float *xrot_dbg, bool q8, hipStream_t s);
 // q8 (here and below): int8 codes [M][K] with scales max / 127 instead of packed int4 and max / 7
-int launch_scale_from_absmax(const uint32_t *amax, float *out, bool q8, hipStream_t s);
+int launch_scale_from_absmax(const uint32_t *amax, float *out, bool q8, hipStream_t s,
+                             int count = 1);
 // fp16 activations with block 64 or 128: MFMA rotation; xperm (optional) holds rows already in
 // zigzag order, written by launch_permute_rows (which also clears zero_row[0..M) when given).
 bool act_uses_permute_pass(int M, int K, int per_token);
@@ -99,7 +100,7 @@ int launch_rotate_quant_hadamard(const void *X, int x_dtype, int M, int K, int64
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                             const uint16_t *xperm, bool q8, hipStream_t s);
+                             const uint16_t *xperm, bool q8, hipStream_t s, int gstride = 0);
 
 // GEMM (k_gemm.hip)
 struct GemmEpilogue {
@@ -118,6 +119,9 @@ constexpr int GEMM_OUT_I32 = 100;
 size_t gemm_workspace(int M, int N, int K, bool q8);
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
                 void *ws, size_t ws_bytes, hipStream_t s, bool q8);
+// group-wise activation scales epi.x_scale[K / 128] (int4, K % 128 == 0, 16-byte aligned operands)
+int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int K,
+                        const GemmEpilogue &epi, hipStream_t s);
 
 // calibration (k_calib.hip)
 size_t zigzag_workspace(int K);
