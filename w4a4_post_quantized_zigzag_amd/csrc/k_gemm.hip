@@ -878,7 +878,7 @@ __global__ void k_splitk_epilogue4(const int32_t *__restrict__ partial, int spli
 }
 
 struct GemmPlan {
-    int kind;  // 0 small-M, 1 = 256x256, 2 = 128x256, 3 = 128x128
+    int kind;  // 0 small-M, 1 = 256x256, 2 = 128x256, 3 = 128x128, 4 = 64x128 (pipelined only)
     int bm, bn, splits, k_split;
 };
 
@@ -886,23 +886,30 @@ struct GemmPlan {
 // units times the per-tile MFMA time (discounted for smaller wave tiles, whose LDS traffic per MFMA
 // is higher), plus the write and read of split-K partials. kg is the k granularity of a stage (128
 // for packed int4, 64 for int8 operands).
-static GemmPlan plan_gemm(int M, int N, int K, int kg)
+static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe)
 {
     GemmPlan best{0, 0, 16, 1, K};
     if (M <= SMALL_M) return best;
+    // 64 x 128 tiles (kind 4) exist only in the pipelined kernel; they double the workgroups of a
+    // grid that would leave compute units idle, at a lower per-tile efficiency
     struct Cand { int kind, bm, bn; double eff; };
-    const Cand cands[] = {{1, 256, 256, 1.0}, {2, 128, 256, 0.85}, {3, 128, 128, 0.6}};
+    const Cand cands[] = {{1, 256, 256, 1.0}, {2, 128, 256, 0.85}, {3, 128, 128, 0.6},
+                          {4, 64, 128, 0.35}};
+    constexpr double ROUND_FIXED = 3e-6;  // prologue, epilogue and drain of one round of tiles
     double best_t = 1e30;
     for (const Cand &c : cands) {
+        if (c.kind == 4 && !pipe) continue;
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         for (int splits = 1; splits <= 16; splits *= 2) {
+            if (c.kind == 4 && splits > 1) continue;
             int k_split = ((K + splits - 1) / splits + kg - 1) / kg * kg;
             if (k_split > MAX_K_SPLIT) continue;
             const int real_splits = (K + k_split - 1) / k_split;
             if (real_splits != splits) continue;
             if (splits > 1 && k_split < 1024) continue;
             const double rounds = std::ceil(tiles * splits / 256.0);
-            const double t_c = rounds * 2.0 * c.bm * c.bn * k_split / (8192.0 * 2.4e9 * c.eff);
+            const double t_c = rounds * (2.0 * c.bm * c.bn * k_split / (8192.0 * 2.4e9 * c.eff) +
+                                         ROUND_FIXED);
             const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 4e12 + 3e-6 : 0.0;
             const double t = t_c + t_r;
             if (t < best_t * 0.98) {
@@ -916,9 +923,15 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg)
 
 size_t gemm_workspace(int M, int N, int K, bool q8)
 {
-    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS);
-    if (p.splits <= 1) return 0;
-    return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t);
+    // the launch plans with or without the pipelined kernel (operand alignment decides): enough
+    // for either
+    size_t need = 0;
+    for (int pipe = 0; pipe < 2; ++pipe) {
+        GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe != 0);
+        if (p.splits > 1)
+            need = std::max(need, (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t));
+    }
+    return need;
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -987,9 +1000,17 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
     if (kind == 1)
         return launch_pipe_t<256, 256, 2, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
                                                  partial);
+    // the GELU epilogue is VALU-heavy: with two waves per SIMD (8 waves on the same tile) one
+    // wave's epilogue runs under the other's matrix work
+    if (kind == 2 && !partial && epi.mode == W4A4_EPI_GELU)
+        return launch_pipe_t<128, 256, 2, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
+                                                 partial);
     if (kind == 2)
         return launch_pipe_t<128, 256, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
                                                  partial);
+    if (kind == 4)
+        return launch_pipe_t<64, 128, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
+                                                partial);
     return launch_pipe_t<128, 128, 2, 2, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
 }
 
@@ -1032,9 +1053,10 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
                 void *ws, size_t ws_bytes, hipStream_t s, bool q8)
 {
     if (M == 0) return W4A4_OK;
-    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS);
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
+    const bool pipe = q8 || (vec && K % BG_KS == 0);
+    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe);
     if (p.kind == 0) {
         dim3 g((N + 15) / 16);
         const int mf = (M + 15) / 16;
@@ -1064,7 +1086,7 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     if (q8) {
         int rc = launch_pipe<true>(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
         if (rc != W4A4_OK) return rc;
-    } else if (vec && K % BG_KS == 0) {
+    } else if (pipe) {
         int rc = launch_pipe<false>(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
         if (rc != W4A4_OK) return rc;
     } else if (p.kind == 1)
