@@ -93,7 +93,11 @@ def test_stack_mixed_w8a8():
     assert [ds.layers[0][n].bits for n in LINEARS] == [4, 8, 4, 8]
     for li in range(L):
         for n in LINEARS:
-            assert np.array_equal(host(ds.layers[li][n].wq), layers[li][n]["pack"]["wq"])
+            lin = ds.layers[li][n]
+            want = layers[li][n]["pack"]["wq"]
+            if lin.row_perm is not None:        # rows stored in the consumer's zigzag order
+                want = want[host(lin.row_perm)]
+            assert np.array_equal(host(lin.wq), want)
     ds.set_tables(tables)
     for t in range(T):
         outs_o, outs_d = [], []
@@ -106,3 +110,23 @@ def test_stack_mixed_w8a8():
     ds2.calibrate(A["X_calib"])
     got = host(ds2.layers[0]["o"].table)
     assert np.allclose(got, tables[0]["o"], rtol=2e-3, atol=0)
+
+
+def test_folded_permutations_change_nothing():
+    # O and down read producer outputs already in their zigzag order (perm = NULL) when the
+    # permutation is folded into QKV's V rows and up's rows: every output must be bit-identical to
+    # the unfolded stack, which gathers through perm
+    L, h, f, M, T = 2, 256, 1024, 300, 1
+    W = inputs.stack_weights(layers=L, hidden=h, ffn=f, seed=31)
+    A = inputs.stack_activations(M=M, hidden=h, steps=T, calib=1, seed=31)
+    layers = oracle.stack_prepare(W, B)
+    tables = oracle.stack_calibrate(layers, A["X_calib"], B)
+    outs = []
+    for fold in (False, True):
+        ds = DeviceStack(W, B, T, calib=_device_calib(layers), fold_perms=fold)
+        ds.set_tables(tables)
+        o = []
+        ds.run(dev(A["X_steps"][0]), 0, outputs=o)
+        outs.append([host(y) for y in o])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

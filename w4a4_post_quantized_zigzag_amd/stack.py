@@ -25,7 +25,12 @@ def _torch():
 
 
 class DeviceLinear:
-    def __init__(self, W, block: int, steps: int, perm=None, U=None, bits: int = 4):
+    """One linear's device state. row_perm (optional, device int64 [N]) reorders the output
+    channels: the packed weights hold rows W[row_perm], so output column j is channel row_perm[j].
+    The zigzag permutation and block SVD are computed on W itself (the row order of W does not
+    change them); only the packed rows move."""
+
+    def __init__(self, W, block: int, steps: int, perm=None, U=None, bits: int = 4, row_perm=None):
         torch = _torch()
         Wd = W if isinstance(W, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(W)).cuda()
         self.N, self.K = Wd.shape
@@ -33,7 +38,9 @@ class DeviceLinear:
         self.perm = bd.zigzag_perm(Wd, block) if perm is None else perm
         self.U = bd.block_svd(Wd, self.perm, block) if U is None else U
         self.bits = bits
-        self.wq, self.w_scale, self.rot = bd.pack_weights(Wd, self.perm, self.U, block, bits=bits)
+        Wp = Wd if row_perm is None else Wd.index_select(0, row_perm).contiguous()
+        self.wq, self.w_scale, self.rot = bd.pack_weights(Wp, self.perm, self.U, block, bits=bits)
+        self.row_perm = row_perm
         self.table = torch.empty(steps, dtype=torch.float32, device="cuda")
         self.steps = steps
 
@@ -60,20 +67,36 @@ class _Buffers:
 class DeviceStack:
     """weights: list (one per layer) of dicts qkv [3h,h], o [h,h], up [f,h], down [h,f] (fp16).
     calib: optional list of per-layer dicts name -> (perm, U) device tensors to use instead of the
-    device calibration kernels. w8: names of the linears run as W8A8 (e.g. ("o", "down"))."""
+    device calibration kernels. w8: names of the linears run as W8A8 (e.g. ("o", "down")).
+    fold_perms: the V slice of QKV and the up-projection output each feed one linear only (O and
+    down), so their producers store them directly in that consumer's zigzag order (QKV's V rows and
+    up's rows are packed permuted) and O and down quantize contiguous rows with perm = NULL. The
+    arithmetic is unchanged: a permutation is exact."""
 
-    def __init__(self, weights, block: int, steps: int, calib=None, w8=()):
+    def __init__(self, weights, block: int, steps: int, calib=None, w8=(), fold_perms: bool = True):
+        torch = _torch()
         self.block, self.steps = block, steps
         self.h = weights[0]["o"].shape[0]
         self.f = weights[0]["up"].shape[0]
+        self.fold = fold_perms
+        h = self.h
         self.layers = []
         for li, lw in enumerate(weights):
             layer = {}
-            for name in LINEARS:
-                pu = calib[li][name] if calib is not None else (None, None)
-                layer[name] = DeviceLinear(lw[name], block, steps, *pu,
-                                           bits=8 if name in w8 else 4)
-            self.layers.append(layer)
+            pu = lambda n: calib[li][n] if calib is not None else (None, None)  # noqa: E731
+            bits = lambda n: 8 if n in w8 else 4  # noqa: E731
+            for name in ("o", "down"):
+                layer[name] = DeviceLinear(lw[name], block, steps, *pu(name), bits=bits(name))
+            rp_qkv = rp_up = None
+            if fold_perms:
+                po = layer["o"].perm.to(torch.int64)
+                rp_qkv = torch.cat([torch.arange(2 * h, device="cuda", dtype=torch.int64), 2 * h + po])
+                rp_up = layer["down"].perm.to(torch.int64)
+            layer["qkv"] = DeviceLinear(lw["qkv"], block, steps, *pu("qkv"), bits=bits("qkv"),
+                                        row_perm=rp_qkv)
+            layer["up"] = DeviceLinear(lw["up"], block, steps, *pu("up"), bits=bits("up"),
+                                       row_perm=rp_up)
+            self.layers.append({n: layer[n] for n in LINEARS})
         self._bufs = {}
 
     def bufs(self, rows: int) -> _Buffers:
@@ -88,13 +111,14 @@ class DeviceStack:
             for name in LINEARS:
                 layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
 
-    def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None):
+    def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None, in_order=False):
         b = lin.bits
+        perm = None if in_order else lin.perm  # in_order: X already holds the zigzag order
         if calib:
-            bd.calibrate_act_scale(X, lin.perm, lin.rot, self.block, out=lin.table[step:step + 1],
+            bd.calibrate_act_scale(X, perm, lin.rot, self.block, out=lin.table[step:step + 1],
                                    ws=bufs.cws[lin.K], bits=b)
         xq = bufs.xq[(lin.K, b)]
-        bd.rotate_quant_act(X, lin.perm, lin.rot, self.block, None if calib else lin.table,
+        bd.rotate_quant_act(X, perm, lin.rot, self.block, None if calib else lin.table,
                             self.steps, step, xq=xq, x_scale=bufs.xs, ws=bufs.ws[lin.K], bits=b)
         bd.gemm(xq, bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
                 ws=bufs.gws[(lin.N, lin.K, b)], bits=b)
@@ -110,13 +134,24 @@ class DeviceStack:
             nxt = bufs.hs[li % 2]
             self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs)
             self._linear(layer["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
-                         bd.EPI_RESIDUAL, cur)
+                         bd.EPI_RESIDUAL, cur, in_order=self.fold)
             self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU)
-            self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2)
+            self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2,
+                         in_order=self.fold)
             if outputs is not None:
-                outputs.extend([bufs.qkv.clone(), bufs.h2.clone(), bufs.g.clone(), nxt.clone()])
+                outputs.extend([self._natural(layer["qkv"], bufs.qkv), bufs.h2.clone(),
+                                self._natural(layer["up"], bufs.g), nxt.clone()])
             cur = nxt
         return cur
+
+    @staticmethod
+    def _natural(lin, Y):
+        """Copy of Y with its columns back in the natural channel order (test hook)."""
+        if lin.row_perm is None:
+            return Y.clone()
+        out = Y.clone()
+        out[:, lin.row_perm] = Y
+        return out
 
     def calibrate(self, X_calib_per_step):
         """X_calib_per_step[t]: list of fp16 numpy arrays [rows, h] (calibration draws of step t)."""
