@@ -1,7 +1,8 @@
 """CPU oracle of the W4A4 quantized linear: zigzag permutation, composite SVD.Hadamard block
 rotation, symmetric int4 RTN / per-step / per-token quantization, integer GEMM and dequantization;
 the same steps on the int8 grid for the W8A8 linears (``bits=8``); group-wise (per rotation block)
-per-step activation scales with their block-wise GEMM (``*_grouped``, linear mode "per_block").
+per-step activation scales with their block-wise GEMM (``*_grouped``, linear mode "per_block");
+the GPTQ weight solver (``gptq_*``).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
 of ``bench.py`` may import this package. It shares no code with the GPU library and never imports
@@ -36,6 +37,10 @@ from .reference import (  # noqa: F401
     dequant_grouped,
     gemm_grouped,
     calibrate_table_grouped,
+    GPTQ_DAMP,
+    gptq_hessian,
+    gptq_factor,
+    gptq_pack,
     linear,
     stack_prepare,
     stack_run,

@@ -71,10 +71,12 @@ def _load():
     lib.orc_act_quant_grouped.argtypes = [_dp, _i64, _i64, _i64, _fp, _fp, _fp, _i8p]
     lib.orc_int_gemm_grouped.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i64, _i64p]
     lib.orc_dequant_grouped.argtypes = [_i64p, _i64, _i64, _i64, _fp, _fp, _fp]
+    lib.orc_gptq_sweep.argtypes = [_dp, _i64, _i64, _dp, _fp, _dp, _i8p]
     for f in ("orc_colnorm2", "orc_hadamard", "orc_rotation", "orc_rotate_rows", "orc_weight_rtn",
               "orc_act_quant", "orc_pack", "orc_unpack", "orc_int_gemm", "orc_int_gemm_sampled",
               "orc_dequant", "orc_gelu", "orc_weight_rtn_q", "orc_act_quant_q",
-              "orc_act_quant_grouped", "orc_int_gemm_grouped", "orc_dequant_grouped"):
+              "orc_act_quant_grouped", "orc_int_gemm_grouped", "orc_dequant_grouped",
+              "orc_gptq_sweep"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -494,6 +496,61 @@ def calibrate_table_grouped(X_samples_per_step, perm, U, B: int, R=None) -> np.n
         for g in range(nb):
             table[t, g] = np.float32(float(amax[g]) / 7.0) if amax[g] > 0 else np.float32(1.0)
     return table
+
+
+# ----------------------------------------------------------------------------------------------
+# GPTQ weight solver on calibration activations [vnrobo "Kien truc thuc thi": the backbone pack is
+# "SVD-Hadamard rotation + GPTQ pack"; "Build LLM pack": --gptq-block-size 128
+# --gptq-damp-percent 0.05]. The plain sequential form of the column sweep; the 128-column lazy
+# batches of the flag only reorder the same updates.
+# ----------------------------------------------------------------------------------------------
+
+GPTQ_DAMP = 0.05
+
+
+def gptq_hessian(X_samples, perm, U, B: int, R=None) -> np.ndarray:
+    """H = sum over the calibration samples of X'^T X' (fp64 [K, K]), X' = X[:, perm] . R the
+    rotated activations the linear quantizes."""
+    if R is None:
+        R = rotation(U, B)
+    H = None
+    for Xs in X_samples:
+        Xr = rotate_rows(Xs, perm, R, B)
+        H = Xr.T @ Xr if H is None else H + Xr.T @ Xr
+    return H
+
+
+def gptq_factor(H, damp_percent: float = GPTQ_DAMP):
+    """Upper Cholesky factor Hf of the damped inverse Hessian (Hf^T Hf = (H + d I)^-1, d =
+    damp_percent * mean(diag H)), after giving dead channels (zero diagonal) a unit diagonal.
+    Returns (Hf, dead)."""
+    H = np.array(H, np.float64, copy=True)
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    H[np.diag_indices_from(H)] += damp_percent * float(np.mean(np.diag(H)))
+    L = np.linalg.cholesky(np.linalg.inv(H))
+    return np.ascontiguousarray(L.T), dead
+
+
+def gptq_pack(W, perm, U, B: int, Hf, dead=None) -> dict:
+    """GPTQ int4 codes of the rotated weights: per-row scales are the RTN scales of W' (fixed before
+    the sweep), dead input channels are zeroed, then every row runs the sequential sweep with Hf.
+    Same outputs as pack_weights (codes, packed wq, w_scale, R)."""
+    R = rotation(U, B)
+    Wr = rotate_rows(W, perm, R, B)
+    s_w, _ = weight_rtn(Wr)
+    Ws = np.array(Wr, copy=True)
+    if dead is not None:
+        Ws[:, np.asarray(dead, bool)] = 0.0
+    Ws = np.ascontiguousarray(Ws)
+    N, K = Ws.shape
+    Hf = np.ascontiguousarray(np.asarray(Hf, np.float64))
+    assert Hf.shape == (K, K)
+    q = np.empty((N, K), np.int8)
+    row = np.empty(K, np.float64)
+    _load().orc_gptq_sweep(_ptr(Ws, _dp), N, K, _ptr(Hf, _dp), _ptr(s_w, _fp), _ptr(row, _dp),
+                           _ptr(q, _i8p))
+    return {"w_rot": Wr, "w_scale": s_w, "codes": q, "wq": pack_int4(q), "R": R}
 
 
 def linear(X, W, B: int, mode: str, table=None, num_steps=None, step=None, perm=None, U=None,

@@ -262,6 +262,29 @@ void orc_dequant_grouped(const int64_t *acc, int64_t nb, int64_t M, int64_t N, c
         }
 }
 
+/* GPTQ column sweep over the rotated weights (optimal-brain-quantization updates with the inverse
+ * Hessian's upper Cholesky factor Hf, row-major K x K): for every row n independently and for
+ * k = 0, 1, ..., K-1 in order, q = clamp(rint(w[k] / s_w[n]), -8, 7) (the row's RTN scale, fixed),
+ * err = (w[k] - q * s_w[n]) / Hf[k][k], and w[j] = w[j] - err * Hf[k][j] for j > k; fp64 with
+ * separate multiply and subtract. `w` is a K-double scratch row. */
+void orc_gptq_sweep(const double *Wr, int64_t N, int64_t K, const double *Hf, const float *s_w,
+                    double *w, int8_t *q)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) w[k] = Wr[n * K + k];
+        double s = (double)s_w[n];
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c = orc_clamp_code(rint(w[k] / s));
+            q[n * K + k] = c;
+            double err = (w[k] - (double)c * s) / Hf[k * K + k];
+            for (int64_t j = k + 1; j < K; ++j) {
+                double t = err * Hf[k * K + j];
+                w[j] = w[j] - t;
+            }
+        }
+    }
+}
+
 /* Two's-complement nibble packing, two codes per byte, low nibble = even k. */
 void orc_pack(const int8_t *q, int64_t rows, int64_t K, uint8_t *out)
 {

@@ -1,0 +1,104 @@
+"""CPU pins of the oracle's GPTQ weight solver (the pages' "SVD-Hadamard rotation + GPTQ pack",
+--gptq-damp-percent 0.05; vnrobo.com "Kien truc thuc thi", "Build LLM pack").
+
+The solver is fixed against things other than itself: a hand-worked sweep with exact binary values
+(the error of column 1 moves column 2 across a rounding boundary), the reduction to round-to-nearest
+when the Hessian has no cross terms, the defining identity of the inverse-Hessian factor, the dead
+channel rule, and the reconstruction error the method exists to lower.
+"""
+import numpy as np
+
+import oracle
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _identity_rotation(K):
+    # block size 1: every rotation block is [1], and the zigzag order is the descending norm order
+    return np.ones((K, 1, 1), np.float32)
+
+
+def test_hand_worked_sweep():
+    # one row, block size 1 (R = 1), columns already in descending-norm order; s = 0.875 / 7 = 1/8
+    W = np.array([[0.875, 0.3, 0.2, 0.0]])
+    perm = oracle.zigzag_perm(W, 1)
+    assert perm.tolist() == [0, 1, 2, 3]
+    U = _identity_rotation(4)
+    Hf = np.array([[1.0, 0.5, 0.25, 0.0],
+                   [0.0, 0.5, 1.0, 0.0],
+                   [0.0, 0.0, 2.0, 3.0],
+                   [0.0, 0.0, 0.0, 1.0]])
+    g = oracle.gptq_pack(W, perm, U, 1, Hf)
+    # k=0: 0.875/s = 7 exactly, no error; k=1: 0.3/s = 2.4 -> 2, err = 0.05 / 0.5 = 0.1, so
+    # w2 = 0.2 - 0.1 * 1.0 = 0.1 -> 0.8 -> 1 (round-to-nearest alone gives 2); k=2: err =
+    # (0.1 - 0.125) / 2 = -0.0125, w3 = 0 + 0.0125 * 3 = 0.0375 -> 0.3 -> 0
+    assert g["w_scale"].tolist() == [0.125]
+    assert g["codes"].tolist() == [[7, 2, 1, 0]]
+    assert oracle.pack_weights(W, perm, U, 1)["codes"].tolist() == [[7, 2, 2, 0]]
+
+
+def test_no_cross_terms_reduce_to_rtn():
+    rng = _rng(1)
+    N, K, B = 40, 256, 64
+    W = rng.normal(0.0, 0.02, (N, K))
+    perm = oracle.zigzag_perm(W, B)
+    U = oracle.block_svd(W, perm, B)
+    H = np.diag(rng.uniform(0.5, 2.0, K))            # uncorrelated channels
+    Hf, dead = oracle.gptq_factor(H)
+    assert not dead.any()
+    assert np.allclose(Hf, np.diag(np.diag(Hf)))        # the factor of a diagonal is diagonal
+    g = oracle.gptq_pack(W, perm, U, B, Hf)
+    r = oracle.pack_weights(W, perm, U, B)
+    assert np.array_equal(g["codes"], r["codes"])
+    assert np.array_equal(g["wq"], r["wq"])
+
+
+def test_factor_identity_and_damping():
+    rng = _rng(2)
+    K = 96
+    A = rng.standard_normal((300, K)) @ rng.standard_normal((K, K))
+    H = A.T @ A
+    Hf, dead = oracle.gptq_factor(H, 0.05)
+    Hd = H + 0.05 * np.mean(np.diag(H)) * np.eye(K)
+    assert np.allclose(np.tril(Hf, -1), 0.0)
+    assert np.all(np.diag(Hf) > 0)
+    assert np.allclose(Hf.T @ Hf @ Hd, np.eye(K), atol=1e-9)
+
+
+def test_dead_channels():
+    rng = _rng(3)
+    N, K, B = 16, 128, 64
+    W = rng.normal(0.0, 0.02, (N, K))
+    perm = oracle.zigzag_perm(W, B)
+    U = oracle.block_svd(W, perm, B)
+    H = np.eye(K) * 2.0
+    H[5, :] = H[:, 5] = 0.0                              # channel 5 never sees an activation
+    Hf, dead = oracle.gptq_factor(H)
+    assert dead.tolist() == [k == 5 for k in range(K)]
+    assert np.isclose(Hf[5, 5], 1.0 / np.sqrt(1.0 + 0.05 * np.mean(np.diag(H) + (np.arange(K) == 5))))
+    g = oracle.gptq_pack(W, perm, U, B, Hf, dead)
+    assert not g["codes"][:, 5].any()
+    r = oracle.pack_weights(W, perm, U, B)
+    assert np.array_equal(g["w_scale"], r["w_scale"])  # scales come from the weights before zeroing
+
+
+def test_gptq_lowers_the_calibration_error():
+    rng = _rng(4)
+    N, K, B = 64, 512, 128
+    W = rng.normal(0.0, 0.02, (N, K))
+    W[:, rng.choice(K, 5, replace=False)] *= 8
+    perm = oracle.zigzag_perm(W, B)
+    U = oracle.block_svd(W, perm, B)
+    mix = np.eye(K) + 0.3 * rng.standard_normal((K, K)) / np.sqrt(K)
+    X = [rng.standard_normal((200, K)) @ mix for _ in range(2)]
+    Hf, dead = oracle.gptq_factor(oracle.gptq_hessian(X, perm, U, B))
+    g = oracle.gptq_pack(W, perm, U, B, Hf, dead)
+    r = oracle.pack_weights(W, perm, U, B)
+    R = oracle.rotation(U, B)
+    Xr = np.concatenate([oracle.rotate_rows(x, perm, R, B) for x in X])
+    err = lambda p: np.linalg.norm(Xr @ (p["w_rot"] - p["codes"] * p["w_scale"][:, None]).T)  # noqa: E731
+    assert err(g) < 0.8 * err(r)
+    # the Hessian is the rotated activations' Gram matrix
+    assert np.allclose(oracle.gptq_hessian(X, perm, U, B), Xr.T @ Xr)
