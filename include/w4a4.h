@@ -234,6 +234,38 @@ int w4a4_gemm_grouped(const uint8_t *xq, const float *x_scales, const uint8_t *w
                       hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * GPTQ weight solver, offline [vnrobo.com "Kien truc thuc thi": the backbone pack is "SVD-Hadamard
+ * rotation + GPTQ pack"; "Build LLM pack": --gptq-block-size 128 --gptq-damp-percent 0.05]. It
+ * replaces round-to-nearest in the weight pack; the runtime calls are unchanged. K <= 4096 (else
+ * W4A4_ERR_UNSUPPORTED); int4 codes.
+ *  - w4a4_gptq_hessian: H = X'^T X' (accumulate != 0: H += X'^T X') in fp64 [K][K], X' = X[:, perm]
+ *    . blockdiag(U_b H_B) the rotated calibration activations (rotated in fp64 with the weight
+ *    pack's fixed-order arithmetic; every entry of H summed over rows in increasing order).
+ *  - w4a4_gptq_factor: dead[k] = (H[k][k] == 0) (dead may be NULL); H' = H with those diagonal
+ *    entries set to 1, plus damp_percent * mean(diag H') on the diagonal; Hf (fp64 [K][K], row-major)
+ *    = the upper Cholesky factor of H'^-1 (Hf^T Hf = H'^-1), computed as the reversed inverse of
+ *    the lower Cholesky factor of the index-reversed H' (no explicit inverse).
+ *  - w4a4_pack_weights_gptq: W' = W[:, perm] . blockdiag(R_b) in fp64 as in w4a4_pack_weights;
+ *    s_w[n] = fp32(max_k |W'[n][k]| / 7) (the RTN scale, fixed); dead input channels are zeroed;
+ *    then for each row and k = 0, 1, ... in order: q = clamp(rint(w[k] / s_w), -8, 7),
+ *    err = (w[k] - q s_w) / Hf[k][k], w[j] -= err * Hf[k][j] for j > k (fp64, separate multiply
+ *    and subtract). Codes packed into wq [N][K/2]; `rot` written as by w4a4_pack_weights. Given Hf,
+ *    wq and w_scale are bit-exact functions of (W, perm, U, Hf, dead).
+ * ------------------------------------------------------------------------------------------- */
+size_t w4a4_gptq_hessian_workspace_bytes(int M, int K, int block);
+int w4a4_gptq_hessian(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                      const int32_t *perm, const float *U, double *H, int accumulate, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+size_t w4a4_gptq_factor_workspace_bytes(int K);
+int w4a4_gptq_factor(const double *H, int K, double damp_percent, double *Hf, uint8_t *dead,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+size_t w4a4_pack_gptq_workspace_bytes(int N, int K, int block);
+int w4a4_pack_weights_gptq(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                           const int32_t *perm, const float *U, const double *Hf,
+                           const uint8_t *dead, uint8_t *wq, float *w_scale, void *rot, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Diagnostics (host only).
  * ------------------------------------------------------------------------------------------- */
 const char *w4a4_last_error(void);

@@ -225,3 +225,26 @@ def test_grouped_empty_batch_and_calibration_checks(L):
                                               NULL, 0, NULL) == bd.W4A4_ERR_ARG
     # the calibration workspace holds one maximum per rotation block even for few rows
     assert L.w4a4_calibrate_workspace_bytes(2, 128 * 512, 128) >= 512 * 4
+
+
+# ---- GPTQ solver: host-side validation
+
+def test_gptq_rejects(L):
+    # K above the solver's limit, bad damping, missing buffers, short workspace
+    assert L.w4a4_gptq_factor(FAKE, 8192, ctypes.c_double(0.05), FAKE, NULL, FAKE, 1 << 30,
+                              NULL) == bd.W4A4_ERR_UNSUPPORTED
+    assert L.w4a4_gptq_factor(FAKE, 256, ctypes.c_double(-1.0), FAKE, NULL, FAKE, 1 << 30,
+                              NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_gptq_factor(NULL, 256, ctypes.c_double(0.05), FAKE, NULL, FAKE, 1 << 30,
+                              NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_gptq_factor(FAKE, 256, ctypes.c_double(0.05), FAKE, NULL, FAKE, 16,
+                              NULL) == bd.W4A4_ERR_WORKSPACE
+    assert L.w4a4_gptq_hessian(FAKE, bd.W4A4_F16, 16, 8192, 8192, 128, FAKE, FAKE, FAKE, 0, FAKE,
+                               1 << 30, NULL) == bd.W4A4_ERR_UNSUPPORTED
+    assert L.w4a4_gptq_hessian(FAKE, bd.W4A4_F16, 16, 256, 256, 128, FAKE, FAKE, NULL, 0, FAKE,
+                               1 << 30, NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_pack_weights_gptq(FAKE, bd.W4A4_F16, 16, 256, 256, 128, FAKE, FAKE, NULL, NULL,
+                                    FAKE, FAKE, FAKE, FAKE, 1 << 30, NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_pack_weights_gptq(FAKE, bd.W4A4_F16, 16, 256, 256, 128, FAKE, FAKE, FAKE, NULL,
+                                    FAKE, FAKE, FAKE, FAKE, 64, NULL) == bd.W4A4_ERR_WORKSPACE
+    assert L.w4a4_pack_gptq_workspace_bytes(16, 256, 128) >= 16 * 256 * 9

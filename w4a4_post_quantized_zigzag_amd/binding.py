@@ -50,6 +50,13 @@ SIGNATURES = {
     "w4a4_rotate_quant_act_grouped": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
                                            _vp, _vp, _sz, _vp]),
     "w4a4_gemm_grouped": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp]),
+    "w4a4_gptq_hessian_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_gptq_hessian": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "w4a4_gptq_factor_workspace_bytes": (_sz, [_i]),
+    "w4a4_gptq_factor": (_i, [_vp, _i, ctypes.c_double, _vp, _vp, _vp, _sz, _vp]),
+    "w4a4_pack_gptq_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_pack_weights_gptq": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _sz, _vp]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_status_string": (ctypes.c_char_p, [_i]),
     "w4a4_abi_version": (_i, []),
@@ -297,3 +304,41 @@ def gemm_grouped(xq, x_scales, wq, w_scale, K: int, block: int, Y=None, epilogue
     check(lib().w4a4_gemm_grouped(_p(xq), _p(x_scales), _p(wq), _p(w_scale), M, N, K, block, _p(Y),
                                   _row_stride(Y), epilogue, _p(residual), ldr, _stream()))
     return Y
+
+
+def gptq_hessian(X, perm, U, block: int, H=None, accumulate: bool = False):
+    """H (+)= X'^T X' in fp64 [K, K] for the rotated calibration activations X' (GPTQ solver)."""
+    torch = _torch()
+    M, K = X.shape
+    if H is None:
+        H = torch.zeros((K, K), dtype=torch.float64, device=X.device)
+    ws, nb = _ws(lib().w4a4_gptq_hessian_workspace_bytes(M, K, block), X.device)
+    check(lib().w4a4_gptq_hessian(_p(X), _dtype_code(X), M, K, _row_stride(X), block, _p(perm),
+                                  _p(U), _p(H), 1 if accumulate else 0, _p(ws), nb, _stream()))
+    return H
+
+
+def gptq_factor(H, damp_percent: float = 0.05):
+    """Upper Cholesky factor of the damped inverse Hessian and the dead-channel flags."""
+    torch = _torch()
+    K = H.shape[0]
+    Hf = torch.empty((K, K), dtype=torch.float64, device=H.device)
+    dead = torch.empty(K, dtype=torch.uint8, device=H.device)
+    ws, nb = _ws(lib().w4a4_gptq_factor_workspace_bytes(K), H.device)
+    check(lib().w4a4_gptq_factor(_p(H), K, float(damp_percent), _p(Hf), _p(dead), _p(ws), nb,
+                                 _stream()))
+    return Hf, dead
+
+
+def pack_weights_gptq(W, perm, U, block: int, Hf, dead=None):
+    """GPTQ-quantized packed int4 weights (same outputs as pack_weights)."""
+    torch = _torch()
+    N, K = W.shape
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    w_scale = torch.empty(N, dtype=torch.float32, device=W.device)
+    rot = torch.empty(lib().w4a4_rot_bytes(K, block), dtype=torch.uint8, device=W.device)
+    ws, nb = _ws(lib().w4a4_pack_gptq_workspace_bytes(N, K, block), W.device)
+    check(lib().w4a4_pack_weights_gptq(_p(W), _dtype_code(W), N, K, _row_stride(W), block, _p(perm),
+                                       _p(U), _p(Hf), _p(dead), _p(wq), _p(w_scale), _p(rot), _p(ws),
+                                       nb, _stream()))
+    return wq, w_scale, rot

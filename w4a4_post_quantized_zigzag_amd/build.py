@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a4.so")
-SOURCES = ["abi.hip", "k_pack.hip", "k_act.hip", "k_gemm.hip", "k_calib.hip"]
+SOURCES = ["abi.hip", "k_pack.hip", "k_act.hip", "k_gemm.hip", "k_calib.hip", "k_gptq.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Device code is built without packed-fp32 instructions (v_pk_*_f32); every unit is gfx950-only.

@@ -623,4 +623,104 @@ int w4a4_gemm_grouped(const uint8_t *xq, const float *x_scales, const uint8_t *w
     return rc ? rc : ok();
 }
 
+// ------------------------------------------------------------------ GPTQ weight solver
+
+static int check_gptq_k(int K, int block)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    if (K > GPTQ_MAX_K)
+        return fail(W4A4_ERR_UNSUPPORTED, "GPTQ solver supports K <= %d (got %d)", GPTQ_MAX_K, K);
+    return W4A4_OK;
+}
+
+size_t w4a4_gptq_hessian_workspace_bytes(int M, int K, int block)
+{
+    if (M < 0 || K <= 0 || !pow2_block(block) || K % block) return 0;
+    return align_up((size_t)K * block * sizeof(double), 256) +
+           align_up((size_t)(M > 0 ? M : 1) * K * sizeof(double), 256);
+}
+
+int w4a4_gptq_hessian(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                      const int32_t *perm, const float *U, double *H, int accumulate, void *ws,
+                      size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_gptq_k(K, block))) return rc;
+    if ((rc = check_matrix(X, x_dtype, M, K, ldx, "X"))) return rc;
+    if (!H) return fail(W4A4_ERR_ARG, "H is NULL");
+    if (!aligned(H, 8) || !aligned(U, 4) || !aligned(perm, 4))
+        return fail(W4A4_ERR_ALIGN, "H / U / perm misaligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_gptq_hessian_workspace_bytes(M, K, block)))) return rc;
+    double *R64 = reinterpret_cast<double *>(ws);
+    double *Xr = reinterpret_cast<double *>(reinterpret_cast<char *>(ws) +
+                                            align_up((size_t)K * block * sizeof(double), 256));
+    if ((rc = launch_rotation(U, K, block, 1.0 / std::sqrt((double)block), R64, nullptr, stream)))
+        return rc;
+    if ((rc = launch_rotate_rows_f64(X, x_dtype, M, K, ldx, block, perm, R64, Xr, stream))) return rc;
+    if ((rc = launch_gram_f64(Xr, M, K, H, accumulate != 0, stream))) return rc;
+    return ok();
+}
+
+size_t w4a4_gptq_factor_workspace_bytes(int K)
+{
+    if (K <= 0) return 0;
+    return align_up(((size_t)K * K + 1) * sizeof(double), 256);
+}
+
+int w4a4_gptq_factor(const double *H, int K, double damp_percent, double *Hf, uint8_t *dead,
+                     void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if (K <= 0) return fail(W4A4_ERR_ARG, "K = %d must be positive", K);
+    if (K > GPTQ_MAX_K)
+        return fail(W4A4_ERR_UNSUPPORTED, "GPTQ solver supports K <= %d (got %d)", GPTQ_MAX_K, K);
+    if (!H || !Hf) return fail(W4A4_ERR_ARG, "H and Hf are required");
+    if (!(damp_percent >= 0.0) || !std::isfinite(damp_percent))
+        return fail(W4A4_ERR_ARG, "damp_percent must be finite and non-negative");
+    if (!aligned(H, 8) || !aligned(Hf, 8)) return fail(W4A4_ERR_ALIGN, "H / Hf misaligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_gptq_factor_workspace_bytes(K)))) return rc;
+    if ((rc = launch_gptq_factor(H, K, damp_percent, Hf, dead, reinterpret_cast<double *>(ws),
+                                 stream)))
+        return rc;
+    return ok();
+}
+
+size_t w4a4_pack_gptq_workspace_bytes(int N, int K, int block)
+{
+    if (N <= 0 || K <= 0 || !pow2_block(block) || K % block) return 0;
+    return align_up((size_t)K * block * sizeof(double), 256) + align_up((size_t)N * 8, 256) +
+           align_up((size_t)N * K * sizeof(double), 256) + align_up((size_t)N * K, 256);
+}
+
+int w4a4_pack_weights_gptq(const void *W, int w_dtype, int N, int K, int64_t ldw, int block,
+                           const int32_t *perm, const float *U, const double *Hf,
+                           const uint8_t *dead, uint8_t *wq, float *w_scale, void *rot, void *ws,
+                           size_t ws_bytes, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_gptq_k(K, block))) return rc;
+    if (N <= 0) return fail(W4A4_ERR_ARG, "N = %d must be positive", N);
+    if ((rc = check_matrix(W, w_dtype, N, K, ldw, "W"))) return rc;
+    if (!wq || !w_scale || !rot || !Hf) return fail(W4A4_ERR_ARG, "wq, w_scale, rot and Hf are required");
+    if (!aligned(U, 4) || !aligned(w_scale, 4) || !aligned(Hf, 8) || !aligned(perm, 4))
+        return fail(W4A4_ERR_ALIGN, "U / w_scale / Hf / perm misaligned");
+    if (!aligned(rot, 16)) return fail(W4A4_ERR_ALIGN, "rot must be 16-byte aligned");
+    if ((rc = check_ws(ws, ws_bytes, w4a4_pack_gptq_workspace_bytes(N, K, block)))) return rc;
+    char *w = reinterpret_cast<char *>(ws);
+    double *R64 = reinterpret_cast<double *>(w);
+    w += align_up((size_t)K * block * sizeof(double), 256);
+    unsigned long long *rowmax = reinterpret_cast<unsigned long long *>(w);
+    w += align_up((size_t)N * 8, 256);
+    double *Wr = reinterpret_cast<double *>(w);
+    w += align_up((size_t)N * K * sizeof(double), 256);
+    int8_t *codes = reinterpret_cast<int8_t *>(w);
+    if ((rc = launch_rotation(U, K, block, 1.0 / std::sqrt((double)block), R64, rot, stream))) return rc;
+    if ((rc = launch_weight_rowmax_rot(W, w_dtype, N, K, ldw, block, perm, R64, rowmax, Wr, stream)))
+        return rc;
+    if ((rc = launch_gptq_sweep(Wr, N, K, Hf, dead, rowmax, codes, w_scale, stream))) return rc;
+    if ((rc = launch_pack_codes(codes, N, K, wq, stream))) return rc;
+    return ok();
+}
+
 }  // extern "C"

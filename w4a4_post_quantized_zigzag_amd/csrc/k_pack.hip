@@ -38,6 +38,7 @@ __global__ void k_rotation(const float *__restrict__ U, int K, int B, double hin
         s = hadamard_negative(i, j) ? -hinv : hinv;
     }
     R64[idx] = s;
+    if (!r32) return;  // fp64 rotation only (the GPTQ Hessian's activation rotation)
     r32[idx] = (float)s;
     // split: hi = fp16(R), lo = fp16((R - hi) * 2^shift)
     __half hi = __float2half_rn((float)s);
@@ -53,9 +54,9 @@ int launch_rotation(const float *U, int K, int B, double hinv, double *R64, void
 {
     RotLayout L = rot_layout(K, B);
     char *base = reinterpret_cast<char *>(rot);
-    float *r32 = reinterpret_cast<float *>(base);
-    __half *rhi = reinterpret_cast<__half *>(base + L.r32);
-    __half *rlo = reinterpret_cast<__half *>(base + L.r32 + L.r16);
+    float *r32 = rot ? reinterpret_cast<float *>(base) : nullptr;
+    __half *rhi = rot ? reinterpret_cast<__half *>(base + L.r32) : nullptr;
+    __half *rlo = rot ? reinterpret_cast<__half *>(base + L.r32 + L.r16) : nullptr;
     const int64_t total = (int64_t)K * B;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
@@ -70,9 +71,11 @@ __global__ void k_fill_u64(unsigned long long *p, int64_t n)
     if (i < n) p[i] = 0ull;
 }
 
-// Weight rotation, two passes over the same fixed-order arithmetic:
+// Weight rotation, passes over the same fixed-order arithmetic:
 //   PASS 0: per-row max |W'| (fp64 bits, atomic max of non-negative values is order independent);
-//   PASS 1: s_w = fp32(max / 7), codes = clamp(rint(W' / s_w), -8, 7), packed two per byte.
+//   PASS 1: s_w = fp32(max / 7), codes = clamp(rint(W' / s_w), -8, 7), packed two per byte;
+//   PASS 2: the rotated rows themselves, fp64 [rows][K] into `wrot` (the GPTQ solver's weights, and
+//           the rotated calibration activations its Hessian is built from).
 // Workgroup = (ROWS output rows) x (a 256-position chunk of K, which holds whole blocks since the
 // block divides 256 or equals it); each thread owns two adjacent positions (one output byte).
 constexpr int WP_ROWS = 8;
@@ -85,7 +88,8 @@ __global__ __launch_bounds__(128) void k_weight_pack(const void *__restrict__ W,
                                                      const double *__restrict__ R64,
                                                      unsigned long long *__restrict__ rowmax,
                                                      uint8_t *__restrict__ wq,
-                                                     float *__restrict__ w_scale, int qmax)
+                                                     float *__restrict__ w_scale, int qmax,
+                                                     double *__restrict__ wrot = nullptr)
 {
 #pragma clang fp contract(off)
     __shared__ double sW[WP_ROWS][WP_CHUNK];
@@ -131,6 +135,17 @@ __global__ __launch_bounds__(128) void k_weight_pack(const void *__restrict__ W,
         }
     }
 
+    if (PASS == 2) {
+        if (!active) return;
+#pragma unroll
+        for (int r = 0; r < WP_ROWS; ++r) {
+            const int n = n0 + r;
+            if (n >= N) continue;
+            wrot[(int64_t)n * K + kp] = acc[r][0];
+            if (kp + 1 < kend) wrot[(int64_t)n * K + kp + 1] = acc[r][1];
+        }
+        return;
+    }
     if (PASS == 0) {
         // row max over this workgroup's positions, then one atomic per row
         const int lane = tid & 63, wave = tid >> 6;
@@ -183,6 +198,30 @@ int launch_weight_pack(const void *W, int wdt, int N, int K, int64_t ldw, int B,
     hipLaunchKernelGGL(k_weight_pack<1>, grid, dim3(WP_CHUNK / 2), 0, s, W, wdt, N, K, ldw, B,
                        perm, R64, rowmax, wq, w_scale, qmax);
     return check_launch("weight pack");
+}
+
+// The GPTQ solver's weight side: per-row max |W'| (for the fixed RTN scales) and the fp64 rows W'.
+int launch_weight_rowmax_rot(const void *W, int wdt, int N, int K, int64_t ldw, int B,
+                             const int32_t *perm, const double *R64, unsigned long long *rowmax,
+                             double *wrot, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_u64, dim3((N + 255) / 256), dim3(256), 0, s, rowmax, (int64_t)N);
+    dim3 grid((N + WP_ROWS - 1) / WP_ROWS, (K + WP_CHUNK - 1) / WP_CHUNK);
+    hipLaunchKernelGGL(k_weight_pack<0>, grid, dim3(WP_CHUNK / 2), 0, s, W, wdt, N, K, ldw, B,
+                       perm, R64, rowmax, nullptr, nullptr, 7, nullptr);
+    hipLaunchKernelGGL(k_weight_pack<2>, grid, dim3(WP_CHUNK / 2), 0, s, W, wdt, N, K, ldw, B,
+                       perm, R64, nullptr, nullptr, nullptr, 7, wrot);
+    return check_launch("weight row max + rotation");
+}
+
+int launch_rotate_rows_f64(const void *A, int adt, int rows, int K, int64_t lda, int B,
+                           const int32_t *perm, const double *R64, double *out, hipStream_t s)
+{
+    if (rows == 0) return W4A4_OK;
+    dim3 grid((rows + WP_ROWS - 1) / WP_ROWS, (K + WP_CHUNK - 1) / WP_CHUNK);
+    hipLaunchKernelGGL(k_weight_pack<2>, grid, dim3(WP_CHUNK / 2), 0, s, A, adt, rows, K, lda, B,
+                       perm, R64, nullptr, nullptr, nullptr, 7, out);
+    return check_launch("rotate rows (fp64)");
 }
 
 }  // namespace w4a4

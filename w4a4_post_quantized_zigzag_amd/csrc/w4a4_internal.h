@@ -74,6 +74,21 @@ int launch_rotation(const float *U, int K, int B, double hinv, double *R64, void
 int launch_weight_pack(const void *W, int wdt, int N, int K, int64_t ldw, int B,
                        const int32_t *perm, const double *R64, unsigned long long *rowmax,
                        uint8_t *wq, float *w_scale, int bits, hipStream_t s);
+int launch_weight_rowmax_rot(const void *W, int wdt, int N, int K, int64_t ldw, int B,
+                             const int32_t *perm, const double *R64, unsigned long long *rowmax,
+                             double *wrot, hipStream_t s);
+// fp64 rows A[:, perm] . blockdiag(R_b) into out [rows][K] (the weight pack's fixed-order arithmetic)
+int launch_rotate_rows_f64(const void *A, int adt, int rows, int K, int64_t lda, int B,
+                           const int32_t *perm, const double *R64, double *out, hipStream_t s);
+// GPTQ solver (k_gptq.hip)
+int launch_gram_f64(const double *A, int rows, int K, double *H, bool accumulate, hipStream_t s);
+int launch_gptq_factor(const double *H, int K, double damp_percent, double *Hf, uint8_t *dead,
+                       double *work, hipStream_t s);
+int launch_gptq_sweep(const double *Wr, int N, int K, const double *Hf, const uint8_t *dead,
+                      const unsigned long long *rowmax, int8_t *codes, float *w_scale,
+                      hipStream_t s);
+int launch_pack_codes(const int8_t *codes, int N, int K, uint8_t *wq, hipStream_t s);
+constexpr int GPTQ_MAX_K = 4096;
 
 // activation side (k_act.hip)
 enum ActMode { ACT_PER_STEP = 0, ACT_TOKEN_MAX = 1, ACT_TOKEN_QUANT = 2, ACT_CALIB_MAX = 3 };
