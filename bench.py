@@ -235,6 +235,34 @@ def grouped_scales(bd, inputs, steps):
     return out
 
 
+def gptq_offline(bd, inputs):
+    """Offline GPTQ pack of the DiT MLP up-projection weights (4096 x 1024) on the device: Hessian
+    over the 80 calibration draws, damped inverse factor, column sweep and pack; wall time of each
+    phase (device synchronized)."""
+    torch = _torch()
+    d = inputs.linear_inputs("dit_mlp_up")
+    W = dev(d["W"])
+    B = d["block"]
+    perm = bd.zigzag_perm(W, B)
+    U = bd.block_svd(W, perm, B)
+    draws = [dev(x) for t in range(d["steps"]) for x in d["X_calib"][t]]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    H = None
+    for x in draws:
+        H = bd.gptq_hessian(x, perm, U, B, H=H, accumulate=H is not None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    Hf, dead = bd.gptq_factor(H)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    bd.pack_weights_gptq(W, perm, U, B, Hf, dead)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    return {"N": int(W.shape[0]), "K": int(W.shape[1]), "calibration_rows": sum(int(x.shape[0]) for x in draws),
+            "hessian_s": t1 - t0, "factor_s": t2 - t1, "sweep_and_pack_s": t3 - t2}
+
+
 def setup_per_token_linear(name, bd, inputs):
     torch = _torch()
     d = inputs.linear_inputs(name)
@@ -485,6 +513,7 @@ def supplementary(bd, inputs, steps):
         torch.cuda.empty_cache()
     out["cold_hbm"] = cold_hbm(bd, inputs)
     out["group_wise_scales"] = grouped_scales(bd, inputs, max(20, steps))
+    out["gptq_offline_pack"] = gptq_offline(bd, inputs)
     for name, w8 in (("action_stack", ()), ("action_stack_mixed", ("o", "down"))):
         info, lins, Xs, rb, step = setup_stack(bd, inputs, w8=w8)
         ms = time_graph(step, max(3, steps // 5), 2)
