@@ -51,6 +51,37 @@ def test_gemm_i32_full_size_sampled(M, N, K):
     assert np.array_equal(acc[mi, ni], ref)
 
 
+# M <= 64 shapes that reach each tile of the weight-streaming kernel (16, 32 or 64 output columns
+# per workgroup, 8 or 4 waves splitting K), through its short-wave loop and its two-chunk prefetch
+# loop, with ragged M, ragged N (a partial last tile) and uneven K ranges per wave; the largest are
+# compared on sampled outputs.
+@pytest.mark.parametrize("M,N,K", [
+    (37, 4100, 2048),     # 16 columns, 8 waves, one chunk per wave
+    (64, 8200, 1536),     # 32 columns, 8 waves, prefetch loop
+    (20, 16400, 1024),    # 64 columns, 8 waves, one chunk per wave
+    (3, 16448, 4096),     # 64 columns, 8 waves, prefetch loop
+    (16, 4096, 16512),    # 16 columns, 4 waves, 129 windows (uneven split)
+    (50, 8192, 12288),    # 32 columns, 4 waves
+    (64, 16384, 9216),    # 64 columns, 4 waves
+    (1, 4097, 8320),      # one row, partial last tile
+])
+def test_gemm_i32_small_m_tiles(M, N, K):
+    xq, wq = _operands(M, N, K, seed=11)
+    acc = host(bd.gemm_i32(dev(xq), dev(wq), K)).astype(np.int64)
+    if M * N * K <= 2 ** 30:
+        ref = oracle.int_gemm(oracle.unpack_int4(xq, K), oracle.unpack_int4(wq, K))
+        assert np.array_equal(acc, ref)
+        return
+    rng = np.random.Generator(np.random.PCG64(M * N + K))
+    mi = np.concatenate([rng.integers(0, M, 2000), [0, M - 1, M - 1, 0]])
+    ni = np.concatenate([rng.integers(0, N, 2000), [0, N - 1, 0, N - 1]])
+    rows, cols = np.unique(mi), np.unique(ni)
+    q = oracle.unpack_int4(xq[rows], K)
+    p = oracle.unpack_int4(wq[cols], K)
+    ref = oracle.int_gemm_sampled(q, p, np.searchsorted(rows, mi), np.searchsorted(cols, ni))
+    assert np.array_equal(acc[mi, ni], ref)
+
+
 @pytest.mark.parametrize("K", [64, 2048, 16384])
 def test_gemm_i32_extremes(K):
     neg = inputs.constant_packed(70, K, 0x88)   # all codes -8
@@ -63,7 +94,8 @@ def test_gemm_i32_extremes(K):
 
 @pytest.mark.parametrize("per_token", [True, False])
 @pytest.mark.parametrize("epi", [EPI_NONE, EPI_RESIDUAL, EPI_GELU])
-@pytest.mark.parametrize("M,N,K", [(50, 4096, 1024), (200, 300, 512), (1024, 2048, 16384)])
+@pytest.mark.parametrize("M,N,K", [(50, 4096, 1024), (40, 16400, 1024), (200, 300, 512),
+                                   (1024, 2048, 16384)])
 def test_gemm_dequant_epilogue(per_token, epi, M, N, K):
     xq, wq = _operands(M, N, K, seed=3)
     sx = inputs.random_scales(M if per_token else 1, seed=M, lo=1e-3, hi=5e-2)

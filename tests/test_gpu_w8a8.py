@@ -41,7 +41,8 @@ def test_pack_weights_int8_bit_exact(N, K, B):
 
 
 @pytest.mark.parametrize("M,N,K", [(50, 512, 1024), (1, 64, 64), (64, 100, 4096), (300, 1000, 2048),
-                                   (1024, 256, 16384), (257, 520, 192)])
+                                   (1024, 256, 16384), (257, 520, 192), (50, 16400, 2048),
+                                   (33, 8200, 4096), (7, 512, 65536)])
 def test_gemm_int8_i32_bit_exact(M, N, K):
     rng = _rng(M + N)
     q = rng.integers(-128, 128, (M, K), dtype=np.int64).astype(np.int8)

@@ -269,6 +269,186 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
     }
 }
 
+// Small-M GEMM with 16 * NF output columns per workgroup, for aligned operands (16-byte rows and
+// pointers). Every workgroup reads the whole activation, so with NF weight fragments per activation
+// fragment the activation is loaded and widened N / (16 NF) times instead of N / 16 times, and each
+// widened activation fragment feeds 2 NF MFMAs. Rows at or beyond M or N are read from clamped (in
+// bounds) addresses and not zeroed: their products only reach accumulator rows and columns that are
+// never stored. Packed rows are a whole number of 64-byte windows (other K go to k_gemm_smallm),
+// so nothing is zeroed. The WV waves of a workgroup split K, so a short grid (few wide tiles) still
+// keeps several waves per SIMD streaming. Each wave sums its k range in one int32 accumulator, exact
+// while a wave covers at most 2^16 k (256 * 64 * 2^16 = 2^30); the waves' partial tiles are added
+// in LDS with integer atomics, which are exact in any order.
+template <int MF, int NF, int WV, int CH, bool Q8>
+__global__ __launch_bounds__(64 * WV) void k_gemm_smallm_wide(const uint8_t *__restrict__ xq,
+                                                              const uint8_t *__restrict__ wq, int M,
+                                                              int N, int K, GemmEpilogue epi)
+{
+#pragma clang fp contract(off)
+    constexpr int NT = 64 * WV, NC = 16 * NF, LDR = NC + 4, RS = NT / NC;
+    constexpr int ER = (MF * 16 + RS - 1) / RS;  // output rows per thread
+    __shared__ int32_t red[MF * 16 * LDR];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * NC;
+    const int ldp = Q8 ? K : K / 2;  // bytes per operand row
+    const int windows = ldp / 64;
+    const int per_wave = (windows + WV - 1) / WV;
+    const int w_begin = wave * per_wave, w_end = min(windows, w_begin + per_wave);
+
+    for (int i = threadIdx.x; i < MF * 16 * LDR; i += NT) red[i] = 0;
+    __syncthreads();
+
+    // Epilogue operands first: this thread owns column n0 + tid % NC and rows tid / NC + RS j.
+    const int ecol = threadIdx.x % NC, erow = threadIdx.x / NC;
+    const int en = min(n0 + ecol, N - 1);
+    const bool scaled = epi.mode != GEMM_OUT_I32;
+    float e_sw = 0.0f, e_sx[ER];
+    uint16_t e_res[ER];
+    if (scaled) {
+        e_sw = epi.w_scale[en];
+        const float sx0 = epi.x_scale_per_token ? 0.0f : epi.x_scale[0];
+#pragma unroll
+        for (int j = 0; j < ER; ++j) {
+            const int m = min(erow + RS * j, M - 1);
+            e_sx[j] = epi.x_scale_per_token ? epi.x_scale[m] : sx0;
+            e_res[j] = (epi.mode == W4A4_EPI_RESIDUAL) ? epi.residual[(int64_t)m * epi.ldr + en]
+                                                       : (uint16_t)0;
+        }
+    }
+
+    const uint8_t *wrow[NF], *xrow[MF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) wrow[j] = wq + (int64_t)min(n0 + 16 * j + r, N - 1) * ldp + 16 * g;
+#pragma unroll
+    for (int f = 0; f < MF; ++f) xrow[f] = xq + (int64_t)min(16 * f + r, M - 1) * ldp + 16 * g;
+
+    v4i acc[MF][NF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[f][j] = v4i{0, 0, 0, 0};
+
+    // One chunk = CH windows. compute() consumes a chunk's loaded operands; nc = live windows.
+    auto compute = [&](const uint4 (&bq)[CH][NF], const uint4 (&aq)[CH][MF], int nc) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (c >= nc) continue;
+            if (Q8) {
+#pragma unroll
+                for (int f = 0; f < MF; ++f)
+#pragma unroll
+                    for (int j = 0; j < NF; ++j)
+                        acc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            *reinterpret_cast<const v4i *>(&aq[c][f]),
+                            *reinterpret_cast<const v4i *>(&bq[c][j]), acc[f][j], 0, 0, 0);
+                continue;
+            }
+            // all fragments widened first, then the MF * NF products of the even k before those of
+            // the odd k, so no MFMA waits for the result of the one just issued
+            uint4 b0[NF], b1[NF], a0[MF], a1[MF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) widen16(bq[c][j], b0[j], b1[j]);
+#pragma unroll
+            for (int f = 0; f < MF; ++f) widen16(aq[c][f], a0[f], a1[f]);
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+                    acc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        *reinterpret_cast<v4i *>(&a0[f]), *reinterpret_cast<v4i *>(&b0[j]),
+                        acc[f][j], 0, 0, 0);
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+                    acc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        *reinterpret_cast<v4i *>(&a1[f]), *reinterpret_cast<v4i *>(&b1[j]),
+                        acc[f][j], 0, 0, 0);
+        }
+    };
+    // t counts the wave's windows; positions past its range re-read its last window (in bounds,
+    // never consumed), so the prefetch loads are unconditional and the compiler can count the
+    // ones still in flight.
+    const int cnt = max(w_end - w_begin, 0);
+    auto window = [&](int t) { return w_begin + min(t, cnt - 1); };
+    auto load = [&](uint4 (&bq)[CH][NF], uint4 (&aq)[CH][MF], int t0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int kb = window(t0 + c) * 64;
+#pragma unroll
+            for (int j = 0; j < NF; ++j) bq[c][j] = *reinterpret_cast<const uint4 *>(wrow[j] + kb);
+#pragma unroll
+            for (int f = 0; f < MF; ++f) aq[c][f] = *reinterpret_cast<const uint4 *>(xrow[f] + kb);
+        }
+    };
+    uint4 bq0[CH][NF], aq0[CH][MF];
+    if (per_wave >= 2 * CH) {
+        // two register sets: the next chunk's loads are in flight while this one computes
+        uint4 bq1[CH][NF], aq1[CH][MF];
+        if (cnt > 0) {
+            load(bq0, aq0, 0);
+            for (int t = 0;;) {
+                // the scheduling barriers keep the next chunk's loads ahead of this chunk's work
+                // (the scheduler would otherwise sink them next to their use)
+                load(bq1, aq1, t + CH);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(bq0, aq0, cnt - t);
+                t += CH;
+                if (t >= cnt) break;
+                load(bq0, aq0, t + CH);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(bq1, aq1, cnt - t);
+                t += CH;
+                if (t >= cnt) break;
+            }
+        }
+    } else {
+        for (int t = 0; t < cnt; t += CH) {
+            const int nc = cnt - t;  // live windows (wave-uniform): only those are loaded
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                if (c >= nc) continue;
+                const int kb = window(t + c) * 64;
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+                    bq0[c][j] = *reinterpret_cast<const uint4 *>(wrow[j] + kb);
+#pragma unroll
+                for (int f = 0; f < MF; ++f)
+                    aq0[c][f] = *reinterpret_cast<const uint4 *>(xrow[f] + kb);
+            }
+            compute(bq0, aq0, nc);
+        }
+    }
+    // accumulator lane layout: row 4 g + i of fragment f, column r of fragment j
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                atomicAdd(&red[(f * 16 + 4 * g + i) * LDR + j * 16 + r],
+                          Q8 ? acc[f][j][i] : (acc[f][j][i] >> 8));
+    __syncthreads();
+    const int n = n0 + ecol;
+    if (n >= N) return;
+#pragma unroll
+    for (int j = 0; j < ER; ++j) {
+        const int m = erow + RS * j;
+        if (m >= M) break;
+        const int32_t v = red[m * LDR + ecol];
+        if (!scaled) {
+            epi.acc_out[(int64_t)m * N + n] = v;
+            continue;
+        }
+        float y = fp32_value((float)v * e_sx[j]);
+        y = fp32_value(y * e_sw);
+        if (epi.mode == W4A4_EPI_GELU) y = fp32_value(gelu_erf(y));
+        else if (epi.mode == W4A4_EPI_RESIDUAL) y = fp32_value(y + __half2float(__ushort_as_half(e_res[j])));
+        epi.Y[(int64_t)m * epi.ldy + n] = f32_to_f16_bits(y);
+    }
+}
+
 // Large-M GEMM. A BM x BN tile per workgroup of WAVES_M x WAVES_N waves, each wave a
 // (BM/WAVES_M) x (BN/WAVES_N) tile of 16x16 fragments. Operands stay packed in LDS (two stages of
 // 128 k: 64 bytes per row), so LDS traffic per MFMA is half that of staging int8; each wave widens
@@ -1047,6 +1227,42 @@ int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int 
     return check_launch("gemm grouped");
 }
 
+// Shape of the wide small-M kernel, measured on MI355X: as many column fragments per workgroup as
+// still give 256 workgroups (wider tiles read and widen the activation fewer times), 8 waves
+// splitting K up to K = 8192 (short weight streams want more waves in flight), 4 beyond (each wave
+// streams longer, and the larger tiles fit in its registers with a two-chunk prefetch).
+struct SmallmShape { int nf, wv; };
+static SmallmShape smallm_shape(int N, int K)
+{
+    const int nf = N >= 4 * 4096 ? 4 : (N >= 2 * 4096 ? 2 : 1);
+    return SmallmShape{nf, K <= 8192 ? 8 : 4};
+}
+
+template <int MF>
+static void launch_smallm_wide(SmallmShape sh, bool q8, hipStream_t s, const uint8_t *xq,
+                               const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi)
+{
+    // (column fragments, waves, windows per chunk)
+#define W4A4_WIDE(NFV, WVV, CHV)                                                                   \
+    {                                                                                              \
+        const dim3 g((N + 16 * NFV - 1) / (16 * NFV)), b(64 * WVV);                                \
+        if (q8) hipLaunchKernelGGL((k_gemm_smallm_wide<MF, NFV, WVV, CHV, true>), g, b, 0, s, xq,   \
+                                   wq, M, N, K, epi);                                              \
+        else hipLaunchKernelGGL((k_gemm_smallm_wide<MF, NFV, WVV, CHV, false>), g, b, 0, s, xq, wq, \
+                                M, N, K, epi);                                                     \
+        return;                                                                                    \
+    }
+    if (sh.wv == 8) {
+        if (sh.nf == 4) W4A4_WIDE(4, 8, 2)
+        if (sh.nf == 2) W4A4_WIDE(2, 8, 1)
+        W4A4_WIDE(1, 8, 4)
+    }
+    if (sh.nf == 4) W4A4_WIDE(4, 4, 2)
+    if (sh.nf == 2) W4A4_WIDE(2, 4, 4)
+    W4A4_WIDE(1, 4, 4)
+#undef W4A4_WIDE
+}
+
 // q8: int8 operands [rows][K] (W8A8); the caller guarantees K % 64 == 0 and 16-byte aligned
 // operands for them.
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
@@ -1058,8 +1274,17 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     const bool pipe = q8 || (vec && K % BG_KS == 0);
     GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe);
     if (p.kind == 0) {
-        dim3 g((N + 15) / 16);
         const int mf = (M + 15) / 16;
+        // the wide kernel: whole 64-byte windows and at most 2^16 k per wave (4 waves)
+        if (vec && row_bytes % 64 == 0 && (q8 || K <= 4 * MAX_K_SPLIT)) {
+            const SmallmShape sh = smallm_shape(N, K);
+            if (mf == 1) launch_smallm_wide<1>(sh, q8, s, xq, wq, M, N, K, epi);
+            else if (mf == 2) launch_smallm_wide<2>(sh, q8, s, xq, wq, M, N, K, epi);
+            else if (mf == 3) launch_smallm_wide<3>(sh, q8, s, xq, wq, M, N, K, epi);
+            else launch_smallm_wide<4>(sh, q8, s, xq, wq, M, N, K, epi);
+            return check_launch("gemm small-M");
+        }
+        dim3 g((N + 15) / 16);
 #define W4A4_SMALLM_Q(MFV, QV)                                                                     \
     if (vec) hipLaunchKernelGGL((k_gemm_smallm<MFV, true, QV>), g, dim3(256), 0, s, xq, wq, M, N, K, \
                                 epi);                                                              \
