@@ -396,8 +396,8 @@ def main():
                               "scale_mode": "per_step"},
                       bandwidth_gbps=bytes_step / (ms * 1e-3) / 1e9)
         result["roofline"] = {"bound": "hbm",
-                              "kernel": "k_gemm_smallm<4> (16 output columns per workgroup, "
-                                        "K split over its 4 waves)",
+                              "kernel": "k_gemm_smallm_wide<4, 1, 8, 4> (16 output columns per "
+                                        "workgroup, K split over its 8 waves)",
                               "achieved": gb / (gemm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": gb / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                               "traffic": traffic_from_profile("k_gemm.hip", name),
