@@ -341,6 +341,92 @@ def cpu_baseline_per_step(d, budget_s=12.0):
         outs
 
 
+def host_cpu():
+    """CPU model and logical core count of the host that runs the oracle."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "nproc": os.cpu_count()}
+
+
+def cpu_oracle_stages(inputs, rows=16, cols=1024):
+    """The oracle's runtime stages (rotation, quantization, integer GEMM, dequantization) timed one
+    by one on a bounded sample: `rows` activation rows and at most `cols` output channels of each
+    linear, on one host thread. Rotation and quantization cost grows with M, the GEMM and the
+    dequantization with M x N, so each stage is extrapolated to the full shape by that factor; the
+    action stack's layer-step (its four linears on inputs of their own shapes) is further scaled by
+    its 128 layer-steps. Weights are packed offline for the sampled output channels only, with
+    identity U blocks (untimed; the stages' cost does not depend on the rotation's values)."""
+    import oracle
+    from oracle.reference import EPI_GELU, EPI_NONE, EPI_RESIDUAL
+
+    def linear(W, X, B, mode, epi):
+        perm = oracle.zigzag_perm(W, B)
+        # the stages' cost does not depend on U's values: identity blocks spare the oracle's SVD
+        U = np.stack([np.eye(B, dtype=np.float32)] * (W.shape[1] // B))
+        n = min(cols, W.shape[0])
+        pw = oracle.pack_weights(W, perm, U, B, rows=np.arange(n))
+        res = np.zeros((X.shape[0], n), np.float16) if epi == EPI_RESIDUAL else None
+        clk = time.perf_counter
+        t0 = clk()
+        Xr = oracle.rotate_rows(X, perm, pw["R"], B)
+        t1 = clk()
+        table = None
+        if mode == "per_step":
+            table = np.array([np.float32(np.max(np.abs(Xr)) / 7.0)], np.float32)
+        t1b = clk()
+        act = oracle.quantize_act(Xr, mode, table, 1 if table is not None else None,
+                                  0 if table is not None else None)
+        t2 = clk()
+        acc = oracle.int_gemm(act["codes"], pw["codes"][:n])
+        t3 = clk()
+        oracle.dequant(acc, act["scale"], mode == "per_token", pw["w_scale"][:n], epi, res)
+        t4 = clk()
+        return {"rotate": t1 - t0, "quantize": t2 - t1b, "int_gemm": t3 - t2, "dequant": t4 - t3,
+                "n": n}
+
+    def scaled(st, M, N, K, reps=1):
+        fm, fn = M / rows, N / st["n"]
+        us = {"rotate": st["rotate"] * fm, "quantize": st["quantize"] * fm,
+              "int_gemm": st["int_gemm"] * fm * fn, "dequant": st["dequant"] * fm * fn}
+        return {k: v * reps * 1e6 for k, v in us.items()}
+
+    out = {"kind": "oracle", "cores": 1, "host": host_cpu(),
+           "sample": f"{rows} activation rows x at most {cols} output channels per linear, "
+                     "each stage extrapolated linearly to the full shape"}
+    rng = np.random.Generator(np.random.PCG64(11))
+    for name in ("prefill_proj", "longk_down"):
+        d = inputs.linear_inputs(name, M=rows)
+        M, K, N = inputs.LINEAR_WORKLOADS[name]["M"], d["K"], d["N"]
+        st = linear(d["W"], d["X"], d["block"], "per_token", EPI_NONE)
+        us = scaled(st, M, N, K)
+        tot = sum(us.values())
+        out[name] = {"M": M, "N": N, "K": K, "stage_us": us, "total_us": tot,
+                     "tops": 2.0 * M * N * K / (tot * 1e-6) / 1e12}
+    S = inputs.STACK
+    lw = inputs.stack_weights(layers=1)[0]
+    h, f, M = S["hidden"], S["ffn"], S["M"]
+    layer = {}
+    ops = 0.0
+    for nm, epi in (("qkv", EPI_NONE), ("o", EPI_RESIDUAL), ("up", EPI_GELU), ("down", EPI_RESIDUAL)):
+        W = lw[nm]
+        X = rng.standard_normal((rows, W.shape[1])).astype(np.float16)
+        st = linear(W, X, S["block"], "per_step", epi)
+        layer[nm] = scaled(st, M, W.shape[0], W.shape[1], reps=S["layers"] * S["steps"])
+        ops += 2.0 * M * W.shape[0] * W.shape[1] * S["layers"] * S["steps"]
+    tot = sum(sum(v.values()) for v in layer.values())
+    stages = {k: sum(v[k] for v in layer.values()) for k in ("rotate", "quantize", "int_gemm", "dequant")}
+    out["action_stack"] = {"M": M, "layer_steps": S["layers"] * S["steps"], "stage_us": stages,
+                           "total_us": tot, "tops": ops / (tot * 1e-6) / 1e12}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,13 +495,15 @@ def main():
         if not args.no_cpu_baseline:
             v, sample, _ = cpu_baseline_per_step(d)
             result["cpu_baseline"] = {"value": v / 1e12, "unit": "TOPS", "cores": 1,
-                                      "kind": "oracle", "sample": sample}
+                                      "kind": "oracle", "sample": sample, "host": host_cpu()}
     else:
         raise SystemExit("use --workload dit_mlp_up or linear_small for the headline line; other "
                          "workloads are reported under 'supplementary'")
 
     if not args.no_supplementary:
         result["supplementary"] = supplementary(bd, inputs, args.supp_steps)
+        if not args.no_cpu_baseline:
+            result["supplementary"]["cpu_oracle_stages"] = cpu_oracle_stages(inputs)
     print(json.dumps(result))
 
 
