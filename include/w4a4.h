@@ -166,31 +166,6 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
               const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
               const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* GEMM with the next linear's per-step rotate-quantize [vnrobo.com "Y tuong paper": each linear
- * looks up its step's activation scale; gist.science "Metodologia" item 1: x' = x[:, perm] R_b].
- * Computes Y exactly as w4a4_gemm and, from the fp16 values stored to Y in columns
- * [col0, col0 + k_next), the next linear's codes xq_next and x_scale_next exactly as
- * w4a4_rotate_quant_act (w4a4_rotate_quant_act_a8 for next_bits = 8) would from that column slice
- * of Y with perm = NULL, rot = rot_next and the step's table entry. The caller owns the channel
- * order: the slice must already be in the next linear's zigzag order (its producer's weight rows
- * permuted accordingly), as for a single-consumer activation. When the GEMM plan allows (a
- * pipelined plan without a K split, tile width dividing col0 and k_next, 4-column aligned Y,
- * w_scale and residual), each output tile is rotated and quantized in the GEMM's epilogue, with
- * no second pass over Y; otherwise the rotate-quantize runs after the GEMM. Either way the codes
- * are bit-identical. xq_next is [M][k_next / 2] (int4) or [M][k_next] (int8), dense;
- * x_scale_next[0] receives the step scale.
- * Errors: block_next != 128 -> W4A4_ERR_UNSUPPORTED; next_bits not 4 or 8, NULL rot_next / table /
- * xq_next / x_scale_next -> W4A4_ERR_ARG; columns that are not whole 128-blocks inside [0, N) ->
- * W4A4_ERR_SHAPE; step outside [0, num_steps) -> W4A4_ERR_STEP_RANGE; misaligned pointers ->
- * W4A4_ERR_ALIGN; plus every w4a4_gemm error. Workspace: w4a4_gemm_workspace_bytes(M, N, K). */
-int w4a4_gemm_next_rq(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
-                      const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
-                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
-                      int k_next, int block_next, const void *rot_next,
-                      const float *act_scale_table_next, int num_steps, int step, int next_bits,
-                      uint8_t *xq_next, float *x_scale_next, void *ws, size_t ws_bytes,
-                      hipStream_t stream);
-
 /* Test hook: the raw int32 accumulators acc [M][N] (row-major, dense) of the same integer GEMM. */
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
                   void *ws, size_t ws_bytes, hipStream_t stream);

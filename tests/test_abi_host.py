@@ -248,30 +248,3 @@ def test_gptq_rejects(L):
     assert L.w4a4_pack_weights_gptq(FAKE, bd.W4A4_F16, 16, 256, 256, 128, FAKE, FAKE, FAKE, NULL,
                                     FAKE, FAKE, FAKE, FAKE, 64, NULL) == bd.W4A4_ERR_WORKSPACE
     assert L.w4a4_pack_gptq_workspace_bytes(16, 256, 128) >= 16 * 256 * 9
-
-
-def _gnq(L, *, M=16, N=512, K=256, col0=256, k_next=256, block=128, rot=FAKE, table=FAKE, steps=8,
-         step=0, bits=4, xqn=FAKE, xsn=FAKE):
-    return L.w4a4_gemm_next_rq(FAKE, FAKE, 0, FAKE, FAKE, M, N, K, FAKE, N, 0, NULL, 0, col0,
-                               k_next, block, rot, table, steps, step, bits, xqn, xsn, NULL, 0, NULL)
-
-
-@pytest.mark.parametrize("kw,code", [
-    (dict(block=64), bd.W4A4_ERR_UNSUPPORTED),           # the fused epilogue rotates 128-blocks
-    (dict(bits=5), bd.W4A4_ERR_ARG),
-    (dict(k_next=200), bd.W4A4_ERR_SHAPE),
-    (dict(col0=100), bd.W4A4_ERR_SHAPE),
-    (dict(col0=384), bd.W4A4_ERR_SHAPE),                 # [384, 640) runs past N = 512
-    (dict(rot=NULL), bd.W4A4_ERR_ARG),
-    (dict(rot=FAKE_ODD), bd.W4A4_ERR_ARG),
-    (dict(table=NULL), bd.W4A4_ERR_ARG),                 # per-step only: no per-token form
-    (dict(step=8), bd.W4A4_ERR_STEP_RANGE),
-    (dict(step=-1), bd.W4A4_ERR_STEP_RANGE),
-    (dict(steps=0), bd.W4A4_ERR_STEP_RANGE),
-    (dict(xqn=NULL), bd.W4A4_ERR_ARG),
-    (dict(xsn=NULL), bd.W4A4_ERR_ARG),
-    (dict(M=16, K=255), bd.W4A4_ERR_SHAPE),              # and every w4a4_gemm check
-])
-def test_gemm_next_rq_rejects(L, kw, code):
-    assert _gnq(L, **kw) == code
-    assert L.w4a4_last_error() != b""

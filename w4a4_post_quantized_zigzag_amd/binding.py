@@ -36,8 +36,6 @@ SIGNATURES = {
     "w4a4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
     "w4a4_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz, _vp]),
     "w4a4_gemm_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
-    "w4a4_gemm_next_rq": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _i,
-                               _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "w4a4_pack_weights_w8": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                   _vp]),
     "w4a4_calibrate_act_scale_a8": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -247,36 +245,6 @@ def gemm(xq, x_scale, per_token: bool, wq, w_scale, K: int, Y=None, epilogue: in
     check(fn(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale), M, N, K, _p(Y),
              _row_stride(Y), epilogue, _p(residual), ldr, _p(ws), nb, _stream()))
     return Y
-
-
-def gemm_next_rq(xq, x_scale, per_token: bool, wq, w_scale, K: int, col0: int, rot_next,
-                 table_next, num_steps: int, step: int, k_next: int, next_bits: int = 4, Y=None,
-                 epilogue: int = EPI_NONE, residual=None, ws=None, xq_next=None, x_scale_next=None,
-                 block_next: int = 128):
-    """W4A4 GEMM that also produces the next linear's per-step codes from output columns
-    [col0, col0 + k_next) (fused into the GEMM epilogue when the plan allows). Returns
-    (Y, xq_next, x_scale_next)."""
-    torch = _torch()
-    M, N = xq.shape[0], wq.shape[0]
-    _code_cols(K, 4)
-    if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float16, device=wq.device)
-    if xq_next is None:
-        cols = k_next // 2 if next_bits == 4 else k_next
-        xq_next = torch.empty((M, cols), dtype=torch.uint8, device=wq.device)
-    if x_scale_next is None:
-        x_scale_next = torch.empty(1, dtype=torch.float32, device=wq.device)
-    need = lib().w4a4_gemm_workspace_bytes(M, N, K)
-    if ws is None:
-        ws, nb = _ws(need, wq.device)
-    else:
-        nb = ws.numel()
-    ldr = _row_stride(residual) if residual is not None else 0
-    check(lib().w4a4_gemm_next_rq(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale),
-                                  M, N, K, _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, col0,
-                                  k_next, block_next, _p(rot_next), _p(table_next), num_steps, step,
-                                  next_bits, _p(xq_next), _p(x_scale_next), _p(ws), nb, _stream()))
-    return Y, xq_next, x_scale_next
 
 
 def gemm_i32(xq, wq, K: int, bits: int = 4):

@@ -444,20 +444,10 @@ static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N,
     return W4A4_OK;
 }
 
-// The next linear's per-step rotate-quantize requested from a GEMM call (w4a4_gemm_next_rq).
-struct NextRq {
-    int col0, k_next;
-    const void *rot;
-    const float *table;
-    int step, bits;
-    uint8_t *xq;
-    float *x_scale;
-};
-
 static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
-                      size_t ws_bytes, hipStream_t stream, bool q8, const NextRq *next = nullptr)
+                      size_t ws_bytes, hipStream_t stream, bool q8)
 {
     int rc;
     if ((rc = check_gemm_common(xq, wq, M, N, K, q8))) return rc;
@@ -484,30 +474,7 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     epi.mode = epilogue;
     epi.residual = residual;
     epi.ldr = ldr;
-    if (!next) {
-        if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8))) return rc;
-        return ok();
-    }
-    const RotLayout RL = rot_layout(next->k_next, 128);
-    const uint16_t *r16 = reinterpret_cast<const uint16_t *>(
-        reinterpret_cast<const char *>(next->rot) + RL.r32);
-    epi.nq_rhi = r16;
-    epi.nq_rlo = r16 + RL.r16 / sizeof(uint16_t);
-    epi.nq_table = next->table;
-    epi.nq_step = next->step;
-    epi.nq_col0 = next->col0;
-    epi.nq_knext = next->k_next;
-    epi.nq_q8 = next->bits == 8;
-    epi.nq_xq = next->xq;
-    epi.nq_ldq = next->bits == 8 ? next->k_next : next->k_next / 2;
-    epi.nq_x_scale = next->x_scale;
-    bool fused = false;
-    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8, &fused))) return rc;
-    if (!fused &&
-        (rc = launch_rotate_quant_mfma(Y + next->col0, M, next->k_next, ldy, 128, nullptr, next->rot,
-                                       next->table, next->step, ACT_PER_STEP, nullptr, next->xq,
-                                       next->x_scale, nullptr, nullptr, next->bits == 8, stream)))
-        return rc;
+    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8))) return rc;
     return ok();
 }
 
@@ -537,40 +504,6 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
 {
     return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
                       residual, ldr, ws, ws_bytes, stream, false);
-}
-
-int w4a4_gemm_next_rq(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
-                      const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
-                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
-                      int k_next, int block_next, const void *rot_next,
-                      const float *act_scale_table_next, int num_steps, int step, int next_bits,
-                      uint8_t *xq_next, float *x_scale_next, void *ws, size_t ws_bytes,
-                      hipStream_t stream)
-{
-    if (block_next != 128)
-        return fail(W4A4_ERR_UNSUPPORTED, "the fused next-layer path needs block 128, not %d",
-                    block_next);
-    if (next_bits != 4 && next_bits != 8)
-        return fail(W4A4_ERR_ARG, "next_bits must be 4 or 8, not %d", next_bits);
-    if (k_next <= 0 || k_next % 128 || col0 < 0 || col0 % 128 || (int64_t)col0 + k_next > N)
-        return fail(W4A4_ERR_SHAPE, "next columns [%d, %d + %d) must be whole 128-blocks inside N = %d",
-                    col0, col0, k_next, N);
-    if (!rot_next || !aligned(rot_next, 16))
-        return fail(W4A4_ERR_ARG, "rot_next must be a 16-byte aligned rotation operand");
-    if (!act_scale_table_next)
-        return fail(W4A4_ERR_ARG, "the next linear's act_scale_table is required (per-step mode)");
-    if (!aligned(act_scale_table_next, 4)) return fail(W4A4_ERR_ALIGN, "table misaligned");
-    if (num_steps <= 0) return fail(W4A4_ERR_STEP_RANGE, "num_steps = %d must be positive", num_steps);
-    if (step < 0 || step >= num_steps)
-        return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
-    if (M > 0 && (!xq_next || !x_scale_next))
-        return fail(W4A4_ERR_ARG, "xq_next and x_scale_next are required");
-    if (!aligned(xq_next, next_bits == 8 ? 4 : 2) || !aligned(x_scale_next, 4))
-        return fail(W4A4_ERR_ALIGN, "xq_next / x_scale_next misaligned");
-    const NextRq next{col0, k_next, rot_next, act_scale_table_next, step, next_bits, xq_next,
-                      x_scale_next};
-    return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
-                      residual, ldr, ws, ws_bytes, stream, false, &next);
 }
 
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,

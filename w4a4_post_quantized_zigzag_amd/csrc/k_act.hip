@@ -8,7 +8,6 @@
 #include <cmath>
 
 #include "w4a4_internal.h"
-#include "rq_device.h"
 
 namespace w4a4 {
 
@@ -26,6 +25,11 @@ int launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t s)
     return check_launch("fill");
 }
 
+__device__ __forceinline__ float step_scale(const float *table, int step)
+{
+    float s = table[step];
+    return (s > 0.0f && s <= 3.402823466e38f) ? s : 1.0f;
+}
 
 // fp32(max / qmax) divided in fp64 (exactly the fp32 quotient, the double rounding being innocuous
 // for an fp32 dividend); 1.0f for a zero max. qmax = 7 for int4 codes, 127 for the int8 codes of
@@ -188,6 +192,8 @@ int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B
 // fp16 parts, R ~= hi + lo * 2^-12: fp16 x fp16 products are exact in fp32, so the result carries
 // fp32 accumulation error plus ~2^-22 relative from the split. Each wave keeps the R_b^T fragments
 // of its B/4 output channels in registers and reuses them over all row tiles of the workgroup.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int MT = 64;  // token rows per tile
 
@@ -398,6 +404,34 @@ __device__ __forceinline__ void rq_wait_vmcnt(int n)
     case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     }
+}
+
+// Four rotated values held as acc = 2^12 x' -> four int4 codes packed low nibble first in the low
+// 16 bits (the bits above are garbage). rs = 2^-12 * fp32(1/s), so acc * rs is the fp32 product
+// x' * fp32(1/s) rounded once (both power-of-two scalings are exact for any x' and 1/s that can
+// give a nonzero code). Adding 1.5 * 2^23 rounds that product to an integer, ties to even, and
+// leaves the integer in the low mantissa bits; the clamp to [-8, 7] is applied in that form and
+// the two's-complement nibble is read off the bit pattern.
+// Q8: int8 codes, clamp to [-128, 127] and one byte per code (four bytes returned).
+template <bool Q8 = false>
+__device__ __forceinline__ uint32_t quant_pack4(v4f acc, float rs)
+{
+#pragma clang fp contract(off)
+    constexpr float MAGIC = 12582912.0f;
+    constexpr float LOQ = Q8 ? -128.0f : -8.0f, HIQ = Q8 ? 127.0f : 7.0f;
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float y = acc[i] * rs;
+        float f = y + MAGIC;
+        f = fminf(fmaxf(f, MAGIC + LOQ), MAGIC + HIQ);
+        n[i] = __float_as_uint(f);
+    }
+    if (Q8)
+        return (n[0] & 0xFFu) | ((n[1] & 0xFFu) << 8) | ((n[2] & 0xFFu) << 16) | (n[3] << 24);
+    uint32_t t = (n[0] & 0xFu) | ((n[1] << 4) & ~0xFu);
+    t = (t & 0xFFu) | ((n[2] << 8) & ~0xFFu);
+    return (t & 0xFFFu) | ((n[3] << 12) & ~0xFFFu);
 }
 
 template <int MODE, int B, bool DBG, bool Q8>

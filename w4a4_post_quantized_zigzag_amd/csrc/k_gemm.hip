@@ -12,7 +12,6 @@
 #include <cmath>
 
 #include "w4a4_internal.h"
-#include "rq_device.h"
 
 namespace w4a4 {
 
@@ -737,81 +736,6 @@ __device__ __forceinline__ void wait_vmcnt(int n)
     }
 }
 
-// Next linear's rotate-quantize on a finished output tile. The tile's fp16 outputs (exactly the
-// values stored to Y) sit in LDS, rows of BN halves padded by 16 bytes so that the 16 rows a
-// fragment read touches fall in different banks. For each 128-channel block of the tile the waves
-// split the block's 8 groups of 16 output channels, hold the R_b^T fragments of their groups
-// (fp16 high part scaled by 2^12, low part as stored) and run, per 16 tokens, the same
-// v_mfma_f32_16x16x32_f16 sequence as the stand-alone rotate-quantize kernels (for each 32-input
-// chunk the low part, then the high part, into one fp32 accumulator), so the codes are
-// bit-identical to rotating Y afterwards. Codes and the step scale follow the activation path.
-constexpr int NQ_B = 128;  // rotation block of the fused path
-
-template <int BM, int BN>
-__host__ __device__ constexpr int nq_row_bytes() { return BN * 2 + 16; }
-
-template <int BM, int BN, int NT>
-__device__ __forceinline__ void next_rotate_quant(const uint8_t *sY, int m0, int n0, int M,
-                                                  const GemmEpilogue &epi)
-{
-#pragma clang fp contract(off)
-    constexpr int KK = NQ_B / 32, NJ = NQ_B / 16, NWV = NT / 64;
-    constexpr int JW = NJ / NWV;  // 16-channel groups per wave
-    static_assert(JW * NWV == NJ, "waves split the block's channel groups evenly");
-    constexpr int SYR = nq_row_bytes<BM, BN>();
-    constexpr float LO = 1.0f / (1 << ROT_LO_SHIFT);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const _Float16 *rhi = reinterpret_cast<const _Float16 *>(epi.nq_rhi);
-    const _Float16 *rlo = reinterpret_cast<const _Float16 *>(epi.nq_rlo);
-    const float s = step_scale(epi.nq_table, epi.nq_step);
-    const float rs = (float)(1.0 / (double)s) * LO;
-    if (n0 == epi.nq_col0 && m0 == 0 && threadIdx.x == 0) epi.nq_x_scale[0] = s;
-#pragma unroll 1
-    for (int bl = 0; bl < BN / NQ_B; ++bl) {
-        const int cb = n0 - epi.nq_col0 + bl * NQ_B;  // first next-layer channel of this block
-        const int b = cb / NQ_B;
-        v8h ahi[JW][KK], alo[JW][KK];
-#pragma unroll
-        for (int jf = 0; jf < JW; ++jf)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int64_t off = rot16_fragment(b, wave * JW + jf, kk, lane, NQ_B);
-                ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off) * (_Float16)(1 << ROT_LO_SHIFT);
-                alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
-            }
-#pragma unroll 2
-        for (int mf = 0; mf < BM / 16; ++mf) {
-            v4f acc[JW];
-#pragma unroll
-            for (int jf = 0; jf < JW; ++jf) acc[jf] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const v8h x = *reinterpret_cast<const v8h *>(
-                    sY + (mf * 16 + r) * SYR + (bl * NQ_B + 32 * kk + 8 * g) * 2);
-#pragma unroll
-                for (int jf = 0; jf < JW; ++jf)
-                    acc[jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jf][kk], x, acc[jf], 0, 0, 0);
-#pragma unroll
-                for (int jf = 0; jf < JW; ++jf)
-                    acc[jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jf][kk], x, acc[jf], 0, 0, 0);
-            }
-            const int m = m0 + mf * 16 + r;
-            if (m >= M) continue;
-#pragma unroll
-            for (int jf = 0; jf < JW; ++jf) {
-                const int c = cb + (wave * JW + jf) * 16 + 4 * g;  // 4 consecutive channels
-                if (epi.nq_q8)
-                    *reinterpret_cast<uint32_t *>(epi.nq_xq + (int64_t)m * epi.nq_ldq + c) =
-                        quant_pack4<true>(acc[jf], rs);
-                else
-                    *reinterpret_cast<uint16_t *>(epi.nq_xq + (int64_t)m * epi.nq_ldq + c / 2) =
-                        (uint16_t)quant_pack4(acc[jf], rs);
-            }
-        }
-    }
-}
-
 // Epilogue kinds of the pipelined kernel (compile-time, so each variant is straight-line code).
 enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_RESIDUAL,
        PE_INT32 = 3 };
@@ -819,9 +743,8 @@ enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_
 // Q8: int8 operands (W8A8): a staged 64-byte row is 64 k, each fragment read is already an MFMA
 // operand (one v_mfma_i32_16x16x64_i8 per fragment pair and stage, no widening) and the sums are
 // not scaled by 256.
-// NQ: the next linear's rotate-quantize is fused into the epilogue (next_rotate_quant).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT, bool Q8,
-          bool GS = false, bool NQ = false>
+          bool GS = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
     int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
@@ -1041,11 +964,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 #pragma unroll
                 for (int j = 0; j < FN; ++j) residual4(mrow + i * 16, ncol + j * 16, rsd[i][j]);
         }
-        // fused next-layer path: the tile lies wholly inside the next linear's input columns
-        // (tile-uniform); the ring's LDS is reused for the fp16 tile once every wave is done with it
-        const bool nq_in = NQ && n0 >= epi.nq_col0 && n0 + BN <= epi.nq_col0 + epi.nq_knext;
-        constexpr int NQ_SYR = nq_row_bytes<BM, BN>();
-        if (nq_in) __syncthreads();
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = mrow + i * 16;
@@ -1068,10 +986,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                         y[r] = fp32_value(y[r] + __half2float(__ushort_as_half((uint16_t)hv)));
                     }
                 }
-                if (nq_in)
-                    *reinterpret_cast<uint2 *>(smem + (wm * WTM + i * 16 + fr) * NQ_SYR +
-                                               (wn * WTN + j * 16 + 4 * fg) * 2) =
-                        make_uint2(f32x2_to_f16x2(y[0], y[1]), f32x2_to_f16x2(y[2], y[3]));
                 if (m >= M) continue;
                 uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
                 if (VEC_OUT && n + 3 < N) {
@@ -1083,10 +997,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                         if (n + r < N) dst[r] = f32_to_f16_bits(y[r]);
                 }
             }
-        }
-        if (nq_in) {
-            __syncthreads();  // every wave's fp16 outputs are in LDS
-            next_rotate_quant<BM, BN, 64 * NW>(smem, m0, n0, M, epi);
         }
     }
 }
@@ -1220,51 +1130,22 @@ static void launch_big(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, co
 
 constexpr int PIPE_STAGES = 4;
 
-template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = false,
-          bool NQ = false>
+template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = false>
 static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
-    // the fused next-layer epilogue reuses the ring's LDS for the fp16 tile
-    const size_t ring = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
-    const size_t tile = NQ ? (size_t)BM * nq_row_bytes<BM, BN>() : 0;
-    const size_t lds = ring > tile ? ring : tile;
-    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS, NQ>;
+    const size_t lds = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
+    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>;
     static bool attr_set = false;  // once per process and instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(W4A4_ERR_HIP, "gemm LDS request: %s", hipGetErrorString(e));
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS, NQ>), grid,
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>), grid,
                        dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
     return W4A4_OK;
-}
-
-// Pipelined GEMM with the next linear's rotate-quantize fused into the epilogue. Qualifies when the
-// tile width divides the next linear's column range (tiles lie wholly inside or outside it) and
-// the outputs take the 4-column vector path; `done` reports whether the launch happened.
-template <int BM, int BN, int WM, int WN>
-static int launch_pipe_nq_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
-                            int N, int K, int tm, int tn, const GemmEpilogue &epi, bool &done)
-{
-    done = false;
-    if (epi.nq_col0 % BN || epi.nq_knext % BN) return W4A4_OK;
-    const bool vo = (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
-                    ((uintptr_t)epi.w_scale % 16 == 0) &&
-                    (epi.mode != W4A4_EPI_RESIDUAL ||
-                     (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
-    if (!vo) return W4A4_OK;
-    done = true;
-    if (epi.mode == W4A4_EPI_GELU)
-        return launch_pipe_e<BM, BN, WM, WN, PE_GELU, true, false, false, true>(
-            grid, s, xq, wq, M, N, K, K, tm, tn, epi, nullptr);
-    if (epi.mode == W4A4_EPI_RESIDUAL)
-        return launch_pipe_e<BM, BN, WM, WN, PE_RESIDUAL, true, false, false, true>(
-            grid, s, xq, wq, M, N, K, K, tm, tn, epi, nullptr);
-    return launch_pipe_e<BM, BN, WM, WN, PE_NONE, true, false, false, true>(
-        grid, s, xq, wq, M, N, K, K, tm, tn, epi, nullptr);
 }
 
 template <int BM, int BN, int WM, int WN, bool Q8, bool GS = false>
@@ -1311,21 +1192,6 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
         return launch_pipe_t<64, 128, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
                                                 partial);
     return launch_pipe_t<128, 128, 2, 2, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
-}
-
-// The fused next-layer launch for plan kind `kind` (same tiles as launch_pipe, no K split).
-static int launch_pipe_nq(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq,
-                          int M, int N, int K, int tm, int tn, const GemmEpilogue &epi, bool &done)
-{
-    if (kind == 1)
-        return launch_pipe_nq_t<256, 256, 2, 4>(grid, s, xq, wq, M, N, K, tm, tn, epi, done);
-    if (kind == 2 && epi.mode == W4A4_EPI_GELU)
-        return launch_pipe_nq_t<128, 256, 2, 4>(grid, s, xq, wq, M, N, K, tm, tn, epi, done);
-    if (kind == 2)
-        return launch_pipe_nq_t<128, 256, 1, 4>(grid, s, xq, wq, M, N, K, tm, tn, epi, done);
-    if (kind == 4)
-        return launch_pipe_nq_t<64, 128, 1, 4>(grid, s, xq, wq, M, N, K, tm, tn, epi, done);
-    return launch_pipe_nq_t<128, 128, 2, 2>(grid, s, xq, wq, M, N, K, tm, tn, epi, done);
 }
 
 // Group-wise GEMM (per rotation block activation scales in epi.x_scale[K / 128]): the grouped
@@ -1400,9 +1266,8 @@ static void launch_smallm_wide(SmallmShape sh, bool q8, hipStream_t s, const uin
 // q8: int8 operands [rows][K] (W8A8); the caller guarantees K % 64 == 0 and 16-byte aligned
 // operands for them.
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
-                void *ws, size_t ws_bytes, hipStream_t s, bool q8, bool *fused)
+                void *ws, size_t ws_bytes, hipStream_t s, bool q8)
 {
-    if (fused) *fused = false;
     if (M == 0) return W4A4_OK;
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
@@ -1433,16 +1298,6 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
 #undef W4A4_SMALLM
 #undef W4A4_SMALLM_Q
         return check_launch("gemm small-M");
-    }
-    if (fused && epi.nq_xq && pipe && !q8 && p.splits == 1) {
-        const int tm = (M + p.bm - 1) / p.bm, tn = (N + p.bn - 1) / p.bn;
-        bool done = false;
-        int rc = launch_pipe_nq(p.kind, dim3(tm * tn, 1), s, xq, wq, M, N, K, tm, tn, epi, done);
-        if (rc != W4A4_OK) return rc;
-        if (done) {
-            *fused = true;
-            return check_launch("gemm with the next rotate-quantize");
-        }
     }
     int32_t *partial = nullptr;
     if (p.splits > 1) {

@@ -128,24 +128,12 @@ struct GemmEpilogue {
     const uint16_t *residual;
     int64_t ldr;
     int32_t *acc_out;  // GEMM_OUT_I32 destination, dense [M][N]
-    // Next linear's rotate-quantize fused into the epilogue (nq_xq != nullptr): output columns
-    // [nq_col0, nq_col0 + nq_knext) are the next linear's input channels in its zigzag order; they
-    // are rotated by its block-128 operand (fp16 parts, rot16 layout) and quantized with its step
-    // scale nq_table[nq_step] into nq_xq [M][nq_ldq] (int4, or int8 with nq_q8).
-    const uint16_t *nq_rhi = nullptr, *nq_rlo = nullptr;
-    const float *nq_table = nullptr;
-    int nq_step = 0, nq_col0 = 0, nq_knext = 0, nq_q8 = 0;
-    uint8_t *nq_xq = nullptr;
-    int64_t nq_ldq = 0;
-    float *nq_x_scale = nullptr;
 };
 constexpr int GEMM_OUT_I32 = 100;
 // q8: int8 operands [rows][K] (W8A8) instead of packed int4 [rows][K/2]
 size_t gemm_workspace(int M, int N, int K, bool q8);
-// fused: when non-null and epi.nq_xq is set, the next linear's rotate-quantize is fused into the
-// epilogue if the plan allows it; *fused reports whether it was (else the caller runs it).
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
-                void *ws, size_t ws_bytes, hipStream_t s, bool q8, bool *fused = nullptr);
+                void *ws, size_t ws_bytes, hipStream_t s, bool q8);
 // group-wise activation scales epi.x_scale[K / 128] (int4, K % 128 == 0, 16-byte aligned operands)
 int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int K,
                         const GemmEpilogue &epi, hipStream_t s);
