@@ -30,6 +30,8 @@ PATHS = {
     "ring_token_permuted_b64": (300, 2048, 64, "per_token", "zigzag", "permutation pass + streaming"),
     "ring_token_ident_nb3": (400, 384, 128, "per_token", "identity", "streaming, 3 blocks"),
     "gather_step": (300, 1024, 128, "per_step", "zigzag", "register-staged gather"),
+    # K beyond the staged-row permutation pass (64 Ki halves): both per-token passes gather
+    "long_k_token_gather": (260, 131072, 128, "per_token", "zigzag", "register-staged gather"),
 }
 
 

@@ -82,7 +82,19 @@ def test_gemm_i32_small_m_tiles(M, N, K):
     assert np.array_equal(acc[mi, ni], ref)
 
 
-@pytest.mark.parametrize("K", [64, 2048, 16384])
+@pytest.mark.parametrize("M,N,K", [
+    (3, 40, 1 << 20),      # small M, more than 2^16 k per wave: the folding small-M kernel
+    (64, 96, 1 << 18),     # small M at the wide kernel's per-wave limit (4 waves x 2^16 k)
+    (130, 64, 1 << 18),    # K split into 64 Ki pieces with an exact int32 reduction
+])
+def test_gemm_i32_long_k(M, N, K):
+    xq, wq = _operands(M, N, K, seed=13)
+    acc = host(bd.gemm_i32(dev(xq), dev(wq), K)).astype(np.int64)
+    ref = oracle.int_gemm(oracle.unpack_int4(xq, K), oracle.unpack_int4(wq, K))
+    assert np.array_equal(acc, ref)
+
+
+@pytest.mark.parametrize("K", [64, 2048, 16384, 1 << 20])
 def test_gemm_i32_extremes(K):
     neg = inputs.constant_packed(70, K, 0x88)   # all codes -8
     pos = inputs.constant_packed(130, K, 0x77)  # all codes +7
