@@ -1,7 +1,7 @@
 """GPU parity of the group-wise (per rotation block) per-step activation scales against the CPU
 oracle, through the C ABI.
 
-Activation codes must equal the oracle's except for certified near-tie flips (each position judged
+Activation codes must equal the oracle's except for certified near-tie flips (each position checked
 with its own block's scale) and the scales written back must be the table row bit for bit. The
 group-wise GEMM folds every block's exact partial into fp32 with one fused multiply-add per block
 in block order on both sides, so its fp16 outputs must equal the oracle's bit for bit (GELU within
