@@ -46,4 +46,9 @@ from .reference import (  # noqa: F401
     stack_run,
     stack_calibrate,
     STACK_LINEARS,
+    e3m2_value,
+    e3m2_encode,
+    f6_bytes,
+    f6_operand,
+    f6_codes,
 )

@@ -653,3 +653,85 @@ def stack_calibrate(layers, X_calib_per_step, B: int):
         X = np.concatenate(draws, axis=0)
         stack_run(layers, X, B, "per_token", steps=T, step=t, record_tables=tables)
     return tables
+
+
+# ------------------------------------------------------------------ FP6 matrix-core operands
+#
+# Not a step of the pages' method: an exact re-encoding of the int4 codes for the GEMM's FP6 matrix
+# instructions. The OCP Microscaling E3M2 six-bit float (sign bit 5, exponent bits 4..2 with bias 3,
+# mantissa bits 1..0; value (-1)^s 2^(e-3) (1 + m/4) for e >= 1 and (-1)^s 2^-2 (m/4) for e = 0)
+# holds every integer in [-8, 7], so a product of two encoded codes is the exact integer product.
+#
+# Operand layout of a [rows][K] code matrix (K % 128 == 0, R2 = rows rounded up to even; row R2-1
+# is all zeros when rows is odd): k is cut into stages of 128 and each stage into four groups of
+# 32 consecutive k. A group's 32 codes, as 6-bit fields with code i at bits 6i..6i+5 of a 192-bit
+# little-endian string, are split into a 16-byte head (bits 0..127) and an 8-byte tail (bits
+# 128..191). Heads: byte offset row*(K/2) + 64*stage + 16*group. Tails: after the R2*(K/2) head
+# bytes, at ((4*stage + group)*R2 + row)*8. Total R2*K*3/4 bytes.
+
+def e3m2_value(code: int) -> float:
+    """Value of a 6-bit E3M2 code, from the format's definition."""
+    code = int(code)
+    if not 0 <= code < 64:
+        raise ValueError("E3M2 codes are 6 bits")
+    s, e, m = (code >> 5) & 1, (code >> 2) & 7, code & 3
+    mag = 2.0 ** (e - 3) * (1.0 + m / 4.0) if e else 2.0 ** -2 * (m / 4.0)
+    return -mag if s else mag
+
+
+def e3m2_encode(q: int) -> int:
+    """The E3M2 code of the integer q in [-8, 7]: the code whose value is q (+0 for 0)."""
+    q = int(q)
+    if not -8 <= q <= 7:
+        raise ValueError("int4 codes lie in [-8, 7]")
+    if q == 0:
+        return 0
+    hits = [c for c in range(64) if e3m2_value(c) == q]
+    assert len(hits) == 1
+    return hits[0]
+
+
+def f6_bytes(rows: int, K: int) -> int:
+    return ((rows + 1) // 2 * 2) * K * 3 // 4
+
+
+def f6_operand(q) -> np.ndarray:
+    """FP6 operand bytes (uint8 [f6_bytes(rows, K)]) of int4 codes q [rows, K] (int8 values)."""
+    q = np.asarray(q, np.int64)
+    rows, K = q.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    R2 = (rows + 1) // 2 * 2
+    lut = np.array([e3m2_encode(v) for v in range(-8, 8)], np.uint64)
+    out = np.zeros(f6_bytes(rows, K), np.uint8)
+    head = out[:R2 * (K // 2)].reshape(R2, K // 2)
+    tail = out[R2 * (K // 2):].reshape(K // 32, R2, 8)
+    for r in range(rows):
+        for sg in range(K // 32):  # sg = 4 * stage + group
+            bits = 0
+            for i in range(32):
+                bits |= int(lut[q[r, 32 * sg + i] + 8]) << (6 * i)
+            raw = bits.to_bytes(24, "little")
+            head[r, 16 * sg:16 * sg + 16] = np.frombuffer(raw[:16], np.uint8)
+            tail[sg, r, :] = np.frombuffer(raw[16:], np.uint8)
+    return out
+
+
+def f6_codes(buf, rows: int, K: int) -> np.ndarray:
+    """Inverse of ``f6_operand``: the int4 codes [rows, K] held by an FP6 operand buffer."""
+    buf = np.asarray(buf, np.uint8)
+    R2 = (rows + 1) // 2 * 2
+    if buf.size != f6_bytes(rows, K):
+        raise ValueError("buffer size does not match rows and K")
+    head = buf[:R2 * (K // 2)].reshape(R2, K // 2)
+    tail = buf[R2 * (K // 2):].reshape(K // 32, R2, 8)
+    q = np.zeros((rows, K), np.int8)
+    for r in range(rows):
+        for sg in range(K // 32):
+            bits = int.from_bytes(bytes(head[r, 16 * sg:16 * sg + 16]) + bytes(tail[sg, r]), "little")
+            for i in range(32):
+                v = e3m2_value((bits >> (6 * i)) & 63)
+                if v != int(v) or not -8 <= v <= 7:
+                    raise ValueError("not an int4 code")
+                q[r, 32 * sg + i] = int(v)
+    return q
