@@ -666,8 +666,8 @@ def stack_calibrate(layers, X_calib_per_step, B: int):
 # is all zeros when rows is odd): k is cut into stages of 128 and each stage into four groups of
 # 32 consecutive k. A group's 32 codes, as 6-bit fields with code i at bits 6i..6i+5 of a 192-bit
 # little-endian string, are split into a 16-byte head (bits 0..127) and an 8-byte tail (bits
-# 128..191). Heads: byte offset row*(K/2) + 64*stage + 16*group. Tails: after the R2*(K/2) head
-# bytes, at ((4*stage + group)*R2 + row)*8. Total R2*K*3/4 bytes.
+# 128..191). Stage s occupies the R2*96 bytes from s*R2*96: first the heads, at row*64 + 16*group,
+# then the tails, at R2*64 + (group*R2 + row)*8. Total R2*K*3/4 bytes.
 
 def e3m2_value(code: int) -> float:
     """Value of a 6-bit E3M2 code, from the format's definition."""
@@ -704,16 +704,17 @@ def f6_operand(q) -> np.ndarray:
     R2 = (rows + 1) // 2 * 2
     lut = np.array([e3m2_encode(v) for v in range(-8, 8)], np.uint64)
     out = np.zeros(f6_bytes(rows, K), np.uint8)
-    head = out[:R2 * (K // 2)].reshape(R2, K // 2)
-    tail = out[R2 * (K // 2):].reshape(K // 32, R2, 8)
+    stages = out.reshape(K // 128, R2 * 96)
     for r in range(rows):
         for sg in range(K // 32):  # sg = 4 * stage + group
+            st, g = divmod(sg, 4)
             bits = 0
             for i in range(32):
                 bits |= int(lut[q[r, 32 * sg + i] + 8]) << (6 * i)
-            raw = bits.to_bytes(24, "little")
-            head[r, 16 * sg:16 * sg + 16] = np.frombuffer(raw[:16], np.uint8)
-            tail[sg, r, :] = np.frombuffer(raw[16:], np.uint8)
+            raw = np.frombuffer(bits.to_bytes(24, "little"), np.uint8)
+            stages[st, r * 64 + 16 * g:r * 64 + 16 * g + 16] = raw[:16]
+            t0 = R2 * 64 + (g * R2 + r) * 8
+            stages[st, t0:t0 + 8] = raw[16:]
     return out
 
 
@@ -723,12 +724,14 @@ def f6_codes(buf, rows: int, K: int) -> np.ndarray:
     R2 = (rows + 1) // 2 * 2
     if buf.size != f6_bytes(rows, K):
         raise ValueError("buffer size does not match rows and K")
-    head = buf[:R2 * (K // 2)].reshape(R2, K // 2)
-    tail = buf[R2 * (K // 2):].reshape(K // 32, R2, 8)
+    stages = buf.reshape(K // 128, R2 * 96)
     q = np.zeros((rows, K), np.int8)
     for r in range(rows):
         for sg in range(K // 32):
-            bits = int.from_bytes(bytes(head[r, 16 * sg:16 * sg + 16]) + bytes(tail[sg, r]), "little")
+            st, g = divmod(sg, 4)
+            t0 = R2 * 64 + (g * R2 + r) * 8
+            bits = int.from_bytes(bytes(stages[st, r * 64 + 16 * g:r * 64 + 16 * g + 16]) +
+                                  bytes(stages[st, t0:t0 + 8]), "little")
             for i in range(32):
                 v = e3m2_value((bits >> (6 * i)) & 63)
                 if v != int(v) or not -8 <= v <= 7:

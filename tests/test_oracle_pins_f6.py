@@ -51,14 +51,16 @@ def test_f6_layout_hand_bytes():
     buf = oracle.f6_operand(q)
     R2 = 4
     assert buf.size == R2 * K * 3 // 4 == oracle.f6_bytes(rows, K)
-    head = buf[:R2 * K // 2].reshape(R2, K // 2)
-    tail = buf[R2 * K // 2:].reshape(K // 32, R2, 8)
+    stage = buf.reshape(K // 128, R2 * 96)
+    head = stage[:, :R2 * 64].reshape(K // 128, R2, 4, 16)   # [stage][row][group][16 bytes]
+    tail = stage[:, R2 * 64:].reshape(K // 128, 4, R2, 8)    # [stage][group][row][8 bytes]
     # bits 0..5 = 0x0C, 6..11 = 0x10, 12..17 = 0x12, 18..23 = 0x2C
-    assert list(head[0, :3]) == [0x0C, 0x24, 0xB1]
-    assert head[0, 15] == 0xC0 and tail[0, 0, 0] == 0x05
-    assert list(tail[0, 1, :2]) == [0xC0, 0x00]
-    assert head[2, 64 + 16] == 0x38 and tail[4 + 1, 2].sum() == 0
-    assert not head[3].any() and not tail[:, 3].any()  # pad row
+    assert list(head[0, 0, 0, :3]) == [0x0C, 0x24, 0xB1]
+    assert head[0, 0, 0, 15] == 0xC0 and tail[0, 0, 0, 0] == 0x05
+    assert list(tail[0, 0, 1, :2]) == [0xC0, 0x00]
+    assert head[1, 2, 1, 0] == 0x38 and tail[1, 1, 2].sum() == 0
+    assert buf[384 + 64 * 2 + 16] == 0x38    # stage 0 is 4 * 96 = 384 bytes; head (2, 1) at 128 + 16
+    assert not head[:, 3].any() and not tail[:, :, 3].any()  # pad row
     assert np.count_nonzero(buf) == 7
 
 
@@ -73,12 +75,14 @@ def test_f6_round_trip_and_dot(rows, K):
 
     def values(buf, n):
         R2 = (n + 1) // 2 * 2
-        head = buf[:R2 * K // 2].reshape(R2, K // 2)
-        tail = buf[R2 * K // 2:].reshape(K // 32, R2, 8)
+        stage = buf.reshape(K // 128, R2 * 96)
+        head = stage[:, :R2 * 64].reshape(K // 128, R2, 4, 16)
+        tail = stage[:, R2 * 64:].reshape(K // 128, 4, R2, 8)
         out = np.zeros((n, K))
         for r in range(n):
             for sg in range(K // 32):
-                bits = int.from_bytes(bytes(head[r, 16 * sg:16 * sg + 16]) + bytes(tail[sg, r]), "little")
+                st, g = divmod(sg, 4)
+                bits = int.from_bytes(bytes(head[st, r, g]) + bytes(tail[st, g, r]), "little")
                 out[r, 32 * sg:32 * sg + 32] = dec([(bits >> (6 * i)) & 63 for i in range(32)])
         return out
 
