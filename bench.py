@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA (POP/s x 1000)
+FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -83,6 +84,24 @@ class Linear:
     def gemm(self, Y, epilogue=0, residual=None):
         self.bd.gemm(self.xq, self.xs, self.table is None, self.wq, self.w_scale, self.K, Y=Y,
                      epilogue=epilogue, residual=residual, ws=self.gemm_ws)
+
+    def f6_buffers(self, M):
+        """FP6 operands for the large-M GEMM: the weights once (offline), the activations per call."""
+        torch = _torch()
+        L = self.bd.lib()
+        self.M6 = M
+        self.wf = self.bd.codes_to_f6(self.wq, self.K)
+        self.xf = torch.empty(max(L.w4a4_f6_operand_bytes(M, self.K), 256), dtype=torch.uint8,
+                              device="cuda")
+        g = L.w4a4_gemm_f6_workspace_bytes(M, self.N, self.K)
+        self.f6_ws = torch.empty(max(g, 256), dtype=torch.uint8, device="cuda")
+
+    def to_f6(self):
+        self.bd.codes_to_f6(self.xq, self.K, out=self.xf)
+
+    def gemm_f6(self, Y, epilogue=0, residual=None):
+        self.bd.gemm_f6(self.xf, self.M6, self.xs, self.table is None, self.wf, self.N, self.w_scale,
+                        self.K, Y=Y, epilogue=epilogue, residual=residual, ws=self.f6_ws)
 
 
 def time_graph(fn, steps, warmup):
@@ -577,6 +596,35 @@ def copy_calibration(reps=3):
     print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}))
 
 
+def square_gemm(bd, n):
+    """Kernel ceiling on a large square GEMM (seeded random codes, per-token scales): the int4
+    pipelined kernel against the FP6-operand kernel, outputs compared bit for bit."""
+    torch = _torch()
+    g = torch.Generator(device="cuda").manual_seed(0)
+    xq = torch.randint(0, 256, (n, n // 2), generator=g, device="cuda", dtype=torch.uint8)
+    wq = torch.randint(0, 256, (n, n // 2), generator=g, device="cuda", dtype=torch.uint8)
+    xs = torch.full((n,), 1e-3, device="cuda")
+    ws_ = torch.full((n,), 1e-3, device="cuda")
+    Y = torch.empty((n, n), dtype=torch.float16, device="cuda")
+    Y6 = torch.empty_like(Y)
+    L = bd.lib()
+    gws = torch.empty(max(L.w4a4_gemm_workspace_bytes(n, n, n), 256), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(max(L.w4a4_gemm_f6_workspace_bytes(n, n, n), 256), dtype=torch.uint8, device="cuda")
+    xf, wf = bd.codes_to_f6(xq, n), bd.codes_to_f6(wq, n)
+    i4 = time_kernel_calls([lambda: bd.gemm(xq, xs, True, wq, ws_, n, Y=Y, ws=gws)], 5)
+    f6 = time_kernel_calls([lambda: bd.gemm_f6(xf, n, xs, True, wf, n, ws_, n, Y=Y6, ws=fws)], 5)
+    torch.cuda.synchronize()
+    ops = 2.0 * n ** 3
+    res = {"M": n, "N": n, "K": n,
+           "int4_gemm_us": i4 * 1e3, "int4_gemm_tops": ops / (i4 * 1e-3) / 1e12,
+           "fp6_gemm_us": f6 * 1e3, "fp6_gemm_tops": ops / (f6 * 1e-3) / 1e12,
+           "fp6_gemm_frac_int8_peak": ops / (f6 * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+           "same_output_bits": bool(torch.equal(Y.view(torch.int16), Y6.view(torch.int16)))}
+    del xq, wq, Y, Y6, xf, wf, gws, fws
+    torch.cuda.empty_cache()
+    return res
+
+
 def supplementary(bd, inputs, steps):
     """Shorter runs of the other workloads (large-M per-token linears and the 16-layer stack)."""
     torch = _torch()
@@ -597,8 +645,33 @@ def supplementary(bd, inputs, steps):
                      "rotate_quant_frac_hbm": rq_bytes(M, K, B, 2, True) / (rq_ms * 1e-3) / 1e9
                      / HBM_PEAK_GBPS,
                      "calibrate_and_pack_s": lin.offline_s}
-        del lin, Xs, Ys
+        # the same linear with FP6 (E3M2) matrix-core operands: weights re-encoded offline, the
+        # activation codes after each rotate-quantize; outputs must be the int4 path's bits
+        lin.f6_buffers(M)
+        Y6 = torch.empty_like(Ys[0])
+
+        def step_f6():
+            lin.rq(Xs[0])
+            lin.to_f6()
+            lin.gemm_f6(Y6)
+
+        ms6 = time_graph(step_f6, steps, 5)
+        f6_ms = time_kernel_calls([lambda: lin.gemm_f6(Y6)], 20)
+        cvt_ms = time_kernel_calls([lin.to_f6], 20)
+        step()
+        step_f6()
+        torch.cuda.synchronize()
+        out[name]["fp6_operands"] = {
+            "linear_ms": ms6, "linear_tops": ops / (ms6 * 1e-3) / 1e12,
+            "gemm_us": f6_ms * 1e3, "gemm_tops": ops / (f6_ms * 1e-3) / 1e12,
+            "gemm_frac_int8_peak": ops / (f6_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+            "gemm_frac_fp6_peak": ops / (f6_ms * 1e-3) / 1e12 / FP6_PEAK_TOPS,
+            "activation_to_fp6_us": cvt_ms * 1e3,
+            "same_output_bits_as_int4_path": bool(torch.equal(Y6.view(torch.int16),
+                                                              Ys[0].view(torch.int16)))}
+        del lin, Xs, Ys, Y6
         torch.cuda.empty_cache()
+    out["square_gemm_8192"] = square_gemm(bd, 8192)
     out["cold_hbm"] = cold_hbm(bd, inputs)
     out["group_wise_scales"] = grouped_scales(bd, inputs, max(20, steps))
     out["gptq_offline_pack"] = gptq_offline(bd, inputs)

@@ -171,6 +171,39 @@ int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * FP6 matrix-core operands for the large-M GEMM [the same integer GEMM as w4a4_gemm; vnrobo.com
+ * "Vi sao W4A4 kho hon W4A16?": the compute path itself must run on the low-bit codes]. Every int4
+ * code is exactly representable in the OCP Microscaling E3M2 six-bit float (sign bit, 3 exponent
+ * bits with bias 3, 2 mantissa bits), and gfx950's FP6 matrix instructions run at twice the int8
+ * rate without any widening work. Products of two codes are exact integers and so is every fp32
+ * partial sum (|sum| <= 64 K < 2^24 for K <= 2^18), so acc and Y equal those of w4a4_gemm /
+ * w4a4_gemm_i32 on the same codes, bit for bit.
+ * Operand layout of a code matrix [rows][K], K % 128 == 0, R2 = rows rounded up to even (the last
+ * row is zeros when rows is odd), total w4a4_f6_operand_bytes(rows, K) = R2 * K * 3/4 bytes: k is
+ * cut into stages of 128 and each stage into four groups of 32 consecutive k; a group's codes, as
+ * E3M2 fields with code i at bits 6i..6i+5 of a 192-bit little-endian string, are split into a
+ * 16-byte head (bits 0..127) and an 8-byte tail (bits 128..191). Stage s occupies the R2*96 bytes
+ * from s*R2*96: heads at row*64 + 16*group, then tails at R2*64 + (group*R2 + row)*8.
+ *  - w4a4_codes_to_f6: packed int4 codes [rows][K/2] -> that layout (out must hold
+ *    w4a4_f6_operand_bytes(rows, K) bytes). Both pointers 16-byte aligned (W4A4_ERR_ALIGN); K not a
+ *    multiple of 128 is W4A4_ERR_SHAPE. Weights are converted once, offline; activation codes after
+ *    each rotate-quantize call. Bit-exact (an encoding).
+ *  - w4a4_gemm_f6 / w4a4_gemm_f6_i32: the arguments, scales, epilogues and outputs of w4a4_gemm /
+ *    w4a4_gemm_i32 with xf / wf FP6 operands of M / N rows. K % 128 == 0 (W4A4_ERR_SHAPE),
+ *    K <= 2^18 (W4A4_ERR_UNSUPPORTED), xf and wf 16-byte aligned (W4A4_ERR_ALIGN). Meant for
+ *    M > 64, where the GEMM is bound by the matrix cores; the workspace holds split-K partials.
+ * ------------------------------------------------------------------------------------------- */
+size_t w4a4_f6_operand_bytes(int rows, int K);
+int w4a4_codes_to_f6(const uint8_t *codes, int rows, int K, uint8_t *out, hipStream_t stream);
+size_t w4a4_gemm_f6_workspace_bytes(int M, int N, int K);
+int w4a4_gemm_f6(const uint8_t *xf, const float *x_scale, int x_scale_per_token, const uint8_t *wf,
+                 const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
+                 const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+int w4a4_gemm_f6_i32(const uint8_t *xf, const uint8_t *wf, int M, int N, int K, int32_t *acc,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * W8A8 linears [radar.vhtltd.com FoldQuantVLA summary, key change 5: the attention-output and FFN
  * down projections kept at W8A8 raise the real-robot success rate at about 1 ms of latency]: the
  * same rotation, scales and calls on the symmetric int8 grid. Codes are int8, one per byte, two's

@@ -248,3 +248,34 @@ def test_gptq_rejects(L):
     assert L.w4a4_pack_weights_gptq(FAKE, bd.W4A4_F16, 16, 256, 256, 128, FAKE, FAKE, FAKE, NULL,
                                     FAKE, FAKE, FAKE, FAKE, 64, NULL) == bd.W4A4_ERR_WORKSPACE
     assert L.w4a4_pack_gptq_workspace_bytes(16, 256, 128) >= 16 * 256 * 9
+
+
+# ---- FP6 operands: host-side validation (nothing is launched on these paths)
+
+def _gemm_f6(L, *, M=256, N=256, K=256, xf=FAKE, wf=FAKE, ws=NULL, wsb=0):
+    return L.w4a4_gemm_f6(xf, FAKE, 1, wf, FAKE, M, N, K, FAKE, N, 0, NULL, 0, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=192), bd.W4A4_ERR_SHAPE),                     # K not a multiple of 128
+    (dict(K=(1 << 18) + 128), bd.W4A4_ERR_UNSUPPORTED),   # 64 K above 2^24
+    (dict(xf=ctypes.c_void_p(0x10008)), bd.W4A4_ERR_ALIGN),
+    (dict(wf=NULL), bd.W4A4_ERR_ARG),
+    (dict(N=0), bd.W4A4_ERR_ARG),
+])
+def test_gemm_f6_rejects(L, kw, code):
+    assert _gemm_f6(L, **kw) == code
+
+
+def test_codes_to_f6_rejects_and_sizes(L):
+    assert L.w4a4_f6_operand_bytes(3, 256) == 4 * 256 * 3 // 4   # rows rounded up to even
+    assert L.w4a4_f6_operand_bytes(4, 256) == 4 * 256 * 3 // 4
+    assert L.w4a4_f6_operand_bytes(4, 200) == 0
+    assert L.w4a4_codes_to_f6(FAKE, 4, 192, FAKE, NULL) == bd.W4A4_ERR_SHAPE
+    assert L.w4a4_codes_to_f6(FAKE_ODD, 4, 256, FAKE, NULL) == bd.W4A4_ERR_ALIGN
+    assert L.w4a4_codes_to_f6(FAKE, 4, 256, NULL, NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_codes_to_f6(FAKE, -1, 256, FAKE, NULL) == bd.W4A4_ERR_ARG
+    assert L.w4a4_codes_to_f6(FAKE, 0, 256, FAKE, NULL) == bd.W4A4_OK  # empty: nothing launched
+    need = L.w4a4_gemm_f6_workspace_bytes(256, 256, 16384)
+    assert need >= 2 * 256 * 256 * 4   # split K
+    assert _gemm_f6(L, K=16384) == bd.W4A4_ERR_WORKSPACE

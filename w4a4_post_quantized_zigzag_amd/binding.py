@@ -45,6 +45,12 @@ SIGNATURES = {
     "w4a4_gemm_w8a8": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz,
                             _vp]),
     "w4a4_gemm_w8a8_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "w4a4_f6_operand_bytes": (_sz, [_i, _i]),
+    "w4a4_codes_to_f6": (_i, [_vp, _i, _i, _vp, _vp]),
+    "w4a4_gemm_f6_workspace_bytes": (_sz, [_i, _i, _i]),
+    "w4a4_gemm_f6": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz,
+                          _vp]),
+    "w4a4_gemm_f6_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "w4a4_calibrate_act_scale_grouped": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _vp, _sz,
                                               _vp]),
     "w4a4_rotate_quant_act_grouped": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
@@ -256,6 +262,43 @@ def gemm_i32(xq, wq, K: int, bits: int = 4):
     ws, nb = _ws(wsb(M, N, K), wq.device)
     fn = lib().w4a4_gemm_i32 if bits == 4 else lib().w4a4_gemm_w8a8_i32
     check(fn(_p(xq), _p(wq), M, N, K, _p(acc), _p(ws), nb, _stream()))
+    return acc
+
+
+def codes_to_f6(codes, K: int, out=None):
+    """FP6 (E3M2) operand bytes of packed int4 codes [rows][K/2] (flat uint8 tensor)."""
+    torch = _torch()
+    rows = codes.shape[0]
+    nbytes = lib().w4a4_f6_operand_bytes(rows, K)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
+    check(lib().w4a4_codes_to_f6(_p(codes), rows, K, _p(out), _stream()))
+    return out
+
+
+def gemm_f6(xf, M: int, x_scale, per_token: bool, wf, N: int, w_scale, K: int, Y=None,
+            epilogue: int = EPI_NONE, residual=None, ws=None):
+    """The W4A4 GEMM on FP6 operands (``codes_to_f6`` of the activation and weight codes)."""
+    torch = _torch()
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=wf.device)
+    need = lib().w4a4_gemm_f6_workspace_bytes(M, N, K)
+    if ws is None:
+        ws, nb = _ws(need, wf.device)
+    else:
+        nb = ws.numel()
+    ldr = _row_stride(residual) if residual is not None else 0
+    check(lib().w4a4_gemm_f6(_p(xf), _p(x_scale), 1 if per_token else 0, _p(wf), _p(w_scale), M, N,
+                             K, _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, _p(ws), nb,
+                             _stream()))
+    return Y
+
+
+def gemm_f6_i32(xf, M: int, wf, N: int, K: int):
+    torch = _torch()
+    acc = torch.empty((M, N), dtype=torch.int32, device=wf.device)
+    ws, nb = _ws(lib().w4a4_gemm_f6_workspace_bytes(M, N, K), wf.device)
+    check(lib().w4a4_gemm_f6_i32(_p(xf), _p(wf), M, N, K, _p(acc), _p(ws), nb, _stream()))
     return acc
 
 

@@ -427,13 +427,29 @@ size_t w4a4_gemm_w8a8_workspace_bytes(int M, int N, int K)
 
 namespace w4a4 {
 
-static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, bool q8)
+// operand formats of the GEMM entry points
+enum { OPF_I4 = 0, OPF_I8 = 1, OPF_F6 = 2 };
+
+static size_t gemm_ws_for(int M, int N, int K, int fmt)
+{
+    return fmt == OPF_F6 ? gemm_f6_workspace(M, N, K) : gemm_workspace(M, N, K, fmt == OPF_I8);
+}
+
+static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int fmt)
 {
     if (M < 0 || N <= 0 || K <= 0) return fail(W4A4_ERR_ARG, "bad sizes M=%d N=%d K=%d", M, N, K);
     if ((M > 0 && !xq) || !wq) return fail(W4A4_ERR_ARG, "xq / wq is NULL");
-    if (!q8) {
+    if (fmt == OPF_I4) {
         if (K % 2) return fail(W4A4_ERR_SHAPE, "K = %d must be even", K);
         if (K > (1 << 24)) return fail(W4A4_ERR_UNSUPPORTED, "K = %d above 2^24", K);
+        return W4A4_OK;
+    }
+    if (fmt == OPF_F6) {
+        if (K % 128) return fail(W4A4_ERR_SHAPE, "fp6 GEMM needs K a multiple of 128, not %d", K);
+        if (K > (1 << 18))
+            return fail(W4A4_ERR_UNSUPPORTED, "fp6 GEMM K = %d above 2^18 (exact fp32 sums)", K);
+        if (!aligned(xq, 16) || !aligned(wq, 16))
+            return fail(W4A4_ERR_ALIGN, "fp6 operands must be 16-byte aligned");
         return W4A4_OK;
     }
     if (K % 64) return fail(W4A4_ERR_SHAPE, "int8 GEMM needs K a multiple of 64, not %d", K);
@@ -447,10 +463,10 @@ static int check_gemm_common(const uint8_t *xq, const uint8_t *wq, int M, int N,
 static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
-                      size_t ws_bytes, hipStream_t stream, bool q8)
+                      size_t ws_bytes, hipStream_t stream, int fmt)
 {
     int rc;
-    if ((rc = check_gemm_common(xq, wq, M, N, K, q8))) return rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K, fmt))) return rc;
     if (epilogue != W4A4_EPI_NONE && epilogue != W4A4_EPI_GELU && epilogue != W4A4_EPI_RESIDUAL)
         return fail(W4A4_ERR_ARG, "unknown epilogue %d", epilogue);
     if (!w_scale || (M > 0 && (!x_scale || !Y)))
@@ -463,7 +479,7 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     }
     if (!aligned(Y, 2) || !aligned(x_scale, 4) || !aligned(w_scale, 4))
         return fail(W4A4_ERR_ALIGN, "Y / scales misaligned");
-    if ((rc = check_ws(ws, ws_bytes, M > 0 ? gemm_workspace(M, N, K, q8) : 0))) return rc;
+    if ((rc = check_ws(ws, ws_bytes, M > 0 ? gemm_ws_for(M, N, K, fmt) : 0))) return rc;
     if (M == 0) return ok();
     GemmEpilogue epi{};
     epi.x_scale = x_scale;
@@ -474,23 +490,27 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     epi.mode = epilogue;
     epi.residual = residual;
     epi.ldr = ldr;
-    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8))) return rc;
+    if ((rc = fmt == OPF_F6 ? launch_gemm_f6(xq, wq, M, N, K, epi, ws, ws_bytes, stream)
+                         : launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, fmt == OPF_I8)))
+        return rc;
     return ok();
 }
 
 static int gemm_i32_entry(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
-                          void *ws, size_t ws_bytes, hipStream_t stream, bool q8)
+                          void *ws, size_t ws_bytes, hipStream_t stream, int fmt)
 {
     int rc;
-    if ((rc = check_gemm_common(xq, wq, M, N, K, q8))) return rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K, fmt))) return rc;
     if (M > 0 && !acc) return fail(W4A4_ERR_ARG, "acc is NULL");
     if (!aligned(acc, 4)) return fail(W4A4_ERR_ALIGN, "acc misaligned");
-    if ((rc = check_ws(ws, ws_bytes, M > 0 ? gemm_workspace(M, N, K, q8) : 0))) return rc;
+    if ((rc = check_ws(ws, ws_bytes, M > 0 ? gemm_ws_for(M, N, K, fmt) : 0))) return rc;
     if (M == 0) return ok();
     GemmEpilogue epi{};
     epi.mode = GEMM_OUT_I32;
     epi.acc_out = acc;
-    if ((rc = launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, q8))) return rc;
+    if ((rc = fmt == OPF_F6 ? launch_gemm_f6(xq, wq, M, N, K, epi, ws, ws_bytes, stream)
+                         : launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, fmt == OPF_I8)))
+        return rc;
     return ok();
 }
 
@@ -503,13 +523,13 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
               const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
-                      residual, ldr, ws, ws_bytes, stream, false);
+                      residual, ldr, ws, ws_bytes, stream, OPF_I4);
 }
 
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
                   void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, false);
+    return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, OPF_I4);
 }
 
 int w4a4_gemm_w8a8(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
@@ -518,13 +538,57 @@ int w4a4_gemm_w8a8(const uint8_t *xq, const float *x_scale, int x_scale_per_toke
                    size_t ws_bytes, hipStream_t stream)
 {
     return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
-                      residual, ldr, ws, ws_bytes, stream, true);
+                      residual, ldr, ws, ws_bytes, stream, OPF_I8);
 }
 
 int w4a4_gemm_w8a8_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
                        void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, true);
+    return gemm_i32_entry(xq, wq, M, N, K, acc, ws, ws_bytes, stream, OPF_I8);
+}
+
+// ------------------------------------------------------------------ FP6 operands
+
+size_t w4a4_f6_operand_bytes(int rows, int K)
+{
+    if (rows <= 0 || K <= 0 || K % 128) return 0;
+    return f6_operand_bytes(rows, K);
+}
+
+int w4a4_codes_to_f6(const uint8_t *codes, int rows, int K, uint8_t *out, hipStream_t stream)
+{
+    if (rows < 0 || K <= 0) return fail(W4A4_ERR_ARG, "bad sizes rows=%d K=%d", rows, K);
+    if (K % 128) return fail(W4A4_ERR_SHAPE, "fp6 operands need K a multiple of 128, not %d", K);
+    if ((int64_t)((rows + 1) & ~1) * (K / 32) > INT32_MAX)
+        return fail(W4A4_ERR_UNSUPPORTED, "fp6 operand of %d x %d beyond int32 indexing", rows, K);
+    if (rows > 0 && (!codes || !out)) return fail(W4A4_ERR_ARG, "codes / out is NULL");
+    if (!aligned(codes, 16) || !aligned(out, 16))
+        return fail(W4A4_ERR_ALIGN, "codes and out must be 16-byte aligned");
+    if (rows == 0) return ok();
+    int rc;
+    if ((rc = launch_codes_to_f6(codes, rows, K, out, stream))) return rc;
+    return ok();
+}
+
+size_t w4a4_gemm_f6_workspace_bytes(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+    return gemm_f6_workspace(M, N, K);
+}
+
+int w4a4_gemm_f6(const uint8_t *xf, const float *x_scale, int x_scale_per_token, const uint8_t *wf,
+                 const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
+                 const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes,
+                 hipStream_t stream)
+{
+    return gemm_entry(xf, x_scale, x_scale_per_token, wf, w_scale, M, N, K, Y, ldy, epilogue,
+                      residual, ldr, ws, ws_bytes, stream, OPF_F6);
+}
+
+int w4a4_gemm_f6_i32(const uint8_t *xf, const uint8_t *wf, int M, int N, int K, int32_t *acc,
+                     void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return gemm_i32_entry(xf, wf, M, N, K, acc, ws, ws_bytes, stream, OPF_F6);
 }
 
 // ------------------------------------------------------------------ group-wise scales
@@ -593,7 +657,7 @@ int w4a4_gemm_grouped(const uint8_t *xq, const float *x_scales, const uint8_t *w
                       hipStream_t stream)
 {
     int rc;
-    if ((rc = check_gemm_common(xq, wq, M, N, K, false))) return rc;
+    if ((rc = check_gemm_common(xq, wq, M, N, K, OPF_I4))) return rc;
     if (block != 128)
         return fail(W4A4_ERR_UNSUPPORTED, "group-wise scales need block 128 (got %d)", block);
     if (K % block) return fail(W4A4_ERR_SHAPE, "K = %d not a multiple of block %d", K, block);

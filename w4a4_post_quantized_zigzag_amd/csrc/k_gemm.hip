@@ -1057,6 +1057,305 @@ __global__ void k_splitk_epilogue4(const int32_t *__restrict__ partial, int spli
         make_uint2(f32x2_to_f16x2(y[0], y[1]), f32x2_to_f16x2(y[2], y[3]));
 }
 
+// ------------------------------------------------------------------ FP6 matrix-core operands
+//
+// The OCP E3M2 six-bit float (the "bf6" operand format of v_mfma_scale_f32_16x16x128_f8f6f4) holds
+// every integer in [-8, 7] exactly, and the FP6 matrix instructions run at twice the int8 rate with
+// no widening work. Products of two codes are exact integers and so is every partial sum of them
+// below 2^24 in the fp32 accumulator (|sum| <= 64 K with K <= 2^18), so the accumulator holds the
+// same integer as the int32 path and the epilogue gives the same bits.
+//
+// Operand layout of a [rows][K] code matrix (K % 128 == 0, R2 = rows rounded up to even, the pad
+// row all zeros): per 128-k stage, four groups of 32 consecutive k, each group's codes as 6-bit
+// fields (code i at bits 6i..6i+5 of a 192-bit little-endian string) -- the lane image of one MFMA
+// operand fragment. Stage s is one block of R2 * 96 bytes at s * R2 * 96: the first 16 bytes of
+// each group ("head") at row * 64 + 16 * group, then the last 8 bytes ("tail") at R2 * 64 +
+// (group * R2 + row) * 8. A tile's stage is thus a few contiguous runs (whole cache lines for the
+// loads into LDS). Heads are staged in LDS like packed int4 rows (XOR-swizzled 64-byte rows) and
+// read with one 16-byte access; tails are staged group-major, so the 16 lanes reading one group's
+// tails touch 128 contiguous bytes: one conflict-free 8-byte access.
+constexpr int F6_KS = 128;         // k per stage
+constexpr int F6_MAX_K = 1 << 18;  // 64 * 2^18 = 2^24: every partial sum is exact in fp32
+
+__host__ __device__ inline int f6_rows2(int rows) { return (rows + 1) & ~1; }
+
+// E3M2 code of a two's-complement nibble: |v| as fp32 gives the exponent (bias 127 -> 3) and the two
+// leading mantissa bits; zero stays zero.
+__device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t nib)
+{
+    const int v = (int)((nib ^ 8u) & 15u) - 8;
+    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+    const uint32_t f = __float_as_uint((float)a);
+    const uint32_t mag = a ? ((((f >> 23) - 124u) << 2) | ((f >> 21) & 3u)) : 0u;
+    return mag | (v < 0 ? 0x20u : 0u);
+}
+
+// One thread per (32-k group, row, 128-k stage), groups fastest: the four threads of a row read
+// its 64 packed bytes of the stage and write its 64 head bytes (consecutive rows are contiguous
+// in the stage block), each also one 8-byte tail (consecutive rows of a group are contiguous);
+// zeros for the pad row.
+__global__ __launch_bounds__(256) void k_codes_to_f6(const uint8_t *__restrict__ q, int rows, int K,
+                                                     uint8_t *__restrict__ out)
+{
+    const int R2 = f6_rows2(rows);
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)R2 * (K / 32)) return;
+    const int g = (int)(t & 3);
+    const int row = (int)((t >> 2) % R2);
+    const int st = (int)((t >> 2) / R2);
+    uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+    if (row < rows) {
+        const uint4 p = *reinterpret_cast<const uint4 *>(q + (int64_t)row * (K / 2) + 64 * st + 16 * g);
+        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const uint32_t c = e3m2_of_nibble(pw[i / 8] >> (4 * (i % 8)));
+            const int bit = 6 * i;
+            w[bit / 32] |= c << (bit % 32);
+            if (bit % 32 > 26) w[bit / 32 + 1] |= c >> (32 - bit % 32);
+        }
+    }
+    uint8_t *blk = out + (int64_t)st * R2 * 96;
+    *reinterpret_cast<uint4 *>(blk + (int64_t)row * 64 + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint2 *>(blk + (int64_t)R2 * 64 + ((int64_t)g * R2 + row) * 8) =
+        make_uint2(w[4], w[5]);
+}
+
+int launch_codes_to_f6(const uint8_t *q, int rows, int K, uint8_t *out, hipStream_t s)
+{
+    const int64_t threads = (int64_t)f6_rows2(rows) * (K / 32);
+    if (threads == 0) return W4A4_OK;
+    hipLaunchKernelGGL(k_codes_to_f6, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, q,
+                       rows, K, out);
+    return check_launch("codes to fp6");
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(n) with lgkmcnt / expcnt at their no-wait values (vmcnt bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Pipelined FP6 GEMM: the int4 pipelined kernel's structure (LDS ring of NSTAGE stages filled by
+// global_load_lds_dwordx4, vmcnt waits + plain barriers, XCD-aware tile order), one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per fragment pair and stage with unit E8M0 scales (127), both
+// operands bf6 (format 3). xf / wf are FP6 operands of M / N rows; LDS stage image: A heads
+// [BM][64] swizzled, A tails [4][BM][8], B heads [BN][64], B tails [4][BN][8].
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_f6(
+    const uint8_t *__restrict__ xf, const uint8_t *__restrict__ wf, int M, int N, int K,
+    int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
+{
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int AH = BM * 64, AT = BM * 32, BH = BN * 64, BT = BN * 32;
+    constexpr int STAGE = AH + AT + BH + BT;
+    constexpr int NI = STAGE / 1024;  // 1 KB DMA instructions per stage
+    constexpr int Q = NI / NW;        // ... per wave
+    constexpr int IAH = BM / 16, IAT = BM / 32, IBH = BN / 16;  // instruction ranges
+    static_assert(BM % 128 == 0 && BN % 128 == 0, "whole-KB tail instructions");
+    static_assert(Q * NW == NI, "whole DMA instructions per wave");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int T = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int per_x = T / 8, rm = T % 8, x = id % 8;
+    const int lin = x * per_x + min(x, rm) + id / 8;
+    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int R2x = f6_rows2(M), R2w = f6_rows2(N);
+    const int st_split = k_split / F6_KS;
+    const int st_begin = blockIdx.y * st_split;
+    const int stages = min(st_split, K / F6_KS - st_begin);
+
+    // per-lane DMA source of each of this wave's instructions at stage 0 of the split, and the
+    // byte step from one stage to the next (one stage block of the operand)
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t *src[Q];
+    int64_t sstep[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int ii = uwave * Q + q;
+        const bool is_a = ii < IAH + IAT;
+        const int i2 = is_a ? ii : ii - IAH - IAT;
+        const int nh = is_a ? IAH : IBH;
+        const int r0 = is_a ? m0 : n0, rows = is_a ? M : N, R2 = is_a ? R2x : R2w;
+        const int bm = is_a ? BM : BN;
+        const uint8_t *blk = (is_a ? xf : wf) + (int64_t)st_begin * R2 * 96;
+        sstep[q] = (int64_t)R2 * 96;
+        if (i2 < nh) {
+            const int row = i2 * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ ((row >> 1) & 3);
+            src[q] = blk + (int64_t)min(r0 + row, rows - 1) * 64 + 16 * c;
+        } else {
+            const int t = i2 - nh, g = t / (bm / 128), part = t % (bm / 128);
+            const int row = min(r0 + part * 128 + 2 * lane, R2 - 2);
+            src[q] = blk + (int64_t)R2 * 64 + ((int64_t)g * R2 + row) * 8;
+        }
+    }
+    const uint32_t lds0 = lds_address(smem);
+    auto issue = [&](int st) {
+        const uint32_t base = lds0 + (uint32_t)((st % NSTAGE) * STAGE);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            dma_to_lds16(src[q] + st * sstep[q], base + (uint32_t)((uwave * Q + q) * 1024));
+    };
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+        if (p < stages) issue(p);
+
+    const int fr = lane & 15, fg = lane >> 4;
+    for (int st = 0; st < stages; ++st) {
+        const int ahead = min(stages - 1 - st, NSTAGE - 2);
+        asm volatile("" ::: "memory");
+        if (ahead == 0) wait_vm<0>();
+        else if (ahead == 1) wait_vm<Q>();
+        else if (NSTAGE > 3 && ahead == 2) wait_vm<(NSTAGE > 3 ? 2 * Q : 0)>();
+        else wait_vm<(NSTAGE > 4 ? 3 * Q : 0)>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (st + NSTAGE - 1 < stages) issue(st + NSTAGE - 1);
+        const uint8_t *sA = smem + (st % NSTAGE) * STAGE;
+        const uint8_t *sAt = sA + AH, *sB = sA + AH + AT, *sBt = sB + BH;
+        v8i fb[FN], fa[FM];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * WTN + j * 16 + fr;
+            const uint4 h = *reinterpret_cast<const uint4 *>(&sB[row * 64 + swz(row, fg)]);
+            const uint2 t = *reinterpret_cast<const uint2 *>(&sBt[(fg * BN + row) * 8]);
+            fb[j] = v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)t.x, (int)t.y, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 16 + fr;
+            const uint4 h = *reinterpret_cast<const uint4 *>(&sA[row * 64 + swz(row, fg)]);
+            const uint2 t = *reinterpret_cast<const uint2 *>(&sAt[(fg * BM + row) * 8]);
+            fa[i] = v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)t.x, (int)t.y, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], acc[i][j], 3, 3,
+                                                                             0, 127, 0, 127);
+        // every fragment read of the stage first, then the MFMAs: one LDS latency per stage
+        // instead of one per activation fragment
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FM + FN), 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * (FM + FN), 0);  // tail register moves
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);        // MFMA
+    }
+
+    // lane (fr, fg) of fragment (i, j): output row m0 + wm * WTM + 16 i + fr, columns
+    // n0 + wn * WTN + 16 j + 4 fg + 0..3 (the weight fragment is the MFMA's A operand)
+    const int mrow = m0 + wm * WTM + fr, ncol = n0 + wn * WTN + 4 * fg;
+    if (PE == PE_INT32) {
+        int32_t *dst = partial ? partial + (int64_t)blockIdx.y * M * N : epi.acc_out;
+        const bool vec4 = (N % 4 == 0) && ((uintptr_t)dst % 16 == 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int m = mrow + i * 16, n = ncol + j * 16;
+                if (m >= M) continue;
+                int v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = (int)acc[i][j][r];
+                if (vec4 && n + 3 < N) {
+                    *reinterpret_cast<int4 *>(&dst[(int64_t)m * N + n]) = make_int4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) dst[(int64_t)m * N + n + r] = v[r];
+                }
+            }
+        return;
+    } else {
+#pragma clang fp contract(off)
+        float xsc[FM];
+        float wsc[FN][4];
+        uint32_t rsd[FM][FN][2];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            xsc[i] = epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = ncol + j * 16;
+            if (VEC_OUT && n + 3 < N) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
+                wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wsc[j][r] = epi.w_scale[min(n + r, N - 1)];
+            }
+        }
+        auto residual4 = [&](int m, int n, uint32_t (&h)[2]) {
+            const uint16_t *rs = epi.residual + (int64_t)min(m, M - 1) * epi.ldr;
+            if (VEC_OUT && n + 3 < N) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(rs + n);
+                h[0] = v.x; h[1] = v.y;
+            } else {
+                uint32_t e[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e[r] = rs[min(n + r, N - 1)];
+                h[0] = e[0] | (e[1] << 16); h[1] = e[2] | (e[3] << 16);
+            }
+        };
+        if (PE == PE_RESIDUAL && VEC_OUT) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) residual4(mrow + i * 16, ncol + j * 16, rsd[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = mrow + i * 16;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = ncol + j * 16;
+                float y[4];
+                if (PE == PE_RESIDUAL && !VEC_OUT) residual4(m, n, rsd[i][j]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // the accumulator is an exact integer: (float)(int) of it is itself
+                    y[r] = fp32_value(acc[i][j][r] * xsc[i]);
+                    y[r] = fp32_value(y[r] * wsc[j][r]);
+                    if (PE == PE_GELU) y[r] = fp32_value(gelu_erf(y[r]));
+                    if (PE == PE_RESIDUAL) {
+                        const uint32_t hv = rsd[i][j][r >> 1] >> (16 * (r & 1));
+                        y[r] = fp32_value(y[r] + __half2float(__ushort_as_half((uint16_t)hv)));
+                    }
+                }
+                if (m >= M) continue;
+                uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
+                if (VEC_OUT && n + 3 < N) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(f32x2_to_f16x2(y[0], y[1]),
+                                                                 f32x2_to_f16x2(y[2], y[3]));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) dst[r] = f32_to_f16_bits(y[r]);
+                }
+            }
+        }
+    }
+}
+
 struct GemmPlan {
     int kind;  // 0 small-M, 1 = 256x256, 2 = 128x256, 3 = 128x128, 4 = 64x128 (pipelined only)
     int bm, bn, splits, k_split;
@@ -1336,6 +1635,126 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
         hipLaunchKernelGGL(k_splitk_epilogue, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                            s, partial, p.splits, M, N, epi);
     return check_launch("gemm split-k epilogue");
+}
+
+// ---- FP6 GEMM launch
+
+// Tile shape and k split of the FP6 GEMM, chosen like plan_gemm's (full rounds of 256 compute units
+// times the per-tile matrix time, plus split-K partial traffic) at the FP6 matrix rate: 256 x 256
+// (8 waves, 3 LDS stages), 128 x 256 (4 waves, 4 stages), 128 x 128 (4 waves, 4 stages).
+static GemmPlan plan_gemm_f6(int M, int N, int K)
+{
+    struct Cand { int kind, bm, bn; double eff; };
+    const Cand cands[] = {{1, 256, 256, 1.0}, {2, 128, 256, 0.85}, {3, 128, 128, 0.6}};
+    constexpr double ROUND_FIXED = 3e-6;
+    GemmPlan best{3, 128, 128, 1, K};
+    double best_t = 1e30;
+    for (const Cand &c : cands) {
+        const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        for (int splits = 1; splits <= 16; splits *= 2) {
+            const int k_split = ((K + splits - 1) / splits + F6_KS - 1) / F6_KS * F6_KS;
+            if ((K + k_split - 1) / k_split != splits) continue;
+            if (splits > 1 && k_split < 1024) continue;
+            const double rounds = std::ceil(tiles * splits / 256.0);
+            const double t_c = rounds * (2.0 * c.bm * c.bn * k_split / (16384.0 * 2.4e9 * c.eff) +
+                                         ROUND_FIXED);
+            const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 4e12 + 3e-6 : 0.0;
+            if (t_c + t_r < best_t * 0.98) {
+                best_t = t_c + t_r;
+                best = GemmPlan{c.kind, c.bm, c.bn, splits, k_split};
+            }
+        }
+    }
+    return best;
+}
+
+size_t gemm_f6_workspace(int M, int N, int K)
+{
+    const GemmPlan p = plan_gemm_f6(M, N, K);
+    return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int PE, bool VO>
+static int launch_f6_e(dim3 grid, hipStream_t s, const uint8_t *xf, const uint8_t *wf, int M,
+                       int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                       int32_t *partial)
+{
+    const size_t lds = (size_t)NS * (BM + BN) * 96;
+    const void *fn = (const void *)k_gemm_f6<BM, BN, WM, WN, NS, PE, VO>;
+    static bool attr_set = false;  // once per process and instantiation
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return fail(W4A4_ERR_HIP, "fp6 gemm LDS request: %s", hipGetErrorString(e));
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gemm_f6<BM, BN, WM, WN, NS, PE, VO>), grid, dim3(64 * WM * WN), lds, s,
+                       xf, wf, M, N, K, k_split, tm, tn, epi, partial);
+    return W4A4_OK;
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+static int launch_f6_t(dim3 grid, hipStream_t s, const uint8_t *xf, const uint8_t *wf, int M,
+                       int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                       int32_t *partial)
+{
+    if (partial || epi.mode == GEMM_OUT_I32)
+        return launch_f6_e<BM, BN, WM, WN, NS, PE_INT32, false>(grid, s, xf, wf, M, N, K, k_split,
+                                                                 tm, tn, epi, partial);
+    const bool vo = (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+                    ((uintptr_t)epi.w_scale % 16 == 0) &&
+                    (epi.mode != W4A4_EPI_RESIDUAL ||
+                     (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
+#define W4A4_F6_E(PEV)                                                                             \
+    return vo ? launch_f6_e<BM, BN, WM, WN, NS, PEV, true>(grid, s, xf, wf, M, N, K, k_split, tm,   \
+                                                           tn, epi, partial)                       \
+              : launch_f6_e<BM, BN, WM, WN, NS, PEV, false>(grid, s, xf, wf, M, N, K, k_split, tm,  \
+                                                            tn, epi, partial);
+    if (epi.mode == W4A4_EPI_GELU) { W4A4_F6_E(PE_GELU) }
+    if (epi.mode == W4A4_EPI_RESIDUAL) { W4A4_F6_E(PE_RESIDUAL) }
+    W4A4_F6_E(PE_NONE)
+#undef W4A4_F6_E
+}
+
+// FP6 operands (see the layout above); the caller guarantees K % 128 == 0, K <= F6_MAX_K and
+// 16-byte aligned operands.
+int launch_gemm_f6(const uint8_t *xf, const uint8_t *wf, int M, int N, int K,
+                   const GemmEpilogue &epi, void *ws, size_t ws_bytes, hipStream_t s)
+{
+    if (M == 0) return W4A4_OK;
+    const GemmPlan p = plan_gemm_f6(M, N, K);
+    int32_t *partial = nullptr;
+    if (p.splits > 1) {
+        const size_t need = gemm_f6_workspace(M, N, K);
+        if (!ws || ws_bytes < need)
+            return fail(W4A4_ERR_WORKSPACE, "fp6 gemm needs %zu workspace bytes", need);
+        partial = reinterpret_cast<int32_t *>(ws);
+    }
+    const int tm = (M + p.bm - 1) / p.bm, tn = (N + p.bn - 1) / p.bn;
+    const dim3 grid(tm * tn, p.splits);
+    int rc;
+    if (p.kind == 1)
+        rc = launch_f6_t<256, 256, 2, 4, 3>(grid, s, xf, wf, M, N, K, p.k_split, tm, tn, epi, partial);
+    else if (p.kind == 2)
+        rc = launch_f6_t<128, 256, 1, 4, 4>(grid, s, xf, wf, M, N, K, p.k_split, tm, tn, epi, partial);
+    else
+        rc = launch_f6_t<128, 128, 2, 2, 4>(grid, s, xf, wf, M, N, K, p.k_split, tm, tn, epi, partial);
+    if (rc != W4A4_OK) return rc;
+    rc = check_launch("fp6 gemm");
+    if (rc != W4A4_OK || p.splits <= 1) return rc;
+    const int64_t total = (int64_t)M * N;
+    const bool out_vec = (epi.mode == GEMM_OUT_I32)
+                             ? ((uintptr_t)epi.acc_out % 16 == 0)
+                             : ((epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+                                ((uintptr_t)epi.w_scale % 16 == 0) &&
+                                (epi.mode != W4A4_EPI_RESIDUAL ||
+                                 (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0)));
+    if (N % 4 == 0 && (uintptr_t)partial % 16 == 0 && out_vec)
+        hipLaunchKernelGGL(k_splitk_epilogue4, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256),
+                           0, s, partial, p.splits, M, N, epi);
+    else
+        hipLaunchKernelGGL(k_splitk_epilogue, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                           s, partial, p.splits, M, N, epi);
+    return check_launch("fp6 gemm split-k epilogue");
 }
 
 }  // namespace w4a4

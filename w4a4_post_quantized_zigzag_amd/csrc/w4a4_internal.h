@@ -138,6 +138,14 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
 int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int K,
                         const GemmEpilogue &epi, hipStream_t s);
 
+// FP6 (E3M2) operands of the FP6 matrix-core GEMM: packed int4 codes [rows][K/2] re-encoded into
+// f6_operand_bytes(rows, K) bytes (K % 128 == 0), and the GEMM on two such operands (K <= 2^18).
+inline size_t f6_operand_bytes(int rows, int K) { return (size_t)((rows + 1) & ~1) * (size_t)K * 3 / 4; }
+int launch_codes_to_f6(const uint8_t *q, int rows, int K, uint8_t *out, hipStream_t s);
+size_t gemm_f6_workspace(int M, int N, int K);
+int launch_gemm_f6(const uint8_t *xf, const uint8_t *wf, int M, int N, int K,
+                   const GemmEpilogue &epi, void *ws, size_t ws_bytes, hipStream_t s);
+
 // calibration (k_calib.hip)
 size_t zigzag_workspace(int K);
 int launch_zigzag(const void *W, int wdt, int N, int K, int64_t ldw, int B, int32_t *perm,
