@@ -1224,10 +1224,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_f6(
     for (int st = 0; st < stages; ++st) {
         const int ahead = min(stages - 1 - st, NSTAGE - 2);
         asm volatile("" ::: "memory");
-        if (ahead == 0) wait_vm<0>();
+        // wait until at most `ahead` stages of loads are in flight (a smaller count where the ring
+        // cannot hold that many: only ever a longer wait)
+        if (ahead <= 0) wait_vm<0>();
         else if (ahead == 1) wait_vm<Q>();
-        else if (NSTAGE > 3 && ahead == 2) wait_vm<(NSTAGE > 3 ? 2 * Q : 0)>();
-        else wait_vm<(NSTAGE > 4 ? 3 * Q : 0)>();
+        else if (ahead == 2) wait_vm<(NSTAGE > 3 ? 2 * Q : 0)>();
+        else if (ahead == 3) wait_vm<(NSTAGE > 4 ? 3 * Q : 0)>();
+        else wait_vm<(NSTAGE > 5 ? 4 * Q : 0)>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (st + NSTAGE - 1 < stages) issue(st + NSTAGE - 1);
@@ -1639,14 +1642,16 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
 
 // ---- FP6 GEMM launch
 
-// Tile shape and k split of the FP6 GEMM, chosen like plan_gemm's (full rounds of 256 compute units
-// times the per-tile matrix time, plus split-K partial traffic) at the FP6 matrix rate: 256 x 256
-// (8 waves, 3 LDS stages), 128 x 256 (4 waves, 4 stages), 128 x 128 (4 waves, 4 stages).
+// Tile shape and k split of the FP6 GEMM. The kernel is bound by the latency of its loads into
+// LDS (the ring holds two or more stages in flight, and at the FP6 matrix rate a stage's MFMAs take
+// less time than its loads), so the model counts stages: full rounds of 256 compute units (one
+// workgroup per CU) times the stages of one split times the time of one stage, measured on MI355X
+// for each tile (256 x 256: 1.4 us, 128 x 256: 0.95 us, 128 x 128: 0.55 us),
+// plus a fixed launch / epilogue cost and the write and read of split-K partials.
 static GemmPlan plan_gemm_f6(int M, int N, int K)
 {
-    struct Cand { int kind, bm, bn; double eff; };
-    const Cand cands[] = {{1, 256, 256, 1.0}, {2, 128, 256, 0.85}, {3, 128, 128, 0.6}};
-    constexpr double ROUND_FIXED = 3e-6;
+    struct Cand { int kind, bm, bn; double t_stage; };
+    const Cand cands[] = {{1, 256, 256, 1.4e-6}, {2, 128, 256, 0.95e-6}, {3, 128, 128, 0.55e-6}};
     GemmPlan best{3, 128, 128, 1, K};
     double best_t = 1e30;
     for (const Cand &c : cands) {
@@ -1656,9 +1661,8 @@ static GemmPlan plan_gemm_f6(int M, int N, int K)
             if ((K + k_split - 1) / k_split != splits) continue;
             if (splits > 1 && k_split < 1024) continue;
             const double rounds = std::ceil(tiles * splits / 256.0);
-            const double t_c = rounds * (2.0 * c.bm * c.bn * k_split / (16384.0 * 2.4e9 * c.eff) +
-                                         ROUND_FIXED);
-            const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 4e12 + 3e-6 : 0.0;
+            const double t_c = rounds * (k_split / F6_KS) * c.t_stage + 4e-6;
+            const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 5e12 + 2e-6 : 0.0;
             if (t_c + t_r < best_t * 0.98) {
                 best_t = t_c + t_r;
                 best = GemmPlan{c.kind, c.bm, c.bn, splits, k_split};
