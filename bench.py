@@ -86,7 +86,8 @@ class Linear:
                      epilogue=epilogue, residual=residual, ws=self.gemm_ws)
 
     def f6_buffers(self, M):
-        """FP6 operands for the large-M GEMM: the weights once (offline), the activations per call."""
+        """FP6 operands for the large-M GEMM: the weights re-encoded once (offline); the activations
+        written in the FP6 layout by the rotate-quantize call itself."""
         torch = _torch()
         L = self.bd.lib()
         self.M6 = M
@@ -95,9 +96,16 @@ class Linear:
                               device="cuda")
         g = L.w4a4_gemm_f6_workspace_bytes(M, self.N, self.K)
         self.f6_ws = torch.empty(max(g, 256), dtype=torch.uint8, device="cuda")
+        a = L.w4a4_act_f6_workspace_bytes(M, self.K, self.B, 1 if self.table is None else 0)
+        self.act_f6_ws = torch.empty(max(a, 256), dtype=torch.uint8, device="cuda")
 
     def to_f6(self):
         self.bd.codes_to_f6(self.xq, self.K, out=self.xf)
+
+    def rq_f6(self, X, step=0):
+        self.bd.rotate_quant_act_f6(X, self.perm, self.rot, self.B, self.table,
+                                    0 if self.table is None else self.table.numel(), step,
+                                    xf=self.xf, x_scale=self.xs, ws=self.act_f6_ws)
 
     def gemm_f6(self, Y, epilogue=0, residual=None):
         self.bd.gemm_f6(self.xf, self.M6, self.xs, self.table is None, self.wf, self.N, self.w_scale,
@@ -651,12 +659,14 @@ def supplementary(bd, inputs, steps):
         Y6 = torch.empty_like(Ys[0])
 
         def step_f6():
-            lin.rq(Xs[0])
-            lin.to_f6()
+            lin.rq_f6(Xs[0])
             lin.gemm_f6(Y6)
 
         ms6 = time_graph(step_f6, steps, 5)
         f6_ms = time_kernel_calls([lambda: lin.gemm_f6(Y6)], 20)
+        rq6 = time_graph(lambda: lin.rq_f6(Xs[0]), 20, 3)
+        rq4 = time_graph(lambda: lin.rq(Xs[0]), 20, 3)
+        lin.rq(Xs[0])
         cvt_ms = time_kernel_calls([lin.to_f6], 20)
         step()
         step_f6()
@@ -666,7 +676,9 @@ def supplementary(bd, inputs, steps):
             "gemm_us": f6_ms * 1e3, "gemm_tops": ops / (f6_ms * 1e-3) / 1e12,
             "gemm_frac_int8_peak": ops / (f6_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
             "gemm_frac_fp6_peak": ops / (f6_ms * 1e-3) / 1e12 / FP6_PEAK_TOPS,
-            "activation_to_fp6_us": cvt_ms * 1e3,
+            "rotate_quant_to_fp6_us": rq6 * 1e3,
+            "rotate_quant_to_int4_us_same_run": rq4 * 1e3,
+            "separate_codes_to_fp6_us": cvt_ms * 1e3,
             "same_output_bits_as_int4_path": bool(torch.equal(Y6.view(torch.int16),
                                                               Ys[0].view(torch.int16)))}
         del lin, Xs, Ys, Y6

@@ -188,6 +188,12 @@ int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int
  *    w4a4_f6_operand_bytes(rows, K) bytes). Both pointers 16-byte aligned (W4A4_ERR_ALIGN); K not a
  *    multiple of 128 is W4A4_ERR_SHAPE. Weights are converted once, offline; activation codes after
  *    each rotate-quantize call. Bit-exact (an encoding).
+ *  - w4a4_rotate_quant_act_f6: w4a4_rotate_quant_act (same arguments, per-step or per-token scales,
+ *    same codes and x_scale) writing the codes in that layout (xf: w4a4_f6_operand_bytes(M, K)
+ *    bytes, 16-byte aligned) instead of packed int4. block must be 128 (W4A4_ERR_UNSUPPORTED), so
+ *    one rotation block is one 128-k stage; no xrot_dbg; workspace
+ *    w4a4_act_f6_workspace_bytes(M, K, block, per_token). The streaming (large-batch) kernel writes
+ *    the layout itself; other batch shapes quantize into the workspace and re-encode from there.
  *  - w4a4_gemm_f6 / w4a4_gemm_f6_i32: the arguments, scales, epilogues and outputs of w4a4_gemm /
  *    w4a4_gemm_i32 with xf / wf FP6 operands of M / N rows. K % 128 == 0 (W4A4_ERR_SHAPE),
  *    K <= 2^18 (W4A4_ERR_UNSUPPORTED), xf and wf 16-byte aligned (W4A4_ERR_ALIGN). Meant for
@@ -195,6 +201,11 @@ int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int
  * ------------------------------------------------------------------------------------------- */
 size_t w4a4_f6_operand_bytes(int rows, int K);
 int w4a4_codes_to_f6(const uint8_t *codes, int rows, int K, uint8_t *out, hipStream_t stream);
+size_t w4a4_act_f6_workspace_bytes(int M, int K, int block, int per_token);
+int w4a4_rotate_quant_act_f6(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, const float *act_scale_table,
+                             int num_steps, int step, uint8_t *xf, float *x_scale, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
 size_t w4a4_gemm_f6_workspace_bytes(int M, int N, int K);
 int w4a4_gemm_f6(const uint8_t *xf, const float *x_scale, int x_scale_per_token, const uint8_t *wf,
                  const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,

@@ -695,46 +695,43 @@ def f6_bytes(rows: int, K: int) -> int:
     return ((rows + 1) // 2 * 2) * K * 3 // 4
 
 
+def _f6_split(buf, rows: int, K: int):
+    """Views of an FP6 operand buffer: heads [stage][row][group][16], tails [stage][group][row][8]."""
+    R2 = (rows + 1) // 2 * 2
+    stage = buf.reshape(K // 128, R2 * 96)
+    return (stage[:, :R2 * 64].reshape(K // 128, R2, 4, 16),
+            stage[:, R2 * 64:].reshape(K // 128, 4, R2, 8))
+
+
 def f6_operand(q) -> np.ndarray:
     """FP6 operand bytes (uint8 [f6_bytes(rows, K)]) of int4 codes q [rows, K] (int8 values)."""
     q = np.asarray(q, np.int64)
     rows, K = q.shape
     if K % 128:
         raise ValueError("K must be a multiple of 128")
-    R2 = (rows + 1) // 2 * 2
-    lut = np.array([e3m2_encode(v) for v in range(-8, 8)], np.uint64)
+    lut = np.array([e3m2_encode(v) for v in range(-8, 8)], np.uint8)
+    codes = lut[q + 8].reshape(rows, K // 128, 4, 32)           # [row][stage][group][field]
+    bits = ((codes[..., None] >> np.arange(6)) & 1).astype(np.uint8)  # field i -> bits 6i..6i+5
+    raw = np.packbits(bits.reshape(rows, K // 128, 4, 192), axis=-1, bitorder="little")
     out = np.zeros(f6_bytes(rows, K), np.uint8)
-    stages = out.reshape(K // 128, R2 * 96)
-    for r in range(rows):
-        for sg in range(K // 32):  # sg = 4 * stage + group
-            st, g = divmod(sg, 4)
-            bits = 0
-            for i in range(32):
-                bits |= int(lut[q[r, 32 * sg + i] + 8]) << (6 * i)
-            raw = np.frombuffer(bits.to_bytes(24, "little"), np.uint8)
-            stages[st, r * 64 + 16 * g:r * 64 + 16 * g + 16] = raw[:16]
-            t0 = R2 * 64 + (g * R2 + r) * 8
-            stages[st, t0:t0 + 8] = raw[16:]
+    head, tail = _f6_split(out, rows, K)
+    head[:, :rows] = raw[..., :16].transpose(1, 0, 2, 3)
+    tail[:, :, :rows] = raw[..., 16:].transpose(1, 2, 0, 3)
     return out
 
 
 def f6_codes(buf, rows: int, K: int) -> np.ndarray:
     """Inverse of ``f6_operand``: the int4 codes [rows, K] held by an FP6 operand buffer."""
     buf = np.asarray(buf, np.uint8)
-    R2 = (rows + 1) // 2 * 2
     if buf.size != f6_bytes(rows, K):
         raise ValueError("buffer size does not match rows and K")
-    stages = buf.reshape(K // 128, R2 * 96)
-    q = np.zeros((rows, K), np.int8)
-    for r in range(rows):
-        for sg in range(K // 32):
-            st, g = divmod(sg, 4)
-            t0 = R2 * 64 + (g * R2 + r) * 8
-            bits = int.from_bytes(bytes(stages[st, r * 64 + 16 * g:r * 64 + 16 * g + 16]) +
-                                  bytes(stages[st, t0:t0 + 8]), "little")
-            for i in range(32):
-                v = e3m2_value((bits >> (6 * i)) & 63)
-                if v != int(v) or not -8 <= v <= 7:
-                    raise ValueError("not an int4 code")
-                q[r, 32 * sg + i] = int(v)
-    return q
+    head, tail = _f6_split(buf, rows, K)
+    raw = np.concatenate([head[:, :rows].transpose(1, 0, 2, 3),
+                          tail[:, :, :rows].transpose(2, 0, 1, 3)], axis=-1)  # [row][stage][group][24]
+    bits = np.unpackbits(raw, axis=-1, bitorder="little").reshape(rows, K // 128, 4, 32, 6)
+    fields = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)
+    value = np.array([e3m2_value(c) for c in range(64)])
+    v = value[fields]
+    if not np.all((v == np.round(v)) & (v >= -8) & (v <= 7)):
+        raise ValueError("not an int4 code")
+    return v.reshape(rows, K).astype(np.int8)

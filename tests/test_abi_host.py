@@ -279,3 +279,15 @@ def test_codes_to_f6_rejects_and_sizes(L):
     need = L.w4a4_gemm_f6_workspace_bytes(256, 256, 16384)
     assert need >= 2 * 256 * 256 * 4   # split K
     assert _gemm_f6(L, K=16384) == bd.W4A4_ERR_WORKSPACE
+
+
+def test_rotate_quant_act_f6_rejects(L):
+    def call(block=128, K=256, xf=FAKE, ws=FAKE, wsb=1 << 30):
+        return L.w4a4_rotate_quant_act_f6(FAKE, bd.W4A4_F16, 300, K, K, block, FAKE, FAKE, NULL, 0, 0,
+                                          xf, FAKE, ws, wsb, NULL)
+    assert call(block=64) == bd.W4A4_ERR_UNSUPPORTED
+    assert call(xf=ctypes.c_void_p(0x10008)) == bd.W4A4_ERR_ALIGN
+    assert call(xf=NULL) == bd.W4A4_ERR_ARG
+    assert call(wsb=16) == bd.W4A4_ERR_WORKSPACE
+    assert L.w4a4_act_f6_workspace_bytes(300, 256, 128, 1) >= 300 * 128 + L.w4a4_act_workspace_bytes(300, 256, 128, 1)
+    assert L.w4a4_act_f6_workspace_bytes(300, 256, 64, 1) == 0

@@ -9,6 +9,9 @@
   (all -8 against all -8 and +7) run up to K = 2^18, where 64 K = 2^24 is the largest sum.
 - w4a4_gemm_f6: the dequantization and epilogues follow the same fp32 sequence as the oracle, so
   fp16 outputs must match bit for bit (GELU within one fp16 ulp, as for the int8 path).
+- w4a4_rotate_quant_act_f6: the FP6 operand, decoded with the oracle's decoder, holds the oracle's
+  codes except for certified near-tie flips (as for the packed int4 output), the pad row is zero,
+  and a whole linear (rotate-quantize into FP6, FP6 GEMM) meets the end-to-end tolerances.
 """
 import numpy as np
 import pytest
@@ -131,3 +134,83 @@ def test_gemm_f6_row_stride_and_empty():
     assert not full[:, :50].any() and not full[:, 50 + N:].any()
     empty = bd.gemm_f6(_f6(xq[:0], K), 0, dev(sx[:0]), True, _f6(wq, K), N, dev(sw), K)
     assert tuple(empty.shape) == (0, N)
+
+
+# ---- rotate-quantize writing the FP6 operand directly
+
+def _act_inputs(M, K, B, perm_kind, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((M, K))
+    X[:, rng.choice(K, max(1, K // 100), replace=False)] *= 15.0
+    X = X.astype(np.float16)
+    W = rng.normal(0.0, 0.02, (64, K))
+    perm = (oracle.zigzag_perm(W, B) if perm_kind == "zigzag" else np.arange(K, dtype=np.int32))
+    return X, perm, oracle.block_svd(W, perm, B)
+
+
+# (M, K, mode, permutation): the streaming kernel writing the layout itself (rows already in
+# zigzag order, or after the permutation pass; odd M exercises the zero pad row), and the shapes
+# that quantize into the workspace and re-encode (few tokens, per-element gather)
+F6_ACT = {
+    "ring_step_ident_odd": (301, 1024, "per_step", "identity"),
+    "ring_token_permuted": (300, 2048, "per_token", "zigzag"),
+    "ring_token_permuted_odd": (517, 4096, "per_token", "zigzag"),
+    "ring_step_permuted": (513, 8192, "per_step", "zigzag"),
+    "few_step": (50, 1024, "per_step", "zigzag"),
+    "few_token_odd": (33, 512, "per_token", "zigzag"),
+    "gather_step": (300, 1024, "per_step", "zigzag"),
+}
+
+
+@pytest.mark.parametrize("tag", list(F6_ACT))
+def test_rotate_quant_act_f6(tag):
+    from parity_util import compare_codes, rotation_error_bound
+    M, K, mode, perm_kind = F6_ACT[tag]
+    B = 128
+    X, perm, U = _act_inputs(M, K, B, perm_kind, seed=len(tag) + M)
+    R = oracle.rotation(U, B)
+    _, _, rot = bd.pack_weights(dev(np.zeros((1, K), np.float32)), dev(perm), dev(U), B)
+    table = None
+    if mode == "per_step":
+        t0 = oracle.calibrate_table([[X]], perm, U, B)[0]
+        table = np.array([t0, t0 / 8], np.float32)
+    dperm = dev(perm) if perm_kind == "zigzag" else None
+    for step in ([0, 1] if table is not None else [0]):
+        xf, xs = bd.rotate_quant_act_f6(dev(X), dperm, rot, B, dev(table) if table is not None else None,
+                                        0 if table is None else len(table), step)
+        buf = host(xf)
+        assert buf.size == bd.lib().w4a4_f6_operand_bytes(M, K)
+        q_dev = oracle.f6_codes(buf, M, K)   # raises on a field that is not an int4 code
+        if M % 2:
+            R2 = M + 1
+            stage = buf.reshape(K // 128, R2 * 96)
+            assert not stage[:, M * 64:R2 * 64].any()
+            assert not stage[:, R2 * 64:].reshape(K // 128, 4, R2, 8)[:, :, M].any()
+        ref = oracle.rotate_quant_act(X, perm, U, B, mode, table, None, step, R=R)
+        eps = rotation_error_bound(X, perm, R, B)
+        s_dev = host(xs)
+        if mode == "per_token":
+            assert np.all(np.abs(s_dev - ref["scale"]) <= np.max(eps, axis=1) / 7 * 1.01
+                          + 2 ** -23 * ref["scale"])
+        else:
+            assert s_dev[0] == table[step]
+        flips = compare_codes(q_dev, ref["codes"], ref["v"], ref["x_rot"], eps,
+                              s_dev if mode == "per_token" else np.full(M, s_dev[0]),
+                              ref["scale"], mode == "per_token")
+        assert flips <= max(3, q_dev.size * 1e-4), flips
+
+
+def test_f6_linear_end_to_end():
+    # rotate-quantize straight into the FP6 operand, FP6 GEMM with the FP6 weights: within the
+    # end-to-end tolerances of the oracle's linear
+    from parity_util import check_y_tolerance
+    M, K, N, B = 600, 2048, 768, 128
+    X, perm, _ = _act_inputs(M, K, B, "zigzag", seed=77)
+    W = np.random.Generator(np.random.PCG64(78)).normal(0.0, 0.02, (N, K)).astype(np.float16)
+    perm = oracle.zigzag_perm(W, B)
+    U = oracle.block_svd(W, perm, B)
+    wq, sw, rot = bd.pack_weights(dev(W), dev(perm), dev(U), B)
+    xf, xs = bd.rotate_quant_act_f6(dev(X), dev(perm), rot, B)
+    Y = host(bd.gemm_f6(xf, M, xs, True, bd.codes_to_f6(wq, K), N, sw, K))
+    ref = oracle.linear(X, W, B, "per_token", perm=perm, U=U)
+    check_y_tolerance(Y, ref["Y"])

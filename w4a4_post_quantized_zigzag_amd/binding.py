@@ -47,6 +47,9 @@ SIGNATURES = {
     "w4a4_gemm_w8a8_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "w4a4_f6_operand_bytes": (_sz, [_i, _i]),
     "w4a4_codes_to_f6": (_i, [_vp, _i, _i, _vp, _vp]),
+    "w4a4_act_f6_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "w4a4_rotate_quant_act_f6": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp,
+                                      _sz, _vp]),
     "w4a4_gemm_f6_workspace_bytes": (_sz, [_i, _i, _i]),
     "w4a4_gemm_f6": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz,
                           _vp]),
@@ -274,6 +277,27 @@ def codes_to_f6(codes, K: int, out=None):
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
     check(lib().w4a4_codes_to_f6(_p(codes), rows, K, _p(out), _stream()))
     return out
+
+
+def rotate_quant_act_f6(X, perm, rot, block: int, table=None, num_steps: int = 0, step: int = 0,
+                        xf=None, x_scale=None, ws=None):
+    """Rotate-quantize with the codes written as an FP6 operand (flat uint8) instead of packed int4."""
+    torch = _torch()
+    M, K = X.shape
+    per_token = table is None
+    L = lib()
+    if xf is None:
+        xf = torch.empty(max(L.w4a4_f6_operand_bytes(M, K), 1), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M if per_token else 1, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws, nb = _ws(L.w4a4_act_f6_workspace_bytes(M, K, block, 1 if per_token else 0), X.device)
+    else:
+        nb = ws.numel()
+    check(L.w4a4_rotate_quant_act_f6(_p(X), _dtype_code(X), M, K, _row_stride(X), block, _p(perm),
+                                     _p(rot), _p(table), num_steps, step, _p(xf), _p(x_scale),
+                                     _p(ws), nb, _stream()))
+    return xf, x_scale
 
 
 def gemm_f6(xf, M: int, x_scale, per_token: bool, wf, N: int, w_scale, K: int, Y=None,

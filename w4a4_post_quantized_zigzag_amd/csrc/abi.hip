@@ -95,13 +95,22 @@ static size_t act_ws_bytes(int M, int K, int B, int kind)
     return n;
 }
 
+// xf (FP6 output, int4 codes only): the codes are written in the FP6 operand layout, by the
+// streaming kernel itself when it runs (block 128), else as packed int4 into the workspace after
+// act_ws_bytes and re-encoded from there.
 static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int B,
                           const int32_t *perm, const void *rot, const float *table, int step,
                           int kind, uint8_t *xq, float *x_scale, float *xrot, void *ws,
-                          float *calib_out, hipStream_t s, bool q8 = false, bool grouped = false)
+                          float *calib_out, hipStream_t s, bool q8 = false, bool grouped = false,
+                          uint8_t *xf = nullptr)
 {
     int rc;
     char *w = reinterpret_cast<char *>(ws);
+    uint8_t *f6_tmp = xf ? reinterpret_cast<uint8_t *>(w + act_ws_bytes(M, K, B, kind)) : nullptr;
+    if (xf) xq = f6_tmp;
+    auto finish_f6 = [&](bool direct) {
+        return (xf && !direct) ? launch_codes_to_f6(f6_tmp, M, K, xf, s) : W4A4_OK;
+    };
     uint32_t *rowmax = reinterpret_cast<uint32_t *>(w);
     const int nb = K / B;
     const int nmax = (kind == KIND_CALIB) ? max(max(M, 1), nb) : max(M, 1);
@@ -127,9 +136,15 @@ static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int
                 return rc;
             xperm = xp;
         }
-        if (kind == KIND_STEP)
-            return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
-                                            nullptr, xq, x_scale, xrot, xperm, q8, s, gstride);
+        const bool f6_direct = xf && B == 128 && !xrot && rq_ring_path(M, X, ldx, perm, xperm, K);
+        uint8_t *qout = f6_direct ? xf : xq;
+        if (kind == KIND_STEP) {
+            if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
+                                               nullptr, qout, x_scale, xrot, xperm, q8, s, gstride,
+                                               f6_direct)))
+                return rc;
+            return finish_f6(f6_direct);
+        }
         if (kind == KIND_CALIB) {
             if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0,
                                                ACT_CALIB_MAX, rowmax, nullptr, nullptr, nullptr,
@@ -140,12 +155,17 @@ static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int
         if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
                                            rowmax, nullptr, nullptr, nullptr, xperm, false, s)))
             return rc;
-        return launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
-                                        rowmax, xq, x_scale, xrot, xperm, q8, s);
+        if ((rc = launch_rotate_quant_mfma(X, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
+                                           rowmax, qout, x_scale, xrot, xperm, q8, s, 0, f6_direct)))
+            return rc;
+        return finish_f6(f6_direct);
     }
-    if (kind == KIND_STEP)
-        return launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
-                                   nullptr, xq, x_scale, xrot, q8, s);
+    if (kind == KIND_STEP) {
+        if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, table, step, ACT_PER_STEP,
+                                      nullptr, xq, x_scale, xrot, q8, s)))
+            return rc;
+        return finish_f6(false);
+    }
     if (kind == KIND_CALIB) {
         if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_CALIB_MAX,
                                       rowmax, nullptr, nullptr, nullptr, false, s)))
@@ -155,8 +175,10 @@ static int run_activation(const void *X, int xdt, int M, int K, int64_t ldx, int
     if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_MAX,
                                   rowmax, nullptr, nullptr, nullptr, false, s)))
         return rc;
-    return launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
-                               rowmax, xq, x_scale, xrot, q8, s);
+    if ((rc = launch_rotate_quant(X, xdt, M, K, ldx, B, perm, rot, nullptr, 0, ACT_TOKEN_QUANT,
+                                  rowmax, xq, x_scale, xrot, q8, s)))
+        return rc;
+    return finish_f6(false);
 }
 
 }  // namespace w4a4
@@ -324,10 +346,16 @@ size_t w4a4_act_workspace_bytes(int M, int K, int block, int per_token)
     return act_ws_bytes(M, K, block, per_token ? KIND_TOKEN : KIND_STEP);
 }
 
+static size_t act_f6_ws_bytes(int M, int K, int block, int per_token)
+{
+    return act_ws_bytes(M, K, block, per_token ? KIND_TOKEN : KIND_STEP) +
+           align_up((size_t)M * (K / 2), 256);
+}
+
 static int rq_entry(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
                     const int32_t *perm, const void *rot, const float *act_scale_table,
                     int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                    void *ws, size_t ws_bytes, hipStream_t stream, bool q8)
+                    void *ws, size_t ws_bytes, hipStream_t stream, bool q8, uint8_t *xf = nullptr)
 {
     int rc;
     if ((rc = check_kb(K, block))) return rc;
@@ -343,16 +371,26 @@ static int rq_entry(const void *X, int x_dtype, int M, int K, int64_t ldx, int b
             return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
         if (!aligned(act_scale_table, 4)) return fail(W4A4_ERR_ALIGN, "table misaligned");
     }
-    if (M > 0 && (!xq || !x_scale)) return fail(W4A4_ERR_ARG, "xq and x_scale are required");
+    if (xf) {
+        if (block != 128)
+            return fail(W4A4_ERR_UNSUPPORTED, "FP6 activation output needs block 128 (got %d)", block);
+        if (!aligned(xf, 16)) return fail(W4A4_ERR_ALIGN, "xf must be 16-byte aligned");
+        if ((int64_t)((M + 1) & ~1) * (K / 32) > INT32_MAX)
+            return fail(W4A4_ERR_UNSUPPORTED, "FP6 operand of %d x %d beyond int32 indexing", M, K);
+    } else if (M > 0 && !xq) {
+        return fail(W4A4_ERR_ARG, "xq and x_scale are required");
+    }
+    if (M > 0 && !x_scale) return fail(W4A4_ERR_ARG, "xq and x_scale are required");
     if (!aligned(x_scale, 4) || !aligned(xrot_dbg, 4))
         return fail(W4A4_ERR_ALIGN, "x_scale / xrot_dbg misaligned");
-    const size_t need = w4a4_act_workspace_bytes(M, K, block, !per_step);
+    const size_t need = xf ? (M > 0 ? act_f6_ws_bytes(M, K, block, !per_step) : 0)
+                           : w4a4_act_workspace_bytes(M, K, block, !per_step);
     if ((rc = check_ws(ws, ws_bytes, need))) return rc;
     if (M == 0) return ok();
     if (q8 && !aligned(xq, 4)) return fail(W4A4_ERR_ALIGN, "int8 xq must be 4-byte aligned");
     if ((rc = run_activation(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, step,
                              per_step ? KIND_STEP : KIND_TOKEN, xq, x_scale, xrot_dbg, ws, nullptr,
-                             stream, q8)))
+                             stream, q8, false, xf)))
         return rc;
     return ok();
 }
@@ -364,6 +402,22 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
 {
     return rq_entry(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, num_steps, step, xq,
                     x_scale, xrot_dbg, ws, ws_bytes, stream, false);
+}
+
+size_t w4a4_act_f6_workspace_bytes(int M, int K, int block, int per_token)
+{
+    if (M <= 0 || K <= 0 || block != 128 || K % block) return 0;
+    return act_f6_ws_bytes(M, K, block, per_token);
+}
+
+int w4a4_rotate_quant_act_f6(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                             const int32_t *perm, const void *rot, const float *act_scale_table,
+                             int num_steps, int step, uint8_t *xf, float *x_scale, void *ws,
+                             size_t ws_bytes, hipStream_t stream)
+{
+    if (M > 0 && !xf) return fail(W4A4_ERR_ARG, "xf is required");
+    return rq_entry(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, num_steps, step,
+                    nullptr, x_scale, nullptr, ws, ws_bytes, stream, false, xf);
 }
 
 int w4a4_rotate_quant_act_a8(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,

@@ -434,7 +434,9 @@ __device__ __forceinline__ uint32_t quant_pack4(v4f acc, float rs)
     return (t & 0xFFFu) | ((n[3] << 12) & ~0xFFFu);
 }
 
-template <int MODE, int B, bool DBG, bool Q8>
+// F6: the codes go out in the FP6 operand layout of the FP6 GEMM instead of packed int4 (B = 128,
+// so a rotation block is one 128-k stage of that layout: xq is the operand, stage b its block b).
+template <int MODE, int B, bool DBG, bool Q8, bool F6 = false>
 __global__ __launch_bounds__(256) void k_rq_ring(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const _Float16 *__restrict__ rhi,
     const _Float16 *__restrict__ rlo, const float *__restrict__ table, int step,
@@ -612,6 +614,23 @@ __global__ __launch_bounds__(256) void k_rq_ring(
                     for (int off = 32; off > 0; off >>= 1) u = fmaxf(u, __shfl_xor(u, off));
                     if (tid == 0) atomicMax(&rowmax[b * gstride], __float_as_uint(u));
                 }
+            }
+        } else if (F6) {
+            // thread -> (tile row, 32-k group): 16-byte head at row * 64 + 16 g of the stage block,
+            // 8-byte tail at R2 * 64 + (g * R2 + row) * 8; with M odd the tile holding row M (the
+            // last row group's last tile) writes that pad row as zeros
+            static_assert(!F6 || (B == 128 && !Q8), "FP6 output: one 128-k stage per block, int4 codes");
+            const int R2 = (M + 1) & ~1;
+            uint8_t *blk = xq + (int64_t)b * R2 * 96;
+            for (int e = tid; e < MT * 4; e += 256) {
+                const int row = e >> 2, g = e & 3, m = m0 + row;
+                const bool live = m < row_end;
+                if (!live && !(m == M && (M & 1))) continue;
+                uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+                if (live) f6_encode_group(*reinterpret_cast<const uint4 *>(&sq[row * OB + 16 * g]), w);
+                *reinterpret_cast<uint4 *>(blk + (int64_t)m * 64 + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint2 *>(blk + (int64_t)R2 * 64 + ((int64_t)g * R2 + m) * 8) =
+                    make_uint2(w[4], w[5]);
             }
         } else {
             // codes of the tile: 16-byte stores (OB / 16 chunks per row)
@@ -1046,12 +1065,25 @@ static int rq_rows_per_wg(int M, int nb)
     return ((mt + rg - 1) / rg) * MT;
 }
 
+bool rq_ring_path(int M, const void *X, int64_t ldx, const int32_t *perm, const uint16_t *xperm,
+                  int K)
+{
+    if (M <= RQ_SMALL_M && !xperm) return false;
+    const uint16_t *src = xperm ? xperm : reinterpret_cast<const uint16_t *>(X);
+    const int64_t ld = xperm ? K : ldx;
+    const bool rows_aligned = ((uintptr_t)src % 16 == 0) && (ld % 8 == 0);
+    return rows_aligned && (xperm || !perm);
+}
+
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                             const uint16_t *xperm, bool q8, hipStream_t s, int gstride)
+                             const uint16_t *xperm, bool q8, hipStream_t s, int gstride, bool f6)
 {
     if (M == 0) return W4A4_OK;
+    if (f6 && (!rq_ring_path(M, X, ldx, perm, xperm, K) || B != 128 || q8 || xrot_dbg ||
+               (uintptr_t)xq % 16 != 0 || (mode != ACT_PER_STEP && mode != ACT_TOKEN_QUANT)))
+        return fail(W4A4_ERR_UNSUPPORTED, "FP6 activation output needs the streaming kernel");
     RotLayout L = rot_layout(K, B);
     const char *base = reinterpret_cast<const char *>(rot);
     const _Float16 *rhi = reinterpret_cast<const _Float16 *>(base + L.r32);
@@ -1095,25 +1127,32 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         const int groups = (M + rpw_r - 1) / rpw_r;
         dim3 grid_r(groups * nb);
         const size_t lds = (size_t)RQ_STAGES * MT * B * sizeof(uint16_t);
-#define W4A4_RING(MODEV, BV, DV, QV)                                                               \
+#define W4A4_RING_K(MODEV, BV, DV, QV, FV)                                                         \
     do {                                                                                           \
         static bool attr_set = false;                                                              \
         if (!attr_set) {                                                                           \
-            hipError_t e = hipFuncSetAttribute((const void *)k_rq_ring<MODEV, BV, DV, QV>,         \
+            hipError_t e = hipFuncSetAttribute((const void *)k_rq_ring<MODEV, BV, DV, QV, FV>,     \
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
             if (e != hipSuccess)                                                                   \
                 return fail(W4A4_ERR_HIP, "rotate-quantize LDS request: %s", hipGetErrorString(e)); \
             attr_set = true;                                                                       \
         }                                                                                          \
-        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV>), grid_r, dim3(256), lds, s, src, ld, M,  \
-                           K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r, groups, \
-                           gstride);                                                               \
+        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV, FV>), grid_r, dim3(256), lds, s, src, ld, \
+                           M, K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r,      \
+                           groups, gstride);                                                       \
     } while (0)
+#define W4A4_RING(MODEV, BV, DV, QV) W4A4_RING_K(MODEV, BV, DV, QV, false)
+#define W4A4_RING_F6(MODEV) W4A4_RING_K(MODEV, 128, false, false, true)
 #define W4A4_RING_B(MODEV, DV, QV)                                                                 \
     if (B == 128) W4A4_RING(MODEV, 128, DV, QV); else W4A4_RING(MODEV, 64, DV, QV);
 #define W4A4_RING_Q(MODEV)                                                                         \
     if (xrot_dbg) { if (q8) { W4A4_RING_B(MODEV, true, true) } else { W4A4_RING_B(MODEV, true, false) } } \
     else { if (q8) { W4A4_RING_B(MODEV, false, true) } else { W4A4_RING_B(MODEV, false, false) } }
+        if (f6) {
+            if (mode == ACT_PER_STEP) W4A4_RING_F6(ACT_PER_STEP);
+            else W4A4_RING_F6(ACT_TOKEN_QUANT);
+            return check_launch("rotate-quantize (ring, FP6 output)");
+        }
         switch (mode) {
         case ACT_PER_STEP: W4A4_RING_Q(ACT_PER_STEP) break;
         case ACT_TOKEN_MAX: W4A4_RING_B(ACT_TOKEN_MAX, false, false) break;
@@ -1122,7 +1161,9 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         }
 #undef W4A4_RING_Q
 #undef W4A4_RING_B
+#undef W4A4_RING_F6
 #undef W4A4_RING
+#undef W4A4_RING_K
         return check_launch("rotate-quantize (ring)");
     }
 #define W4A4_RQ(MODEV, BV, GV, QV)                                                                 \

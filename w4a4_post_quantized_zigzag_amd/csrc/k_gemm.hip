@@ -1079,17 +1079,6 @@ constexpr int F6_MAX_K = 1 << 18;  // 64 * 2^18 = 2^24: every partial sum is exa
 
 __host__ __device__ inline int f6_rows2(int rows) { return (rows + 1) & ~1; }
 
-// E3M2 code of a two's-complement nibble: |v| as fp32 gives the exponent (bias 127 -> 3) and the two
-// leading mantissa bits; zero stays zero.
-__device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t nib)
-{
-    const int v = (int)((nib ^ 8u) & 15u) - 8;
-    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
-    const uint32_t f = __float_as_uint((float)a);
-    const uint32_t mag = a ? ((((f >> 23) - 124u) << 2) | ((f >> 21) & 3u)) : 0u;
-    return mag | (v < 0 ? 0x20u : 0u);
-}
-
 // One thread per (32-k group, row, 128-k stage), groups fastest: the four threads of a row read
 // its 64 packed bytes of the stage and write its 64 head bytes (consecutive rows are contiguous
 // in the stage block), each also one 8-byte tail (consecutive rows of a group are contiguous);
@@ -1104,17 +1093,8 @@ __global__ __launch_bounds__(256) void k_codes_to_f6(const uint8_t *__restrict__
     const int row = (int)((t >> 2) % R2);
     const int st = (int)((t >> 2) / R2);
     uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-    if (row < rows) {
-        const uint4 p = *reinterpret_cast<const uint4 *>(q + (int64_t)row * (K / 2) + 64 * st + 16 * g);
-        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const uint32_t c = e3m2_of_nibble(pw[i / 8] >> (4 * (i % 8)));
-            const int bit = 6 * i;
-            w[bit / 32] |= c << (bit % 32);
-            if (bit % 32 > 26) w[bit / 32 + 1] |= c >> (32 - bit % 32);
-        }
-    }
+    if (row < rows)
+        f6_encode_group(*reinterpret_cast<const uint4 *>(q + (int64_t)row * (K / 2) + 64 * st + 16 * g), w);
     uint8_t *blk = out + (int64_t)st * R2 * 96;
     *reinterpret_cast<uint4 *>(blk + (int64_t)row * 64 + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint2 *>(blk + (int64_t)R2 * 64 + ((int64_t)g * R2 + row) * 8) =

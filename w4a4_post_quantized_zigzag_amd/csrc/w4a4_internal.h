@@ -30,6 +30,33 @@ __device__ __forceinline__ double load_as_f64(const void *p, int dtype, int64_t 
     return (double)load_as_f32(p, dtype, idx);
 }
 
+// FP6 operand encoding (see the FP6 GEMM in k_gemm.hip): E3M2 code of a two's-complement nibble --
+// |v| as fp32 gives the exponent (bias 127 -> 3) and the two leading mantissa bits; zero stays zero.
+__device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t nib)
+{
+    const int v = (int)((nib ^ 8u) & 15u) - 8;
+    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+    const uint32_t f = __float_as_uint((float)a);
+    const uint32_t mag = a ? ((((f >> 23) - 124u) << 2) | ((f >> 21) & 3u)) : 0u;
+    return mag | (v < 0 ? 0x20u : 0u);
+}
+
+// 16 packed bytes (32 int4 codes, low nibble first) -> the 192-bit string of their E3M2 fields,
+// code i at bits 6i..6i+5: w[0..3] is the group's head, w[4..5] its tail.
+__device__ __forceinline__ void f6_encode_group(const uint4 p, uint32_t (&w)[6])
+{
+    const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int d = 0; d < 6; ++d) w[d] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t c = e3m2_of_nibble(pw[i / 8] >> (4 * (i % 8)));
+        const int bit = 6 * i;
+        w[bit / 32] |= c << (bit % 32);
+        if (bit % 32 > 26) w[bit / 32 + 1] |= c >> (32 - bit % 32);
+    }
+}
+
 // Natural-order Sylvester Hadamard sign: (-1)^popcount(l & j).
 __device__ __forceinline__ bool hadamard_negative(int l, int j) { return __popc(l & j) & 1; }
 
@@ -112,10 +139,16 @@ size_t hadamard_lds_bytes(int M, int K, int B, int x_dtype, int *rows_per_wg);
 int launch_rotate_quant_hadamard(const void *X, int x_dtype, int M, int K, int64_t ldx, int B,
                                  const int32_t *perm, const float *table, int step, uint8_t *xq,
                                  float *x_scale, float *xrot_dbg, hipStream_t s);
+// f6: xq is an FP6 operand (the layout of launch_gemm_f6) written by the streaming kernel (B = 128,
+// int4 codes, per-step or per-token quantize pass); only where rq_ring_path holds.
 int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, const int32_t *perm,
                              const void *rot, const float *table, int step, ActMode mode,
                              uint32_t *rowmax, uint8_t *xq, float *x_scale, float *xrot_dbg,
-                             const uint16_t *xperm, bool q8, hipStream_t s, int gstride = 0);
+                             const uint16_t *xperm, bool q8, hipStream_t s, int gstride = 0,
+                             bool f6 = false);
+// whether launch_rotate_quant_mfma takes the streaming (LDS-ring) kernel for these rows
+bool rq_ring_path(int M, const void *X, int64_t ldx, const int32_t *perm, const uint16_t *xperm,
+                  int K);
 
 // GEMM (k_gemm.hip)
 struct GemmEpilogue {
