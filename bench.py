@@ -664,8 +664,8 @@ def supplementary(bd, inputs, steps):
 
         ms6 = time_graph(step_f6, steps, 5)
         f6_ms = time_kernel_calls([lambda: lin.gemm_f6(Y6)], 20)
-        rq6 = time_graph(lambda: lin.rq_f6(Xs[0]), 20, 3)
-        rq4 = time_graph(lambda: lin.rq(Xs[0]), 20, 3)
+        rq6 = time_kernel_calls([lambda: lin.rq_f6(Xs[0])], 20)
+        rq4 = time_kernel_calls([lambda: lin.rq(Xs[0])], 20)
         lin.rq(Xs[0])
         cvt_ms = time_kernel_calls([lin.to_f6], 20)
         step()

@@ -30,15 +30,23 @@ __device__ __forceinline__ double load_as_f64(const void *p, int dtype, int64_t 
     return (double)load_as_f32(p, dtype, idx);
 }
 
-// FP6 operand encoding (see the FP6 GEMM in k_gemm.hip): E3M2 code of a two's-complement nibble --
-// |v| as fp32 gives the exponent (bias 127 -> 3) and the two leading mantissa bits; zero stays zero.
-__device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t nib)
+// FP6 operand encoding (see the FP6 GEMM in k_gemm.hip).
+// E3M2 codes of four two's-complement nibbles held one per byte (values 0..15): two byte lookups
+// with v_perm_b32 (nibbles 0..7 -> codes of 0..7, nibbles 8..15 -> codes of -8..-1) blended on bit 3.
+__device__ __forceinline__ uint32_t e3m2_of_nibble_bytes(uint32_t nb)
 {
-    const int v = (int)((nib ^ 8u) & 15u) - 8;
-    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
-    const uint32_t f = __float_as_uint((float)a);
-    const uint32_t mag = a ? ((((f >> 23) - 124u) << 2) | ((f >> 21) & 3u)) : 0u;
-    return mag | (v < 0 ? 0x20u : 0u);
+    const uint32_t sel = nb & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(0x17161514u, 0x12100C00u, sel);  // 0x00 0x0C 0x10 0x12 0x14..0x17
+    const uint32_t neg = __builtin_amdgcn_perm(0x2C303234u, 0x35363738u, sel);  // 0x38 0x37 0x36 0x35 0x34 0x32 0x30 0x2C
+    const uint32_t b = (nb >> 3) & 0x01010101u;
+    const uint32_t m = (b << 6) - b;  // 0x3F in the bytes of negative nibbles
+    return (neg & m) | (pos & ~m);
+}
+
+// Four 6-bit values held one per byte -> one 24-bit run, byte i at bits 6i..6i+5.
+__device__ __forceinline__ uint32_t pack6x4(uint32_t x)
+{
+    return (x & 0x3Fu) | ((x >> 2) & 0xFC0u) | ((x >> 4) & 0x3F000u) | ((x >> 6) & 0xFC0000u);
 }
 
 // 16 packed bytes (32 int4 codes, low nibble first) -> the 192-bit string of their E3M2 fields,
@@ -46,15 +54,21 @@ __device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t nib)
 __device__ __forceinline__ void f6_encode_group(const uint4 p, uint32_t (&w)[6])
 {
     const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+    uint32_t c[8];  // 24-bit runs of k = 4j .. 4j+3
 #pragma unroll
-    for (int d = 0; d < 6; ++d) w[d] = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const uint32_t c = e3m2_of_nibble(pw[i / 8] >> (4 * (i % 8)));
-        const int bit = 6 * i;
-        w[bit / 32] |= c << (bit % 32);
-        if (bit % 32 > 26) w[bit / 32 + 1] |= c >> (32 - bit % 32);
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = e3m2_of_nibble_bytes(pw[d] & 0x0F0F0F0Fu);          // k = 8d + 0, 2, 4, 6
+        const uint32_t hi = e3m2_of_nibble_bytes((pw[d] >> 4) & 0x0F0F0F0Fu);   // k = 8d + 1, 3, 5, 7
+        c[2 * d] = pack6x4(__builtin_amdgcn_perm(hi, lo, 0x05010400u));        // k = 8d .. 8d+3
+        c[2 * d + 1] = pack6x4(__builtin_amdgcn_perm(hi, lo, 0x07030602u));    // k = 8d+4 .. 8d+7
     }
+    // run j starts at bit 24 j
+    w[0] = c[0] | (c[1] << 24);
+    w[1] = (c[1] >> 8) | (c[2] << 16);
+    w[2] = (c[2] >> 16) | (c[3] << 8);
+    w[3] = c[4] | (c[5] << 24);
+    w[4] = (c[5] >> 8) | (c[6] << 16);
+    w[5] = (c[6] >> 16) | (c[7] << 8);
 }
 
 // Natural-order Sylvester Hadamard sign: (-1)^popcount(l & j).
