@@ -2,7 +2,8 @@
  * w4a4.h -- C ABI of libw4a4.so, an MI355X (gfx950) implementation of the W4A4 quantized linear of
  * Omega-QVLA: zigzag channel permutation, blockwise composite SVD.Hadamard rotation, symmetric int4
  * activations (per-denoising-step table scale or dynamic per-token scale), int4 RTN weights with a
- * per-output-channel scale, integer GEMM on int8 MFMA, fp16 output.
+ * per-output-channel scale, integer GEMM on int8 MFMA (for large batches also on FP6 MFMA, with the
+ * codes re-encoded exactly as E3M2 floats), fp16 output.
  *
  * Passages the calls follow (pages cited by title and section):
  *  - gist.science (pt/fr) summary of arXiv 2605.28803, "Metodologia" / "Methodologie", item 1: the SVD
