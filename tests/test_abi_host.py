@@ -291,3 +291,10 @@ def test_rotate_quant_act_f6_rejects(L):
     assert call(wsb=16) == bd.W4A4_ERR_WORKSPACE
     assert L.w4a4_act_f6_workspace_bytes(300, 256, 128, 1) >= 300 * 128 + L.w4a4_act_workspace_bytes(300, 256, 128, 1)
     assert L.w4a4_act_f6_workspace_bytes(300, 256, 64, 1) == 0
+
+
+def test_f6_empty_batches_are_valid(L):
+    assert L.w4a4_rotate_quant_act_f6(FAKE, bd.W4A4_F16, 0, 256, 256, 128, FAKE, FAKE, NULL, 0, 0,
+                                      NULL, NULL, NULL, 0, NULL) == bd.W4A4_OK
+    assert L.w4a4_gemm_f6(NULL, NULL, 1, FAKE, FAKE, 0, 64, 256, NULL, 64, 0, NULL, 0, NULL, 0,
+                          NULL) == bd.W4A4_OK
