@@ -110,3 +110,26 @@ def test_calibration_paths(M, K, B, perm_kind):
                                       B))[0]
     eps = np.max(rotation_error_bound(X, perm, oracle.rotation(U, B), B))
     assert abs(got - want) <= eps / 7 * 1.01 + 2 ** -23 * want
+
+
+def test_permute_pass_lds_grows():
+    # the permutation pass stages a whole row in LDS: after a call with short rows, a call whose
+    # rows take 80 KB must still launch (the kernel's LDS limit is raised when a launch needs more);
+    # per-token quantization is row-local, so sampled rows are compared with the oracle
+    from parity_util import compare_codes, rotation_error_bound
+    B, M = 128, 260
+    for K in (2048, 40960):
+        X, perm, U = _inputs(M, K, B, "zigzag", seed=K)
+        R = oracle.rotation(U, B)
+        _, _, rot = bd.pack_weights(dev(np.zeros((1, K), np.float32)), dev(perm), dev(U), B)
+        xq, xs = bd.rotate_quant_act(dev(X), dev(perm), rot, B)
+        rows = np.array([0, 1, 2, 129, M - 1])
+        ref = oracle.rotate_quant_act(X[rows], perm, U, B, "per_token", R=R)
+        eps = rotation_error_bound(X[rows], perm, R, B)
+        q_dev = oracle.unpack_int4(host(xq)[rows], K)
+        s_dev = host(xs)[rows]
+        assert np.all(np.abs(s_dev - ref["scale"]) <= np.max(eps, axis=1) / 7 * 1.01
+                      + 2 ** -23 * ref["scale"])
+        flips = compare_codes(q_dev, ref["codes"], ref["v"], ref["x_rot"], eps, s_dev,
+                              ref["scale"], True)
+        assert flips <= max(3, q_dev.size * 1e-4), flips

@@ -3,6 +3,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "w4a4_internal.h"
 
@@ -23,6 +26,22 @@ int check_launch(const char *what)
 {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(W4A4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return W4A4_OK;
+}
+
+int ensure_dynamic_lds(const void *kernel, size_t bytes, const char *what)
+{
+    static std::mutex mu;
+    static std::map<std::pair<const void *, int>, size_t> granted;  // (kernel, device) -> bytes
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4A4_ERR_HIP, "%s LDS request: %s", what, hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(mu);
+    size_t &have = granted[{kernel, dev}];
+    if (have >= bytes) return W4A4_OK;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return fail(W4A4_ERR_HIP, "%s LDS request: %s", what, hipGetErrorString(e));
+    have = bytes;
     return W4A4_OK;
 }
 

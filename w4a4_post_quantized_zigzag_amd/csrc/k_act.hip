@@ -978,15 +978,9 @@ int launch_rotate_quant_hadamard(const void *X, int x_dtype, int M, int K, int64
     const bool per_step = table != nullptr;
 #define W4A4_HD_LAUNCH(MODEV, BV, XTV, DV)                                                         \
     do {                                                                                           \
-        static bool attr_set = false;                                                              \
-        if (lds > 64 * 1024 && !attr_set) {                                                        \
-            hipError_t e = hipFuncSetAttribute((const void *)k_rq_hadamard<MODEV, BV, XTV, DV>,    \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,         \
-                                               HD_MAX_LDS);                                        \
-            if (e != hipSuccess)                                                                   \
-                return fail(W4A4_ERR_HIP, "Hadamard rotate LDS request: %s", hipGetErrorString(e)); \
-            attr_set = true;                                                                       \
-        }                                                                                          \
+        const int lrc = ensure_dynamic_lds((const void *)k_rq_hadamard<MODEV, BV, XTV, DV>, lds,   \
+                                           "Hadamard rotate");                                     \
+        if (lrc != W4A4_OK) return lrc;                                                            \
         hipLaunchKernelGGL((k_rq_hadamard<MODEV, BV, XTV, DV>), grid, dim3(256), lds, s,           \
                            reinterpret_cast<const XTV *>(X), ldx, M, K, rpw, vec, hinv, perm,      \
                            table, step, xq, x_scale, xrot_dbg);                                    \
@@ -1129,14 +1123,9 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         const size_t lds = (size_t)RQ_STAGES * MT * B * sizeof(uint16_t);
 #define W4A4_RING_K(MODEV, BV, DV, QV, FV)                                                         \
     do {                                                                                           \
-        static bool attr_set = false;                                                              \
-        if (!attr_set) {                                                                           \
-            hipError_t e = hipFuncSetAttribute((const void *)k_rq_ring<MODEV, BV, DV, QV, FV>,     \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-            if (e != hipSuccess)                                                                   \
-                return fail(W4A4_ERR_HIP, "rotate-quantize LDS request: %s", hipGetErrorString(e)); \
-            attr_set = true;                                                                       \
-        }                                                                                          \
+        const int lrc = ensure_dynamic_lds((const void *)k_rq_ring<MODEV, BV, DV, QV, FV>, lds,    \
+                                           "rotate-quantize");                                     \
+        if (lrc != W4A4_OK) return lrc;                                                            \
         hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV, FV>), grid_r, dim3(256), lds, s, src, ld, \
                            M, K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r,      \
                            groups, gstride);                                                       \
@@ -1194,10 +1183,7 @@ int launch_permute_rows(const void *X, int M, int K, int64_t ldx, const int32_t 
     const bool vec = (K % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
                      ((uintptr_t)perm % 16 == 0);
     const void *fn = vec ? (const void *)k_permute_rows<true> : (const void *)k_permute_rows<false>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return fail(W4A4_ERR_HIP, "permute LDS request: %s", hipGetErrorString(e));
-    }
+    if (int rc = ensure_dynamic_lds(fn, lds, "permute")) return rc;
     const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
     if (vec)
         hipLaunchKernelGGL(k_permute_rows<true>, dim3(M), dim3(256), lds, s, x, ldx, K, perm, xp,

@@ -289,11 +289,7 @@ int launch_block_svd(const void *W, int wdt, int N, int K, int64_t ldw, int B, c
     int rc = check_launch("gram");
     if (rc != W4A4_OK) return rc;
     const size_t lds = (size_t)B * B * sizeof(double);
-    if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_jacobi,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return fail(W4A4_ERR_HIP, "jacobi LDS request: %s", hipGetErrorString(e));
-    }
+    if ((rc = ensure_dynamic_lds((const void *)k_jacobi, lds, "jacobi"))) return rc;
     hipLaunchKernelGGL(k_jacobi, dim3(nb), dim3(256), lds, s, partial, nchunks, B, V, U);
     return check_launch("jacobi");
 }

@@ -1419,12 +1419,7 @@ static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
 {
     const size_t lds = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
     const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>;
-    static bool attr_set = false;  // once per process and instantiation
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return fail(W4A4_ERR_HIP, "gemm LDS request: %s", hipGetErrorString(e));
-        attr_set = true;
-    }
+    if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>), grid,
                        dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
     return W4A4_OK;
@@ -1665,12 +1660,7 @@ static int launch_f6_e(dim3 grid, hipStream_t s, const uint8_t *xf, const uint8_
 {
     const size_t lds = (size_t)NS * (BM + BN) * 96;
     const void *fn = (const void *)k_gemm_f6<BM, BN, WM, WN, NS, PE, VO>;
-    static bool attr_set = false;  // once per process and instantiation
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return fail(W4A4_ERR_HIP, "fp6 gemm LDS request: %s", hipGetErrorString(e));
-        attr_set = true;
-    }
+    if (int rc = ensure_dynamic_lds(fn, lds, "fp6 gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_f6<BM, BN, WM, WN, NS, PE, VO>), grid, dim3(64 * WM * WN), lds, s,
                        xf, wf, M, N, K, k_split, tm, tn, epi, partial);
     return W4A4_OK;

@@ -242,14 +242,8 @@ int launch_gptq_sweep(const double *Wr, int N, int K, const double *Hf, const ui
     const size_t lds = 2 * (size_t)K * sizeof(double);
 #define W4A4_SWEEP(SL, RW)                                                                         \
     do {                                                                                           \
-        static bool attr_set = false;                                                              \
-        if (!attr_set) {                                                                           \
-            hipError_t e = hipFuncSetAttribute((const void *)k_gptq_sweep<SL, RW>,                 \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,         \
-                                               (int)(2 * GPTQ_MAX_K * sizeof(double)));            \
-            if (e != hipSuccess) return fail(W4A4_ERR_HIP, "gptq LDS request: %s", hipGetErrorString(e)); \
-            attr_set = true;                                                                       \
-        }                                                                                          \
+        const int lrc = ensure_dynamic_lds((const void *)k_gptq_sweep<SL, RW>, lds, "gptq sweep"); \
+        if (lrc != W4A4_OK) return lrc;                                                            \
         hipLaunchKernelGGL((k_gptq_sweep<SL, RW>), dim3((N + RW - 1) / RW), dim3(64 * RW), lds, s, \
                            Wr, N, K, Hf, dead, rowmax, codes, w_scale);                            \
     } while (0)

@@ -14,6 +14,9 @@ namespace w4a4 {
 // ---- host-side status handling ---------------------------------------------------------------
 int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int check_launch(const char *what);  // W4A4_OK, or W4A4_ERR_HIP with the HIP error text
+// Allows `kernel` at least `bytes` of dynamic LDS on the current device: the limit is raised once
+// per (kernel, device) and again only when a launch needs more (thread-safe).
+int ensure_dynamic_lds(const void *kernel, size_t bytes, const char *what);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
