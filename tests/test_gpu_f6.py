@@ -214,3 +214,31 @@ def test_f6_linear_end_to_end():
     Y = host(bd.gemm_f6(xf, M, xs, True, bd.codes_to_f6(wq, K), N, sw, K))
     ref = oracle.linear(X, W, B, "per_token", perm=perm, U=U)
     check_y_tolerance(Y, ref["Y"])
+
+
+@pytest.mark.parametrize("M,mode", [(300, "per_step"), (300, "per_token"), (1, "per_token")])
+def test_rotate_quant_act_f6_strided_and_single_row(M, mode):
+    # rows 4 halves longer than K (no 16-byte tile loads: the element gather and the re-encoding
+    # fallback) and a one-token batch; codes against the oracle as above
+    from parity_util import compare_codes, rotation_error_bound
+    torch = __import__("torch")
+    K, B = 512, 128
+    X, perm, U = _act_inputs(M, K, B, "zigzag", seed=M + 11)
+    R = oracle.rotation(U, B)
+    _, _, rot = bd.pack_weights(dev(np.zeros((1, K), np.float32)), dev(perm), dev(U), B)
+    wide = np.zeros((M, K + 4), np.float16)
+    wide[:, :K] = X
+    xd = torch.from_numpy(wide).cuda()[:, :K]
+    table = None
+    if mode == "per_step":
+        table = np.array([oracle.calibrate_table([[X]], perm, U, B)[0]], np.float32)
+    xf, xs = bd.rotate_quant_act_f6(xd, dev(perm), rot, B, dev(table) if table is not None else None,
+                                    0 if table is None else 1, 0)
+    q_dev = oracle.f6_codes(host(xf), M, K)
+    ref = oracle.rotate_quant_act(X, perm, U, B, mode, table, None, 0, R=R)
+    eps = rotation_error_bound(X, perm, R, B)
+    s_dev = host(xs)
+    flips = compare_codes(q_dev, ref["codes"], ref["v"], ref["x_rot"], eps,
+                          s_dev if mode == "per_token" else np.full(M, s_dev[0]), ref["scale"],
+                          mode == "per_token")
+    assert flips <= max(3, q_dev.size * 1e-4), flips
