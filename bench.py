@@ -543,6 +543,7 @@ def cold_hbm(bd, inputs):
     last-level cache has been flushed by the others.
     - small-M GEMM sweep, M in {16, 50, 64} with N = K = 16384 (128 MB of packed weights per copy),
       where the weight stream is long enough for its bandwidth to be measurable;
+    - the prefill GEMM (1024 x 16384 x 2048) with int4 and FP6 operands, cycling weight copies;
     - rotate-quantize of the prefill and long-K workloads (per-token, zigzag order), cycling copies
       of X (4 MB and 32 MB)."""
     torch = _torch()
@@ -569,6 +570,40 @@ def cold_hbm(bd, inputs):
                                     "frac_hbm": gbps / HBM_PEAK_GBPS,
                                     "tops": 2.0 * M * N * K / (ms * 1e-3) / 1e12})
     del wqs
+    torch.cuda.empty_cache()
+    # large-M GEMM (prefill shape) with cold weights, int4 and FP6 operands: the weight bytes per
+    # launch are 16 MB and 24 MB, a small part of the operand traffic of a compute-bound tile loop
+    M, N, K = 1024, 16384, 2048
+    xq = torch.randint(0, 256, (M, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+    xs = torch.full((M,), 1e-3, device="cuda")
+    w_scale = torch.rand(N, generator=g, device="cuda") * 1e-2
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    L = bd.lib()
+    gws = torch.empty(max(256, L.w4a4_gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(max(256, L.w4a4_gemm_f6_workspace_bytes(M, N, K)), dtype=torch.uint8,
+                      device="cuda")
+    xf = bd.codes_to_f6(xq, K)
+    res = {"M": M, "N": N, "K": K}
+    ops = 2.0 * M * N * K
+    for fmt, wbytes in (("int4", N * K // 2), ("fp6", L.w4a4_f6_operand_bytes(N, K))):
+        copies = max(2, COLD_BYTES // wbytes)
+        ws_ = []
+        for _ in range(copies):
+            w = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+            ws_.append(w if fmt == "int4" else bd.codes_to_f6(w, K))
+        if fmt == "int4":
+            calls = [lambda w=w: bd.gemm(xq, xs, True, w, w_scale, K, Y=Y, ws=gws) for w in ws_]
+        else:
+            calls = [lambda w=w: bd.gemm_f6(xf, M, xs, True, w, N, w_scale, K, Y=Y, ws=fws)
+                     for w in ws_]
+        ms = time_kernel_calls(calls, 4)
+        res[fmt] = {"weight_copies": copies, "gemm_us": ms * 1e3,
+                    "tops": ops / (ms * 1e-3) / 1e12,
+                    "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+        del ws_, calls
+        torch.cuda.empty_cache()
+    out["large_m_gemm_prefill"] = res
+    del xq, xf, Y, gws, fws
     torch.cuda.empty_cache()
     for name in ("prefill_proj", "longk_down"):
         d = inputs.linear_inputs(name, M=1)  # weights only; X copies are drawn on the device
