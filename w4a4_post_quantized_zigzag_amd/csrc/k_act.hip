@@ -686,24 +686,38 @@ __global__ __launch_bounds__(256) void k_rq_small(
     const int r = lane & 15, g = lane >> 4;
     const int jbase = wave * JW;
 
-    // gather: thread -> input column tid % B of the block, rows tid / B + RSTEP * i (clamped)
+    // gather: thread -> input column tid % B of the block, rows tid / B + RSTEP * i (clamped).
+    // Issue order: the permutation entry, then the R_b fragments (independent of it), then the
+    // gathers that need it -- loads retire in order, so the wait for the entry does not also wait
+    // for the fragments, and their latency overlaps the entry's.
+    // The entry is loaded unconditionally (from any readable word, here the rotation operand, when
+    // the identity is meant) and the identity is selected only where the address is formed:
+    // consuming the loaded value right away, as a branch's join would, waits for it at once.
     const int gc = tid % B, gr0 = tid / B;
-    const int64_t src_col = perm ? (int64_t)perm[b * B + gc] : (int64_t)b * B + gc;
-    uint16_t xv[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int m = min(m0 + gr0 + RSTEP * i, M - 1);
-        xv[i] = X[(int64_t)m * ldx + src_col];
-    }
+    const int32_t *pidx = perm ? perm + (b * B + gc) : reinterpret_cast<const int32_t *>(rhi);
+    const int praw = *pidx;
+    __builtin_amdgcn_sched_barrier(0);
     v8h ahi[JF][KK], alo[JF][KK];
 #pragma unroll
     for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const int64_t off = rot16_fragment(b, jbase / 16 + jf, kk, lane, B);
-            ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off) * (_Float16)(1 << ROT_LO_SHIFT);
+            ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off);
             alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
         }
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t src_col = perm ? (int64_t)praw : (int64_t)(b * B + gc);
+    uint16_t xv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int m = min(m0 + gr0 + RSTEP * i, M - 1);
+        xv[i] = X[(int64_t)m * ldx + src_col];
+    }
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ahi[jf][kk] = ahi[jf][kk] * (_Float16)(1 << ROT_LO_SHIFT);
     float rs = 0.0f;
     if (MODE == ACT_PER_STEP) {
         const float s = step_scale(table, step + b * gstride);
