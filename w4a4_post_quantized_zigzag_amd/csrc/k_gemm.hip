@@ -164,22 +164,23 @@ __global__ __launch_bounds__(256) void k_gemm_smallm(const uint8_t *__restrict__
     const int per_wave = (windows + 3) / 4;
     const int w_begin = wave * per_wave, w_end = min(windows, w_begin + per_wave);
 
-    // Epilogue operands are fetched first, so their latency hides under the operand loads. The
-    // epilogue thread owns column n0 + (tid % 16) and rows tid / 16 + 16 f.
+    // Epilogue operands are fetched first, so their latency hides under the operand loads (with
+    // unconditional loads on selected addresses, as in the wide kernel). The epilogue thread owns
+    // column n0 + (tid % 16) and rows tid / 16 + 16 f.
     const int ecol = threadIdx.x & 15, erow = threadIdx.x >> 4;
+    const int en = min(n0 + ecol, N - 1);
     const bool scaled = epi.mode != GEMM_OUT_I32;
-    float e_sw = 0.0f, e_sx[MF];
+    const bool has_res = epi.mode == W4A4_EPI_RESIDUAL;
+    const float *stand_in = reinterpret_cast<const float *>(wq);
+    const float e_sw = *(scaled ? epi.w_scale + en : stand_in);
+    float e_sx[MF];
     uint16_t e_res[MF];
-    if (scaled) {
-        e_sw = epi.w_scale[min(n0 + ecol, N - 1)];
 #pragma unroll
-        for (int f = 0; f < MF; ++f) {
-            const int m = min(erow + 16 * f, M - 1);
-            e_sx[f] = epi.x_scale_per_token ? epi.x_scale[m] : epi.x_scale[0];
-            e_res[f] = (epi.mode == W4A4_EPI_RESIDUAL)
-                           ? epi.residual[(int64_t)m * epi.ldr + min(n0 + ecol, N - 1)]
-                           : (uint16_t)0;
-        }
+    for (int f = 0; f < MF; ++f) {
+        const int m = min(erow + 16 * f, M - 1);
+        e_sx[f] = *(scaled ? epi.x_scale + (epi.x_scale_per_token ? m : 0) : stand_in);
+        e_res[f] = *(has_res ? epi.residual + (int64_t)m * epi.ldr + en
+                             : reinterpret_cast<const uint16_t *>(wq));
     }
 
     v4i total[MF];
@@ -300,21 +301,23 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_smallm_wide(const uint8_t *__r
     __syncthreads();
 
     // Epilogue operands first: this thread owns column n0 + tid % NC and rows tid / NC + RS j.
+    // The loads are unconditional, on selected addresses (a word of the packed weights stands in
+    // for an operand the mode does not have; its value is never used): a load inside a branch on
+    // the mode would be waited for at the branch's join, before the first operand load issues.
     const int ecol = threadIdx.x % NC, erow = threadIdx.x / NC;
     const int en = min(n0 + ecol, N - 1);
     const bool scaled = epi.mode != GEMM_OUT_I32;
-    float e_sw = 0.0f, e_sx[ER];
+    const bool has_res = epi.mode == W4A4_EPI_RESIDUAL;
+    const float *stand_in = reinterpret_cast<const float *>(wq);
+    const float e_sw = *(scaled ? epi.w_scale + en : stand_in);
+    float e_sx[ER];
     uint16_t e_res[ER];
-    if (scaled) {
-        e_sw = epi.w_scale[en];
-        const float sx0 = epi.x_scale_per_token ? 0.0f : epi.x_scale[0];
 #pragma unroll
-        for (int j = 0; j < ER; ++j) {
-            const int m = min(erow + RS * j, M - 1);
-            e_sx[j] = epi.x_scale_per_token ? epi.x_scale[m] : sx0;
-            e_res[j] = (epi.mode == W4A4_EPI_RESIDUAL) ? epi.residual[(int64_t)m * epi.ldr + en]
-                                                       : (uint16_t)0;
-        }
+    for (int j = 0; j < ER; ++j) {
+        const int m = min(erow + RS * j, M - 1);
+        e_sx[j] = *(scaled ? epi.x_scale + (epi.x_scale_per_token ? m : 0) : stand_in);
+        e_res[j] = *(has_res ? epi.residual + (int64_t)m * epi.ldr + en
+                             : reinterpret_cast<const uint16_t *>(wq));
     }
 
     const uint8_t *wrow[NF], *xrow[MF];
@@ -632,12 +635,12 @@ __global__ __launch_bounds__(256) void k_gemm_smallm_g(const uint8_t *__restrict
     const int ecol = tid & 15, erow = tid >> 4;
     const int en = min(n0 + ecol, N - 1);
     const float e_sw = epi.w_scale[en];
+    const bool has_res = epi.mode == W4A4_EPI_RESIDUAL;
     uint16_t e_res[MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f)
-        e_res[f] = (epi.mode == W4A4_EPI_RESIDUAL)
-                       ? epi.residual[(int64_t)min(erow + 16 * f, M - 1) * epi.ldr + en]
-                       : (uint16_t)0;
+    for (int f = 0; f < MF; ++f)  // unconditional load on a selected address (see the wide kernel)
+        e_res[f] = *(has_res ? epi.residual + (int64_t)min(erow + 16 * f, M - 1) * epi.ldr + en
+                             : reinterpret_cast<const uint16_t *>(wq));
     float y[MF];
 #pragma unroll
     for (int f = 0; f < MF; ++f) y[f] = 0.0f;
