@@ -1,16 +1,21 @@
 """Benchmark of the W4A4 quantized linear on one MI355X.
 
-Default workload: the DiT-action-head MLP up-projection (X fp16 [50, 1024] per denoising step,
-W fp16 [4096, 1024], block-128 rotation, per-step act_scale_table, 8 denoising steps run in order).
-One bench step = the whole runtime path for one batch: for each of the 8 denoising steps, the
-rotate-quantize call (zigzag gather, block rotation, step scale, int4 pack) and the W4A4 GEMM
-(int8 MFMA, fused dequantization, fp16 store). The offline side (device zigzag, block SVD, weight
-rotate + RTN pack, table calibration) runs once before timing and is reported separately.
+Default workload (the headline): the full synthetic DiT action-head stack -- 16 layers x 8
+denoising steps, M = 1600 tokens (32 episodes x 50 action tokens), hidden 1024, ffn 4096; per layer
+QKV 1024->3072, O 1024->1024 on the V slice (attention is the identity) with a residual, up
+1024->4096 with erf-GELU, down 4096->1024 with a residual; every linear W4A4 with block-128
+composite rotation and its own per-step act_scale_table. One bench step = one pass over all 8
+denoising steps: 512 rotate-quantize calls (zigzag gather, block rotation, step scale, int4 pack)
+and 512 W4A4 GEMMs (int8 MFMA, fused dequantization and epilogue, fp16 store). The offline side
+(device zigzag, block SVD, weight rotate + RTN pack, table calibration) runs once before timing
+and is reported separately.
 
-Timing: inputs and packed weights are resident in HBM; W warmup steps, then K steps replayed from a
-HIP graph of one step, bracketed by synchronizations, timed with HIP events on the launch stream.
-The dominant kernel's average duration is measured separately with HIP events around each of its
-launches on the same stream. Prints one JSON line.
+Timing: inputs, packed weights and tables are resident in HBM; W warmup steps, then K steps replayed
+from a HIP graph of one pass, bracketed by synchronizations, timed with HIP events on the launch
+stream. value = integer operations of the 512 GEMMs (2 M N K each) per second. The dominant
+kernel's average launch duration is measured with HIP events on the same stream (a graph of
+back-to-back launches of that kernel with the stack's own buffers). Prints one JSON line.
+Other workloads: --workload dit_mlp_up | linear_small (few-token per-step linears).
 """
 from __future__ import annotations
 
@@ -454,14 +459,180 @@ def cpu_oracle_stages(inputs, rows=16, cols=1024):
     return out
 
 
+STACK_LINEAR_SHAPES = (("qkv", "N=3072, K=1024"), ("o", "N=1024, K=1024"), ("up", "N=4096, K=1024"),
+                       ("down", "N=1024, K=4096"))
+
+
+def stack_kernel_times(bd, ds, Xs, reps=30):
+    """Average launch duration (ms) of each linear's rotate-quantize and GEMM call in the stack, on
+    the stack's own buffers (layer 0, step 0), each from a HIP graph of back-to-back launches timed
+    with HIP events on the launch stream."""
+    bufs = ds.bufs(Xs[0].shape[0])
+    lay = ds.layers[0]
+    h = ds.h
+    wiring = {"qkv": (Xs[0], bufs.qkv, bd.EPI_NONE, None, False),
+              "o": (bufs.qkv[:, 2 * h:3 * h], bufs.h2, bd.EPI_RESIDUAL, Xs[0], ds.fold),
+              "up": (bufs.h2, bufs.g, bd.EPI_GELU, None, False),
+              "down": (bufs.g, bufs.hs[0], bd.EPI_RESIDUAL, bufs.h2, ds.fold)}
+    out = {}
+    for name, (X, Y, epi, res, in_order) in wiring.items():
+        lin = lay[name]
+        perm = None if in_order else lin.perm
+        xq = bufs.xq[(lin.K, 4)]
+
+        def rq(X=X, lin=lin, perm=perm, xq=xq):
+            bd.rotate_quant_act(X, perm, lin.rot, ds.block, lin.table, ds.steps, 0, xq=xq,
+                                x_scale=bufs.xs, ws=bufs.ws[lin.K])
+
+        def gm(lin=lin, xq=xq, Y=Y, epi=epi, res=res):
+            bd.gemm(xq, bufs.xs, False, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
+                    residual=res, ws=bufs.gws[(lin.N, lin.K, 4)])
+
+        rq()
+        gm()
+        out[name] = {"N": lin.N, "K": lin.K, "rotate_quant_ms": time_kernel_calls([rq], reps),
+                     "gemm_ms": time_kernel_calls([gm], reps)}
+    return out
+
+
+def cpu_baseline_stack(inputs, M=1600):
+    """The oracle (single-threaded C, fp64) on one layer-step of the stack: the four linears of
+    layer 0 at step 0 on all M tokens (rotate-quantize, integer GEMM, dequantization with the
+    layer's epilogues), chained as in the stack. Weights are packed and the per-step scales set
+    before the clock starts. Returns the integer ops per second (one layer-step is 1/128 of a pass,
+    so the rate is that of a pass) and a description of the sample."""
+    import oracle
+    from oracle.reference import EPI_GELU, EPI_NONE, EPI_RESIDUAL
+    S = inputs.STACK
+    B, h = S["block"], S["hidden"]
+    lw = inputs.stack_weights(layers=1)[0]
+    X = inputs.stack_activations(M=M, steps=1, calib=0)["X_steps"][0]
+    lin = {}
+    for nm in ("qkv", "o", "up", "down"):
+        W = lw[nm]
+        perm = oracle.zigzag_perm(W, B)
+        U = oracle.block_svd(W, perm, B)
+        lin[nm] = {"perm": perm, "U": U, "pack": oracle.pack_weights(W, perm, U, B)}
+
+    def run(name, Xin, epi, res, table):
+        L = lin[name]
+        act = oracle.rotate_quant_act(Xin, L["perm"], L["U"], B, "per_step", table, 1, 0,
+                                      R=L["pack"]["R"])
+        return oracle.gemm(act["codes"], act["scale"], False, L["pack"]["codes"],
+                           L["pack"]["w_scale"], epi, res)["Y"]
+
+    # per-step scales: the absmax of each linear's rotated input on the first 16 tokens (an untimed
+    # dry run of the chain; the values do not change the work)
+    tables = {}
+
+    def linear(name, xin, epi, res):
+        if name not in tables:
+            L = lin[name]
+            tables[name] = oracle.calibrate_table([[xin]], L["perm"], L["U"], B, R=L["pack"]["R"])
+        return run(name, xin, epi, res, tables[name])
+
+    def chain(x):
+        qkv = linear("qkv", x, EPI_NONE, None)
+        h2 = linear("o", np.ascontiguousarray(qkv[:, 2 * h:3 * h]), EPI_RESIDUAL, x)
+        g = linear("up", h2, EPI_GELU, None)
+        return linear("down", g, EPI_RESIDUAL, h2)
+
+    chain(X[:16])
+    t0 = time.perf_counter()
+    chain(X)
+    el = time.perf_counter() - t0
+    ops = 2.0 * M * (3 * h * h + h * h + S["ffn"] * h + h * S["ffn"])
+    return ops / el, el, (f"one layer-step of the same stack (QKV, O, up, down of layer 0 at step 0, "
+                          f"all {M} tokens, rotate-quantize + integer GEMM + dequantization); the "
+                          f"pass is 128 such layer-steps, so the rate is extrapolated x128 "
+                          f"({el:.1f} s measured for the layer-step)")
+
+
+def stack_headline(bd, inputs, args, result):
+    torch = _torch()
+    info, ds, Xs, _, step = setup_stack(bd, inputs)
+    M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]
+    if args.profile_timed_only:
+        _roctx(True)
+    ms = time_graph(step, args.steps, args.warmup)
+    if args.profile_timed_only:
+        _roctx(False)
+    ops = T * L * 2.0 * M * (3 * h * h + h * h + f * h + h * f)
+    kt = stack_kernel_times(bd, ds, Xs)
+    calls = T * L  # launches of each linear's kernels per pass
+    # the dominant kernel: the largest total time per pass among the eight per-linear kernels
+    totals = {}
+    for name, d in kt.items():
+        totals[(name, "gemm")] = d["gemm_ms"] * calls
+        totals[(name, "rotate_quant")] = d["rotate_quant_ms"] * calls
+    (dn, dk) = max(totals, key=totals.get)
+    d = kt[dn]
+    if dk == "gemm":
+        op = 2.0 * M * d["N"] * d["K"]
+        ach = op / (d["gemm_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": f"{dn} GEMM ({M}x{d['N']}x{d['K']}, int8 MFMA)",
+                "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                "frac": ach / INT8_PEAK_TOPS,
+                "traffic": traffic_from_profile("k_gemm.hip", f"action_stack_{dn}_gemm"),
+                "algorithmic_ops_per_launch": op, "avg_launch_us": d["gemm_ms"] * 1e3}
+    else:
+        by = rq_bytes(M, d["K"], ds.block, 2, False)
+        ach = by / (d["rotate_quant_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": f"{dn} rotate-quantize ({M}x{d['K']})", "achieved": ach,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                "traffic": traffic_from_profile("k_act.hip", f"action_stack_{dn}_rq"),
+                "algorithmic_bytes_per_launch": by, "avg_launch_us": d["rotate_quant_ms"] * 1e3}
+    kernels = {}
+    for name, d in kt.items():
+        op = 2.0 * M * d["N"] * d["K"]
+        by = rq_bytes(M, d["K"], ds.block, 2, False)
+        kernels[name] = {"gemm_us": d["gemm_ms"] * 1e3,
+                         "gemm_tops": op / (d["gemm_ms"] * 1e-3) / 1e12,
+                         "gemm_frac_int8_peak": op / (d["gemm_ms"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                         "rotate_quant_us": d["rotate_quant_ms"] * 1e3,
+                         "rotate_quant_gbps": by / (d["rotate_quant_ms"] * 1e-3) / 1e9,
+                         "rotate_quant_frac_hbm": by / (d["rotate_quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    result.update(
+        value=ops / (ms * 1e-3) / 1e12, ms_per_step=ms,
+        config={"workload": f"action_stack: {L} layers x {T} denoising steps, M = {M} tokens "
+                            f"(32 episodes x 50), hidden {h}, ffn {f}; per layer QKV, O (+residual), "
+                            f"up (+erf-GELU), down (+residual), all W4A4, block {ds.block}, "
+                            f"per-linear per-step act_scale_tables",
+                "M": M, "hidden": h, "ffn": f, "layers": L, "denoising_steps": T,
+                "block": ds.block, "linear_calls_per_step": 4 * L * T, "scale_mode": "per_step"},
+        roofline=roof, kernels=kernels,
+        frac_int8_peak_whole_pass=ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+        offline={"device_zigzag_svd_pack_s": info["offline_s"],
+                 "device_table_calibration_s": info["calib_s"]})
+    if not args.no_cpu_baseline:
+        v, el, sample = cpu_baseline_stack(inputs, M)
+        result["cpu_baseline"] = {"value": v / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+                                  "sample": sample, "host": host_cpu()}
+    del ds, Xs, step
+    torch.cuda.empty_cache()
+
+
+_ROCTX = None
+
+
+def _roctx(resume: bool):
+    """Bracket the timed region for `rocprofv3 --selected-regions` (no effect without it)."""
+    global _ROCTX
+    import ctypes
+    if _ROCTX is None:
+        _ROCTX = ctypes.CDLL("/opt/rocm/lib/librocprofiler-sdk-roctx.so")
+    (_ROCTX.roctxProfilerResume if resume else _ROCTX.roctxProfilerPause)(0)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dit_mlp_up",
-                    choices=["dit_mlp_up", "linear_small", "prefill_proj", "longk_down",
-                             "action_stack"])
+    ap.add_argument("--workload", default="action_stack",
+                    choices=["action_stack", "dit_mlp_up", "linear_small"])
+    ap.add_argument("--profile-timed-only", action="store_true",
+                    help="mark the timed region for rocprofv3 --selected-regions")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-supplementary", action="store_true")
     ap.add_argument("--supp-steps", type=int, default=30)
@@ -491,7 +662,9 @@ def main():
                       "random-init weights)"}
 
     name = args.workload
-    if name in ("dit_mlp_up", "linear_small"):
+    if name == "action_stack":
+        stack_headline(bd, inputs, args, result)
+    elif name in ("dit_mlp_up", "linear_small"):
         d, lin, Xs, Ys, step = setup_per_step_linear(name, bd, inputs)
         M, K, N, B, T = d["M"], d["K"], d["N"], d["block"], d["steps"]
         ms = time_graph(step, args.steps, args.warmup)
@@ -523,9 +696,6 @@ def main():
             v, sample, _ = cpu_baseline_per_step(d)
             result["cpu_baseline"] = {"value": v / 1e12, "unit": "TOPS", "cores": 1,
                                       "kind": "oracle", "sample": sample, "host": host_cpu()}
-    else:
-        raise SystemExit("use --workload dit_mlp_up or linear_small for the headline line; other "
-                         "workloads are reported under 'supplementary'")
 
     if not args.no_supplementary:
         result["supplementary"] = supplementary(bd, inputs, args.supp_steps)
@@ -668,8 +838,33 @@ def square_gemm(bd, n):
     return res
 
 
+def few_token_line(bd, inputs, name, steps):
+    """The few-token per-step linear (the DiT MLP up-projection, X fp16 [50, 1024] x 8 denoising
+    steps, W [4096, 1024]): one step = the 8 denoising steps in order; plus each kernel's average
+    launch duration."""
+    d, lin, Xs, Ys, step = setup_per_step_linear(name, bd, inputs)
+    M, K, N, B, T = d["M"], d["K"], d["N"], d["block"], d["steps"]
+    ms = time_graph(step, steps, 10)
+    gemm_ms = time_kernel_calls([lambda t=t: lin.gemm(Ys[t]) for t in range(T)], 50)
+    lin.rq(Xs[0], 0)
+    rq_ms = time_kernel_calls([lambda t=t: lin.rq(Xs[t], t) for t in range(T)], 50)
+    gb = gemm_bytes(M, N, K, False)
+    xb = 2 if d["xdtype"] == np.float16 else 4
+    return {"M": M, "K": K, "N": N, "block": B, "denoising_steps": T, "ms_per_step": ms,
+            "tops": T * 2.0 * M * N * K / (ms * 1e-3) / 1e12,
+            "gemm_us": gemm_ms * 1e3, "gemm_gbps": gb / (gemm_ms * 1e-3) / 1e9,
+            "gemm_frac_hbm": gb / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "rotate_quant_us": rq_ms * 1e3,
+            "rotate_quant_gbps": rq_bytes(M, K, B, xb, False) / (rq_ms * 1e-3) / 1e9,
+            "traffic_gemm_bytes_per_launch": traffic_from_profile("k_gemm.hip", name),
+            "note": "single launches of 2.5 MB (GEMM) and 0.1 MB (rotate-quantize) are bound by "
+                    "launch and two dependent load latencies, not by HBM bandwidth"}
+
+
 def supplementary(bd, inputs, steps):
-    """Shorter runs of the other workloads (large-M per-token linears and the 16-layer stack)."""
+    """Shorter runs of the other workloads: the few-token DiT linear, the large-M per-token
+    linears (int4 and FP6 operands), a square GEMM, cold-HBM sweeps, group-wise scales, the GPTQ
+    pack and the mixed W4A4/W8A8 stack."""
     torch = _torch()
     out = {}
     for name in ("prefill_proj", "longk_down"):
@@ -722,7 +917,8 @@ def supplementary(bd, inputs, steps):
     out["cold_hbm"] = cold_hbm(bd, inputs)
     out["group_wise_scales"] = grouped_scales(bd, inputs, max(20, steps))
     out["gptq_offline_pack"] = gptq_offline(bd, inputs)
-    for name, w8 in (("action_stack", ()), ("action_stack_mixed", ("o", "down"))):
+    out["dit_mlp_up"] = few_token_line(bd, inputs, "dit_mlp_up", max(50, steps))
+    for name, w8 in (("action_stack_mixed", ("o", "down")),):
         info, lins, Xs, rb, step = setup_stack(bd, inputs, w8=w8)
         ms = time_graph(step, max(3, steps // 5), 2)
         M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]

@@ -126,8 +126,10 @@ int w4a4_pack_weights(const void *W, int w_dtype, int N, int K, int64_t ldw, int
  * on the device in fp32, activation scale, int4 quantization and packing.
  *  - Per-step mode (act_scale_table != NULL) [vnrobo.com "Y tuong paper"]: s = table[step] for every
  *    row; step must lie in [0, num_steps) (else W4A4_ERR_STEP_RANGE) and the table must hold at
- *    least num_steps device floats. x_scale[0] receives s. Entries must be positive and finite; the
- *    kernel quantizes with 1.0f where one is not, instead of producing NaN codes.
+ *    least num_steps device floats. x_scale[0] receives s. Only a positive finite entry is a
+ *    scale: for any other entry (zero, negative, infinite, NaN -- an uncalibrated or damaged table)
+ *    every code is 0 and x_scale[0] receives NaN, so every output of the GEMM that consumes them is
+ *    NaN (the device cannot report the table's contents through the return value without a wait).
  *  - Per-token mode (act_scale_table == NULL) [FoldQuantVLA key change 2]: s_m = fp32(max_k |x'_mk|
  *    / 7) (1.0f for a zero row); x_scale[m] receives s_m for m in [0, M). num_steps/step ignored.
  *  Codes: r = fp32(1/s), q = clamp(rint(fp32(x' * r)), -8, 7), packed into xq [M][K/2].
@@ -258,7 +260,8 @@ int w4a4_gemm_w8a8_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K
  *  - Rotate-quantize: act_scale_table is [num_steps][K/128] device floats; position k of step
  *    `step` is quantized with s = table[step][k / 128] (r = fp32(1/s), q = clamp(rint(fp32(x' *
  *    r)), -8, 7)); x_scale[g] receives the K/128 scales used. Step range and entry rules as in the
- *    per-step mode. Workspace: w4a4_act_workspace_bytes(M, K, block, 0).
+ *    per-step mode, block by block (an unusable entry zeroes that block's codes and its x_scale[g]
+ *    is NaN). Workspace: w4a4_act_workspace_bytes(M, K, block, 0).
  *  - GEMM: acc_g[m][n] = sum over k in block g of q p (exact), y = 0 then y = fmaf(float(acc_g),
  *    x_scales[g], y) for g = 0, 1, ... in order (one correctly rounded fused multiply-add per
  *    block), then Y = fp16(fp32(y * w_scale[n])) with the epilogues of w4a4_gemm. xq and wq must

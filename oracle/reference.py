@@ -156,7 +156,9 @@ def block_svd(W, perm, B: int, return_fp64: bool = False):
     sig = np.zeros((nb, B), np.float64)
     for b in range(nb):
         Wb = W64[:, perm[b * B:(b + 1) * B]]
-        _, s, Vt = np.linalg.svd(Wb, full_matrices=True)
+        # the thin decomposition already holds all B right singular vectors when N >= B; the full
+        # one (an N x N left factor) is needed only to complete the basis when N < B
+        _, s, Vt = np.linalg.svd(Wb, full_matrices=N < B)
         V = Vt.T.copy()
         idx = np.argmax(np.abs(V), axis=0)
         sgn = np.where(V[idx, np.arange(B)] < 0, -1.0, 1.0)
@@ -289,8 +291,6 @@ def quantize_act(Xr, mode: str, table=None, num_steps: int | None = None, step: 
         if step is None or not (0 <= step < num_steps):
             raise ValueError(f"step {step} outside [0, {num_steps})")
         s = float(table[step])
-        if not (s > 0 and np.isfinite(s)):
-            raise ValueError("act_scale_table entry must be positive and finite")
         imode, ts = 0, s
     elif mode == "per_token":
         imode, ts = 1, 1.0
@@ -306,8 +306,20 @@ def quantize_act(Xr, mode: str, table=None, num_steps: int | None = None, step: 
     else:
         _load().orc_act_quant_q(_ptr(Xr, _dp), M, K, imode, ts, _qmax(bits), _ptr(x32, _fp),
                                 _ptr(v, _fp), _ptr(q, _i8p), _ptr(sc, _fp))
+    if mode == "per_step" and not _usable_scale(ts):
+        # an entry that is not a positive finite number is no scale: no code is produced (all 0)
+        # and the NaN scale carries into every dequantized output
+        v[:] = 0.0
+        q[:] = 0
+        sc[:] = np.float32(np.nan)
     xq = pack_codes(q, bits) if (bits == 8 or K % 2 == 0) else None
     return {"x32": x32, "v": v, "codes": q, "scale": sc, "xq": xq}
+
+
+def _usable_scale(s) -> bool:
+    """A table entry is a scale only if it is a positive finite fp32 number."""
+    s = np.float32(s)
+    return bool(s > 0 and np.isfinite(s))
 
 
 def rotate_quant_act(X, perm, U, B: int, mode: str, table=None, num_steps=None, step=None, R=None,
@@ -431,13 +443,18 @@ def quantize_act_grouped(Xr, B: int, table, num_steps=None, step=None) -> dict:
     if step is None or not (0 <= step < num_steps):
         raise ValueError(f"step {step} outside [0, {num_steps})")
     sg = np.ascontiguousarray(table[step])
-    if not np.all((sg > 0) & np.isfinite(sg)):
-        raise ValueError("act_scale_table entries must be positive and finite")
+    bad = ~((sg > 0) & np.isfinite(sg))
     x32 = np.empty((M, K), np.float32)
     v = np.empty((M, K), np.float32)
     q = np.empty((M, K), np.int8)
-    _load().orc_act_quant_grouped(_ptr(Xr, _dp), M, K, B, _ptr(sg, _fp), _ptr(x32, _fp),
-                                  _ptr(v, _fp), _ptr(q, _i8p))
+    _load().orc_act_quant_grouped(_ptr(Xr, _dp), M, K, B, _ptr(np.where(bad, np.float32(1), sg), _fp),
+                                  _ptr(x32, _fp), _ptr(v, _fp), _ptr(q, _i8p))
+    if bad.any():
+        # blocks whose entry is no scale (see quantize_act): codes 0 and a NaN scale
+        for g in np.nonzero(bad)[0]:
+            v[:, g * B:(g + 1) * B] = 0.0
+            q[:, g * B:(g + 1) * B] = 0
+        sg = np.where(bad, np.float32(np.nan), sg).astype(np.float32)
     xq = pack_int4(q) if K % 2 == 0 else None
     return {"x32": x32, "v": v, "codes": q, "scale": sg.copy(), "xq": xq}
 

@@ -67,6 +67,16 @@ def rotation_error_bound(X, perm, R, B, mfma_split: bool = True) -> np.ndarray:
     return 2.0 * rel * A + 2.0 * U32
 
 
+def propagated_difference(dX, perm, R, B) -> np.ndarray:
+    """Bound on how far a difference dX of the inputs moves the rotated values: |dX[:, perm]| . |R_b|
+    block by block (exact propagation through the rotation, in absolute value)."""
+    Xp = np.abs(np.asarray(dX, np.float64)[:, np.asarray(perm)])
+    out = np.empty_like(Xp)
+    for b in range(Xp.shape[1] // B):
+        out[:, b * B:(b + 1) * B] = Xp[:, b * B:(b + 1) * B] @ np.abs(R[b])
+    return out
+
+
 def compare_codes(q_dev, q_orc, v_orc, x_orc, eps, scale_dev, scale_orc, per_token: bool):
     """Codes agree, or differ by one where the oracle's value v = x32 * r sits within tau of the
     boundary between the two codes. tau covers the rotation error (eps * r) and, per token, the

@@ -148,6 +148,15 @@ def test_gemm_split_k_workspace_is_required(L):
     assert _gemm(L, M=1024, N=2048, K=16384, ldy=2048, ws=FAKE, wsb=need - 1) == bd.W4A4_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("M,K", [(130, (1 << 20) + 128), (130, 1 << 21), (65, 1 << 24)])
+def test_gemm_beyond_one_int32_split_plans_k_pieces(L, M, K):
+    # more than 2^16 k per tile accumulator: the plan cuts K into pieces of at most 2^16 k, whose
+    # exact int32 partials need a workspace of at least ceil(K / 2^16) partial tiles
+    need = L.w4a4_gemm_workspace_bytes(M, 64, K)
+    assert need >= -(-K // (1 << 16)) * M * 64 * 4
+    assert _gemm(L, M=M, N=64, K=K, ldy=64) == bd.W4A4_ERR_WORKSPACE
+
+
 def test_pack_and_calibration_reject(L):
     ws = L.w4a4_pack_workspace_bytes(256, 256, 64)
     assert ws >= 256 * 64 * 8

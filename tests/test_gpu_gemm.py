@@ -94,6 +94,28 @@ def test_gemm_i32_long_k(M, N, K):
     assert np.array_equal(acc, ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(130, 40, (1 << 20) + 128), (70, 24, 1 << 21)])
+def test_gemm_long_k_beyond_one_split(M, N, K):
+    # more than 2^16 k per tile accumulator: K is cut into pieces with exact int32 partials; every
+    # row is written (rows beyond 64 were once left unwritten) -- sampled outputs plus the dequant
+    xq, wq = _operands(M, N, K, seed=17)
+    acc = host(bd.gemm_i32(dev(xq), dev(wq), K)).astype(np.int64)
+    rows = np.array([0, 63, 64, 65, M - 1])
+    q = oracle.unpack_int4(xq[rows], K)
+    p = oracle.unpack_int4(wq, K)
+    ref = oracle.int_gemm(q, p)
+    assert np.array_equal(acc[rows], ref)
+    sx = inputs.random_scales(M, seed=1)
+    sw = inputs.random_scales(N, seed=2, lo=1e-5, hi=1e-4)
+    Y = host(bd.gemm(dev(xq), dev(sx), True, dev(wq), dev(sw), K))
+    want, _ = oracle.dequant(ref, sx[rows], True, sw)
+    assert np.array_equal(Y[rows].view(np.uint16), want.view(np.uint16))
+    # the all -8 closed form on every row
+    neg = inputs.constant_packed(M, K, 0x88)
+    a = host(bd.gemm_i32(dev(neg), dev(neg[:N]), K))
+    assert np.all(a == 64 * K)
+
+
 @pytest.mark.parametrize("K", [64, 2048, 16384, 1 << 20])
 def test_gemm_i32_extremes(K):
     neg = inputs.constant_packed(70, K, 0x88)   # all codes -8

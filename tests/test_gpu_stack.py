@@ -37,7 +37,7 @@ def test_stack_reduced_end_to_end():
         oracle.stack_run(layers, A["X_steps"][t], B, "per_step", tables, T, t, outputs=outs_o)
         ds.run(dev(A["X_steps"][t]), t, outputs=outs_d)
         assert len(outs_o) == len(outs_d) == 4 * L
-        for yd, yo in zip(outs_d, outs_o):
+        for (yd, _, _), yo in zip(outs_d, outs_o):
             check_y_tolerance(host(yd), yo)
 
 
@@ -103,7 +103,7 @@ def test_stack_mixed_w8a8():
         outs_o, outs_d = [], []
         oracle.stack_run(layers, A["X_steps"][t], B, "per_step", tables, T, t, outputs=outs_o)
         ds.run(dev(A["X_steps"][t]), t, outputs=outs_d)
-        for yd, yo in zip(outs_d, outs_o):
+        for (yd, _, _), yo in zip(outs_d, outs_o):
             check_y_tolerance(host(yd), yo)
     # device calibration of the mixed stack records max/127 for the int8 linears
     ds2 = DeviceStack(W, B, T, calib=_device_calib(layers), w8=w8)
@@ -127,6 +127,6 @@ def test_folded_permutations_change_nothing():
         ds.set_tables(tables)
         o = []
         ds.run(dev(A["X_steps"][0]), 0, outputs=o)
-        outs.append([host(y) for y in o])
+        outs.append([host(y) for y, _, _ in o])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

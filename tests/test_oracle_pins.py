@@ -253,6 +253,27 @@ def test_per_step_selects_scale_and_rejects_bad_step():
         oracle.quantize_act(X, "per_step", table[:5], 8, 2)
 
 
+@pytest.mark.parametrize("bad", [0.0, -1.0, np.inf, -np.inf, np.nan])
+def test_per_step_unusable_entry_poisons_output(bad):
+    # an entry that is not a positive finite scale produces no code (all 0) and a NaN scale, so the
+    # dequantized output is NaN everywhere: a wrong or truncated table is a failure mode
+    # (aiexpert.news) and must not look like a valid result; the neighbouring entries are unaffected
+    table = np.array([0.25, bad, 0.5], np.float32)
+    X = _rng(13).normal(0, 3, (6, 32))
+    out = oracle.quantize_act(X, "per_step", table, 3, 1)
+    assert not out["codes"].any() and np.all(np.isnan(out["scale"]))
+    p = _rng(14).integers(-8, 8, (5, 32)).astype(np.int8)
+    y = oracle.gemm(out["codes"], out["scale"][:1], False, p, np.full(5, 0.1, np.float32))["Y"]
+    assert np.all(np.isnan(y.astype(np.float32)))
+    ok = oracle.quantize_act(X, "per_step", table, 3, 2)
+    x32 = X.astype(np.float32).astype(np.float64)
+    assert np.array_equal(ok["codes"], np.clip(np.rint(x32 * 2.0), -8, 7))
+    og = oracle.quantize_act_grouped(X, 16, np.array([[0.5, bad]], np.float32), 1, 0)
+    assert np.isnan(og["scale"][1]) and og["scale"][0] == np.float32(0.5)
+    assert not og["codes"][:, 16:].any()
+    assert np.array_equal(og["codes"][:, :16], np.clip(np.rint(x32[:, :16] * 2.0), -8, 7))
+
+
 def test_rne_ties_at_half_steps():
     # exact half-steps round to the even code
     X = np.array([[0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 6.5, -7.5]])

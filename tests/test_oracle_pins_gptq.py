@@ -102,3 +102,47 @@ def test_gptq_lowers_the_calibration_error():
     assert err(g) < 0.8 * err(r)
     # the Hessian is the rotated activations' Gram matrix
     assert np.allclose(oracle.gptq_hessian(X, perm, U, B), Xr.T @ Xr)
+
+
+def test_hessian_hand_worked():
+    # three calibration rows, K = 4, block 2 with U = I (R_b = H_2 = [[1, 1], [1, -1]] / sqrt 2), so
+    # X' = A / sqrt 2 with A written out by hand and H = A^T A / 2 (integers halved):
+    #   row (1, 0, 2, 0) -> (1, 1, 2, 2);  row (0, 1, 0, 3) -> (1, -1, 3, -3);
+    #   row (1, 1, 1, 1) -> (2, 0, 2, 0)
+    X = np.array([[1, 0, 2, 0], [0, 1, 0, 3], [1, 1, 1, 1]], np.float32)
+    U = np.broadcast_to(np.eye(2, dtype=np.float32), (2, 2, 2)).copy()
+    want = 0.5 * np.array([[6, 0, 9, -1], [0, 2, -1, 5], [9, -1, 17, -5], [-1, 5, -5, 13]], float)
+    H = oracle.gptq_hessian([X], np.arange(4, dtype=np.int32), U, 2)
+    assert np.max(np.abs(H - want)) < 1e-12
+    # two samples accumulate
+    H2 = oracle.gptq_hessian([X[:2], X[2:]], np.arange(4, dtype=np.int32), U, 2)
+    assert np.max(np.abs(H2 - want)) < 1e-12
+    # the permutation is applied before the rotation: perm = [2, 0, 3, 1] gathers the columns
+    # (x2, x0, x3, x1), i.e. rows (2, 1, 0, 0), (0, 0, 3, 1), (1, 1, 1, 1), so
+    # A = [[3, 1, 0, 0], [0, 0, 4, 2], [2, 0, 2, 0]] and H = A^T A / 2
+    perm = np.array([2, 0, 3, 1], np.int32)
+    Ap = np.array([[3, 1, 0, 0], [0, 0, 4, 2], [2, 0, 2, 0]], float)
+    Hp = oracle.gptq_hessian([X], perm, U, 2)
+    assert np.max(np.abs(Hp - Ap.T @ Ap / 2)) < 1e-12
+    # a mis-permuted Hessian is a different matrix
+    assert np.max(np.abs(Hp - H)) > 1.0
+
+
+def test_hessian_products_and_energy():
+    # H v = X'^T (X' v) for the rotated rows of the weight pack's rotation, and the trace is the
+    # Frobenius energy of X (an orthogonal rotation preserves it); an unrotated Gram matrix differs
+    rng = _rng(41)
+    K, B = 64, 16
+    X = rng.standard_normal((50, K))
+    W = rng.standard_normal((20, K))
+    perm = oracle.zigzag_perm(W, B)
+    U = oracle.block_svd(W, perm, B)
+    H = oracle.gptq_hessian([X], perm, U, B)
+    R = oracle.rotation(U, B)
+    Xr = oracle.rotate_rows(X, perm, R, B)
+    for _ in range(3):
+        v = rng.standard_normal(K)
+        assert np.allclose(H @ v, Xr.T @ (Xr @ v), rtol=1e-12, atol=1e-10)
+    Xe = X.astype(np.float32).astype(np.float64)
+    assert abs(np.trace(H) - np.sum(Xe ** 2)) < 1e-6 * np.sum(Xe ** 2)
+    assert np.max(np.abs(H - Xe.T @ Xe)) > 1.0

@@ -123,8 +123,9 @@ def test_step_and_table_shape_errors():
         oracle.quantize_act_grouped(Xr, 64, t, 4, 0)            # table shorter than num_steps
     with pytest.raises(ValueError):
         oracle.quantize_act_grouped(Xr, 64, np.ones((3, 3), np.float32), 3, 0)  # wrong width
-    with pytest.raises(ValueError):
-        oracle.quantize_act_grouped(Xr, 64, np.zeros((3, 2), np.float32), 3, 0)  # zero scale
+    # a zero scale is no scale: codes 0 and a NaN scale for that block (not an exception)
+    z = oracle.quantize_act_grouped(Xr + 1.0, 64, np.zeros((3, 2), np.float32), 3, 0)
+    assert not z["codes"].any() and np.all(np.isnan(z["scale"]))
 
 
 def test_grouped_table_relates_to_per_step_table():

@@ -25,10 +25,18 @@ int launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t s)
     return check_launch("fill");
 }
 
-__device__ __forceinline__ float step_scale(const float *table, int step)
+// A per-step table entry and its reciprocal fp32(1/s). Only a positive finite entry is a scale.
+// Any other entry (zero, negative, infinite or NaN: an uncalibrated or damaged table) yields the
+// scale NaN and the reciprocal 0, so every code becomes 0 and every output of the GEMM that
+// consumes them is NaN: the failure shows in the result instead of a plausible-looking value.
+struct StepScale {
+    float s, rcp;
+};
+__device__ __forceinline__ StepScale step_scale(const float *table, int idx)
 {
-    float s = table[step];
-    return (s > 0.0f && s <= 3.402823466e38f) ? s : 1.0f;
+    const float s = table[idx];
+    if (s > 0.0f && s <= 3.402823466e38f) return StepScale{s, (float)(1.0 / (double)s)};
+    return StepScale{__builtin_nanf(""), 0.0f};
 }
 
 // fp32(max / qmax) divided in fp64 (exactly the fp32 quotient, the double rounding being innocuous
@@ -135,9 +143,15 @@ __global__ __launch_bounds__(128) void k_rotate_quant_valu(
     for (int r = 0; r < RQ_ROWS; ++r) {
         const int m = m0 + r;
         if (m >= M) continue;
-        float s;
-        if (MODE == ACT_PER_STEP) s = step_scale(table, step);
-        else s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[m]));
+        float s, rcp;
+        if (MODE == ACT_PER_STEP) {
+            const StepScale ss = step_scale(table, step);
+            s = ss.s;
+            rcp = ss.rcp;
+        } else {
+            s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[m]));
+            rcp = (float)(1.0 / (double)s);
+        }
         if (blockIdx.y == 0 && tid == 0) {
             if (MODE == ACT_PER_STEP) {
                 if (blockIdx.x == 0 && r == 0) x_scale[0] = s;
@@ -146,7 +160,6 @@ __global__ __launch_bounds__(128) void k_rotate_quant_valu(
             }
         }
         if (!active) continue;
-        const float rcp = (float)(1.0 / (double)s);
         const int q0 = quant_code_q<Q8>(acc[r][0], rcp);
         const int q1 = quant_code_q<Q8>(acc[r][1], rcp);
         if (Q8)
@@ -230,8 +243,9 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
 
     float s_step = 1.0f, rcp_step = 1.0f;
     if (MODE == ACT_PER_STEP) {
-        s_step = step_scale(table, step + b * gstride);
-        rcp_step = (float)(1.0 / (double)s_step);
+        const StepScale ss = step_scale(table, step + b * gstride);
+        s_step = ss.s;
+        rcp_step = ss.rcp;
         if (blockIdx.x == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s_step;
     }
 
@@ -523,9 +537,9 @@ __global__ __launch_bounds__(256) void k_rq_ring(
         }
     float rs_step = 0.0f;
     if (MODE == ACT_PER_STEP) {
-        const float s = step_scale(table, step + b * gstride);
-        rs_step = (float)(1.0 / (double)s) * LO;
-        if (rgi == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s;
+        const StepScale ss = step_scale(table, step + b * gstride);
+        rs_step = ss.rcp * LO;
+        if (rgi == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = ss.s;
     }
     if (MODE == ACT_TOKEN_QUANT) __syncthreads();
 
@@ -722,9 +736,9 @@ __global__ __launch_bounds__(64 * NW) void k_rq_small(
         for (int kk = 0; kk < KK; ++kk) ahi[jf][kk] = ahi[jf][kk] * (_Float16)(1 << ROT_LO_SHIFT);
     float rs = 0.0f;
     if (MODE == ACT_PER_STEP) {
-        const float s = step_scale(table, step + b * gstride);
-        rs = (float)(1.0 / (double)s) * LO;
-        if (si == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s;
+        const StepScale ss = step_scale(table, step + b * gstride);
+        rs = ss.rcp * LO;
+        if (si == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = ss.s;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -921,9 +935,9 @@ __global__ __launch_bounds__(256) void k_rq_hadamard(
     };
 
     if (MODE == ACT_PER_STEP) {
-        const float s = step_scale(table, step);
-        const float r = (float)(1.0 / (double)s);
-        if (blockIdx.x == 0 && tid == 0) x_scale[0] = s;
+        const StepScale ss = step_scale(table, step);
+        const float r = ss.rcp;
+        if (blockIdx.x == 0 && tid == 0) x_scale[0] = ss.s;
         for (int u = slot; u < units; u += HD_UNITS) {
             float x[EPT];
             transform(u, x);

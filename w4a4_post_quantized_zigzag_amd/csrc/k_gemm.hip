@@ -10,6 +10,7 @@
 // (|sum| <= 64 K, so 256 * 64 K stays below 2^31 for the at most 2^16 k values of one split). Both
 // operands go through the same even/odd reordering of k, so the dot products match.
 #include <cmath>
+#include <type_traits>
 
 #include "w4a4_internal.h"
 
@@ -19,6 +20,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int MAX_K_SPLIT = 1 << 16;  // 256 * 64 * 2^16 = 2^30 fits int32
 constexpr int SMALL_M = 64;           // rows up to which the weight-streaming kernel is used
+// tile kinds of the software-pipelined GEMM (k_gemm_sp) in the GEMM plan
+enum SpKind { SP_128x192 = 11, SP_128x128 = 12, SP_64x128 = 13 };
 
 __device__ __forceinline__ void widen16(const uint4 &p, uint4 &lo, uint4 &hi)
 {
@@ -739,6 +742,15 @@ __device__ __forceinline__ void wait_vmcnt(int n)
     }
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N <= 63 (the count's low four bits at 3:0, its high two
+// bits at 15:14; expcnt and lgkmcnt at their no-wait values).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Epilogue kinds of the pipelined kernel (compile-time, so each variant is straight-line code).
 enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_RESIDUAL,
        PE_INT32 = 3 };
@@ -926,13 +938,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                 }
             }
         return;
-    } else {
+    } else if (VEC_OUT) {
 #pragma clang fp contract(off)
-        // VEC_OUT: Y, the residual and the weight scales are read or written 4 columns at a time
-        // (the host checks their alignment and row strides); columns past N take the element path.
+        // Staged epilogue (Y and residual rows 16-byte aligned, N % 8 == 0, checked by the host):
+        // the output tile goes through LDS so that global memory sees whole 128-byte lines. Each
+        // lane's accumulator holds four consecutive columns of one row, so a direct store from
+        // the fragment layout writes 16 rows x 32 bytes per instruction, a quarter line per row,
+        // and the partial-line writes cost several times the bytes they carry. The ring is free
+        // once every wave has passed the last stage's fragment reads.
+        constexpr int TP = BN * 2 + 16;  // LDS row pitch in bytes (the pad spreads the fragment
+                                         // writes of 16 rows over all banks)
+        constexpr int CPR = BN / 8;      // 16-byte chunks per tile row
+        constexpr int NT = NW * 64;
+        const int rows_here = min(BM, M - m0), cols_here = min(BN, N - n0);
+        __syncthreads();
+        if (PE == PE_RESIDUAL) {
+            for (int c = tid; c < BM * CPR; c += NT) {
+                const int r = c / CPR, cc = c % CPR;
+                if (r < rows_here && cc * 8 < cols_here)
+                    *reinterpret_cast<uint4 *>(&smem[r * TP + cc * 16]) = *reinterpret_cast<const uint4 *>(
+                        epi.residual + (int64_t)(m0 + r) * epi.ldr + n0 + cc * 8);
+            }
+            __syncthreads();
+        }
         float xsc[FM];
         float wsc[FN][4];
-        uint32_t rsd[FM][FN][2];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             xsc[i] = GS ? 0.0f
@@ -940,7 +970,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = ncol + j * 16;
-            if (VEC_OUT && n + 3 < N) {
+            if (n + 3 < N) {
                 const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
                 wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
             } else {
@@ -948,33 +978,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                 for (int r = 0; r < 4; ++r) wsc[j][r] = epi.w_scale[min(n + r, N - 1)];
             }
         }
-        // residual values: prefetched 4 at a time on the vector path, read one by one otherwise
-        auto residual4 = [&](int m, int n, uint32_t (&h)[2]) {
-            const uint16_t *src = epi.residual + (int64_t)min(m, M - 1) * epi.ldr;
-            if (VEC_OUT && n + 3 < N) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(src + n);
-                h[0] = v.x; h[1] = v.y;
-            } else {
-                uint32_t e[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) e[r] = src[min(n + r, N - 1)];
-                h[0] = e[0] | (e[1] << 16); h[1] = e[2] | (e[3] << 16);
-            }
-        };
-        if (PE == PE_RESIDUAL && VEC_OUT) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) residual4(mrow + i * 16, ncol + j * 16, rsd[i][j]);
-        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int m = mrow + i * 16;
+            const int rl = wm * WTM + i * 16 + fr;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int n = ncol + j * 16;
+                const int cl = wn * WTN + j * 16 + 4 * fg;
+                uint2 *cell = reinterpret_cast<uint2 *>(&smem[rl * TP + cl * 2]);
+                uint2 rv = make_uint2(0u, 0u);
+                if (PE == PE_RESIDUAL) rv = *cell;
+                const uint32_t rh[2] = {rv.x, rv.y};
                 float y[4];
-                if (PE == PE_RESIDUAL && !VEC_OUT) residual4(m, n, rsd[i][j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (GS) {
@@ -984,14 +998,347 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                         y[r] = fp32_value(y[r] * wsc[j][r]);
                     }
                     if (PE == PE_GELU) y[r] = fp32_value(gelu_erf(y[r]));
+                    if (PE == PE_RESIDUAL)
+                        y[r] = fp32_value(y[r] + __half2float(__ushort_as_half(
+                                                     (uint16_t)(rh[r >> 1] >> (16 * (r & 1))))));
+                }
+                *cell = make_uint2(f32x2_to_f16x2(y[0], y[1]), f32x2_to_f16x2(y[2], y[3]));
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < BM * CPR; c += NT) {
+            const int r = c / CPR, cc = c % CPR;
+            if (r < rows_here && cc * 8 < cols_here)
+                *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) =
+                    *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
+        }
+    } else {
+#pragma clang fp contract(off)
+        // element path (rows not 16-byte aligned): each lane dequantizes and stores its four
+        // columns one fp16 at a time
+        float xsc[FM];
+        float wsc[FN][4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            xsc[i] = GS ? 0.0f
+                        : epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = ncol + j * 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wsc[j][r] = epi.w_scale[min(n + r, N - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = mrow + i * 16;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = ncol + j * 16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (n + r >= N) continue;
+                    float y;
+                    if (GS) {
+                        y = fp32_value(yf[GS ? i : 0][GS ? j : 0][r] * wsc[j][r]);
+                    } else {
+                        y = fp32_value((float)(acc[i][j][r] >> SHIFT) * xsc[i]);
+                        y = fp32_value(y * wsc[j][r]);
+                    }
+                    if (PE == PE_GELU) y = fp32_value(gelu_erf(y));
+                    if (PE == PE_RESIDUAL)
+                        y = fp32_value(y + __half2float(__ushort_as_half(
+                                               epi.residual[(int64_t)m * epi.ldr + n + r])));
+                    epi.Y[(int64_t)m * epi.ldy + n + r] = f32_to_f16_bits(y);
+                }
+            }
+        }
+    }
+}
+
+// Software-pipelined large-M GEMM for packed int4 operands (K and the k split multiples of 128,
+// 16-byte aligned operands), the kernel for batches of a few thousand tokens whose grids hold about
+// one tile per compute unit. Eight waves, two per SIMD: waves 0-3 and 4-7 form two k groups, and
+// wave (g, c) owns columns [c BN/4, (c+1) BN/4) of the tile for the k half g of every 128-k stage
+// (the low or high 8 bytes of each lane's 16-byte fragment, i.e. one of the two MFMAs a packed
+// fragment pair feeds). One SIMD thus always holds a second wave whose matrix work can run while
+// the first widens nibbles, reads LDS or waits. Operand stages go from global memory into an
+// NS-stage LDS ring with global_load_lds_dwordx4, issued by the waves of group 0 only; a barrier
+// after their load waits publishes each stage to all eight waves. A stage's fragments are read one
+// iteration ahead; the steady-state loop waits with a compile-time load count; the epilogue
+// operands are fetched before the loop. At the end each group hands the partial sums of the tile
+// rows the other group finalizes through LDS (int32 adds are exact in any order), and each wave
+// dequantizes and stores half of its fragments.
+// At iteration s the ring holds stage s (already in registers), s+1 (being read) and up to NS-2
+// stages in flight; the slot refilled at iteration s held stage s-1, whose fragment reads every
+// wave finished before the barrier of iteration s.
+template <int BM, int BN, int NS, int KS, int PE, bool VO>
+__global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
+                                                 const uint8_t *__restrict__ wq, int M, int N,
+                                                 int K, int k_split, int tiles_m, int tiles_n,
+                                                 GemmEpilogue epi, int32_t *__restrict__ partial)
+{
+    constexpr int NC = 4;  // column waves per k group
+    constexpr int WTN = BN / NC;
+    constexpr int FM = BM / 16, FN = WTN / 16;
+    constexpr int FMH = FM / 2;  // fragment rows each k group finalizes
+    // a ring slot holds KS sub-stages of 128 k, each [A rows x 64 B][B rows x 64 B]
+    constexpr int A_BYTES = BM * BG_ROWB, B_BYTES = BN * BG_ROWB, STAGE = A_BYTES + B_BYTES;
+    constexpr int SLOT = KS * STAGE;
+    constexpr int QA = A_BYTES / 1024 / NC, QB = B_BYTES / 1024 / NC;  // DMA instrs per sub-stage
+    constexpr int L = KS * (QA + QB);                                  // DMA instrs per slot
+    constexpr int NF = FM + FN;
+    constexpr bool RES_EARLY = (PE == PE_RESIDUAL) && (FMH * FN <= 16);
+    static_assert(QA * 1024 * NC == A_BYTES && QB * 1024 * NC == B_BYTES, "whole KB per wave");
+    static_assert(NS >= 2 && FN >= 1 && FM % 2 == 0, "ring of at least two slots");
+    static_assert((size_t)BM * BN * 4 <= (size_t)NS * SLOT, "partial sums fit in the ring");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int T = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int per_x = T / 8, rm = T % 8, x = id % 8;
+    const int lin = x * per_x + min(x, rm) + id / 8;
+    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wc = wave & 3, kgrp = wave >> 2;
+    const int ugrp = __builtin_amdgcn_readfirstlane(kgrp);
+    const int ldp = K / 2;
+    const int kb_begin = blockIdx.y * (k_split / 2);
+    const int kb_end = min(kb_begin + k_split / 2, ldp);
+    const int stages = (kb_end - kb_begin) / (BG_ROWB * KS);  // ring slots of KS sub-stages
+    const int fr = lane & 15, fg = lane >> 4;
+    // this wave finalizes fragment rows i = kgrp * FMH .. kgrp * FMH + FMH - 1
+    const int mrow = m0 + kgrp * FMH * 16 + fr, ncol = n0 + wc * WTN + 4 * fg;
+
+    // epilogue operands first: their latency hides under the operand stream
+    float xsc[FMH];
+    float wsc[FN][4];
+    uint32_t rsd[RES_EARLY ? FMH : 1][RES_EARLY ? FN : 1][2];
+    if (PE != PE_INT32) {
+#pragma unroll
+        for (int i = 0; i < FMH; ++i)
+            xsc[i] = epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = ncol + j * 16;
+            if (VO && n + 3 < N) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
+                wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wsc[j][r] = epi.w_scale[min(n + r, N - 1)];
+            }
+        }
+        if (RES_EARLY) {
+#pragma unroll
+            for (int i = 0; i < (RES_EARLY ? FMH : 1); ++i)
+#pragma unroll
+                for (int j = 0; j < (RES_EARLY ? FN : 1); ++j) {
+                    const int m = min(mrow + i * 16, M - 1), n = ncol + j * 16;
+                    const uint16_t *src = epi.residual + (int64_t)m * epi.ldr;
+                    if (VO && n + 3 < N) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(src + n);
+                        rsd[i][j][0] = v.x; rsd[i][j][1] = v.y;
+                    } else {
+                        uint32_t e[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e[r] = src[min(n + r, N - 1)];
+                        rsd[i][j][0] = e[0] | (e[1] << 16); rsd[i][j][1] = e[2] | (e[3] << 16);
+                    }
+                }
+        }
+    }
+
+    const uint8_t *srcA[QA];
+    const uint8_t *srcB[QB];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int row = (wc * QA + q) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 1) & 3);
+        srcA[q] = xq + (int64_t)min(m0 + row, M - 1) * ldp + kb_begin + 16 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int row = (wc * QB + q) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 1) & 3);
+        srcB[q] = wq + (int64_t)min(n0 + row, N - 1) * ldp + kb_begin + 16 * c;
+    }
+    const int uwc = __builtin_amdgcn_readfirstlane(wc);
+    const uint32_t lds0 = lds_address(smem);
+    auto issue = [&](int st) {
+        if (ugrp != 0) return;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t base = lds0 + (uint32_t)((st % NS) * SLOT + ks * STAGE);
+            const int koff = (st * KS + ks) * BG_ROWB;
+#pragma unroll
+            for (int q = 0; q < QA; ++q)
+                dma_to_lds16(srcA[q] + koff, base + (uint32_t)((uwc * QA + q) * 1024));
+#pragma unroll
+            for (int q = 0; q < QB; ++q)
+                dma_to_lds16(srcB[q] + koff, base + (uint32_t)(A_BYTES + (uwc * QB + q) * 1024));
+        }
+    };
+    // this group's 8 bytes of each fragment: A rows 16 i + fr (all tile rows), B rows of this
+    // wave's columns
+    const int half = 8 * kgrp;
+    auto read_frags = [&](int st, uint2 (&F)[KS][NF]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint8_t *sA = smem + (st % NS) * SLOT + ks * STAGE;
+            const uint8_t *sB = sA + A_BYTES;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int row = wc * WTN + j * 16 + fr;
+                F[ks][FM + j] =
+                    *reinterpret_cast<const uint2 *>(&sB[row * BG_ROWB + swz(row, fg) + half]);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = i * 16 + fr;
+                F[ks][i] = *reinterpret_cast<const uint2 *>(&sA[row * BG_ROWB + swz(row, fg) + half]);
+            }
+        }
+    };
+
+    v4i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    // 8 packed bytes -> the 16 int8 operand bytes 16 * code (the order widen16 gives either half)
+    auto widen8 = [](const uint2 &p) {
+        return v4i{(int)((p.x << 4) & 0xF0F0F0F0u), (int)(p.x & 0xF0F0F0F0u),
+                   (int)((p.y << 4) & 0xF0F0F0F0u), (int)(p.y & 0xF0F0F0F0u)};
+    };
+    auto compute = [&](const uint2 (&F)[KS][NF]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            v4i b[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = widen8(F[ks][FM + j]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const v4i a = widen8(F[ks][i]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[j], a, acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+    // Iteration s: wait until slot s has landed (with every slot up to s+NS-2 issued, exactly
+    // NS-2 younger slots may stay in flight; near the end it waits for everything), barrier (slot s
+    // is visible to all waves, and every wave has finished reading slot s-1), refill slot s-1's
+    // place with slot s+NS-1, then read slot s's fragments and compute.
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < stages) issue(p);
+    uint2 F[KS][NF];
+    for (int s = 0; s < stages; ++s) {
+        asm volatile("" ::: "memory");
+        if (s + NS - 2 <= stages - 1 && ugrp == 0) wait_vm<(NS - 2) * L>();
+        else wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + NS - 1 < stages) issue(s + NS - 1);
+        read_frags(s, F);
+        compute(F);
+    }
+
+    // Exchange the k groups' partial sums through LDS: group g keeps fragment rows i in its half
+    // and sends the other half. Slot layout: [sender group][fragment row in half][FN][column wave]
+    // x 64 lanes x 16 bytes. The group index is made a compile-time constant (one copy of the
+    // epilogue per group) so that the accumulators stay in registers.
+    __syncthreads();  // every wave is past its last fragment read
+    auto finish = [&](auto G) {
+        constexpr int g = decltype(G)::value, other = 1 - g;
+        int4 *xch = reinterpret_cast<int4 *>(smem);
+#pragma unroll
+        for (int ih = 0; ih < FMH; ++ih)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int slot = ((g * FMH + ih) * FN + j) * NC + wc;
+                const v4i v = acc[other * FMH + ih][j];
+                xch[slot * 64 + lane] = make_int4(v[0], v[1], v[2], v[3]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int ih = 0; ih < FMH; ++ih)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int slot = ((other * FMH + ih) * FN + j) * NC + wc;
+                const int4 v = xch[slot * 64 + lane];
+                v4i &a = acc[g * FMH + ih][j];
+                a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
+            }
+        if (PE == PE_INT32) {
+            int32_t *dst = partial ? partial + (int64_t)blockIdx.y * M * N : epi.acc_out;
+            const bool vec4 = (N % 4 == 0) && ((uintptr_t)dst % 16 == 0);
+#pragma unroll
+            for (int ih = 0; ih < FMH; ++ih)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const v4i &a = acc[g * FMH + ih][j];
+                    const int m = mrow + ih * 16, n = ncol + j * 16;
+                    if (m >= M) continue;
+                    if (vec4 && n + 3 < N) {
+                        *reinterpret_cast<int4 *>(&dst[(int64_t)m * N + n]) =
+                            make_int4(a[0] >> 8, a[1] >> 8, a[2] >> 8, a[3] >> 8);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N) dst[(int64_t)m * N + n + r] = a[r] >> 8;
+                    }
+                }
+            return;
+        }
+        {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int ih = 0; ih < FMH; ++ih) {
+            const int m = mrow + ih * 16;
+            uint32_t rl[FN][2];
+            if (PE == PE_RESIDUAL) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    if (RES_EARLY) {
+                        rl[j][0] = rsd[RES_EARLY ? ih : 0][RES_EARLY ? j : 0][0];
+                        rl[j][1] = rsd[RES_EARLY ? ih : 0][RES_EARLY ? j : 0][1];
+                        continue;
+                    }
+                    const int n = ncol + j * 16;
+                    const uint16_t *src = epi.residual + (int64_t)min(m, M - 1) * epi.ldr;
+                    if (VO && n + 3 < N) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(src + n);
+                        rl[j][0] = v.x; rl[j][1] = v.y;
+                    } else {
+                        uint32_t e[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e[r] = src[min(n + r, N - 1)];
+                        rl[j][0] = e[0] | (e[1] << 16); rl[j][1] = e[2] | (e[3] << 16);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const v4i &a = acc[g * FMH + ih][j];
+                const int n = ncol + j * 16;
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    y[r] = fp32_value((float)(a[r] >> 8) * xsc[ih]);
+                    y[r] = fp32_value(y[r] * wsc[j][r]);
+                    if (PE == PE_GELU) y[r] = fp32_value(gelu_erf(y[r]));
                     if (PE == PE_RESIDUAL) {
-                        const uint32_t hv = rsd[i][j][r >> 1] >> (16 * (r & 1));
+                        const uint32_t hv = rl[j][r >> 1] >> (16 * (r & 1));
                         y[r] = fp32_value(y[r] + __half2float(__ushort_as_half((uint16_t)hv)));
                     }
                 }
                 if (m >= M) continue;
                 uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
-                if (VEC_OUT && n + 3 < N) {
+                if (VO && n + 3 < N) {
                     *reinterpret_cast<uint2 *>(dst) = make_uint2(f32x2_to_f16x2(y[0], y[1]),
                                                                  f32x2_to_f16x2(y[2], y[3]));
                 } else {
@@ -1001,7 +1348,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                 }
             }
         }
-    }
+        }
+    };
+    if (ugrp == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
 }
 
 // Split-K reduction of exact int32 partials, then the same epilogue.
@@ -1115,14 +1465,6 @@ int launch_codes_to_f6(const uint8_t *q, int rows, int K, uint8_t *out, hipStrea
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-
-// s_waitcnt vmcnt(n) with lgkmcnt / expcnt at their no-wait values (vmcnt bits 3:0 and 15:14)
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 
 // Pipelined FP6 GEMM: the int4 pipelined kernel's structure (LDS ring of NSTAGE stages filled by
 // global_load_lds_dwordx4, vmcnt waits + plain barriers, XCD-aware tile order), one
@@ -1343,38 +1685,51 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_f6(
 }
 
 struct GemmPlan {
-    int kind;  // 0 small-M, 1 = 256x256, 2 = 128x256, 3 = 128x128, 4 = 64x128 (pipelined only)
+    // 0 small-M; 1 = 256x256, 2 = 128x256, 3 = 128x128, 4 = 64x128 (k_gemm_pipe / k_gemm_big);
+    // SP_* (k_gemm_sp, packed int4 with K % 128 == 0 and aligned operands)
+    int kind;
     int bm, bn, splits, k_split;
 };
 
 // Pick the tile shape and k split with the smallest estimated time: full rounds of 256 compute
-// units times the per-tile MFMA time (discounted for smaller wave tiles, whose LDS traffic per MFMA
-// is higher), plus the write and read of split-K partials. kg is the k granularity of a stage (128
-// for packed int4, 64 for int8 operands).
-static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe)
+// units (one workgroup per unit) times the per-tile time, plus the write and read of split-K
+// partials. kg is the k granularity of a stage (128 for packed int4, 64 for int8 operands); sp
+// allows the software-pipelined kernel, whose per-stage times were measured on MI355X.
+static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = false)
 {
     GemmPlan best{0, 0, 16, 1, K};
     if (M <= SMALL_M) return best;
-    // 64 x 128 tiles (kind 4) exist only in the pipelined kernel; they double the workgroups of a
-    // grid that would leave compute units idle, at a lower per-tile efficiency
-    struct Cand { int kind, bm, bn; double eff; };
-    const Cand cands[] = {{1, 256, 256, 1.0}, {2, 128, 256, 0.85}, {3, 128, 128, 0.6},
-                          {4, 64, 128, 0.35}};
-    constexpr double ROUND_FIXED = 3e-6;  // prologue, epilogue and drain of one round of tiles
+    // eff: fraction of the MFMA rate in the main loop; t_stage: measured seconds per 128-k stage
+    // (0 = use eff); fixed: launch ramp, first loads and epilogue of a round
+    // gran: k granularity of the kernel's ring (a k split must be a whole number of it)
+    struct Cand { int kind, bm, bn; double eff, t_stage, fixed; int gran; };
+    const Cand pipe_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg}, {2, 128, 256, 0.85, 0, 3e-6, kg},
+                               {3, 128, 128, 0.6, 0, 3e-6, kg}, {4, 64, 128, 0.35, 0, 3e-6, kg}};
+    const Cand sp_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg},
+                             {SP_128x128, 128, 128, 0, 0.32e-6, 2.5e-6, 256},
+                             {SP_64x128, 64, 128, 0, 0.20e-6, 2.5e-6, 512}};
+    const Cand *cands = sp ? sp_cands : pipe_cands;
+    const int ncand = sp ? 3 : 4;
     double best_t = 1e30;
-    for (const Cand &c : cands) {
+    for (int ci = 0; ci < ncand; ++ci) {
+        const Cand &c = cands[ci];
         if (c.kind == 4 && !pipe) continue;
+        if (K % c.gran) continue;
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-        for (int splits = 1; splits <= 16; splits *= 2) {
+        // up to 256 splits: K <= 2^24 then always fits pieces of at most MAX_K_SPLIT k, the most
+        // one int32 accumulator of the tile kernels holds
+        for (int splits = 1; splits <= 256; splits *= 2) {
             if (c.kind == 4 && splits > 1) continue;
-            int k_split = ((K + splits - 1) / splits + kg - 1) / kg * kg;
+            int k_split = ((K + splits - 1) / splits + c.gran - 1) / c.gran * c.gran;
             if (k_split > MAX_K_SPLIT) continue;
             const int real_splits = (K + k_split - 1) / k_split;
             if (real_splits != splits) continue;
             if (splits > 1 && k_split < 1024) continue;
             const double rounds = std::ceil(tiles * splits / 256.0);
-            const double t_c = rounds * (2.0 * c.bm * c.bn * k_split / (8192.0 * 2.4e9 * c.eff) +
-                                         ROUND_FIXED);
+            const double per_tile = c.t_stage > 0
+                                        ? (k_split / (double)BG_KS) * c.t_stage
+                                        : 2.0 * c.bm * c.bn * k_split / (8192.0 * 2.4e9 * c.eff);
+            const double t_c = rounds * (per_tile + c.fixed);
             const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 4e12 + 3e-6 : 0.0;
             const double t = t_c + t_r;
             if (t < best_t * 0.98) {
@@ -1391,8 +1746,8 @@ size_t gemm_workspace(int M, int N, int K, bool q8)
     // the launch plans with or without the pipelined kernel (operand alignment decides): enough
     // for either
     size_t need = 0;
-    for (int pipe = 0; pipe < 2; ++pipe) {
-        GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe != 0);
+    for (int pipe = 0; pipe < 3; ++pipe) {
+        GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe != 0, pipe == 2 && !q8);
         if (p.splits > 1)
             need = std::max(need, (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t));
     }
@@ -1420,7 +1775,10 @@ static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
-    const size_t lds = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
+    // the staged epilogue reuses the ring for the output tile (BM rows of BN fp16 plus a pad)
+    const size_t ring = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
+    const size_t tile = (PE != PE_INT32 && VO) ? (size_t)BM * (BN * 2 + 16) : 0;
+    const size_t lds = ring > tile ? ring : tile;
     const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>), grid,
@@ -1436,11 +1794,11 @@ static int launch_pipe_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
     if (!GS && (partial || epi.mode == GEMM_OUT_I32))
         return launch_pipe_e<BM, BN, WM, WN, PE_INT32, false, Q8>(grid, s, xq, wq, M, N, K, k_split,
                                                                  tm, tn, epi, partial);
-    // 4-column groups: 8-byte Y / residual accesses and 16-byte weight-scale loads
-    const bool vo = (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+    // staged epilogue: whole 16-byte chunks of Y / residual rows and 16-byte weight-scale loads
+    const bool vo = (N % 8 == 0) && (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0) &&
                     ((uintptr_t)epi.w_scale % 16 == 0) &&
                     (epi.mode != W4A4_EPI_RESIDUAL ||
-                     (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
+                     (epi.ldr % 8 == 0 && (uintptr_t)epi.residual % 16 == 0));
 #define W4A4_PIPE_E(PEV)                                                                           \
     return vo ? launch_pipe_e<BM, BN, WM, WN, PEV, true, Q8, GS>(grid, s, xq, wq, M, N, K, k_split, \
                                                                  tm, tn, epi, partial)             \
@@ -1472,6 +1830,60 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
         return launch_pipe_t<64, 128, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
                                                 partial);
     return launch_pipe_t<128, 128, 2, 2, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+}
+
+// ---- software-pipelined GEMM launch (plan kinds SP_*)
+
+template <int BM, int BN, int NS, int KS, int PE, bool VO>
+static int launch_sp_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
+                       int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                       int32_t *partial)
+{
+    const size_t lds = (size_t)NS * KS * (BM + BN) * BG_ROWB;
+    const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO>;
+    if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
+    hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO>), grid, dim3(512), lds, s, xq, wq, M, N,
+                       K, k_split, tm, tn, epi, partial);
+    return W4A4_OK;
+}
+
+template <int BM, int BN, int NS, int KS>
+static int launch_sp_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
+                       int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                       int32_t *partial)
+{
+    if (partial || epi.mode == GEMM_OUT_I32)
+        return launch_sp_e<BM, BN, NS, KS, PE_INT32, false>(grid, s, xq, wq, M, N, K, k_split, tm,
+                                                            tn, epi, partial);
+    // 4-column groups: 8-byte Y / residual accesses and 16-byte weight-scale loads
+    const bool vo = (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+                    ((uintptr_t)epi.w_scale % 16 == 0) &&
+                    (epi.mode != W4A4_EPI_RESIDUAL ||
+                     (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
+#define W4A4_SP_E(PEV)                                                                             \
+    return vo ? launch_sp_e<BM, BN, NS, KS, PEV, true>(grid, s, xq, wq, M, N, K, k_split, tm, tn,   \
+                                                       epi, partial)                               \
+              : launch_sp_e<BM, BN, NS, KS, PEV, false>(grid, s, xq, wq, M, N, K, k_split, tm, tn,  \
+                                                        epi, partial);
+    if (epi.mode == W4A4_EPI_GELU) { W4A4_SP_E(PE_GELU) }
+    if (epi.mode == W4A4_EPI_RESIDUAL) { W4A4_SP_E(PE_RESIDUAL) }
+    W4A4_SP_E(PE_NONE)
+#undef W4A4_SP_E
+}
+
+// Launch one software-pipelined GEMM tile kind (also the tile sweep's entry point).
+int launch_gemm_sp_kind(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq,
+                        int M, int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
+                        int32_t *partial)
+{
+    switch (kind) {
+    case SP_128x128:
+        return launch_sp_t<128, 128, 4, 2>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+    case SP_64x128:
+        return launch_sp_t<64, 128, 3, 4>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+    default:
+        return fail(W4A4_ERR_ARG, "unknown GEMM tile kind %d", kind);
+    }
 }
 
 // Group-wise GEMM (per rotation block activation scales in epi.x_scale[K / 128]): the grouped
@@ -1552,7 +1964,7 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     const bool pipe = q8 || (vec && K % BG_KS == 0);
-    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe);
+    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe, pipe && !q8);
     if (p.kind == 0) {
         const int mf = (M + 15) / 16;
         // the wide kernel: whole 64-byte windows and at most 2^16 k per wave (4 waves)
@@ -1590,6 +2002,10 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     dim3 grid(tm * tn, p.splits);
     if (q8) {
         int rc = launch_pipe<true>(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);
+        if (rc != W4A4_OK) return rc;
+    } else if (p.kind >= SP_128x192) {
+        int rc = launch_gemm_sp_kind(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi,
+                                     partial);
         if (rc != W4A4_OK) return rc;
     } else if (pipe) {
         int rc = launch_pipe<false>(p.kind, grid, s, xq, wq, M, N, K, p.k_split, tm, tn, epi, partial);

@@ -111,7 +111,8 @@ class DeviceStack:
             for name in LINEARS:
                 layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
 
-    def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None, in_order=False):
+    def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None, in_order=False,
+                record=None):
         b = lin.bits
         perm = None if in_order else lin.perm  # in_order: X already holds the zigzag order
         if calib:
@@ -120,27 +121,42 @@ class DeviceStack:
         xq = bufs.xq[(lin.K, b)]
         bd.rotate_quant_act(X, perm, lin.rot, self.block, None if calib else lin.table,
                             self.steps, step, xq=xq, x_scale=bufs.xs, ws=bufs.ws[lin.K], bits=b)
+        if record is not None:
+            record(xq, bufs.xs[:X.shape[0] if calib else 1])
         bd.gemm(xq, bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
                 ws=bufs.gws[(lin.N, lin.K, b)], bits=b)
 
-    def run(self, X, step: int, calib: bool = False, outputs=None):
+    def run(self, X, step: int, calib: bool = False, outputs=None, codes=None, rows=None):
         """One pass of the stack for denoising step `step` on X fp16 [rows, h] (device). In calib
-        mode the linears quantize per token and record their table entry for `step`. If `outputs`
-        is a list, each linear's output tensor is appended (test hook)."""
+        mode the linears quantize per token and record their table entry for `step`. Test hooks:
+        if `outputs` is a list, each linear's output (columns in natural channel order) and its
+        input are appended as (output, input, residual or None); if `codes` is a list, each linear's
+        activation codes and scale are appended as (codes, x_scale). `rows` (device int64 index)
+        keeps only those token rows in what the hooks record."""
         bufs = self.bufs(X.shape[0])
         h = self.h
         cur = X
+        pick = (lambda t: t.clone()) if rows is None else (lambda t: t.index_select(0, rows))
+        cr = None
+        if codes is not None:
+            def cr(xq, xs):
+                codes.append((pick(xq), xs.clone() if xs.numel() == 1 else pick(xs)))
         for li, layer in enumerate(self.layers):
             nxt = bufs.hs[li % 2]
-            self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs)
+            x_in = pick(cur) if outputs is not None else None
+            self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs, record=cr)
             self._linear(layer["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
-                         bd.EPI_RESIDUAL, cur, in_order=self.fold)
-            self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU)
+                         bd.EPI_RESIDUAL, cur, in_order=self.fold, record=cr)
+            self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU, record=cr)
             self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2,
-                         in_order=self.fold)
+                         in_order=self.fold, record=cr)
             if outputs is not None:
-                outputs.extend([self._natural(layer["qkv"], bufs.qkv), bufs.h2.clone(),
-                                self._natural(layer["up"], bufs.g), nxt.clone()])
+                qkv = pick(self._natural(layer["qkv"], bufs.qkv))
+                h2 = pick(bufs.h2)
+                g = pick(self._natural(layer["up"], bufs.g))
+                out = pick(nxt)
+                outputs.extend([(qkv, x_in, None), (h2, qkv[:, 2 * h:3 * h], x_in), (g, h2, None),
+                                (out, g, h2)])
             cur = nxt
         return cur
 
