@@ -953,11 +953,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         const int rows_here = min(BM, M - m0), cols_here = min(BN, N - n0);
         __syncthreads();
         if (PE == PE_RESIDUAL) {
-            for (int c = tid; c < BM * CPR; c += NT) {
-                const int r = c / CPR, cc = c % CPR;
-                if (r < rows_here && cc * 8 < cols_here)
-                    *reinterpret_cast<uint4 *>(&smem[r * TP + cc * 16]) = *reinterpret_cast<const uint4 *>(
-                        epi.residual + (int64_t)(m0 + r) * epi.ldr + n0 + cc * 8);
+            // every chunk is loaded from a clamped in-bounds address with no branch, all loads of a
+            // thread before its LDS writes (chunks past M or N hold stand-in values, never stored)
+            static_assert((BM * CPR) % NT == 0, "whole rounds of residual chunks");
+            constexpr int RC = BM * CPR / NT;
+            uint4 rv[RC];
+#pragma unroll
+            for (int t = 0; t < RC; ++t) {
+                const int c = tid + t * NT, r = c / CPR, cc = c % CPR;
+                rv[t] = *reinterpret_cast<const uint4 *>(
+                    epi.residual + (int64_t)min(m0 + r, M - 1) * epi.ldr + min(n0 + cc * 8, N - 8));
+            }
+#pragma unroll
+            for (int t = 0; t < RC; ++t) {
+                const int c = tid + t * NT, r = c / CPR, cc = c % CPR;
+                *reinterpret_cast<uint4 *>(&smem[r * TP + cc * 16]) = rv[t];
             }
             __syncthreads();
         }
@@ -969,14 +979,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                         : epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int n = ncol + j * 16;
-            if (n + 3 < N) {
-                const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
-                wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) wsc[j][r] = epi.w_scale[min(n + r, N - 1)];
-            }
+            const int n = ncol + j * 16;  // N % 8 == 0: a clamped column is a whole float4
+            const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + min(n, N - 4));
+            wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -1006,11 +1011,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
             }
         }
         __syncthreads();
+#pragma unroll 4
         for (int c = tid; c < BM * CPR; c += NT) {
             const int r = c / CPR, cc = c % CPR;
+            const uint4 v = *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
             if (r < rows_here && cc * 8 < cols_here)
-                *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) =
-                    *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
+                *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
         }
     } else {
 #pragma clang fp contract(off)
@@ -1120,11 +1126,14 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
 #pragma unroll
         for (int i = 0; i < FMH; ++i)
             xsc[i] = epi.x_scale_per_token ? epi.x_scale[min(mrow + i * 16, M - 1)] : epi.x_scale[0];
+        // VO (N % 4 == 0, aligned rows, checked by the host): one vector load per operand from a
+        // clamped in-bounds column, with no branch, so the loads stay in flight under the main
+        // loop (columns past N are computed from stand-in values and never stored)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = ncol + j * 16;
-            if (VO && n + 3 < N) {
-                const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + n);
+            if (VO) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(epi.w_scale + min(n, N - 4));
                 wsc[j][0] = w4.x; wsc[j][1] = w4.y; wsc[j][2] = w4.z; wsc[j][3] = w4.w;
             } else {
 #pragma unroll
@@ -1138,8 +1147,8 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                 for (int j = 0; j < (RES_EARLY ? FN : 1); ++j) {
                     const int m = min(mrow + i * 16, M - 1), n = ncol + j * 16;
                     const uint16_t *src = epi.residual + (int64_t)m * epi.ldr;
-                    if (VO && n + 3 < N) {
-                        const uint2 v = *reinterpret_cast<const uint2 *>(src + n);
+                    if (VO) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(src + min(n, N - 4));
                         rsd[i][j][0] = v.x; rsd[i][j][1] = v.y;
                     } else {
                         uint32_t e[4];
@@ -1310,8 +1319,8 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                     }
                     const int n = ncol + j * 16;
                     const uint16_t *src = epi.residual + (int64_t)min(m, M - 1) * epi.ldr;
-                    if (VO && n + 3 < N) {
-                        const uint2 v = *reinterpret_cast<const uint2 *>(src + n);
+                    if (VO) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(src + min(n, N - 4));
                         rl[j][0] = v.x; rl[j][1] = v.y;
                     } else {
                         uint32_t e[4];
@@ -1338,7 +1347,8 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                 }
                 if (m >= M) continue;
                 uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
-                if (VO && n + 3 < N) {
+                if (VO) {
+                    if (n >= N) continue;
                     *reinterpret_cast<uint2 *>(dst) = make_uint2(f32x2_to_f16x2(y[0], y[1]),
                                                                  f32x2_to_f16x2(y[2], y[3]));
                 } else {
@@ -1705,16 +1715,17 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = fals
     struct Cand { int kind, bm, bn; double eff, t_stage, fixed; int gran; };
     const Cand pipe_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg}, {2, 128, 256, 0.85, 0, 3e-6, kg},
                                {3, 128, 128, 0.6, 0, 3e-6, kg}, {4, 64, 128, 0.35, 0, 3e-6, kg}};
-    const Cand sp_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg},
+    const Cand sp_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg}, {2, 128, 256, 0.85, 0, 3e-6, kg},
+                             {3, 128, 128, 0.6, 0, 3e-6, kg}, {4, 64, 128, 0.35, 0, 3e-6, kg},
                              {SP_128x128, 128, 128, 0, 0.32e-6, 2.5e-6, 256},
                              {SP_64x128, 64, 128, 0, 0.20e-6, 2.5e-6, 512}};
     const Cand *cands = sp ? sp_cands : pipe_cands;
-    const int ncand = sp ? 3 : 4;
+    const int ncand = sp ? 6 : 4;
     double best_t = 1e30;
     for (int ci = 0; ci < ncand; ++ci) {
         const Cand &c = cands[ci];
         if (c.kind == 4 && !pipe) continue;
-        if (K % c.gran) continue;
+        if (c.kind >= SP_128x128 && K % c.gran) continue;  // whole ring slots only
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         // up to 256 splits: K <= 2^24 then always fits pieces of at most MAX_K_SPLIT k, the most
         // one int32 accumulator of the tile kernels holds
@@ -1856,7 +1867,7 @@ static int launch_sp_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_
         return launch_sp_e<BM, BN, NS, KS, PE_INT32, false>(grid, s, xq, wq, M, N, K, k_split, tm,
                                                             tn, epi, partial);
     // 4-column groups: 8-byte Y / residual accesses and 16-byte weight-scale loads
-    const bool vo = (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
+    const bool vo = (N % 4 == 0) && (epi.ldy % 4 == 0) && ((uintptr_t)epi.Y % 8 == 0) &&
                     ((uintptr_t)epi.w_scale % 16 == 0) &&
                     (epi.mode != W4A4_EPI_RESIDUAL ||
                      (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
@@ -1965,6 +1976,10 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     const bool pipe = q8 || (vec && K % BG_KS == 0);
     GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe, pipe && !q8);
+    // the small-M kernels cover at most SMALL_M rows: a plan without a tile kernel beyond that
+    // would leave rows unwritten, so it is refused loudly (no such plan exists for K <= 2^24)
+    if (p.kind == 0 && M > SMALL_M)
+        return fail(W4A4_ERR_UNSUPPORTED, "no GEMM tile plan for M = %d, N = %d, K = %d", M, N, K);
     if (p.kind == 0) {
         const int mf = (M + 15) / 16;
         // the wide kernel: whole 64-byte windows and at most 2^16 k per wave (4 waves)
