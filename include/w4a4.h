@@ -142,6 +142,25 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
                           int num_steps, int step, uint8_t *xq, float *x_scale, float *xrot_dbg,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Allocation-free variant of w4a4_rotate_quant_act, for callers that cannot allocate device
+ * memory or own a workspace (code under HIP graph capture that may not allocate, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, modes, layouts, outputs and errors as
+ * w4a4_rotate_quant_act without ws / ws_bytes: the scratch it needs (per-token row maxima, the
+ * staged zigzag-ordered rows of large batches) lives in a fixed device array inside the library,
+ * w4a4_noalloc_scratch_bytes() = 16 MiB, one copy per GPU, held until the process ends. A call
+ * whose w4a4_act_workspace_bytes(M, K, block, per_token) exceeds that maximum returns
+ * W4A4_ERR_UNSUPPORTED and launches nothing. The call performs no allocation or free of any kind.
+ * All calls on one GPU share that array and it keeps the last call's contents (everything that
+ * must start at zero is cleared by a kernel of the call): calls that can overlap on one GPU --
+ * on different streams, or from different host threads -- race and must be serialized by the
+ * caller. */
+size_t w4a4_noalloc_scratch_bytes(void);
+int w4a4_rotate_quant_act_noalloc(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                                  const int32_t *perm, const void *rot,
+                                  const float *act_scale_table, int num_steps, int step,
+                                  uint8_t *xq, float *x_scale, float *xrot_dbg,
+                                  hipStream_t stream);
+
 /* Hadamard-only rotation mode: the same runtime call for R_b = H_B (U_b = I), the block Hadamard
  * transform on its own [FoldQuantVLA summary, key change 2: block Hadamard transform with dynamic
  * per-token quantization; gist.science Metodologia 1 names the Hadamard factor of the composite

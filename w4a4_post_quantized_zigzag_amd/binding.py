@@ -33,6 +33,9 @@ SIGNATURES = {
                                    _vp, _sz, _vp]),
     "w4a4_rotate_quant_act_hadamard": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _i, _i, _vp, _vp,
                                             _vp, _vp]),
+    "w4a4_noalloc_scratch_bytes": (_sz, []),
+    "w4a4_rotate_quant_act_noalloc": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp,
+                                           _vp, _vp, _vp]),
     "w4a4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
     "w4a4_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp, _sz, _vp]),
     "w4a4_gemm_i32": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -216,6 +219,23 @@ def rotate_quant_act(X, perm, rot, block: int, table=None, num_steps: int = 0, s
     fn = lib().w4a4_rotate_quant_act if bits == 4 else lib().w4a4_rotate_quant_act_a8
     check(fn(_p(X), _dtype_code(X), M, K, _row_stride(X), block, _p(perm), _p(rot), _p(table),
              num_steps, step, _p(xq), _p(x_scale), _p(xrot_dbg), _p(ws), nb, _stream()))
+    return xq, x_scale
+
+
+def rotate_quant_act_noalloc(X, perm, rot, block: int, table=None, num_steps: int = 0,
+                             step: int = 0, xq=None, x_scale=None, xrot_dbg=None):
+    """rotate_quant_act through the allocation-free entry point (int4 codes; the library's own
+    scratch instead of a workspace). xq and x_scale are allocated here only when not given."""
+    torch = _torch()
+    M, K = X.shape
+    per_token = table is None
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(max(M, 1) if per_token else 1, dtype=torch.float32, device=X.device)
+    check(lib().w4a4_rotate_quant_act_noalloc(_p(X), _dtype_code(X), M, K, _row_stride(X), block,
+                                              _p(perm), _p(rot), _p(table), num_steps, step, _p(xq),
+                                              _p(x_scale), _p(xrot_dbg), _stream()))
     return xq, x_scale
 
 

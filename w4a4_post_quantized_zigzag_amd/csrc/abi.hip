@@ -423,6 +423,65 @@ int w4a4_rotate_quant_act(const void *X, int x_dtype, int M, int K, int64_t ldx,
                     x_scale, xrot_dbg, ws, ws_bytes, stream, false);
 }
 
+// ---- rotate-quantize without allocation: scratch in a file-scope device array ---------------
+//
+// The array is part of the library's code object, so every GPU the library runs on holds its own
+// copy from module load until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is a stand-in symbol, not a device address): the device address is taken
+// once per device with hipGetSymbolAddress, with that device current, and kept per device.
+}  // extern "C"
+
+namespace w4a4 {
+namespace {
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+int scratch_for_current_device(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4A4_ERR_HIP, "scratch: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(W4A4_ERR_UNSUPPORTED, "scratch: device %d beyond %d", dev, NOALLOC_MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(W4A4_ERR_HIP, "scratch: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A4_OK;
+}
+}  // namespace
+}  // namespace w4a4
+
+extern "C" {
+
+size_t w4a4_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+int w4a4_rotate_quant_act_noalloc(const void *X, int x_dtype, int M, int K, int64_t ldx, int block,
+                                  const int32_t *perm, const void *rot,
+                                  const float *act_scale_table, int num_steps, int step,
+                                  uint8_t *xq, float *x_scale, float *xrot_dbg, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_kb(K, block))) return rc;
+    const size_t need = w4a4_act_workspace_bytes(M, K, block, act_scale_table == nullptr);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(W4A4_ERR_UNSUPPORTED,
+                    "rotate-quantize of %d x %d needs %zu scratch bytes, above the %zu-byte maximum "
+                    "of the allocation-free call", M, K, need, NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0 && (rc = scratch_for_current_device(&ws))) return rc;
+    return rq_entry(X, x_dtype, M, K, ldx, block, perm, rot, act_scale_table, num_steps, step, xq,
+                    x_scale, xrot_dbg, ws, need > 0 ? NOALLOC_SCRATCH_BYTES : 0, stream, false);
+}
+
 size_t w4a4_act_f6_workspace_bytes(int M, int K, int block, int per_token)
 {
     if (M <= 0 || K <= 0 || block != 128 || K % block) return 0;
