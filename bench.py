@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA (POP/s x 1000)
+PROFILE_TABLE_ENTRY = 0.5    # per-step scale of every linear in kernel-trace mode
 FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -312,11 +313,13 @@ def setup_per_token_linear(name, bd, inputs):
     return d, lin, [X], [Y], step
 
 
-def setup_stack(bd, inputs, layers=None, w8=()):
+def setup_stack(bd, inputs, layers=None, w8=(), calibrate=True):
     """Synthetic action-head stack (16 layers of QKV -> V slice -> O + residual -> up + GELU -> down
     + residual, M = 1600 tokens, 8 denoising steps): device calibration (zigzag, block SVD, pack,
     per-linear per-step tables from the stacked calibration draws), then one pass = 8 steps x 16
-    layers x 4 linears (W4A4, or W8A8 for the names in w8)."""
+    layers x 4 linears (W4A4, or W8A8 for the names in w8). calibrate=False sets every table entry
+    to PROFILE_TABLE_ENTRY instead of running the calibration chain (for kernel traces that must
+    hold only the pass's launches; no kernel's duration depends on the table's values)."""
     from w4a4_post_quantized_zigzag_amd.stack import DeviceStack
     torch = _torch()
     cfg = inputs.STACK
@@ -329,7 +332,11 @@ def setup_stack(bd, inputs, layers=None, w8=()):
     offline = time.perf_counter() - t0
     del Wl
     t1 = time.perf_counter()
-    ds.calibrate(act["X_calib"])
+    if calibrate:
+        ds.calibrate(act["X_calib"])
+    else:
+        ds.set_tables([{n: np.full(T, PROFILE_TABLE_ENTRY, np.float32) for n in ds.layers[0]}
+                       for _ in ds.layers])
     calib_s = time.perf_counter() - t1
     Xs = [dev(x) for x in act["X_steps"]]
     ds.bufs(M)
@@ -550,14 +557,16 @@ def cpu_baseline_stack(inputs, M=1600):
 
 def stack_headline(bd, inputs, args, result):
     torch = _torch()
-    info, ds, Xs, _, step = setup_stack(bd, inputs)
+    info, ds, Xs, _, step = setup_stack(bd, inputs, calibrate=not args.profile_timed_only)
     M, h, f, T, L = info["M"], info["hidden"], info["ffn"], info["steps"], info["layers"]
-    if args.profile_timed_only:
-        _roctx(True)
     ms = time_graph(step, args.steps, args.warmup)
-    if args.profile_timed_only:
-        _roctx(False)
     ops = T * L * 2.0 * M * (3 * h * h + h * h + f * h + h * f)
+    if args.profile_timed_only:
+        # the trace holds the offline pack and the timed passes only: no calibration chain, no
+        # per-kernel timing graphs, no oracle
+        result.update(value=ops / (ms * 1e-3) / 1e12, ms_per_step=ms,
+                      config={"workload": "action_stack (kernel-trace mode: fixed per-step tables)"})
+        return
     kt = stack_kernel_times(bd, ds, Xs)
     calls = T * L  # launches of each linear's kernels per pass
     # the dominant kernel: the largest total time per pass among the eight per-linear kernels
@@ -612,18 +621,6 @@ def stack_headline(bd, inputs, args, result):
     torch.cuda.empty_cache()
 
 
-_ROCTX = None
-
-
-def _roctx(resume: bool):
-    """Bracket the timed region for `rocprofv3 --selected-regions` (no effect without it)."""
-    global _ROCTX
-    import ctypes
-    if _ROCTX is None:
-        _ROCTX = ctypes.CDLL("/opt/rocm/lib/librocprofiler-sdk-roctx.so")
-    (_ROCTX.roctxProfilerResume if resume else _ROCTX.roctxProfilerPause)(0)
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -632,7 +629,8 @@ def main():
     ap.add_argument("--workload", default="action_stack",
                     choices=["action_stack", "dit_mlp_up", "linear_small"])
     ap.add_argument("--profile-timed-only", action="store_true",
-                    help="mark the timed region for rocprofv3 --selected-regions")
+                    help="kernel-trace mode: fixed per-step tables instead of the calibration "
+                         "chain, and nothing launched after the timed passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-supplementary", action="store_true")
     ap.add_argument("--supp-steps", type=int, default=30)

@@ -226,7 +226,14 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     __shared__ __attribute__((aligned(16))) uint16_t sx[MT * LDSR];
     __shared__ float smax[4][MT];
 
-    const int b = blockIdx.y;
+    // Workgroup -> (row group, block). Workgroups are dealt round-robin to the 8 XCDs, each with
+    // its own L2; consecutive workgroups of one XCD take the blocks of one row group, so a row
+    // (whose zigzag gather spreads every block's channels over the whole row) is fetched into one
+    // XCD's L2 only, not into all eight.
+    const int nb = K / B, T = gridDim.x;
+    const int per_x = T / 8, rm = T % 8, xcd = blockIdx.x % 8;
+    const int lin = xcd * per_x + min(xcd, rm) + blockIdx.x / 8;
+    const int b = lin % nb, rg = lin / nb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int jbase = wave * JW;
@@ -246,10 +253,10 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
         const StepScale ss = step_scale(table, step + b * gstride);
         s_step = ss.s;
         rcp_step = ss.rcp;
-        if (blockIdx.x == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s_step;
+        if (rg == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s_step;
     }
 
-    const int row_begin = blockIdx.x * rows_per_wg;
+    const int row_begin = rg * rows_per_wg;
     const int row_end = min(M, row_begin + rows_per_wg);
 
     // Tile staging, prefetched one tile ahead into registers. Loads are unconditional from clamped
@@ -1143,7 +1150,7 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         return check_launch("rotate-quantize (few tokens)");
     }
     const int rpw = rq_rows_per_wg(M, nb);
-    dim3 grid((M + rpw - 1) / rpw, nb);
+    dim3 grid(((M + rpw - 1) / rpw) * nb);  // (row group, block) pairs, XCD-aware in the kernel
     const uint16_t *src = xperm ? xperm : reinterpret_cast<const uint16_t *>(X);
     const int64_t ld = xperm ? K : ldx;
     // contiguous 16-byte tile loads need 16-byte aligned rows; otherwise gather element-wise

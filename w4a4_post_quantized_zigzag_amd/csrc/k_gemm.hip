@@ -23,6 +23,33 @@ constexpr int SMALL_M = 64;           // rows up to which the weight-streaming k
 // tile kinds of the software-pipelined GEMM (k_gemm_sp) in the GEMM plan
 enum SpKind { SP_128x192 = 11, SP_128x128 = 12, SP_64x128 = 13 };
 
+// Tile order of the tiled GEMM kernels. Dispatch id i runs on XCD i % 8, and XCD x takes a
+// contiguous 1/8 of the order. The order walks bands of `band` column tiles, row-major inside a
+// band, so the tiles of one XCD form a compact block: its L2 holds a few activation row tiles and a
+// few weight column tiles, each read by several of its workgroups (band = 1 is column-major: one
+// XCD then reads every activation row tile once, all from the last-level cache or HBM).
+__device__ __forceinline__ void xcd_tile(int id, int tiles_m, int tiles_n, int band, int &tm,
+                                         int &tn)
+{
+    const int T = tiles_m * tiles_n;
+    const int per_x = T / 8, rm = T % 8, x = id % 8;
+    const int lin = x * per_x + min(x, rm) + id / 8;
+    const int b = lin / (band * tiles_m);
+    const int w = min(band, tiles_n - b * band);  // the last band may be narrower
+    const int r = lin - b * band * tiles_m;
+    tm = r / w;
+    tn = b * band + r % w;
+}
+
+// Band width that minimizes the operand bytes one XCD's block of tiles touches: about
+// rows * bm + band * bn per k, with rows * band = its share of the tiles.
+static int tile_band(int tiles_m, int tiles_n, int bm, int bn)
+{
+    const double per_x = (double)tiles_m * (double)tiles_n / 8.0;
+    const int g = (int)std::lround(std::sqrt(per_x * (double)bm / (double)bn));
+    return std::max(1, std::min(g, tiles_n));
+}
+
 __device__ __forceinline__ void widen16(const uint4 &p, uint4 &lo, uint4 &hi)
 {
     // 16 packed bytes (k = 0..31 of a half step) -> 32 int8 values, two dwords per packed dword
@@ -762,7 +789,8 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC
           bool GS = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
-    int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
+    int k_split, int tiles_m, int tiles_n, int band, GemmEpilogue epi,
+    int32_t *__restrict__ partial)
 {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -774,11 +802,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     static_assert(QA * 1024 * NW == A_BYTES && QB * 1024 * NW == B_BYTES, "whole KB per wave");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-    const int T = tiles_m * tiles_n;
-    const int id = blockIdx.x;
-    const int per_x = T / 8, rm = T % 8, x = id % 8;
-    const int lin = x * per_x + min(x, rm) + id / 8;
-    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    int tm, tn;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, band, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1082,6 +1107,7 @@ template <int BM, int BN, int NS, int KS, int PE, bool VO>
 __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                                                  const uint8_t *__restrict__ wq, int M, int N,
                                                  int K, int k_split, int tiles_m, int tiles_n,
+                                                 int band,
                                                  GemmEpilogue epi, int32_t *__restrict__ partial)
 {
     constexpr int NC = 4;  // column waves per k group
@@ -1100,11 +1126,8 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
     static_assert((size_t)BM * BN * 4 <= (size_t)NS * SLOT, "partial sums fit in the ring");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-    const int T = tiles_m * tiles_n;
-    const int id = blockIdx.x;
-    const int per_x = T / 8, rm = T % 8, x = id % 8;
-    const int lin = x * per_x + min(x, rm) + id / 8;
-    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    int tm, tn;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, band, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1484,7 +1507,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_f6(
     const uint8_t *__restrict__ xf, const uint8_t *__restrict__ wf, int M, int N, int K,
-    int k_split, int tiles_m, int tiles_n, GemmEpilogue epi, int32_t *__restrict__ partial)
+    int k_split, int tiles_m, int tiles_n, int band, GemmEpilogue epi,
+    int32_t *__restrict__ partial)
 {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -1498,11 +1522,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_f6(
     static_assert(Q * NW == NI, "whole DMA instructions per wave");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-    const int T = tiles_m * tiles_n;
-    const int id = blockIdx.x;
-    const int per_x = T / 8, rm = T % 8, x = id % 8;
-    const int lin = x * per_x + min(x, rm) + id / 8;
-    const int tn = lin / tiles_m, tm = lin % tiles_m;
+    int tm, tn;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, band, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1705,21 +1726,32 @@ struct GemmPlan {
 // units (one workgroup per unit) times the per-tile time, plus the write and read of split-K
 // partials. kg is the k granularity of a stage (128 for packed int4, 64 for int8 operands); sp
 // allows the software-pipelined kernel, whose per-stage times were measured on MI355X.
-static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = false)
+static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = false,
+                          bool gelu = false)
 {
     GemmPlan best{0, 0, 16, 1, K};
     if (M <= SMALL_M) return best;
-    // eff: fraction of the MFMA rate in the main loop; t_stage: measured seconds per 128-k stage
-    // (0 = use eff); fixed: launch ramp, first loads and epilogue of a round
-    // gran: k granularity of the kernel's ring (a k split must be a whole number of it)
-    struct Cand { int kind, bm, bn; double eff, t_stage, fixed; int gran; };
-    const Cand pipe_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg}, {2, 128, 256, 0.85, 0, 3e-6, kg},
-                               {3, 128, 128, 0.6, 0, 3e-6, kg}, {4, 64, 128, 0.35, 0, 3e-6, kg}};
-    const Cand sp_cands[] = {{1, 256, 256, 1.0, 0, 3e-6, kg}, {2, 128, 256, 0.85, 0, 3e-6, kg},
-                             {3, 128, 128, 0.6, 0, 3e-6, kg}, {4, 64, 128, 0.35, 0, 3e-6, kg},
-                             {SP_128x128, 128, 128, 0, 0.32e-6, 2.5e-6, 256},
-                             {SP_64x128, 64, 128, 0, 0.20e-6, 2.5e-6, 512}};
-    const Cand *cands = sp ? sp_cands : pipe_cands;
+    // Per tile kind, times measured on MI355X (microseconds; tile sweeps over the 1600-token stack
+    // linears and the prefill and long-K projections):
+    //   f     launch, first operand loads and epilogue of one workgroup
+    //   s     one 128-k stage of one workgroup alone on its CU
+    //   beta  slowdown of each stage per extra workgroup sharing the CU (occ > 1: co-resident
+    //         workgroups overlap one another's loads, epilogues and matrix work)
+    //   e     each further round of workgroups on a CU
+    //   occ   workgroups one CU holds at once (LDS and registers)
+    //   gran  k granularity of the ring (a k split is a whole number of it)
+    // Per CU: w = ceil(tiles * splits / 256) workgroups, co = min(w, occ) of them at once:
+    //   t = f + stages * s * (1 + beta (co - 1)) * w / co + (ceil(w / occ) - 1) e
+    // plus, for the GELU epilogue, its VALU time per output a thread owns (exposed once per
+    // workgroup when it runs alone on its CU, co times when co workgroups finish together), and
+    // for a K split the int32 partials written and read back plus the reduction launch.
+    struct Cand { int kind, bm, bn, threads, occ; double f, s, beta, e; int gran; };
+    const Cand cands[] = {{1, 256, 256, 512, 1, 3.7, 1.79, 0.0, 3.0, kg},
+                          {2, 128, 256, 512, 1, 6.0, 1.01, 0.0, 3.0, kg},
+                          {3, 128, 128, 256, 2, 4.6, 0.61, 0.68, 3.0, kg},
+                          {4, 64, 128, 256, 3, 3.9, 0.49, 0.57, 3.0, kg},
+                          {SP_128x128, 128, 128, 512, 1, 6.96, 0.58, 0.0, 2.95, 256},
+                          {SP_64x128, 64, 128, 512, 1, 5.3, 0.2875, 0.0, 3.05, 512}};
     const int ncand = sp ? 6 : 4;
     double best_t = 1e30;
     for (int ci = 0; ci < ncand; ++ci) {
@@ -1736,13 +1768,18 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = fals
             const int real_splits = (K + k_split - 1) / k_split;
             if (real_splits != splits) continue;
             if (splits > 1 && k_split < 1024) continue;
-            const double rounds = std::ceil(tiles * splits / 256.0);
-            const double per_tile = c.t_stage > 0
-                                        ? (k_split / (double)BG_KS) * c.t_stage
-                                        : 2.0 * c.bm * c.bn * k_split / (8192.0 * 2.4e9 * c.eff);
-            const double t_c = rounds * (per_tile + c.fixed);
-            const double t_r = splits > 1 ? (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 4e12 + 3e-6 : 0.0;
-            const double t = t_c + t_r;
+            const double stages = k_split / (double)BG_KS;
+            const double w = std::ceil(tiles * splits / 256.0);
+            const double co = std::min(w, (double)c.occ);
+            double t = c.f + stages * c.s * (1.0 + c.beta * (co - 1.0)) * w / co +
+                       (std::ceil(w / c.occ) - 1.0) * c.e;
+            if (gelu) {
+                const double per_thread = (double)c.bm * c.bn / c.threads;
+                t += c.occ == 1 ? 0.065 * per_thread
+                                : 0.031 * per_thread * (w <= c.occ ? co : 1.0);
+            }
+            if (splits > 1)
+                t += (2.0 * splits * M * (double)N * 4 + M * (double)N * 2) / 5e12 * 1e6 + 2.0;
             if (t < best_t * 0.98) {
                 best_t = t;
                 best = GemmPlan{c.kind, c.bm, c.bn, splits, k_split};
@@ -1757,11 +1794,13 @@ size_t gemm_workspace(int M, int N, int K, bool q8)
     // the launch plans with or without the pipelined kernel (operand alignment decides): enough
     // for either
     size_t need = 0;
-    for (int pipe = 0; pipe < 3; ++pipe) {
-        GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe != 0, pipe == 2 && !q8);
-        if (p.splits > 1)
-            need = std::max(need, (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t));
-    }
+    for (int pipe = 0; pipe < 3; ++pipe)
+        for (int gelu = 0; gelu < 2; ++gelu) {
+            GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe != 0, pipe == 2 && !q8,
+                                   gelu != 0);
+            if (p.splits > 1)
+                need = std::max(need, (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t));
+        }
     return need;
 }
 
@@ -1793,7 +1832,8 @@ static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
     const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>), grid,
-                       dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+                       dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn,
+                       tile_band(tm, tn, BM, BN), epi, partial);
     return W4A4_OK;
 }
 
@@ -1854,7 +1894,7 @@ static int launch_sp_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_
     const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO>), grid, dim3(512), lds, s, xq, wq, M, N,
-                       K, k_split, tm, tn, epi, partial);
+                       K, k_split, tm, tn, tile_band(tm, tn, BM, BN), epi, partial);
     return W4A4_OK;
 }
 
@@ -1975,7 +2015,8 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     const bool pipe = q8 || (vec && K % BG_KS == 0);
-    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe, pipe && !q8);
+    GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe, pipe && !q8,
+                           epi.mode == W4A4_EPI_GELU);
     // the small-M kernels cover at most SMALL_M rows: a plan without a tile kernel beyond that
     // would leave rows unwritten, so it is refused loudly (no such plan exists for K <= 2^24)
     if (p.kind == 0 && M > SMALL_M)
@@ -2096,7 +2137,7 @@ static int launch_f6_e(dim3 grid, hipStream_t s, const uint8_t *xf, const uint8_
     const void *fn = (const void *)k_gemm_f6<BM, BN, WM, WN, NS, PE, VO>;
     if (int rc = ensure_dynamic_lds(fn, lds, "fp6 gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_f6<BM, BN, WM, WN, NS, PE, VO>), grid, dim3(64 * WM * WN), lds, s,
-                       xf, wf, M, N, K, k_split, tm, tn, epi, partial);
+                       xf, wf, M, N, K, k_split, tm, tn, tile_band(tm, tn, BM, BN), epi, partial);
     return W4A4_OK;
 }
 
