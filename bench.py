@@ -471,34 +471,51 @@ STACK_LINEAR_SHAPES = (("qkv", "N=3072, K=1024"), ("o", "N=1024, K=1024"), ("up"
 
 
 def stack_kernel_times(bd, ds, Xs, reps=30):
-    """Average launch duration (ms) of each linear's rotate-quantize and GEMM call in the stack, on
-    the stack's own buffers (layer 0, step 0), each from a HIP graph of back-to-back launches timed
-    with HIP events on the launch stream."""
+    """Average launch duration (ms) of each linear's calls in the stack pass, on the stack's own
+    buffers (layer 0, step 0), each from a HIP graph of back-to-back launches timed with HIP events
+    on the launch stream. Where the pass fuses the next linear's rotate-quantize into a GEMM (QKV
+    produces O's codes, up produces down's), that linear's GEMM entry is the fused call and the
+    consumer has no rotate-quantize of its own (None)."""
     bufs = ds.bufs(Xs[0].shape[0])
     lay = ds.layers[0]
     h = ds.h
-    wiring = {"qkv": (Xs[0], bufs.qkv, bd.EPI_NONE, None, False),
-              "o": (bufs.qkv[:, 2 * h:3 * h], bufs.h2, bd.EPI_RESIDUAL, Xs[0], ds.fold),
-              "up": (bufs.h2, bufs.g, bd.EPI_GELU, None, False),
-              "down": (bufs.g, bufs.hs[0], bd.EPI_RESIDUAL, bufs.h2, ds.fold)}
+    fused = ds.fold and all(lay[n].bits == 4 for n in ("qkv", "o", "up", "down"))
+    wiring = {"qkv": (Xs[0], bufs.qkv, bd.EPI_NONE, None, False, "o", 2 * h),
+              "o": (bufs.qkv[:, 2 * h:3 * h], bufs.h2, bd.EPI_RESIDUAL, Xs[0], ds.fold, None, 0),
+              "up": (bufs.h2, bufs.g, bd.EPI_GELU, None, False, "down", 0),
+              "down": (bufs.g, bufs.hs[0], bd.EPI_RESIDUAL, bufs.h2, ds.fold, None, 0)}
     out = {}
-    for name, (X, Y, epi, res, in_order) in wiring.items():
+    for name, (X, Y, epi, res, in_order, nxt, col0) in wiring.items():
         lin = lay[name]
         perm = None if in_order else lin.perm
-        xq = bufs.xq[(lin.K, 4)]
+        pre = fused and name in ("o", "down")
+        xq = bufs.xqn[lin.K] if pre else bufs.xq[(lin.K, 4)]
+        xs = bufs.xsn if pre else bufs.xs
 
         def rq(X=X, lin=lin, perm=perm, xq=xq):
             bd.rotate_quant_act(X, perm, lin.rot, ds.block, lin.table, ds.steps, 0, xq=xq,
                                 x_scale=bufs.xs, ws=bufs.ws[lin.K])
 
-        def gm(lin=lin, xq=xq, Y=Y, epi=epi, res=res):
-            bd.gemm(xq, bufs.xs, False, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
-                    residual=res, ws=bufs.gws[(lin.N, lin.K, 4)])
+        if fused and nxt is not None:
+            nl = lay[nxt]
 
-        rq()
+            def gm(lin=lin, xq=xq, Y=Y, epi=epi, res=res, nl=nl, col0=col0):
+                bd.gemm_rq_next(xq, bufs.xs, False, lin.wq, lin.w_scale, lin.K, col0, nl.K,
+                                ds.block, nl.rot, nl.table, ds.steps, 0, Y=Y, epilogue=epi,
+                                residual=res, xq_next=bufs.xqn[nl.K], x_scale_next=bufs.xsn,
+                                ws=bufs.fws[(lin.N, lin.K, nl.K)])
+        else:
+            def gm(lin=lin, xq=xq, xs=xs, Y=Y, epi=epi, res=res):
+                bd.gemm(xq, xs, False, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
+                        residual=res, ws=bufs.gws[(lin.N, lin.K, 4)])
+
+        if not pre:
+            rq()
         gm()
-        out[name] = {"N": lin.N, "K": lin.K, "rotate_quant_ms": time_kernel_calls([rq], reps),
-                     "gemm_ms": time_kernel_calls([gm], reps)}
+        out[name] = {"N": lin.N, "K": lin.K,
+                     "rotate_quant_ms": None if pre else time_kernel_calls([rq], reps),
+                     "gemm_ms": time_kernel_calls([gm], reps),
+                     "gemm_fuses_rotate_quant_of": nxt if fused else None}
     return out
 
 
@@ -573,13 +590,17 @@ def stack_headline(bd, inputs, args, result):
     totals = {}
     for name, d in kt.items():
         totals[(name, "gemm")] = d["gemm_ms"] * calls
-        totals[(name, "rotate_quant")] = d["rotate_quant_ms"] * calls
+        if d["rotate_quant_ms"] is not None:
+            totals[(name, "rotate_quant")] = d["rotate_quant_ms"] * calls
     (dn, dk) = max(totals, key=totals.get)
     d = kt[dn]
     if dk == "gemm":
         op = 2.0 * M * d["N"] * d["K"]
         ach = op / (d["gemm_ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": f"{dn} GEMM ({M}x{d['N']}x{d['K']}, int8 MFMA)",
+        also = d.get("gemm_fuses_rotate_quant_of")
+        kname = f"{dn} GEMM ({M}x{d['N']}x{d['K']}, int8 MFMA)" + (
+            f", with {also}'s rotate-quantize in its epilogue" if also else "")
+        roof = {"bound": "mfma", "kernel": kname,
                 "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                 "frac": ach / INT8_PEAK_TOPS,
                 "traffic": traffic_from_profile("k_gemm.hip", f"action_stack_{dn}_gemm"),
@@ -598,9 +619,14 @@ def stack_headline(bd, inputs, args, result):
         kernels[name] = {"gemm_us": d["gemm_ms"] * 1e3,
                          "gemm_tops": op / (d["gemm_ms"] * 1e-3) / 1e12,
                          "gemm_frac_int8_peak": op / (d["gemm_ms"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
-                         "rotate_quant_us": d["rotate_quant_ms"] * 1e3,
-                         "rotate_quant_gbps": by / (d["rotate_quant_ms"] * 1e-3) / 1e9,
-                         "rotate_quant_frac_hbm": by / (d["rotate_quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                         "gemm_fuses_rotate_quant_of": d["gemm_fuses_rotate_quant_of"]}
+        if d["rotate_quant_ms"] is not None:
+            kernels[name].update(
+                rotate_quant_us=d["rotate_quant_ms"] * 1e3,
+                rotate_quant_gbps=by / (d["rotate_quant_ms"] * 1e-3) / 1e9,
+                rotate_quant_frac_hbm=by / (d["rotate_quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+        else:
+            kernels[name]["rotate_quant_us"] = "in the producing GEMM's epilogue"
     result.update(
         value=ops / (ms * 1e-3) / 1e12, ms_per_step=ms,
         config={"workload": f"action_stack: {L} layers x {T} denoising steps, M = {M} tokens "

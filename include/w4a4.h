@@ -188,6 +188,30 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
               const float *w_scale, int M, int N, int K, uint16_t *Y, int64_t ldy, int epilogue,
               const uint16_t *residual, int64_t ldr, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The GEMM above followed by the next linear's per-step rotate-quantize of part of its output:
+ * the columns [col0, col0 + K_next) of Y, which the caller has arranged to hold the next linear's
+ * input already in that linear's zigzag order (its perm folded into this linear's weight rows
+ * offline), become the next linear's packed int4 codes xq_next [M][K_next / 2] and its scale
+ * x_scale_next[0] = act_scale_table_next[step], exactly as
+ *   w4a4_rotate_quant_act(Y + col0, W4A4_F16, M, K_next, ldy, block_next, NULL, rot_next,
+ *                         table_next, num_steps, step, xq_next, x_scale_next, NULL, ...)
+ * would give them after this GEMM [gist.science summary, "Metodologia" 1: rotate, then quantize the
+ * next layer's input; vnrobo.com "Y tuong paper": the step's scale is a table lookup]. Y is still
+ * written in full. With block_next 128 and a 128-column tile plan (M above 64, no K split, 16-byte
+ * aligned rows) the rotation and quantization run in the GEMM's epilogue on the finished fp16 tile,
+ * with the same arithmetic as the standalone call, so the codes are identical bit for bit; any other
+ * case runs the standalone call on the same stream after the GEMM. Arguments and errors as
+ * w4a4_gemm and w4a4_rotate_quant_act (per-step scale only: table_next is required); every argument
+ * is checked before anything is launched. ws: w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next,
+ * block_next) bytes, 256-byte aligned. */
+size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int block_next);
+int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
+                      const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
+                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
+                      int K_next, int block_next, const void *rot_next, const float *table_next,
+                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
 /* Test hook: the raw int32 accumulators acc [M][N] (row-major, dense) of the same integer GEMM. */
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,
                   void *ws, size_t ws_bytes, hipStream_t stream);

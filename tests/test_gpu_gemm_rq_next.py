@@ -1,0 +1,129 @@
+"""GPU parity of w4a4_gemm_rq_next: the W4A4 GEMM followed by the next linear's per-step
+rotate-quantize of a column range of its output, through the C ABI.
+
+The contract is "w4a4_gemm, then w4a4_rotate_quant_act on Y[:, col0:col0+K_next] with perm = NULL"
+(the columns already hold the next linear's input in its zigzag order). So, on every case:
+  - Y equals w4a4_gemm's output bit for bit;
+  - the codes and the scale equal the standalone rotate-quantize of the device's own Y slice bit for
+    bit (the fused epilogue runs the streaming kernel's arithmetic in the same order; the fallback
+    runs the standalone call itself), and the standalone call is pinned to the oracle's quantizer by
+    the quantize-stage tests;
+  - on one shape the codes are also compared with the oracle's fp64 rotate-quantize of that slice
+    directly (certified near-tie flips only).
+Cases cover the two stack shapes that use the fused epilogue (QKV feeding O through its V columns,
+the up-projection with GELU feeding down), a ragged row count with the residual epilogue, shapes
+that take the fallback (few tokens, block 64, a K split), the empty call and the argument errors.
+
+Pages: gist.science (pt) "Metodologia" 1 (rotation of each linear's input before quantization) and 2
+(per-step scale looked up from the table).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.reference import EPI_GELU, EPI_NONE, EPI_RESIDUAL
+from w4a4_post_quantized_zigzag_amd import binding as bd
+
+from parity_util import compare_codes, dev, host, rotation_error_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(M, N, K, K_next, B, epi, seed):
+    torch = __import__("torch")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    xq = dev(rng.integers(0, 256, (M, K // 2), dtype=np.uint8))
+    wq = dev(rng.integers(0, 256, (N, K // 2), dtype=np.uint8))
+    xs = dev(np.array([0.02], np.float32))
+    ws = dev(rng.uniform(0.5, 1.5, N).astype(np.float32) * np.float32(0.02 / np.sqrt(K)))
+    res = dev(rng.standard_normal((M, N)).astype(np.float16)) if epi == EPI_RESIDUAL else None
+    Wn = rng.normal(0.0, 0.02, (64, K_next))
+    perm_n = oracle.zigzag_perm(Wn, B)
+    U_n = oracle.block_svd(Wn, perm_n, B)
+    _, _, rot_n = bd.pack_weights(dev(np.zeros((1, K_next), np.float32)), dev(perm_n), dev(U_n), B)
+    # per-step scales: the largest per-token scale of the slice at step 0, a quarter of it at step 1
+    Y0 = bd.gemm(xq, xs, False, wq, ws, K, epilogue=epi, residual=res)
+    return dict(xq=xq, wq=wq, xs=xs, ws=ws, res=res, rot=rot_n, U=U_n, Y0=Y0, torch=torch)
+
+
+def _table_for(d, col0, K_next, B):
+    _, s_tok = bd.rotate_quant_act(d["Y0"][:, col0:col0 + K_next], None, d["rot"], B)
+    smax = float(host(s_tok).max())
+    return dev(np.array([smax, smax / 4], np.float32))
+
+
+def _same(a, b):
+    return np.array_equal(host(a).view(np.uint8), host(b).view(np.uint8))
+
+
+CASES = {
+    # name: (M, N, K, col0, K_next, block, epilogue)
+    "qkv_to_o": (1600, 3072, 1024, 2048, 1024, 128, EPI_NONE),
+    "up_to_down_gelu": (1600, 4096, 1024, 0, 4096, 128, EPI_GELU),
+    "ragged_residual": (333, 768, 512, 256, 512, 128, EPI_RESIDUAL),
+    "rows_130_mid_cols": (130, 512, 256, 128, 256, 128, EPI_NONE),
+    "few_tokens_fallback": (50, 1024, 1024, 0, 1024, 128, EPI_GELU),
+    "block64_fallback": (300, 512, 512, 0, 512, 64, EPI_NONE),
+    "k_split_fallback": (260, 256, 16384, 0, 256, 128, EPI_NONE),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_gemm_rq_next_matches_gemm_then_rotate_quantize(name):
+    M, N, K, col0, K_next, B, epi = CASES[name]
+    d = _case(M, N, K, K_next, B, epi, 11 + list(CASES).index(name))
+    table = _table_for(d, col0, K_next, B)
+    for step in (0, 1):
+        Y, q, s = bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], K, col0, K_next, B,
+                                  d["rot"], table, 2, step, epilogue=epi, residual=d["res"])
+        assert _same(Y, d["Y0"]), (name, step)
+        q_ref, s_ref = bd.rotate_quant_act(d["Y0"][:, col0:col0 + K_next], None, d["rot"], B,
+                                           table, 2, step)
+        assert _same(s, s_ref), (name, step)
+        qa, qb = host(q), host(q_ref)
+        if not np.array_equal(qa, qb):
+            bad = np.argwhere(qa != qb)[:5]
+            raise AssertionError(f"{name} step {step}: {int((qa != qb).sum())} code bytes differ, "
+                                 f"e.g. {bad.tolist()}")
+
+
+def test_gemm_rq_next_codes_against_the_oracle():
+    M, N, K, col0, K_next, B, epi = 200, 1024, 512, 512, 512, 128, EPI_NONE
+    d = _case(M, N, K, K_next, B, epi, 7)
+    table = _table_for(d, col0, K_next, B)
+    Y, q, s = bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], K, col0, K_next, B,
+                              d["rot"], table, 2, 0)
+    Xs = host(Y)[:, col0:col0 + K_next].astype(np.float64)
+    ident = np.arange(K_next, dtype=np.int32)
+    tab = host(table)
+    ref = oracle.rotate_quant_act(Xs, ident, d["U"], B, "per_step", tab, 2, 0)
+    assert host(s)[0] == tab[0]
+    q_dev = oracle.unpack_int4(host(q), K_next)
+    eps = rotation_error_bound(Xs, ident, oracle.rotation(d["U"], B), B)
+    flips = compare_codes(q_dev, ref["codes"], ref["v"], ref["x_rot"], eps,
+                          np.full(M, host(s)[0]), ref["scale"], False)
+    assert flips <= max(3, q_dev.size * 1e-4), flips
+
+
+def test_gemm_rq_next_empty_and_errors():
+    torch = __import__("torch")
+    d = _case(130, 512, 256, 256, 128, EPI_NONE, 3)
+    table = dev(np.array([0.1, 0.2], np.float32))
+    # M = 0: nothing to do, no error
+    e = torch.empty((0, 128), dtype=torch.uint8, device="cuda")
+    Y0 = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    bd.gemm_rq_next(e, d["xs"], False, d["wq"], d["ws"], 256, 0, 256, 128, d["rot"], table, 2, 0,
+                    Y=Y0)
+    bad = [
+        (dict(col0=384, K_next=256), bd.W4A4_ERR_SHAPE),      # columns past N
+        (dict(col0=0, K_next=200), bd.W4A4_ERR_SHAPE),        # not a multiple of the block
+        (dict(step=2), bd.W4A4_ERR_STEP_RANGE),               # step outside the table
+        (dict(table=None), bd.W4A4_ERR_ARG),                  # per-step scale is required
+    ]
+    for kw, code in bad:
+        args = dict(col0=0, K_next=256, step=0, table=table)
+        args.update(kw)
+        with pytest.raises(bd.W4A4Error) as ei:
+            bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], 256, args["col0"],
+                            args["K_next"], 128, d["rot"], args["table"], 2, args["step"])
+        assert ei.value.status == code, (kw, ei.value)

@@ -7,7 +7,7 @@
 // taken in fp32.
 #include <cmath>
 
-#include "w4a4_internal.h"
+#include "rq_core.h"
 
 namespace w4a4 {
 
@@ -23,20 +23,6 @@ int launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t s)
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, p, value,
                        count);
     return check_launch("fill");
-}
-
-// A per-step table entry and its reciprocal fp32(1/s). Only a positive finite entry is a scale.
-// Any other entry (zero, negative, infinite or NaN: an uncalibrated or damaged table) yields the
-// scale NaN and the reciprocal 0, so every code becomes 0 and every output of the GEMM that
-// consumes them is NaN: the failure shows in the result instead of a plausible-looking value.
-struct StepScale {
-    float s, rcp;
-};
-__device__ __forceinline__ StepScale step_scale(const float *table, int idx)
-{
-    const float s = table[idx];
-    if (s > 0.0f && s <= 3.402823466e38f) return StepScale{s, (float)(1.0 / (double)s)};
-    return StepScale{__builtin_nanf(""), 0.0f};
 }
 
 // fp32(max / qmax) divided in fp64 (exactly the fp32 quotient, the double rounding being innocuous
@@ -205,9 +191,6 @@ int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B
 // fp16 parts, R ~= hi + lo * 2^-12: fp16 x fp16 products are exact in fp32, so the result carries
 // fp32 accumulation error plus ~2^-22 relative from the split. Each wave keeps the R_b^T fragments
 // of its B/4 output channels in registers and reuses them over all row tiles of the workgroup.
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int MT = 64;  // token rows per tile
 
 template <int MODE, int B, bool GATHER, bool Q8>
@@ -427,34 +410,6 @@ __device__ __forceinline__ void rq_wait_vmcnt(int n)
     }
 }
 
-// Four rotated values held as acc = 2^12 x' -> four int4 codes packed low nibble first in the low
-// 16 bits (the bits above are garbage). rs = 2^-12 * fp32(1/s), so acc * rs is the fp32 product
-// x' * fp32(1/s) rounded once (both power-of-two scalings are exact for any x' and 1/s that can
-// give a nonzero code). Adding 1.5 * 2^23 rounds that product to an integer, ties to even, and
-// leaves the integer in the low mantissa bits; the clamp to [-8, 7] is applied in that form and
-// the two's-complement nibble is read off the bit pattern.
-// Q8: int8 codes, clamp to [-128, 127] and one byte per code (four bytes returned).
-template <bool Q8 = false>
-__device__ __forceinline__ uint32_t quant_pack4(v4f acc, float rs)
-{
-#pragma clang fp contract(off)
-    constexpr float MAGIC = 12582912.0f;
-    constexpr float LOQ = Q8 ? -128.0f : -8.0f, HIQ = Q8 ? 127.0f : 7.0f;
-    uint32_t n[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float y = acc[i] * rs;
-        float f = y + MAGIC;
-        f = fminf(fmaxf(f, MAGIC + LOQ), MAGIC + HIQ);
-        n[i] = __float_as_uint(f);
-    }
-    if (Q8)
-        return (n[0] & 0xFFu) | ((n[1] & 0xFFu) << 8) | ((n[2] & 0xFFu) << 16) | (n[3] << 24);
-    uint32_t t = (n[0] & 0xFu) | ((n[1] << 4) & ~0xFu);
-    t = (t & 0xFFu) | ((n[2] << 8) & ~0xFFu);
-    return (t & 0xFFFu) | ((n[3] << 12) & ~0xFFFu);
-}
-
 // F6: the codes go out in the FP6 operand layout of the FP6 GEMM instead of packed int4 (B = 128,
 // so a rotation block is one 128-k stage of that layout: xq is the operand, stage b its block b).
 template <int MODE, int B, bool DBG, bool Q8, bool F6 = false>
@@ -531,17 +486,9 @@ __global__ __launch_bounds__(256) void k_rq_ring(
             if (b == 0) x_scale[row_begin + i] = s;
         }
     }
-    // R_b^T fragments of this wave's output channels; the high part is scaled by 2^12 (exact, as
-    // |R| <= 1) so that x.hi and x.lo accumulate in one fp32 accumulator at the same scale
+    // R_b^T fragments of this wave's output channels (high part pre-scaled by 2^12)
     v8h ahi[JF][KK], alo[JF][KK];
-#pragma unroll
-    for (int jf = 0; jf < JF; ++jf)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int64_t off = rot16_fragment(b, jbase / 16 + jf, kk, lane, B);
-            ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off) * (_Float16)(1 << ROT_LO_SHIFT);
-            alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
-        }
+    load_rot_frags<JF, KK>(rhi, rlo, b, jbase, lane, B, ahi, alo);
     float rs_step = 0.0f;
     if (MODE == ACT_PER_STEP) {
         const StepScale ss = step_scale(table, step + b * gstride);
@@ -563,30 +510,11 @@ __global__ __launch_bounds__(256) void k_rq_ring(
         // acc[mf][jf] = 2^12 x' for tokens mf*16 + (lane % 16), channels jbase + 16 jf + 4 (lane / 16)
         // + 0..3; consecutive MFMAs go to different accumulators
         v4f acc[MF][JF];
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-            for (int jf = 0; jf < JF; ++jf) acc[mf][jf] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            v8h xb[MF];
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf) {
-                const int row = mf * 16 + r;
-                const int c = (4 * kk + g) ^ (row % CPR);
-                xb[mf] = *reinterpret_cast<const v8h *>(&tile[row * ROWB + 16 * c]);
-            }
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-                for (int jf = 0; jf < JF; ++jf)
-                    acc[mf][jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jf][kk], xb[mf], acc[mf][jf], 0, 0, 0);
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-                for (int jf = 0; jf < JF; ++jf)
-                    acc[mf][jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jf][kk], xb[mf], acc[mf][jf], 0, 0, 0);
-        }
+        rotate_acc<MF, JF, KK>(ahi, alo, [&](int mf, int kk) {
+            const int row = mf * 16 + r;
+            const int c = (4 * kk + g) ^ (row % CPR);
+            return *reinterpret_cast<const v8h *>(&tile[row * ROWB + 16 * c]);
+        }, acc);
 
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) {

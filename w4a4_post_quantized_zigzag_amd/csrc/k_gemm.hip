@@ -12,7 +12,7 @@
 #include <cmath>
 #include <type_traits>
 
-#include "w4a4_internal.h"
+#include "rq_core.h"
 
 namespace w4a4 {
 
@@ -786,7 +786,7 @@ enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_
 // operand (one v_mfma_i32_16x16x64_i8 per fragment pair and stage, no widening) and the sums are
 // not scaled by 256.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT, bool Q8,
-          bool GS = false>
+          bool GS = false, bool RQN = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
     int k_split, int tiles_m, int tiles_n, int band, GemmEpilogue epi,
@@ -976,6 +976,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         constexpr int CPR = BN / 8;      // 16-byte chunks per tile row
         constexpr int NT = NW * 64;
         const int rows_here = min(BM, M - m0), cols_here = min(BN, N - n0);
+        // RQN: when this tile's 128 columns are rotation block rb of the next linear's input, the
+        // finished fp16 tile is rotated and quantized here as well. The fragments of R_rb and the
+        // step scale are loaded first, so their latency hides under the dequantization.
+        static_assert(!RQN || (BN == 128 && 128 % (NW * 16) == 0 && !Q8 && !GS),
+                      "fused rotate-quantize: 128-column int4 tiles");
+        constexpr int RJF = RQN ? 128 / (NW * 16) : 1;  // 16-channel fragments of R per wave
+        const bool rq_tile = RQN && n0 >= epi.rq.col0 && n0 < epi.rq.col0 + epi.rq.kn;
+        const int rb = RQN ? (n0 - epi.rq.col0) / 128 : 0;
+        v8h rqh[RJF][4], rql[RJF][4];
+        StepScale rss{0.0f, 0.0f};
+        if (RQN && rq_tile) {
+            load_rot_frags<RJF, 4>(epi.rq.rhi, epi.rq.rlo, rb, wave * RJF * 16, lane, 128, rqh, rql);
+            rss = step_scale(epi.rq.table, epi.rq.step);
+        }
+        // keep those loads here: left to itself the scheduler sinks them next to the rotation (to
+        // shorten their registers' lives) and the whole L2 latency shows after the dequantization
+        if (RQN) __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         if (PE == PE_RESIDUAL) {
             // every chunk is loaded from a clamped in-bounds address with no branch, all loads of a
@@ -1036,12 +1053,39 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
             }
         }
         __syncthreads();
+        uint8_t *sq = smem + BM * TP;  // RQN: the tile's codes, 64 bytes per row
+        if (RQN && rq_tile) {
+            // x' = y R_rb on the fp16 tile exactly as the streaming rotate-quantize computes it:
+            // lane inputs are 8 consecutive columns 8 (4 kk + fg) of row 16 mf + fr
+            v4f racc[BM / 16][RJF];
+            rotate_acc<BM / 16, RJF, 4>(rqh, rql, [&](int mf, int kk) {
+                return *reinterpret_cast<const v8h *>(&smem[(mf * 16 + fr) * TP + 16 * (4 * kk + fg)]);
+            }, racc);
+            const float rs = rss.rcp * (1.0f / (1 << ROT_LO_SHIFT));
+#pragma unroll
+            for (int mf = 0; mf < BM / 16; ++mf)
+#pragma unroll
+                for (int jf = 0; jf < RJF; ++jf)
+                    *reinterpret_cast<uint16_t *>(&sq[(mf * 16 + fr) * 64 + (wave * RJF * 16 + 16 * jf + 4 * fg) / 2]) =
+                        (uint16_t)quant_pack4(racc[mf][jf], rs);
+        }
 #pragma unroll 4
         for (int c = tid; c < BM * CPR; c += NT) {
             const int r = c / CPR, cc = c % CPR;
             const uint4 v = *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
             if (r < rows_here && cc * 8 < cols_here)
                 *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+        }
+        if (RQN && rq_tile) {
+            __syncthreads();  // every wave's codes are in LDS
+            const int64_t ldq = epi.rq.kn / 2;
+            for (int c = tid; c < BM * 4; c += NT) {
+                const int r = c >> 2, ch = c & 3;
+                if (r < rows_here)
+                    *reinterpret_cast<uint4 *>(epi.rq.xq + (int64_t)(m0 + r) * ldq + rb * 64 + 16 * ch) =
+                        *reinterpret_cast<const uint4 *>(&sq[r * 64 + 16 * ch]);
+            }
+            if (m0 == 0 && rb == 0 && tid == 0) epi.rq.x_scale[0] = rss.s;
         }
     } else {
 #pragma clang fp contract(off)
@@ -1497,7 +1541,6 @@ int launch_codes_to_f6(const uint8_t *q, int rows, int K, uint8_t *out, hipStrea
 }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Pipelined FP6 GEMM: the int4 pipelined kernel's structure (LDS ring of NSTAGE stages filled by
 // global_load_lds_dwordx4, vmcnt waits + plain barriers, XCD-aware tile order), one
@@ -1727,7 +1770,7 @@ struct GemmPlan {
 // partials. kg is the k granularity of a stage (128 for packed int4, 64 for int8 operands); sp
 // allows the software-pipelined kernel, whose per-stage times were measured on MI355X.
 static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = false,
-                          bool gelu = false)
+                          bool gelu = false, bool bn128_pipe = false)
 {
     GemmPlan best{0, 0, 16, 1, K};
     if (M <= SMALL_M) return best;
@@ -1757,6 +1800,7 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = fals
     for (int ci = 0; ci < ncand; ++ci) {
         const Cand &c = cands[ci];
         if (c.kind == 4 && !pipe) continue;
+        if (bn128_pipe && c.kind != 3 && c.kind != 4) continue;  // the fused rotate-quantize tiles
         if (c.kind >= SP_128x128 && K % c.gran) continue;  // whole ring slots only
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         // up to 256 splits: K <= 2^24 then always fits pieces of at most MAX_K_SPLIT k, the most
@@ -1820,21 +1864,38 @@ static void launch_big(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, co
 
 constexpr int PIPE_STAGES = 4;
 
-template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = false>
+template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = false,
+          bool RQN = false>
 static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                          int32_t *partial)
 {
-    // the staged epilogue reuses the ring for the output tile (BM rows of BN fp16 plus a pad)
+    // the staged epilogue reuses the ring for the output tile (BM rows of BN fp16 plus a pad) and,
+    // with the fused rotate-quantize, for the tile's codes (64 bytes per row) after it
     const size_t ring = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
-    const size_t tile = (PE != PE_INT32 && VO) ? (size_t)BM * (BN * 2 + 16) : 0;
+    const size_t tile = (PE != PE_INT32 && VO) ? (size_t)BM * (BN * 2 + 16) + (RQN ? BM * 64 : 0) : 0;
     const size_t lds = ring > tile ? ring : tile;
-    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>;
+    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS, RQN>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
-    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS>), grid,
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS, RQN>), grid,
                        dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn,
                        tile_band(tm, tn, BM, BN), epi, partial);
     return W4A4_OK;
+}
+
+// the 128-column tiles with the next linear's rotate-quantize in the staged epilogue
+template <int BM, int WM, int WN>
+static int launch_pipe_rq(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
+                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi)
+{
+    if (epi.mode == W4A4_EPI_GELU)
+        return launch_pipe_e<BM, 128, WM, WN, PE_GELU, true, false, false, true>(
+            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr);
+    if (epi.mode == W4A4_EPI_RESIDUAL)
+        return launch_pipe_e<BM, 128, WM, WN, PE_RESIDUAL, true, false, false, true>(
+            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr);
+    return launch_pipe_e<BM, 128, WM, WN, PE_NONE, true, false, false, true>(
+        grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr);
 }
 
 template <int BM, int BN, int WM, int WN, bool Q8, bool GS = false>
@@ -2009,14 +2070,35 @@ static void launch_smallm_wide(SmallmShape sh, bool q8, hipStream_t s, const uin
 // q8: int8 operands [rows][K] (W8A8); the caller guarantees K % 64 == 0 and 16-byte aligned
 // operands for them.
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
-                void *ws, size_t ws_bytes, hipStream_t s, bool q8)
+                void *ws, size_t ws_bytes, hipStream_t s, bool q8, bool *rq_done)
 {
+    if (rq_done) *rq_done = false;
     if (M == 0) return W4A4_OK;
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     const bool pipe = q8 || (vec && K % BG_KS == 0);
     GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe, pipe && !q8,
                            epi.mode == W4A4_EPI_GELU);
+    // the next linear's rotate-quantize in the epilogue: a 128-column pipelined tile plan without a
+    // K split, the staged (16-byte) epilogue, 128-aligned columns; else the caller runs it
+    const bool vo_rows = (N % 8 == 0) && (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0) &&
+                         ((uintptr_t)epi.w_scale % 16 == 0) &&
+                         (epi.mode != W4A4_EPI_RESIDUAL ||
+                          (epi.ldr % 8 == 0 && (uintptr_t)epi.residual % 16 == 0));
+    if (epi.rq.xq && !q8 && pipe && vo_rows && epi.mode != GEMM_OUT_I32 &&
+        epi.rq.col0 % 128 == 0 && epi.rq.kn % 128 == 0 && (uintptr_t)epi.rq.xq % 16 == 0) {
+        const GemmPlan f = plan_gemm(M, N, K, BG_KS, true, false, epi.mode == W4A4_EPI_GELU, true);
+        if ((f.kind == 3 || f.kind == 4) && f.splits == 1) {
+            const int tm = (M + f.bm - 1) / f.bm, tn = (N + f.bn - 1) / f.bn;
+            const dim3 grid(tm * tn, 1);
+            const int rc = f.kind == 4
+                               ? launch_pipe_rq<64, 1, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi)
+                               : launch_pipe_rq<128, 2, 2>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
+            if (rc != W4A4_OK) return rc;
+            if (rq_done) *rq_done = true;
+            return check_launch("gemm + next rotate-quantize");
+        }
+    }
     // the small-M kernels cover at most SMALL_M rows: a plan without a tile kernel beyond that
     // would leave rows unwritten, so it is refused loudly (no such plan exists for K <= 2^24)
     if (p.kind == 0 && M > SMALL_M)

@@ -168,6 +168,16 @@ bool rq_ring_path(int M, const void *X, int64_t ldx, const int32_t *perm, const 
                   int K);
 
 // GEMM (k_gemm.hip)
+// The next linear's rotate-quantize fused into a GEMM epilogue (per-step scale, block 128): the
+// output columns [col0, col0 + kn), which hold that linear's input in its zigzag order, become its
+// packed int4 codes xq [M][kn / 2] and its scale x_scale[0] = table[step]. xq == nullptr: none.
+struct RqNext {
+    const _Float16 *rhi, *rlo;  // the next linear's rotation operand (fp16 high and low parts)
+    const float *table;
+    int step, col0, kn;
+    uint8_t *xq;
+    float *x_scale;
+};
 struct GemmEpilogue {
     const float *x_scale;
     int x_scale_per_token;
@@ -178,12 +188,15 @@ struct GemmEpilogue {
     const uint16_t *residual;
     int64_t ldr;
     int32_t *acc_out;  // GEMM_OUT_I32 destination, dense [M][N]
+    RqNext rq;
 };
 constexpr int GEMM_OUT_I32 = 100;
 // q8: int8 operands [rows][K] (W8A8) instead of packed int4 [rows][K/2]
 size_t gemm_workspace(int M, int N, int K, bool q8);
+// With epi.rq.xq set, *rq_done tells whether the GEMM kernel also wrote the next linear's codes
+// (a 128-column tile plan with the staged epilogue); otherwise the caller runs the rotate-quantize.
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
-                void *ws, size_t ws_bytes, hipStream_t s, bool q8);
+                void *ws, size_t ws_bytes, hipStream_t s, bool q8, bool *rq_done = nullptr);
 // group-wise activation scales epi.x_scale[K / 128] (int4, K % 128 == 0, 16-byte aligned operands)
 int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int K,
                         const GemmEpilogue &epi, hipStream_t s);

@@ -62,6 +62,12 @@ class _Buffers:
                                            bd.lib().w4a4_gemm_w8a8_workspace_bytes)(rows, N, K)),
                                  torch.uint8)
                     for N, K in ((3 * h, h), (h, h), (f, h), (h, f)) for b in (4, 8)}
+        # codes and scale of O's and down's inputs written by the producing GEMM (QKV, up): apart
+        # from xq / xs, which that GEMM is still reading
+        self.xqn = {K: e((rows, K // 2), torch.uint8) for K in (h, f)}
+        self.xsn = e(1, torch.float32)
+        self.fws = {(N, K, Kn): e(max(256, bd.lib().w4a4_gemm_rq_next_workspace_bytes(
+            rows, N, K, Kn, block)), torch.uint8) for N, K, Kn in ((3 * h, h, h), (f, h, f))}
 
 
 class DeviceStack:
@@ -112,18 +118,30 @@ class DeviceStack:
                 layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
 
     def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None, in_order=False,
-                record=None):
+                record=None, pre=False, nxt=None, col0=0):
+        """Rotate-quantize X (unless pre: the producing GEMM already wrote this linear's codes into
+        bufs.xqn / bufs.xsn), then the GEMM; with nxt (the next linear, whose input is Y[:, col0:]
+        in its zigzag order), the GEMM also writes nxt's codes (w4a4_gemm_rq_next)."""
         b = lin.bits
         perm = None if in_order else lin.perm  # in_order: X already holds the zigzag order
-        if calib:
-            bd.calibrate_act_scale(X, perm, lin.rot, self.block, out=lin.table[step:step + 1],
-                                   ws=bufs.cws[lin.K], bits=b)
-        xq = bufs.xq[(lin.K, b)]
-        bd.rotate_quant_act(X, perm, lin.rot, self.block, None if calib else lin.table,
-                            self.steps, step, xq=xq, x_scale=bufs.xs, ws=bufs.ws[lin.K], bits=b)
+        if pre:
+            xq, xs = bufs.xqn[lin.K], bufs.xsn
+        else:
+            if calib:
+                bd.calibrate_act_scale(X, perm, lin.rot, self.block, out=lin.table[step:step + 1],
+                                       ws=bufs.cws[lin.K], bits=b)
+            xq, xs = bufs.xq[(lin.K, b)], bufs.xs
+            bd.rotate_quant_act(X, perm, lin.rot, self.block, None if calib else lin.table,
+                                self.steps, step, xq=xq, x_scale=xs, ws=bufs.ws[lin.K], bits=b)
         if record is not None:
-            record(xq, bufs.xs[:X.shape[0] if calib else 1])
-        bd.gemm(xq, bufs.xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
+            record(xq, xs[:X.shape[0] if calib else 1])
+        if nxt is not None:
+            bd.gemm_rq_next(xq, xs, False, lin.wq, lin.w_scale, lin.K, col0, nxt.K, self.block,
+                            nxt.rot, nxt.table, self.steps, step, Y=Y, epilogue=epi, residual=res,
+                            xq_next=bufs.xqn[nxt.K], x_scale_next=bufs.xsn,
+                            ws=bufs.fws[(lin.N, lin.K, nxt.K)])
+            return
+        bd.gemm(xq, xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
                 ws=bufs.gws[(lin.N, lin.K, b)], bits=b)
 
     def run(self, X, step: int, calib: bool = False, outputs=None, codes=None, rows=None):
@@ -144,12 +162,18 @@ class DeviceStack:
         for li, layer in enumerate(self.layers):
             nxt = bufs.hs[li % 2]
             x_in = pick(cur) if outputs is not None else None
-            self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs, record=cr)
+            # O's and down's inputs are quantized by the GEMM that produces them when both sides
+            # are W4A4 and their channels come out in the consumer's zigzag order
+            fo = self.fold and not calib and layer["qkv"].bits == 4 and layer["o"].bits == 4
+            fd = self.fold and not calib and layer["up"].bits == 4 and layer["down"].bits == 4
+            self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs, record=cr,
+                         nxt=layer["o"] if fo else None, col0=2 * h)
             self._linear(layer["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
-                         bd.EPI_RESIDUAL, cur, in_order=self.fold, record=cr)
-            self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU, record=cr)
+                         bd.EPI_RESIDUAL, cur, in_order=self.fold, record=cr, pre=fo)
+            self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU, record=cr,
+                         nxt=layer["down"] if fd else None)
             self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2,
-                         in_order=self.fold, record=cr)
+                         in_order=self.fold, record=cr, pre=fd)
             if outputs is not None:
                 qkv = pick(self._natural(layer["qkv"], bufs.qkv))
                 h2 = pick(bufs.h2)
