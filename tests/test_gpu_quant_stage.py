@@ -199,3 +199,27 @@ def test_unusable_table_entry_grouped():
     assert np.isnan(refg["scale"][2]) and np.isnan(refg["scale"][5])
     for g in (2, 5):
         assert not q[:, g * B:(g + 1) * B].any() and not refg["codes"][:, g * B:(g + 1) * B].any()
+
+
+@pytest.mark.parametrize("perm_kind", ["zigzag", "identity"])
+@pytest.mark.parametrize("mode", ["per_step", "per_token"])
+def test_codes_at_an_unaligned_address(perm_kind, mode):
+    # int4 codes may start at any byte: the kernels that stage a tile's codes for 16-byte stores
+    # fall back to byte stores there; the bytes must equal those written to an aligned buffer
+    torch = __import__("torch")
+    M, K, B = 300, 1024, 128
+    X, perm, U = _inputs(M, K, B, np.float16, perm_kind, seed=21)
+    rot = _rot(perm, U, B, K, 4)
+    pd = dev(perm) if perm_kind == "zigzag" else None
+    table = None
+    if mode == "per_step":
+        table = dev(np.array([oracle.calibrate_table([[X]], perm, U, B)[0]], np.float32))
+    T = 1 if table is not None else 0
+    q_ref, s_ref = bd.rotate_quant_act(dev(X), pd, rot, B, table, T, 0)
+    raw = torch.zeros(M * (K // 2) + 16, dtype=torch.uint8, device="cuda")
+    q_odd = raw[1:1 + M * (K // 2)].view(M, K // 2)
+    assert q_odd.data_ptr() % 16 == 1
+    _, s_odd = bd.rotate_quant_act(dev(X), pd, rot, B, table, T, 0, xq=q_odd)
+    assert np.array_equal(host(q_odd), host(q_ref))
+    assert np.array_equal(host(s_odd).view(np.uint32), host(s_ref).view(np.uint32))
+    assert host(raw)[0] == 0 and not host(raw)[1 + M * (K // 2):].any()

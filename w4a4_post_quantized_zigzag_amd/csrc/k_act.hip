@@ -205,9 +205,15 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     constexpr int KK = B / 32;       // 32-wide k steps
     constexpr int JW = B / 4;        // output channels per wave
     constexpr int JF = JW / 16;      // 16-channel fragments per wave
+    constexpr int MF = MT / 16;      // 16-token fragments per tile
     constexpr int LDSR = B + 8;      // halves per staged row (16-byte pad)
+    constexpr int OB = Q8 ? B : B / 2;  // output code bytes per row of one block
+    constexpr int OCH = MT * OB / 16;   // 16-byte output chunks per tile
+    constexpr float LO = 1.0f / (1 << ROT_LO_SHIFT);
+    const int64_t ldq = Q8 ? K : K / 2;
     __shared__ __attribute__((aligned(16))) uint16_t sx[MT * LDSR];
     __shared__ float smax[4][MT];
+    __shared__ __attribute__((aligned(16))) uint8_t sq[MT * OB];
 
     // Workgroup -> (row group, block). Workgroups are dealt round-robin to the 8 XCDs, each with
     // its own L2; consecutive workgroups of one XCD take the blocks of one row group, so a row
@@ -221,22 +227,15 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     const int r = lane & 15, g = lane >> 4;
     const int jbase = wave * JW;
 
+    // R_b^T fragments of this wave's output channels (high part pre-scaled by 2^12)
     v8h ahi[JF][KK], alo[JF][KK];
-#pragma unroll
-    for (int jf = 0; jf < JF; ++jf)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int64_t off = rot16_fragment(b, jbase / 16 + jf, kk, lane, B);
-            ahi[jf][kk] = *reinterpret_cast<const v8h *>(rhi + off);
-            alo[jf][kk] = *reinterpret_cast<const v8h *>(rlo + off);
-        }
+    load_rot_frags<JF, KK>(rhi, rlo, b, jbase, lane, B, ahi, alo);
 
-    float s_step = 1.0f, rcp_step = 1.0f;
+    float rs_step = 0.0f;
     if (MODE == ACT_PER_STEP) {
         const StepScale ss = step_scale(table, step + b * gstride);
-        s_step = ss.s;
-        rcp_step = ss.rcp;
-        if (rg == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = s_step;
+        rs_step = ss.rcp * LO;
+        if (rg == 0 && (gstride || b == 0) && tid == 0) x_scale[b * gstride] = ss.s;
     }
 
     const int row_begin = rg * rows_per_wg;
@@ -294,70 +293,57 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
         tile_store(m0);
         __syncthreads();
         if (m0 + MT < row_end) tile_load(m0 + MT);
-#pragma unroll 1
-        for (int mf = 0; mf < MT / 16; ++mf) {
-            v4f chi[JF], clo[JF];
-#pragma unroll
-            for (int jf = 0; jf < JF; ++jf) chi[jf] = clo[jf] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const v8h xb = *reinterpret_cast<const v8h *>(&sx[(mf * 16 + r) * LDSR + 32 * kk + 8 * g]);
-#pragma unroll
-                for (int jf = 0; jf < JF; ++jf) {
-                    chi[jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jf][kk], xb, chi[jf], 0, 0, 0);
-                    clo[jf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jf][kk], xb, clo[jf], 0, 0, 0);
-                }
-            }
-            const int m = m0 + mf * 16 + r;
-            const bool live = m < row_end;
-            float v[JF][4];
-#pragma unroll
-            for (int jf = 0; jf < JF; ++jf)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[jf][i] = chi[jf][i] + clo[jf][i] * (1.0f / (1 << ROT_LO_SHIFT));
 
+        // acc[mf][jf] = 2^12 x' for tokens m0 + mf*16 + (lane % 16), channels jbase + 16 jf +
+        // 4 (lane / 16) + 0..3: the streaming kernel's arithmetic, in the same order
+        v4f acc[MF][JF];
+        rotate_acc<MF, JF, KK>(ahi, alo, [&](int mf, int kk) {
+            return *reinterpret_cast<const v8h *>(&sx[(mf * 16 + r) * LDSR + 8 * (4 * kk + g)]);
+        }, acc);
+
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+            const int row = mf * 16 + r;
+            const int m = m0 + row;
+            const bool live = m < row_end;
             if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
                 float a = 0.0f;
 #pragma unroll
                 for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(v[jf][i]));
+                    for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(acc[mf][jf][i]));
                 a = fmaxf(a, __shfl_xor(a, 16));
                 a = fmaxf(a, __shfl_xor(a, 32));
-                if (g == 0) smax[wave][mf * 16 + r] = live ? a : 0.0f;
+                if (g == 0) smax[wave][row] = live ? a * LO : 0.0f;
                 continue;
             }
-            if (!live) continue;
-            const int jcol = b * B + jbase + 4 * g;
-            if (xrot_dbg) {
+            const int jl = jbase + 4 * g;  // first of this lane's 4 channels within the block
+            if (xrot_dbg && live) {
 #pragma unroll
                 for (int jf = 0; jf < JF; ++jf)
-                    *reinterpret_cast<float4 *>(&xrot_dbg[(int64_t)m * K + jcol + 16 * jf]) =
-                        make_float4(v[jf][0], v[jf][1], v[jf][2], v[jf][3]);
+                    *reinterpret_cast<float4 *>(&xrot_dbg[(int64_t)m * K + b * B + jl + 16 * jf]) =
+                        make_float4(acc[mf][jf][0] * LO, acc[mf][jf][1] * LO, acc[mf][jf][2] * LO,
+                                    acc[mf][jf][3] * LO);
             }
-            float rcp = rcp_step;
+            float rs = rs_step;
             if (MODE == ACT_TOKEN_QUANT) {
-                const float s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[m]));
-                rcp = (float)(1.0 / (double)s);
-                if (b == 0 && wave == 0 && g == 0) x_scale[m] = s;
+                const int mc = min(m, row_end - 1);
+                const float sc = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[mc]));
+                rs = (float)(1.0 / (double)sc) * LO;
+                if (b == 0 && wave == 0 && g == 0 && live) x_scale[m] = sc;
             }
 #pragma unroll
             for (int jf = 0; jf < JF; ++jf) {
-                const int q0 = quant_code_q<Q8>(v[jf][0], rcp), q1 = quant_code_q<Q8>(v[jf][1], rcp);
-                const int q2 = quant_code_q<Q8>(v[jf][2], rcp), q3 = quant_code_q<Q8>(v[jf][3], rcp);
-                if (Q8) {
-                    *reinterpret_cast<uint32_t *>(&xq[(int64_t)m * K + jcol + 16 * jf]) =
-                        (uint32_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) |
-                                   ((uint32_t)(q3 & 0xFF) << 24));
-                    continue;
-                }
-                const uint16_t packed = (uint16_t)((q0 & 0xF) | ((q1 & 0xF) << 4) |
-                                                   ((q2 & 0xF) << 8) | ((q3 & 0xF) << 12));
-                *reinterpret_cast<uint16_t *>(&xq[(int64_t)m * (K / 2) + (jcol + 16 * jf) / 2]) = packed;
+                if (Q8)
+                    *reinterpret_cast<uint32_t *>(&sq[row * OB + jl + 16 * jf]) =
+                        quant_pack4<true>(acc[mf][jf], rs);
+                else
+                    *reinterpret_cast<uint16_t *>(&sq[row * OB + (jl + 16 * jf) / 2]) =
+                        (uint16_t)quant_pack4(acc[mf][jf], rs);
             }
         }
+        __syncthreads();
         if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
-            __syncthreads();
             if (tid < MT) {
                 const int m = m0 + tid;
                 const float a = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
@@ -369,6 +355,20 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
                     for (int off = 32; off > 0; off >>= 1) t = fmaxf(t, __shfl_xor(t, off));
                     if (tid == 0) atomicMax(&rowmax[b * gstride], __float_as_uint(t));
                 }
+            }
+        } else if (((uintptr_t)xq & 15) == 0) {
+            // the tile's codes: 16-byte stores (OB / 16 chunks per row)
+            for (int e = tid; e < OCH; e += 256) {
+                const int row = e / (OB / 16), ch = e % (OB / 16);
+                if (m0 + row < row_end)
+                    *reinterpret_cast<uint4 *>(&xq[(int64_t)(m0 + row) * ldq + b * OB + 16 * ch]) =
+                        *reinterpret_cast<const uint4 *>(&sq[row * OB + 16 * ch]);
+            }
+        } else {
+            // xq without 16-byte alignment (allowed for int4 codes): byte stores
+            for (int e = tid; e < MT * OB; e += 256) {
+                const int row = e / OB, c = e % OB;
+                if (m0 + row < row_end) xq[(int64_t)(m0 + row) * ldq + b * OB + c] = sq[row * OB + c];
             }
         }
     }
