@@ -954,6 +954,32 @@ def supplementary(bd, inputs, steps):
                      "offline_pack_s": info["offline_s"], "calibration_s": info["calib_s"]}
         del lins, Xs, step
         torch.cuda.empty_cache()
+    out["vendor_int8_gemm_reference"] = vendor_int8_gemm_reference(max(20, steps))
+    return out
+
+
+def vendor_int8_gemm_reference(reps):
+    """The vendor library's int8 GEMM (torch._int_mm, int8 operands [M,K] x [K,N] -> int32) on the
+    benchmark's GEMM shapes, timed like the library's kernels: a measured reference for what the
+    matrix cores reach at these shapes, not part of the W4A4 path (its operands are int8, twice the
+    packed int4 bytes, and it has no dequantization epilogue)."""
+    torch = _torch()
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for name, M, N, K in (("stack_qkv", 1600, 3072, 1024), ("stack_o", 1600, 1024, 1024),
+                          ("stack_up", 1600, 4096, 1024), ("stack_down", 1600, 1024, 4096),
+                          ("prefill_proj", 1024, 16384, 2048), ("longk_down", 1024, 2048, 16384)):
+        A = torch.randint(-8, 8, (M, K), generator=g, dtype=torch.int8, device="cuda")
+        Bt = torch.randint(-8, 8, (N, K), generator=g, dtype=torch.int8, device="cuda")
+        try:
+            torch._int_mm(A, Bt.t())
+            us = time_kernel_calls([lambda: torch._int_mm(A, Bt.t())], reps) * 1e3
+        except RuntimeError as e:  # not every torch build has the int8 product on this device
+            out[name] = {"error": str(e)[:200]}
+            continue
+        tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out[name] = {"M": M, "N": N, "K": K, "us": us, "tops": tops,
+                     "frac_int8_peak": tops / INT8_PEAK_TOPS}
     return out
 
 
