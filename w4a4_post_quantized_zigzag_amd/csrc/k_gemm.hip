@@ -1868,34 +1868,39 @@ template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = fa
           bool RQN = false>
 static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                          int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
-                         int32_t *partial)
+                         int32_t *partial, int band = 0)
 {
     // the staged epilogue reuses the ring for the output tile (BM rows of BN fp16 plus a pad) and,
     // with the fused rotate-quantize, for the tile's codes (64 bytes per row) after it
-    const size_t ring = (size_t)PIPE_STAGES * (BM + BN) * BG_ROWB;
+    constexpr int NS = PIPE_STAGES;
+    const size_t ring = (size_t)NS * (BM + BN) * BG_ROWB;
     const size_t tile = (PE != PE_INT32 && VO) ? (size_t)BM * (BN * 2 + 16) + (RQN ? BM * 64 : 0) : 0;
     const size_t lds = ring > tile ? ring : tile;
-    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS, RQN>;
+    const void *fn = (const void *)k_gemm_pipe<BM, BN, WM, WN, NS, PE, VO, Q8, GS, RQN>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
-    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, PIPE_STAGES, PE, VO, Q8, GS, RQN>), grid,
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, NS, PE, VO, Q8, GS, RQN>), grid,
                        dim3(64 * WM * WN), lds, s, xq, wq, M, N, K, k_split, tm, tn,
-                       tile_band(tm, tn, BM, BN), epi, partial);
+                       band > 0 ? band : tile_band(tm, tn, BM, BN), epi, partial);
     return W4A4_OK;
 }
 
-// the 128-column tiles with the next linear's rotate-quantize in the staged epilogue
+// the 128-column tiles with the next linear's rotate-quantize in the staged epilogue. When only
+// some column tiles carry it (the next linear's input is part of the output), the tiles go to the
+// XCDs in row bands (every XCD gets all column tiles of its rows), so that extra epilogue work is
+// spread evenly instead of landing on the XCDs that own those columns.
 template <int BM, int WM, int WN>
 static int launch_pipe_rq(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                           int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi)
 {
+    const int band = (epi.rq.col0 > 0 || epi.rq.kn < N) ? tn : 0;
     if (epi.mode == W4A4_EPI_GELU)
         return launch_pipe_e<BM, 128, WM, WN, PE_GELU, true, false, false, true>(
-            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr);
+            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
     if (epi.mode == W4A4_EPI_RESIDUAL)
         return launch_pipe_e<BM, 128, WM, WN, PE_RESIDUAL, true, false, false, true>(
-            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr);
+            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
     return launch_pipe_e<BM, 128, WM, WN, PE_NONE, true, false, false, true>(
-        grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr);
+        grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
 }
 
 template <int BM, int BN, int WM, int WN, bool Q8, bool GS = false>
