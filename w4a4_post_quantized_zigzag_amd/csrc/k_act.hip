@@ -193,8 +193,8 @@ int launch_rotate_quant(const void *X, int xdt, int M, int K, int64_t ldx, int B
 // of its B/4 output channels in registers and reuses them over all row tiles of the workgroup.
 constexpr int MT = 64;  // token rows per tile
 
-template <int MODE, int B, bool GATHER, bool Q8>
-__global__ __launch_bounds__(256) void k_rq_mfma(
+template <int MODE, int B, bool GATHER, bool Q8, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_rq_mfma(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const int32_t *__restrict__ perm,
     const _Float16 *__restrict__ rhi, const _Float16 *__restrict__ rlo,
     const float *__restrict__ table, int step, uint32_t *__restrict__ rowmax,
@@ -203,7 +203,8 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
 {
 #pragma clang fp contract(off)
     constexpr int KK = B / 32;       // 32-wide k steps
-    constexpr int JW = B / 4;        // output channels per wave
+    constexpr int NT = 64 * NW;      // threads
+    constexpr int JW = B / NW;       // output channels per wave
     constexpr int JF = JW / 16;      // 16-channel fragments per wave
     constexpr int MF = MT / 16;      // 16-token fragments per tile
     constexpr int LDSR = B + 8;      // halves per staged row (16-byte pad)
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     constexpr float LO = 1.0f / (1 << ROT_LO_SHIFT);
     const int64_t ldq = Q8 ? K : K / 2;
     __shared__ __attribute__((aligned(16))) uint16_t sx[MT * LDSR];
-    __shared__ float smax[4][MT];
+    __shared__ float smax[NW][MT];
     __shared__ __attribute__((aligned(16))) uint8_t sq[MT * OB];
 
     // Workgroup -> (row group, block). Workgroups are dealt round-robin to the 8 XCDs, each with
@@ -244,10 +245,11 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
     // Tile staging, prefetched one tile ahead into registers. Loads are unconditional from clamped
     // in-bounds rows (the clamped rows are zeroed when stored), so they stay in flight during the
     // previous tile's MFMA work.
-    //  gather:     thread -> one source column (fixed for the kernel), rows tid/B + t*(256/B)
-    //  contiguous: thread -> 16-byte chunks e = tid + t*256 of the tile (row e/(B/8), chunk e%(B/8))
-    constexpr int RSTEP = 256 / B, NLD = MT / RSTEP;
-    constexpr int C8 = B / 8, NCH = MT * C8 / 256;
+    //  gather:     thread -> one source column (fixed for the kernel), rows tid/B + t*(NT/B)
+    //  contiguous: thread -> 16-byte chunks e = tid + t*NT of the tile (row e/(B/8), chunk e%(B/8))
+    constexpr int RSTEP = NT / B, NLD = MT / RSTEP;
+    constexpr int C8 = B / 8, NCH = MT * C8 / NT;
+    static_assert(NLD * RSTEP == MT && NCH * NT == MT * C8 && JW % 16 == 0, "whole rounds");
     const int gi = tid % B, grr0 = tid / B;
     const int64_t gcol = GATHER ? (perm ? perm[b * B + gi] : b * B + gi) : 0;
     uint16_t pv[GATHER ? NLD : 1];
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
         } else {
 #pragma unroll
             for (int t = 0; t < NCH; ++t) {
-                const int e = tid + t * 256;
+                const int e = tid + t * NT;
                 const int m = min(m0 + e / C8, row_end - 1);
                 pc[t] = *reinterpret_cast<const uint4 *>(X + (int64_t)m * ldx + b * B + 8 * (e % C8));
             }
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
         } else {
 #pragma unroll
             for (int t = 0; t < NCH; ++t) {
-                const int e = tid + t * 256, rr = e / C8;
+                const int e = tid + t * NT, rr = e / C8;
                 const bool live = m0 + rr < row_end;
                 const uint4 v = make_uint4(live ? pc[t].x : 0u, live ? pc[t].y : 0u,
                                            live ? pc[t].z : 0u, live ? pc[t].w : 0u);
@@ -346,7 +348,9 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
         if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
             if (tid < MT) {
                 const int m = m0 + tid;
-                const float a = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+                float a = smax[0][tid];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) a = fmaxf(a, smax[w][tid]);
                 if (MODE == ACT_TOKEN_MAX) {
                     if (m < row_end) atomicMax(&rowmax[m], __float_as_uint(a));
                 } else {
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
             }
         } else if (((uintptr_t)xq & 15) == 0) {
             // the tile's codes: 16-byte stores (OB / 16 chunks per row)
-            for (int e = tid; e < OCH; e += 256) {
+            for (int e = tid; e < OCH; e += NT) {
                 const int row = e / (OB / 16), ch = e % (OB / 16);
                 if (m0 + row < row_end)
                     *reinterpret_cast<uint4 *>(&xq[(int64_t)(m0 + row) * ldq + b * OB + 16 * ch]) =
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(256) void k_rq_mfma(
             }
         } else {
             // xq without 16-byte alignment (allowed for int4 codes): byte stores
-            for (int e = tid; e < MT * OB; e += 256) {
+            for (int e = tid; e < MT * OB; e += NT) {
                 const int row = e / OB, c = e % OB;
                 if (m0 + row < row_end) xq[(int64_t)(m0 + row) * ldq + b * OB + c] = sq[row * OB + c];
             }
@@ -1125,9 +1129,11 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
 #undef W4A4_RING_K
         return check_launch("rotate-quantize (ring)");
     }
+    // block 128: 8 waves of 16 channels (each thread gathers half as many inputs per tile)
 #define W4A4_RQ(MODEV, BV, GV, QV)                                                                 \
-    hipLaunchKernelGGL((k_rq_mfma<MODEV, BV, GV, QV>), grid, dim3(256), 0, s, src, ld, M, K, perm, \
-                       rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw, gstride)
+    hipLaunchKernelGGL((k_rq_mfma<MODEV, BV, GV, QV, (BV == 128 ? 8 : 4)>), grid,                  \
+                       dim3(BV == 128 ? 512 : 256), 0, s, src, ld, M, K, perm, rhi, rlo, table,     \
+                       step, rowmax, xq, x_scale, xrot_dbg, rpw, gstride)
 #define W4A4_RQ_B(MODEV, QV)                                                                       \
     if (B == 128) { if (gather) W4A4_RQ(MODEV, 128, true, QV); else W4A4_RQ(MODEV, 128, false, QV); } \
     else { if (gather) W4A4_RQ(MODEV, 64, true, QV); else W4A4_RQ(MODEV, 64, false, QV); }
