@@ -416,27 +416,29 @@ __device__ __forceinline__ void rq_wait_vmcnt(int n)
 
 // F6: the codes go out in the FP6 operand layout of the FP6 GEMM instead of packed int4 (B = 128,
 // so a rotation block is one 128-k stage of that layout: xq is the operand, stage b its block b).
-template <int MODE, int B, bool DBG, bool Q8, bool F6 = false>
-__global__ __launch_bounds__(256) void k_rq_ring(
+template <int MODE, int B, bool DBG, bool Q8, bool F6 = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_rq_ring(
     const uint16_t *__restrict__ X, int64_t ldx, int M, int K, const _Float16 *__restrict__ rhi,
     const _Float16 *__restrict__ rlo, const float *__restrict__ table, int step,
     uint32_t *__restrict__ rowmax, uint8_t *__restrict__ xq, float *__restrict__ x_scale,
     float *__restrict__ xrot_dbg, int rows_per_wg, int row_groups, int gstride)
 {
 #pragma clang fp contract(off)
-    constexpr int KK = B / 32, JW = B / 4, JF = JW / 16, MF = MT / 16;
+    constexpr int NT = 64 * NW;  // threads
+    constexpr int KK = B / 32, JW = B / NW, JF = JW / 16, MF = MT / 16;
     constexpr float LO = 1.0f / (1 << ROT_LO_SHIFT);
     constexpr int NXCD = 8;
     constexpr int ROWB = B * 2;                   // bytes per staged row
     constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
     constexpr int TILE = MT * ROWB;               // bytes per tile
-    constexpr int QPW = TILE / 1024 / 4;          // DMA instructions per wave per tile
+    constexpr int QPW = TILE / 1024 / NW;         // DMA instructions per wave per tile
+    static_assert(QPW * 1024 * NW == TILE && JF * 16 * NW == B, "whole DMA instructions and fragments per wave");
     constexpr int RPI = 1024 / ROWB;              // rows per DMA instruction
     constexpr int OB = Q8 ? B : B / 2;            // output code bytes per row of one block
     constexpr int OCH = MT * OB / 16;             // 16-byte output chunks per tile
     const int64_t ldq = Q8 ? K : K / 2;           // output row stride in bytes
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
-    __shared__ float smax[4][MT];
+    __shared__ float smax[NW][MT];
     __shared__ __attribute__((aligned(16))) uint8_t sq[MT * OB];
     __shared__ float srcp[MODE == ACT_TOKEN_QUANT ? RQ_RING_MAX_ROWS : 1];
 
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
     // per-token reciprocal scales (times 2^-12) of this workgroup's rows, staged in LDS: a global
     // load inside the tile loop would make the compiler wait for every DMA issued before it
     if (MODE == ACT_TOKEN_QUANT) {
-        for (int i = tid; i < row_end - row_begin; i += 256) {
+        for (int i = tid; i < row_end - row_begin; i += NT) {
             const float s = scale_from_absmax_q<Q8>(__uint_as_float(rowmax[row_begin + i]));
             srcp[i] = (float)(1.0 / (double)s) * LO;
             if (b == 0) x_scale[row_begin + i] = s;
@@ -559,7 +561,9 @@ __global__ __launch_bounds__(256) void k_rq_ring(
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (MODE == ACT_TOKEN_MAX || MODE == ACT_CALIB_MAX) {
             if (tid < MT) {
-                const float a = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+                float a = smax[0][tid];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) a = fmaxf(a, smax[w][tid]);
                 if (MODE == ACT_TOKEN_MAX) {
                     if (m0 + tid < row_end) atomicMax(&rowmax[m0 + tid], __float_as_uint(a));
                 } else {
@@ -575,7 +579,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
             static_assert(!F6 || (B == 128 && !Q8), "FP6 output: one 128-k stage per block, int4 codes");
             const int R2 = (M + 1) & ~1;
             uint8_t *blk = xq + (int64_t)b * R2 * 96;
-            for (int e = tid; e < MT * 4; e += 256) {
+            for (int e = tid; e < MT * 4; e += NT) {
                 const int row = e >> 2, g = e & 3, m = m0 + row;
                 const bool live = m < row_end;
                 if (!live && !(m == M && (M & 1))) continue;
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(256) void k_rq_ring(
             }
         } else {
             // codes of the tile: 16-byte stores (OB / 16 chunks per row)
-            for (int e = tid; e < OCH; e += 256) {
+            for (int e = tid; e < OCH; e += NT) {
                 const int row = e / (OB / 16), ch = e % (OB / 16);
                 if (m0 + row < row_end)
                     *reinterpret_cast<uint4 *>(&xq[(int64_t)(m0 + row) * ldq + b * OB + 16 * ch]) =
@@ -1095,14 +1099,16 @@ int launch_rotate_quant_mfma(const void *X, int M, int K, int64_t ldx, int B, co
         const int groups = (M + rpw_r - 1) / rpw_r;
         dim3 grid_r(groups * nb);
         const size_t lds = (size_t)RQ_STAGES * MT * B * sizeof(uint16_t);
+    // block 128: 8 waves of 16 channels (twice the waves in flight on the same tiles)
 #define W4A4_RING_K(MODEV, BV, DV, QV, FV)                                                         \
     do {                                                                                           \
-        const int lrc = ensure_dynamic_lds((const void *)k_rq_ring<MODEV, BV, DV, QV, FV>, lds,    \
-                                           "rotate-quantize");                                     \
+        constexpr int RNW = BV == 128 ? 8 : 4;                                                     \
+        const int lrc = ensure_dynamic_lds((const void *)k_rq_ring<MODEV, BV, DV, QV, FV, RNW>,    \
+                                           lds, "rotate-quantize");                                \
         if (lrc != W4A4_OK) return lrc;                                                            \
-        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV, FV>), grid_r, dim3(256), lds, s, src, ld, \
-                           M, K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, rpw_r,      \
-                           groups, gstride);                                                       \
+        hipLaunchKernelGGL((k_rq_ring<MODEV, BV, DV, QV, FV, RNW>), grid_r, dim3(64 * RNW), lds,   \
+                           s, src, ld, M, K, rhi, rlo, table, step, rowmax, xq, x_scale, xrot_dbg, \
+                           rpw_r, groups, gstride);                                                \
     } while (0)
 #define W4A4_RING(MODEV, BV, DV, QV) W4A4_RING_K(MODEV, BV, DV, QV, false)
 #define W4A4_RING_F6(MODEV) W4A4_RING_K(MODEV, 128, false, false, true)
