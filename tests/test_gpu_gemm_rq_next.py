@@ -127,3 +127,28 @@ def test_gemm_rq_next_empty_and_errors():
             bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], 256, args["col0"],
                             args["K_next"], 128, d["rot"], args["table"], 2, args["step"])
         assert ei.value.status == code, (kw, ei.value)
+
+
+@pytest.mark.parametrize("per_token_in,ld_pad", [(True, 0), (False, 64), (True, 192)])
+def test_gemm_rq_next_per_token_input_and_strided_output(per_token_in, ld_pad):
+    # the GEMM's own input scales per token, and Y a view into a wider buffer (ldy = N + ld_pad):
+    # the fused epilogue must address Y, the residual and the codes by their own strides
+    torch = __import__("torch")
+    M, N, K, col0, K_next, B, epi = 400, 768, 512, 256, 512, 128, EPI_RESIDUAL
+    d = _case(M, N, K, K_next, B, epi, 41 + ld_pad)
+    xs = d["xs"]
+    if per_token_in:
+        rng = np.random.Generator(np.random.PCG64(7))
+        xs = dev(rng.uniform(0.01, 0.03, M).astype(np.float32))
+    Y0 = bd.gemm(d["xq"], xs, per_token_in, d["wq"], d["ws"], K, epilogue=epi, residual=d["res"])
+    d["Y0"] = Y0
+    table = _table_for(d, col0, K_next, B)
+    big = torch.full((M, N + ld_pad), 7.0, dtype=torch.float16, device="cuda")
+    Yv = big[:, :N]
+    Y, q, s = bd.gemm_rq_next(d["xq"], xs, per_token_in, d["wq"], d["ws"], K, col0, K_next, B,
+                              d["rot"], table, 2, 1, Y=Yv, epilogue=epi, residual=d["res"])
+    assert _same(Yv, Y0)
+    if ld_pad:
+        assert np.all(host(big[:, N:]).astype(np.float32) == 7.0)  # the padding is untouched
+    q_ref, s_ref = bd.rotate_quant_act(Y0[:, col0:col0 + K_next], None, d["rot"], B, table, 2, 1)
+    assert _same(q, q_ref) and _same(s, s_ref)
