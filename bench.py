@@ -503,7 +503,7 @@ def stack_kernel_times(bd, ds, Xs, reps=30):
                 bd.gemm_rq_next(xq, bufs.xs, False, lin.wq, lin.w_scale, lin.K, col0, nl.K,
                                 ds.block, nl.rot, nl.table, ds.steps, 0, Y=Y, epilogue=epi,
                                 residual=res, xq_next=bufs.xqn[nl.K], x_scale_next=bufs.xsn,
-                                ws=bufs.fws[(lin.N, lin.K, nl.K)])
+                                ws=bufs.fws[(lin.N, lin.K, nl.K)], store_next_cols=False)
         else:
             def gm(lin=lin, xq=xq, xs=xs, Y=Y, epi=epi, res=res):
                 bd.gemm(xq, xs, False, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,

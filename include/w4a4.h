@@ -196,9 +196,13 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
  *   w4a4_rotate_quant_act(Y + col0, W4A4_F16, M, K_next, ldy, block_next, NULL, rot_next,
  *                         table_next, num_steps, step, xq_next, x_scale_next, NULL, ...)
  * would give them after this GEMM [gist.science summary, "Metodologia" 1: rotate, then quantize the
- * next layer's input; vnrobo.com "Y tuong paper": the step's scale is a table lookup]. Y is still
- * written in full. With block_next 128 and a 128-column tile plan (M above 64, no K split, 16-byte
- * aligned rows) the rotation and quantization run in the GEMM's epilogue on the finished fp16 tile,
+ * next layer's input; vnrobo.com "Y tuong paper": the step's scale is a table lookup]. Y is written
+ * in full when store_next_cols != 0; with store_next_cols == 0 the columns [col0, col0 + K_next) of
+ * Y may be left unwritten (their contents are then unspecified: for a caller whose only consumer of
+ * them is the next linear), but Y must still be a valid [M][N] buffer, since the non-fused case
+ * below computes them there. With block_next 128 and a 128-column tile plan (M above 64, no K
+ * split, 16-byte aligned rows) the rotation and quantization run in the GEMM's epilogue on the
+ * finished fp16 tile,
  * with the same arithmetic as the standalone call, so the codes are identical bit for bit; any other
  * case runs the standalone call on the same stream after the GEMM. Arguments and errors as
  * w4a4_gemm and w4a4_rotate_quant_act (per-step scale only: table_next is required); every argument
@@ -209,8 +213,8 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
                       int K_next, int block_next, const void *rot_next, const float *table_next,
-                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next, void *ws,
-                      size_t ws_bytes, hipStream_t stream);
+                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next,
+                      int store_next_cols, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Test hook: the raw int32 accumulators acc [M][N] (row-major, dense) of the same integer GEMM. */
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,

@@ -73,18 +73,28 @@ def test_gemm_rq_next_matches_gemm_then_rotate_quantize(name):
     M, N, K, col0, K_next, B, epi = CASES[name]
     d = _case(M, N, K, K_next, B, epi, 11 + list(CASES).index(name))
     table = _table_for(d, col0, K_next, B)
-    for step in (0, 1):
+    torch = d["torch"]
+    for step, store in ((0, True), (1, True), (1, False)):
+        # store=False: the next linear's columns of Y may be left unwritten (pre-filled here with
+        # a stand-in value); the other columns, the codes and the scale are unchanged
+        Yb = torch.full(tuple(d["Y0"].shape), -3.0, dtype=torch.float16, device="cuda")
         Y, q, s = bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], K, col0, K_next, B,
-                                  d["rot"], table, 2, step, epilogue=epi, residual=d["res"])
-        assert _same(Y, d["Y0"]), (name, step)
+                                  d["rot"], table, 2, step, Y=Yb, epilogue=epi, residual=d["res"],
+                                  store_next_cols=store)
+        if store:
+            assert _same(Y, d["Y0"]), (name, step)
+        else:
+            keep = np.ones(d["Y0"].shape[1], bool)
+            keep[col0:col0 + K_next] = False
+            assert np.array_equal(host(Y)[:, keep].view(np.uint16), host(d["Y0"])[:, keep].view(np.uint16))
         q_ref, s_ref = bd.rotate_quant_act(d["Y0"][:, col0:col0 + K_next], None, d["rot"], B,
                                            table, 2, step)
-        assert _same(s, s_ref), (name, step)
+        assert _same(s, s_ref), (name, step, store)
         qa, qb = host(q), host(q_ref)
         if not np.array_equal(qa, qb):
             bad = np.argwhere(qa != qb)[:5]
-            raise AssertionError(f"{name} step {step}: {int((qa != qb).sum())} code bytes differ, "
-                                 f"e.g. {bad.tolist()}")
+            raise AssertionError(f"{name} step {step} store {store}: {int((qa != qb).sum())} code "
+                                 f"bytes differ, e.g. {bad.tolist()}")
 
 
 def test_gemm_rq_next_codes_against_the_oracle():

@@ -672,8 +672,8 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
                       int K_next, int block_next, const void *rot_next, const float *table_next,
-                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next, void *ws,
-                      size_t ws_bytes, hipStream_t stream)
+                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next,
+                      int store_next_cols, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     // every argument of the rotate-quantize half is checked before anything is launched
     int rc;
@@ -701,7 +701,7 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     const char *rb = reinterpret_cast<const char *>(rot_next);
     const RqNext rq{reinterpret_cast<const _Float16 *>(rb + L.r32),
                     reinterpret_cast<const _Float16 *>(rb + L.r32 + L.r16),
-                    table_next, step, col0, K_next, xq_next, x_scale_next};
+                    table_next, step, col0, K_next, xq_next, x_scale_next, store_next_cols ? 1 : 0};
     bool done = false;
     if ((rc = gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
                          residual, ldr, ws, ws_bytes, stream, OPF_I4,

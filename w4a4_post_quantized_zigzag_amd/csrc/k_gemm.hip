@@ -1069,11 +1069,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
                     *reinterpret_cast<uint16_t *>(&sq[(mf * 16 + fr) * 64 + (wave * RJF * 16 + 16 * jf + 4 * fg) / 2]) =
                         (uint16_t)quant_pack4(racc[mf][jf], rs);
         }
+        // the fp16 tile, unless it only feeds the next linear (its codes are written below) and the
+        // caller does not need it
+        const bool store_tile = !(RQN && rq_tile && !epi.rq.store_y);
 #pragma unroll 4
         for (int c = tid; c < BM * CPR; c += NT) {
             const int r = c / CPR, cc = c % CPR;
             const uint4 v = *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
-            if (r < rows_here && cc * 8 < cols_here)
+            if (store_tile && r < rows_here && cc * 8 < cols_here)
                 *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
         }
         if (RQN && rq_tile) {

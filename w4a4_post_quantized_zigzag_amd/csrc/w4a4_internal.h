@@ -177,6 +177,7 @@ struct RqNext {
     int step, col0, kn;
     uint8_t *xq;
     float *x_scale;
+    int store_y;  // 0: the columns [col0, col0 + kn) of Y need not be written
 };
 struct GemmEpilogue {
     const float *x_scale;

@@ -118,10 +118,11 @@ class DeviceStack:
                 layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
 
     def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None, in_order=False,
-                record=None, pre=False, nxt=None, col0=0):
+                record=None, pre=False, nxt=None, col0=0, keep=False):
         """Rotate-quantize X (unless pre: the producing GEMM already wrote this linear's codes into
         bufs.xqn / bufs.xsn), then the GEMM; with nxt (the next linear, whose input is Y[:, col0:]
-        in its zigzag order), the GEMM also writes nxt's codes (w4a4_gemm_rq_next)."""
+        in its zigzag order), the GEMM also writes nxt's codes (w4a4_gemm_rq_next) and, unless keep
+        (the test hooks read them), does not store those fp16 columns, whose only consumer is nxt."""
         b = lin.bits
         perm = None if in_order else lin.perm  # in_order: X already holds the zigzag order
         if pre:
@@ -139,7 +140,7 @@ class DeviceStack:
             bd.gemm_rq_next(xq, xs, False, lin.wq, lin.w_scale, lin.K, col0, nxt.K, self.block,
                             nxt.rot, nxt.table, self.steps, step, Y=Y, epilogue=epi, residual=res,
                             xq_next=bufs.xqn[nxt.K], x_scale_next=bufs.xsn,
-                            ws=bufs.fws[(lin.N, lin.K, nxt.K)])
+                            ws=bufs.fws[(lin.N, lin.K, nxt.K)], store_next_cols=keep)
             return
         bd.gemm(xq, xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
                 ws=bufs.gws[(lin.N, lin.K, b)], bits=b)
@@ -166,12 +167,13 @@ class DeviceStack:
             # are W4A4 and their channels come out in the consumer's zigzag order
             fo = self.fold and not calib and layer["qkv"].bits == 4 and layer["o"].bits == 4
             fd = self.fold and not calib and layer["up"].bits == 4 and layer["down"].bits == 4
+            keep = outputs is not None
             self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs, record=cr,
-                         nxt=layer["o"] if fo else None, col0=2 * h)
+                         nxt=layer["o"] if fo else None, col0=2 * h, keep=keep)
             self._linear(layer["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
                          bd.EPI_RESIDUAL, cur, in_order=self.fold, record=cr, pre=fo)
             self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU, record=cr,
-                         nxt=layer["down"] if fd else None)
+                         nxt=layer["down"] if fd else None, keep=keep)
             self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2,
                          in_order=self.fold, record=cr, pre=fd)
             if outputs is not None:
