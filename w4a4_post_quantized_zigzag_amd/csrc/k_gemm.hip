@@ -1150,7 +1150,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 // At iteration s the ring holds stage s (already in registers), s+1 (being read) and up to NS-2
 // stages in flight; the slot refilled at iteration s held stage s-1, whose fragment reads every
 // wave finished before the barrier of iteration s.
-template <int BM, int BN, int NS, int KS, int PE, bool VO>
+template <int BM, int BN, int NS, int KS, int PE, bool VO, bool ST = false>
 __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                                                  const uint8_t *__restrict__ wq, int M, int N,
                                                  int K, int k_split, int tiles_m, int tiles_n,
@@ -1171,6 +1171,12 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
     static_assert(QA * 1024 * NC == A_BYTES && QB * 1024 * NC == B_BYTES, "whole KB per wave");
     static_assert(NS >= 2 && FN >= 1 && FM % 2 == 0, "ring of at least two slots");
     static_assert((size_t)BM * BN * 4 <= (size_t)NS * SLOT, "partial sums fit in the ring");
+    // ST (staged output): the fp16 tile goes through LDS after the exchange area, for 16-byte
+    // stores of whole row segments instead of each lane's 8 bytes
+    constexpr int XCH_BYTES = 2 * (BM / 32) * (BN / 64) * 4 * 64 * 16;
+    constexpr int STP = BN * 2 + 16;  // staged row pitch in bytes (pad spreads the banks)
+    static_assert(!ST || (VO && (size_t)XCH_BYTES + (size_t)BM * STP <= (size_t)NS * SLOT),
+                  "staged tile fits in the ring after the exchange");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     int tm, tn;
@@ -1415,6 +1421,12 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                         y[r] = fp32_value(y[r] + __half2float(__ushort_as_half((uint16_t)hv)));
                     }
                 }
+                if (ST) {
+                    const int rl = (g * FMH + ih) * 16 + fr, cl = wc * WTN + j * 16 + 4 * fg;
+                    *reinterpret_cast<uint2 *>(smem + XCH_BYTES + rl * STP + cl * 2) =
+                        make_uint2(f32x2_to_f16x2(y[0], y[1]), f32x2_to_f16x2(y[2], y[3]));
+                    continue;
+                }
                 if (m >= M) continue;
                 uint16_t *dst = epi.Y + (int64_t)m * epi.ldy + n;
                 if (VO) {
@@ -1432,6 +1444,18 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
     };
     if (ugrp == 0) finish(std::integral_constant<int, 0>{});
     else finish(std::integral_constant<int, 1>{});
+    if constexpr (ST && PE != PE_INT32) {
+        __syncthreads();  // every wave's part of the tile is in LDS
+        constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+        const int rows_here = min(BM, M - m0), cols_here = min(BN, N - n0);
+#pragma unroll 2
+        for (int c = tid; c < BM * CPR; c += 512) {
+            const int r = c / CPR, cc = c % CPR;
+            const uint4 v = *reinterpret_cast<const uint4 *>(smem + XCH_BYTES + r * STP + cc * 16);
+            if (r < rows_here && cc * 8 < cols_here)
+                *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+        }
+    }
 }
 
 // Split-K reduction of exact int32 partials, then the same epilogue.
@@ -1954,16 +1978,16 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
 
 // ---- software-pipelined GEMM launch (plan kinds SP_*)
 
-template <int BM, int BN, int NS, int KS, int PE, bool VO>
+template <int BM, int BN, int NS, int KS, int PE, bool VO, bool ST = false>
 static int launch_sp_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                        int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                        int32_t *partial)
 {
     const size_t lds = (size_t)NS * KS * (BM + BN) * BG_ROWB;
-    const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO>;
+    const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO, ST>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
-    hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO>), grid, dim3(512), lds, s, xq, wq, M, N,
-                       K, k_split, tm, tn, tile_band(tm, tn, BM, BN), epi, partial);
+    hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO, ST>), grid, dim3(512), lds, s, xq, wq, M,
+                       N, K, k_split, tm, tn, tile_band(tm, tn, BM, BN), epi, partial);
     return W4A4_OK;
 }
 
@@ -1980,7 +2004,11 @@ static int launch_sp_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_
                     ((uintptr_t)epi.w_scale % 16 == 0) &&
                     (epi.mode != W4A4_EPI_RESIDUAL ||
                      (epi.ldr % 4 == 0 && (uintptr_t)epi.residual % 8 == 0));
+    // whole 16-byte row segments of Y: the output tile is staged in LDS
+    const bool st = vo && (N % 8 == 0) && (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0);
 #define W4A4_SP_E(PEV)                                                                             \
+    if (st) return launch_sp_e<BM, BN, NS, KS, PEV, true, true>(grid, s, xq, wq, M, N, K, k_split, \
+                                                                tm, tn, epi, partial);             \
     return vo ? launch_sp_e<BM, BN, NS, KS, PEV, true>(grid, s, xq, wq, M, N, K, k_split, tm, tn,   \
                                                        epi, partial)                               \
               : launch_sp_e<BM, BN, NS, KS, PEV, false>(grid, s, xq, wq, M, N, K, k_split, tm, tn,  \
