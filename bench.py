@@ -472,51 +472,35 @@ STACK_LINEAR_SHAPES = (("qkv", "N=3072, K=1024"), ("o", "N=1024, K=1024"), ("up"
 
 def stack_kernel_times(bd, ds, Xs, reps=30):
     """Average launch duration (ms) of each linear's calls in the stack pass, on the stack's own
-    buffers (layer 0, step 0), each from a HIP graph of back-to-back launches timed with HIP events
-    on the launch stream. Where the pass fuses the next linear's rotate-quantize into a GEMM (QKV
-    produces O's codes, up produces down's), that linear's GEMM entry is the fused call and the
-    consumer has no rotate-quantize of its own (None)."""
+    buffers and wiring (layer 1 at step 0, a layer whose every input arrives quantized by the
+    producing GEMM when the residual stream is folded), each from a HIP graph of back-to-back
+    launches timed with HIP events on the launch stream. Where a GEMM writes the next linear's
+    codes in its epilogue, that GEMM entry is the fused call and the consumer has no rotate-quantize
+    of its own (None). layer0_input_rotate_quant_ms: the rotate-quantize of layer 0's QKV input
+    (the stack's input, gathered through QKV's zigzag permutation), once per step."""
     bufs = ds.bufs(Xs[0].shape[0])
-    lay = ds.layers[0]
-    h = ds.h
-    fused = ds.fold and all(lay[n].bits == 4 for n in ("qkv", "o", "up", "down"))
-    wiring = {"qkv": (Xs[0], bufs.qkv, bd.EPI_NONE, None, False, "o", 2 * h),
-              "o": (bufs.qkv[:, 2 * h:3 * h], bufs.h2, bd.EPI_RESIDUAL, Xs[0], ds.fold, None, 0),
-              "up": (bufs.h2, bufs.g, bd.EPI_GELU, None, False, "down", 0),
-              "down": (bufs.g, bufs.hs[0], bd.EPI_RESIDUAL, bufs.h2, ds.fold, None, 0)}
+    li = 1 if len(ds.layers) > 1 else 0
+    plan = ds.layer_plan(li, bufs.hs[0], bufs.hs[1], False, bufs)
     out = {}
-    for name, (X, Y, epi, res, in_order, nxt, col0) in wiring.items():
-        lin = lay[name]
-        perm = None if in_order else lin.perm
-        pre = fused and name in ("o", "down")
-        xq = bufs.xqn[lin.K] if pre else bufs.xq[(lin.K, 4)]
-        xs = bufs.xsn if pre else bufs.xs
-
-        def rq(X=X, lin=lin, perm=perm, xq=xq):
-            bd.rotate_quant_act(X, perm, lin.rot, ds.block, lin.table, ds.steps, 0, xq=xq,
-                                x_scale=bufs.xs, ws=bufs.ws[lin.K])
-
-        if fused and nxt is not None:
-            nl = lay[nxt]
-
-            def gm(lin=lin, xq=xq, Y=Y, epi=epi, res=res, nl=nl, col0=col0):
-                bd.gemm_rq_next(xq, bufs.xs, False, lin.wq, lin.w_scale, lin.K, col0, nl.K,
-                                ds.block, nl.rot, nl.table, ds.steps, 0, Y=Y, epilogue=epi,
-                                residual=res, xq_next=bufs.xqn[nl.K], x_scale_next=bufs.xsn,
-                                ws=bufs.fws[(lin.N, lin.K, nl.K)], store_next_cols=False)
-        else:
-            def gm(lin=lin, xq=xq, xs=xs, Y=Y, epi=epi, res=res):
-                bd.gemm(xq, xs, False, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi,
-                        residual=res, ws=bufs.gws[(lin.N, lin.K, 4)])
-
-        if not pre:
+    for e in plan:
+        lin = e["lin"]
+        rq = (lambda e=e: ds.rotate_quant_call(e, 0, False, bufs)) if e.get("X") is not None else None
+        gm = lambda e=e: ds.gemm_call(e, 0, False, bufs)  # noqa: E731
+        if rq is not None:
             rq()
         gm()
-        out[name] = {"N": lin.N, "K": lin.K,
-                     "rotate_quant_ms": None if pre else time_kernel_calls([rq], reps),
-                     "gemm_ms": time_kernel_calls([gm], reps),
-                     "gemm_fuses_rotate_quant_of": nxt if fused else None}
-    return out
+        nxt = e.get("nxt")
+        fuses = None if nxt is None else ("next layer's qkv" if e["name"] == "down" else
+                                          next(n for n, l2 in ds.layers[li].items() if l2 is nxt))
+        out[e["name"]] = {"N": lin.N, "K": lin.K,
+                          "rotate_quant_ms": None if rq is None else time_kernel_calls([rq], reps),
+                          "gemm_ms": time_kernel_calls([gm], reps),
+                          "gemm_fuses_rotate_quant_of": fuses,
+                          "residual_column_map": e.get("res_map") is not None}
+    e0 = ds.layer_plan(0, Xs[0], bufs.hs[1], False, bufs)[0]
+    rq0 = lambda: ds.rotate_quant_call(e0, 0, False, bufs)  # noqa: E731
+    rq0()
+    return out, time_kernel_calls([rq0], reps)
 
 
 def cpu_baseline_stack(inputs, M=1600):
@@ -584,9 +568,9 @@ def stack_headline(bd, inputs, args, result):
         result.update(value=ops / (ms * 1e-3) / 1e12, ms_per_step=ms,
                       config={"workload": "action_stack (kernel-trace mode: fixed per-step tables)"})
         return
-    kt = stack_kernel_times(bd, ds, Xs)
+    kt, rq0_ms = stack_kernel_times(bd, ds, Xs)
     calls = T * L  # launches of each linear's kernels per pass
-    # the dominant kernel: the largest total time per pass among the eight per-linear kernels
+    # the dominant kernel: the largest total time per pass among the per-linear kernels
     totals = {}
     for name, d in kt.items():
         totals[(name, "gemm")] = d["gemm_ms"] * calls
@@ -619,7 +603,8 @@ def stack_headline(bd, inputs, args, result):
         kernels[name] = {"gemm_us": d["gemm_ms"] * 1e3,
                          "gemm_tops": op / (d["gemm_ms"] * 1e-3) / 1e12,
                          "gemm_frac_int8_peak": op / (d["gemm_ms"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
-                         "gemm_fuses_rotate_quant_of": d["gemm_fuses_rotate_quant_of"]}
+                         "gemm_fuses_rotate_quant_of": d["gemm_fuses_rotate_quant_of"],
+                         "residual_column_map": d["residual_column_map"]}
         if d["rotate_quant_ms"] is not None:
             kernels[name].update(
                 rotate_quant_us=d["rotate_quant_ms"] * 1e3,
@@ -627,6 +612,12 @@ def stack_headline(bd, inputs, args, result):
                 rotate_quant_frac_hbm=by / (d["rotate_quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS)
         else:
             kernels[name]["rotate_quant_us"] = "in the producing GEMM's epilogue"
+    by0 = rq_bytes(M, h, ds.block, 2, False)
+    kernels["layer0_input"] = {
+        "rotate_quant_us": rq0_ms * 1e3, "launches_per_pass": T,
+        "rotate_quant_gbps": by0 / (rq0_ms * 1e-3) / 1e9,
+        "note": "the stack input's rotate-quantize (gather through layer 0's QKV permutation); "
+                "every later activation is quantized in its producer's epilogue"}
     result.update(
         value=ops / (ms * 1e-3) / 1e12, ms_per_step=ms,
         config={"workload": f"action_stack: {L} layers x {T} denoising steps, M = {M} tokens "

@@ -202,19 +202,30 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
  * them is the next linear), but Y must still be a valid [M][N] buffer, since the non-fused case
  * below computes them there. With block_next 128 and a 128-column tile plan (M above 64, no K
  * split, 16-byte aligned rows) the rotation and quantization run in the GEMM's epilogue on the
- * finished fp16 tile,
- * with the same arithmetic as the standalone call, so the codes are identical bit for bit; any other
- * case runs the standalone call on the same stream after the GEMM. Arguments and errors as
- * w4a4_gemm and w4a4_rotate_quant_act (per-step scale only: table_next is required); every argument
- * is checked before anything is launched. ws: w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next,
- * block_next) bytes, 256-byte aligned. */
-size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int block_next);
+ * finished fp16 tile, with the same arithmetic as the standalone call, so the codes are identical
+ * bit for bit; any other case runs the standalone call on the same stream after the GEMM.
+ * K_next == 0 (with col0 == 0) means no next linear: the call is the GEMM alone, and block_next,
+ * rot_next, table_next, num_steps, step, xq_next, x_scale_next and store_next_cols are ignored.
+ * res_cols (optional, device int32 [N], 4-byte aligned; residual epilogue only, N <= 65536): a
+ * residual column map, so that output column n adds residual[m][res_cols[n]] instead of
+ * residual[m][n]. It lets a residual stream be kept in one linear's zigzag order while the next
+ * linear's output comes out in another's. Entries must lie in [0, N); the kernels clamp any other
+ * entry into that range (no out-of-bounds access, but the sum is then meaningless). The tile plan
+ * of the stack's 64 x 128 split-group GEMM gathers the mapped residual in its epilogue; other plans
+ * gather it into the workspace first.
+ * Arguments and errors as w4a4_gemm and w4a4_rotate_quant_act (per-step scale only: table_next is
+ * required when K_next > 0); every argument is checked before anything is launched. ws:
+ * w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next, block_next, res_cols != NULL) bytes, 256-byte
+ * aligned. */
+size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int block_next,
+                                         int mapped_residual);
 int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
-                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
-                      int K_next, int block_next, const void *rot_next, const float *table_next,
-                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next,
-                      int store_next_cols, void *ws, size_t ws_bytes, hipStream_t stream);
+                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr,
+                      const int32_t *res_cols, int col0, int K_next, int block_next,
+                      const void *rot_next, const float *table_next, int num_steps, int step,
+                      uint8_t *xq_next, float *x_scale_next, int store_next_cols, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 /* Test hook: the raw int32 accumulators acc [M][N] (row-major, dense) of the same integer GEMM. */
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,

@@ -10,9 +10,10 @@ The contract is "w4a4_gemm, then w4a4_rotate_quant_act on Y[:, col0:col0+K_next]
     the quantize-stage tests;
   - on one shape the codes are also compared with the oracle's fp64 rotate-quantize of that slice
     directly (certified near-tie flips only).
-Cases cover the two stack shapes that use the fused epilogue (QKV feeding O through its V columns,
-the up-projection with GELU feeding down), a ragged row count with the residual epilogue, shapes
-that take the fallback (few tokens, block 64, a K split), the empty call and the argument errors.
+Cases cover the stack shapes that use the fused epilogue (QKV feeding O through its V columns, the
+up-projection with GELU feeding down, O and down over all their columns on the split-group tiles),
+ragged row counts, shapes that take the fallback (few tokens, block 64, a K split), the empty call
+and the argument errors.
 
 Pages: gist.science (pt) "Metodologia" 1 (rotation of each linear's input before quantization) and 2
 (per-step scale looked up from the table).
@@ -65,6 +66,13 @@ CASES = {
     "few_tokens_fallback": (50, 1024, 1024, 0, 1024, 128, EPI_GELU),
     "block64_fallback": (300, 512, 512, 0, 512, 64, EPI_NONE),
     "k_split_fallback": (260, 256, 16384, 0, 256, 128, EPI_NONE),
+    # the split-group tile kind (64 x 128, two k groups per tile) with the fused epilogue: the
+    # stack's O and down shapes over all columns, a ragged row count feeding part of the columns
+    # (tiles ordered by row band), and GELU with a long K
+    "o_shape_split_group": (1600, 1024, 1024, 0, 1024, 128, EPI_RESIDUAL),
+    "down_shape_split_group": (1600, 1024, 4096, 0, 1024, 128, EPI_RESIDUAL),
+    "split_group_ragged_part": (700, 512, 2048, 128, 256, 128, EPI_NONE),
+    "split_group_gelu": (1000, 1024, 4096, 256, 512, 128, EPI_GELU),
 }
 
 
@@ -162,3 +170,75 @@ def test_gemm_rq_next_per_token_input_and_strided_output(per_token_in, ld_pad):
         assert np.all(host(big[:, N:]).astype(np.float32) == 7.0)  # the padding is untouched
     q_ref, s_ref = bd.rotate_quant_act(Y0[:, col0:col0 + K_next], None, d["rot"], B, table, 2, 1)
     assert _same(q, q_ref) and _same(s, s_ref)
+
+
+# residual column map: output column n adds residual[:, res_cols[n]]. Expected Y: w4a4_gemm with the
+# residual's columns gathered on the host side of the comparison (torch indexing), bit for bit; the
+# codes, when a next linear is given, as the standalone rotate-quantize of that Y's columns.
+MAP_CASES = {
+    # name: (M, N, K, col0, K_next, per_token input scales)
+    "o_shape_fused_split_group": (1600, 1024, 1024, 0, 1024, False),   # map read in the epilogue
+    "down_shape_last_layer": (1600, 1024, 4096, 0, 0, False),          # no next linear
+    "ragged_fused_split_group": (700, 1024, 2048, 0, 1024, False),
+    "pipelined_plan": (333, 768, 512, 256, 512, False),     # residual gathered into the workspace
+    "few_tokens": (50, 1024, 1024, 0, 0, False),            # small-M kernel, gathered first
+    "per_token_calibration": (300, 1024, 1024, 0, 0, True),
+    "k_split": (260, 256, 16384, 0, 0, False),               # split-K partials and the gather
+}
+
+
+@pytest.mark.parametrize("name", list(MAP_CASES))
+def test_gemm_residual_column_map(name):
+    torch = __import__("torch")
+    M, N, K, col0, K_next, per_tok = MAP_CASES[name]
+    B = 128
+    idx = list(MAP_CASES).index(name)
+    d = _case(M, N, K, K_next or 128, B, EPI_RESIDUAL, 101 + idx)
+    rng = np.random.Generator(np.random.PCG64(201 + idx))
+    # a permutation, except one case that maps several outputs to the same residual column
+    cols = rng.permutation(N) if idx % 2 == 0 else rng.integers(0, N, N)
+    rmap = dev(cols.astype(np.int32))
+    xs = d["xs"]
+    if per_tok:
+        xs = dev(rng.uniform(0.01, 0.03, M).astype(np.float32))
+    res_g = d["res"][:, torch.from_numpy(cols).cuda()].contiguous()
+    Y_ref = bd.gemm(d["xq"], xs, per_tok, d["wq"], d["ws"], K, epilogue=EPI_RESIDUAL, residual=res_g)
+    table = dev(np.array([0.05, 0.02], np.float32))
+    if K_next:
+        table = _table_for(dict(d, Y0=Y_ref), col0, K_next, B)
+    Y, q, s = bd.gemm_rq_next(d["xq"], xs, per_tok, d["wq"], d["ws"], K, col0, K_next, B, d["rot"],
+                              table, 2, 1, epilogue=EPI_RESIDUAL, residual=d["res"], res_cols=rmap)
+    assert _same(Y, Y_ref), name
+    if K_next:
+        q_ref, s_ref = bd.rotate_quant_act(Y_ref[:, col0:col0 + K_next], None, d["rot"], B, table,
+                                           2, 1)
+        assert _same(q, q_ref) and _same(s, s_ref), name
+
+
+def test_gemm_residual_column_map_against_the_oracle():
+    # the mapped residual through the oracle's integer GEMM and dequantization, bit for bit
+    M, N, K = 200, 512, 512
+    d = _case(M, N, K, 128, 128, EPI_RESIDUAL, 5)
+    cols = np.random.Generator(np.random.PCG64(6)).permutation(N)
+    Y, _, _ = bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], K, 0, 0, 128, None, None,
+                              1, 0, epilogue=EPI_RESIDUAL, residual=d["res"],
+                              res_cols=dev(cols.astype(np.int32)))
+    ref = oracle.gemm(oracle.unpack_int4(host(d["xq"]), K), host(d["xs"]), False,
+                      oracle.unpack_int4(host(d["wq"]), K), host(d["ws"]), EPI_RESIDUAL,
+                      host(d["res"])[:, cols])["Y"]
+    assert np.array_equal(host(Y).view(np.uint16), ref.view(np.uint16))
+
+
+def test_gemm_residual_column_map_errors():
+    d = _case(130, 512, 256, 128, 128, EPI_NONE, 3)
+    rmap = dev(np.arange(512, dtype=np.int32))
+    table = dev(np.array([0.1], np.float32))
+    # a map without the residual epilogue; K_next = 0 with col0 != 0
+    with pytest.raises(bd.W4A4Error) as ei:
+        bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], 256, 0, 0, 128, None, None, 1, 0,
+                        res_cols=rmap)
+    assert ei.value.status == bd.W4A4_ERR_ARG
+    with pytest.raises(bd.W4A4Error) as ei:
+        bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], 256, 128, 0, 128, d["rot"], table,
+                        1, 0)
+    assert ei.value.status == bd.W4A4_ERR_SHAPE

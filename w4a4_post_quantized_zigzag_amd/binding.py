@@ -33,9 +33,9 @@ SIGNATURES = {
                                    _vp, _sz, _vp]),
     "w4a4_rotate_quant_act_hadamard": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _i, _i, _vp, _vp,
                                             _vp, _vp]),
-    "w4a4_gemm_rq_next_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
-    "w4a4_gemm_rq_next": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _i, _i,
-                               _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "w4a4_gemm_rq_next_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "w4a4_gemm_rq_next": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp,
+                               _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "w4a4_noalloc_scratch_bytes": (_sz, []),
     "w4a4_rotate_quant_act_noalloc": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp,
                                            _vp, _vp, _vp]),
@@ -282,33 +282,37 @@ def gemm(xq, x_scale, per_token: bool, wq, w_scale, K: int, Y=None, epilogue: in
 def gemm_rq_next(xq, x_scale, per_token: bool, wq, w_scale, K: int, col0: int, K_next: int,
                  block_next: int, rot_next, table_next, num_steps: int, step: int, Y=None,
                  epilogue: int = EPI_NONE, residual=None, xq_next=None, x_scale_next=None, ws=None,
-                 store_next_cols: bool = True):
+                 store_next_cols: bool = True, res_cols=None):
     """W4A4 GEMM, then the next linear's per-step rotate-quantize of Y[:, col0:col0+K_next]
     (fused into the GEMM epilogue where the tile plan allows). store_next_cols=False lets the
-    library leave those columns of Y unwritten. Returns (Y, xq_next, x_scale_next)."""
+    library leave those columns of Y unwritten. K_next = 0: no next linear. res_cols (device int32
+    [N]): residual column map, output column n adds residual[:, res_cols[n]]. Returns
+    (Y, xq_next, x_scale_next)."""
     torch = _torch()
     M, N = xq.shape[0], wq.shape[0]
     _code_cols(K, 4)
-    _code_cols(K_next, 4)
     dev_ = wq.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev_)
-    if xq_next is None:
-        xq_next = torch.empty((M, K_next // 2), dtype=torch.uint8, device=dev_)
-    if x_scale_next is None:
-        x_scale_next = torch.empty(1, dtype=torch.float32, device=dev_)
+    if K_next > 0:
+        _code_cols(K_next, 4)
+        if xq_next is None:
+            xq_next = torch.empty((M, K_next // 2), dtype=torch.uint8, device=dev_)
+        if x_scale_next is None:
+            x_scale_next = torch.empty(1, dtype=torch.float32, device=dev_)
     L = lib()
-    need = L.w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next, block_next)
+    need = L.w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next, block_next,
+                                               0 if res_cols is None else 1)
     if ws is None:
         ws, nb = _ws(need, dev_)
     else:
         nb = ws.numel()
     ldr = _row_stride(residual) if residual is not None else 0
     check(L.w4a4_gemm_rq_next(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale), M, N,
-                              K, _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, col0, K_next,
-                              block_next, _p(rot_next), _p(table_next), num_steps, step,
-                              _p(xq_next), _p(x_scale_next), 1 if store_next_cols else 0, _p(ws),
-                              nb, _stream()))
+                              K, _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, _p(res_cols),
+                              col0, K_next, block_next, _p(rot_next), _p(table_next), num_steps,
+                              step, _p(xq_next), _p(x_scale_next), 1 if store_next_cols else 0,
+                              _p(ws), nb, _stream()))
     return Y, xq_next, x_scale_next
 
 

@@ -597,7 +597,7 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
                       size_t ws_bytes, hipStream_t stream, int fmt, const RqNext *rq = nullptr,
-                      bool *rq_done = nullptr)
+                      bool *rq_done = nullptr, const int32_t *res_cols = nullptr)
 {
     int rc;
     if ((rc = check_gemm_common(xq, wq, M, N, K, fmt))) return rc;
@@ -624,6 +624,7 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     epi.mode = epilogue;
     epi.residual = residual;
     epi.ldr = ldr;
+    epi.res_cols = res_cols;
     if (rq) epi.rq = *rq;
     if ((rc = fmt == OPF_F6 ? launch_gemm_f6(xq, wq, M, N, K, epi, ws, ws_bytes, stream)
                          : launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, fmt == OPF_I8,
@@ -662,41 +663,59 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
                       residual, ldr, ws, ws_bytes, stream, OPF_I4);
 }
 
-size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int block_next)
+size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int block_next,
+                                         int mapped_residual)
 {
-    return std::max(w4a4_gemm_workspace_bytes(M, N, K),
-                    w4a4_act_workspace_bytes(M, K_next, block_next, 0));
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    const size_t gemm = mapped_residual ? gemm_mapped_residual_workspace(M, N, K)
+                                        : w4a4_gemm_workspace_bytes(M, N, K);
+    return K_next > 0 ? std::max(gemm, w4a4_act_workspace_bytes(M, K_next, block_next, 0)) : gemm;
 }
 
 int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
-                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, int col0,
-                      int K_next, int block_next, const void *rot_next, const float *table_next,
-                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next,
-                      int store_next_cols, void *ws, size_t ws_bytes, hipStream_t stream)
+                      int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr,
+                      const int32_t *res_cols, int col0, int K_next, int block_next,
+                      const void *rot_next, const float *table_next, int num_steps, int step,
+                      uint8_t *xq_next, float *x_scale_next, int store_next_cols, void *ws,
+                      size_t ws_bytes, hipStream_t stream)
 {
-    // every argument of the rotate-quantize half is checked before anything is launched
+    // every argument of the rotate-quantize half and of the residual map is checked before
+    // anything is launched
     int rc;
-    if (col0 < 0 || K_next <= 0 || (int64_t)col0 + K_next > N)
+    if (res_cols) {
+        if (epilogue != W4A4_EPI_RESIDUAL)
+            return fail(W4A4_ERR_ARG, "res_cols needs the residual epilogue");
+        if (!aligned(res_cols, 4)) return fail(W4A4_ERR_ALIGN, "res_cols misaligned");
+        if (N > 65536) return fail(W4A4_ERR_UNSUPPORTED, "res_cols with N = %d > 65536", N);
+    }
+    if (K_next < 0 || col0 < 0 || (int64_t)col0 + K_next > N || (K_next == 0 && col0 != 0))
         return fail(W4A4_ERR_SHAPE, "columns [%d, %d + %d) outside the N = %d outputs", col0, col0,
                     K_next, N);
-    if ((rc = check_kb(K_next, block_next))) return rc;
-    if (!rot_next) return fail(W4A4_ERR_ARG, "rot_next is NULL");
-    if (!aligned(rot_next, 16)) return fail(W4A4_ERR_ALIGN, "rot_next must be 16-byte aligned");
-    if (!table_next) return fail(W4A4_ERR_ARG, "table_next is required (per-step scale)");
-    if (!aligned(table_next, 4)) return fail(W4A4_ERR_ALIGN, "table_next misaligned");
-    if (num_steps <= 0)
-        return fail(W4A4_ERR_STEP_RANGE, "num_steps = %d must be positive", num_steps);
-    if (step < 0 || step >= num_steps)
-        return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
-    if (M > 0 && (!xq_next || !x_scale_next))
-        return fail(W4A4_ERR_ARG, "xq_next and x_scale_next are required");
-    if (!aligned(x_scale_next, 4)) return fail(W4A4_ERR_ALIGN, "x_scale_next misaligned");
+    if (K_next > 0) {
+        if ((rc = check_kb(K_next, block_next))) return rc;
+        if (!rot_next) return fail(W4A4_ERR_ARG, "rot_next is NULL");
+        if (!aligned(rot_next, 16)) return fail(W4A4_ERR_ALIGN, "rot_next must be 16-byte aligned");
+        if (!table_next) return fail(W4A4_ERR_ARG, "table_next is required (per-step scale)");
+        if (!aligned(table_next, 4)) return fail(W4A4_ERR_ALIGN, "table_next misaligned");
+        if (num_steps <= 0)
+            return fail(W4A4_ERR_STEP_RANGE, "num_steps = %d must be positive", num_steps);
+        if (step < 0 || step >= num_steps)
+            return fail(W4A4_ERR_STEP_RANGE, "step %d outside [0, %d)", step, num_steps);
+        if (M > 0 && (!xq_next || !x_scale_next))
+            return fail(W4A4_ERR_ARG, "xq_next and x_scale_next are required");
+        if (!aligned(x_scale_next, 4)) return fail(W4A4_ERR_ALIGN, "x_scale_next misaligned");
+    }
     if (M > 0 && (!Y || !aligned(Y + col0, 2)))
         return fail(W4A4_ERR_ARG, "Y is required");
     if ((rc = check_ws(ws, ws_bytes,
-                       M > 0 ? w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next, block_next) : 0)))
+                       M > 0 ? w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next, block_next,
+                                                                 res_cols != nullptr)
+                             : 0)))
         return rc;
+    if (K_next == 0)
+        return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
+                          residual, ldr, ws, ws_bytes, stream, OPF_I4, nullptr, nullptr, res_cols);
     const RotLayout L = rot_layout(K_next, block_next);
     const char *rb = reinterpret_cast<const char *>(rot_next);
     const RqNext rq{reinterpret_cast<const _Float16 *>(rb + L.r32),
@@ -705,7 +724,7 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     bool done = false;
     if ((rc = gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
                          residual, ldr, ws, ws_bytes, stream, OPF_I4,
-                         block_next == 128 ? &rq : nullptr, &done)))
+                         block_next == 128 ? &rq : nullptr, &done, res_cols)))
         return rc;
     if (done || M == 0) return ok();
     // no fused tile plan for this shape: the rotate-quantize of the columns, after the GEMM on

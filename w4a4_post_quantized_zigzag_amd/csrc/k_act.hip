@@ -1000,15 +1000,17 @@ __global__ __launch_bounds__(256) void k_permute_rows(const uint16_t *__restrict
         for (int c = tid * 8; c < K; c += 256 * 8) {
             const int4 p0 = *reinterpret_cast<const int4 *>(&perm[c]);
             const int4 p1 = *reinterpret_cast<const int4 *>(&perm[c + 4]);
+            // entries outside [0, K) (not a permutation) read a clamped element, never past the row
+            auto at = [&](int i) { return (uint32_t)srow[min(max(i, 0), K - 1)]; };
             uint4 v;
-            v.x = (uint32_t)srow[p0.x] | ((uint32_t)srow[p0.y] << 16);
-            v.y = (uint32_t)srow[p0.z] | ((uint32_t)srow[p0.w] << 16);
-            v.z = (uint32_t)srow[p1.x] | ((uint32_t)srow[p1.y] << 16);
-            v.w = (uint32_t)srow[p1.z] | ((uint32_t)srow[p1.w] << 16);
+            v.x = at(p0.x) | (at(p0.y) << 16);
+            v.y = at(p0.z) | (at(p0.w) << 16);
+            v.z = at(p1.x) | (at(p1.y) << 16);
+            v.w = at(p1.z) | (at(p1.w) << 16);
             *reinterpret_cast<uint4 *>(&out[c]) = v;
         }
     } else {
-        for (int c = tid; c < K; c += 256) out[c] = srow[perm[c]];
+        for (int c = tid; c < K; c += 256) out[c] = srow[min(max(perm[c], 0), K - 1)];
     }
 }
 

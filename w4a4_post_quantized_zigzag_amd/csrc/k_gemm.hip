@@ -1150,7 +1150,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
 // At iteration s the ring holds stage s (already in registers), s+1 (being read) and up to NS-2
 // stages in flight; the slot refilled at iteration s held stage s-1, whose fragment reads every
 // wave finished before the barrier of iteration s.
-template <int BM, int BN, int NS, int KS, int PE, bool VO, bool ST = false>
+template <int BM, int BN, int NS, int KS, int PE, bool VO, bool ST = false, bool RQN = false,
+          bool RMAP = false>
 __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                                                  const uint8_t *__restrict__ wq, int M, int N,
                                                  int K, int k_split, int tiles_m, int tiles_n,
@@ -1167,7 +1168,7 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
     constexpr int QA = A_BYTES / 1024 / NC, QB = B_BYTES / 1024 / NC;  // DMA instrs per sub-stage
     constexpr int L = KS * (QA + QB);                                  // DMA instrs per slot
     constexpr int NF = FM + FN;
-    constexpr bool RES_EARLY = (PE == PE_RESIDUAL) && (FMH * FN <= 16);
+    constexpr bool RES_EARLY = (PE == PE_RESIDUAL) && (FMH * FN <= 16) && !RMAP;
     static_assert(QA * 1024 * NC == A_BYTES && QB * 1024 * NC == B_BYTES, "whole KB per wave");
     static_assert(NS >= 2 && FN >= 1 && FM % 2 == 0, "ring of at least two slots");
     static_assert((size_t)BM * BN * 4 <= (size_t)NS * SLOT, "partial sums fit in the ring");
@@ -1177,6 +1178,18 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
     constexpr int STP = BN * 2 + 16;  // staged row pitch in bytes (pad spreads the banks)
     static_assert(!ST || (VO && (size_t)XCH_BYTES + (size_t)BM * STP <= (size_t)NS * SLOT),
                   "staged tile fits in the ring after the exchange");
+    // RQN: the next linear's rotate-quantize of the staged tile (a 128-column rotation block), its
+    // codes staged after the tile (64 bytes per row)
+    static_assert(!RQN || (ST && BN == 128 && PE != PE_INT32 &&
+                           (size_t)XCH_BYTES + (size_t)BM * (STP + 64) <= (size_t)NS * SLOT),
+                  "fused rotate-quantize: staged 128-column tiles");
+    // RMAP (residual column map epi.res_cols): the tile's residual is gathered row by row into LDS
+    // after the codes area, and the epilogue reads it from there in the fragment layout
+    constexpr int RES_OFF = XCH_BYTES + BM * STP + (RQN ? BM * 64 : 0);
+    constexpr int RPT = BM * BN / 512;  // residual elements each thread gathers
+    static_assert(!RMAP || (ST && PE == PE_RESIDUAL && BN <= 512 && 512 % BN == 0 &&
+                            (size_t)RES_OFF + (size_t)BM * STP <= (size_t)NS * SLOT),
+                  "mapped residual: staged tiles with room for the residual tile");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     int tm, tn;
@@ -1235,6 +1248,14 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                 }
         }
     }
+
+    // RMAP: thread -> tile column tid % BN and rows tid / BN + r (512 / BN) of the residual gather.
+    // Its source column is read now; the gather itself is issued in the last main-loop iteration,
+    // under that iteration's matrix work. Columns and map entries are clamped into [0, N).
+    const int rcol = tid % BN, rrow0 = tid / BN;
+    int rsrc = 0;
+    if (RMAP) rsrc = min(max(epi.res_cols[min(n0 + rcol, N - 1)], 0), N - 1);
+    uint16_t rgv[RMAP ? RPT : 1];
 
     const uint8_t *srcA[QA];
     const uint8_t *srcB[QB];
@@ -1328,15 +1349,43 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (s + NS - 1 < stages) issue(s + NS - 1);
+        if (RMAP && s == stages - 1) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int m = min(m0 + rrow0 + r * (512 / BN), M - 1);
+                rgv[r] = epi.residual[(int64_t)m * epi.ldr + rsrc];
+            }
+        }
         read_frags(s, F);
         compute(F);
     }
+
+    // RQN: when this tile's 128 columns are rotation block rb of the next linear's input, each
+    // wave rotates 16 of its channels once the fp16 tile is staged. The R_rb fragments and the
+    // step scale are loaded here, so their latency hides under the exchange and the dequantization.
+    const bool rq_tile = RQN && n0 >= epi.rq.col0 && n0 < epi.rq.col0 + epi.rq.kn;
+    const int rb = RQN ? (n0 - epi.rq.col0) / 128 : 0;
+    v8h rqh[1][4], rql[1][4];
+    StepScale rss{0.0f, 0.0f};
+    if (RQN && rq_tile) {
+        load_rot_frags<1, 4>(epi.rq.rhi, epi.rq.rlo, rb, wave * 16, lane, 128, rqh, rql);
+        rss = step_scale(epi.rq.table, epi.rq.step);
+    }
+    if (RQN) __builtin_amdgcn_sched_barrier(0);
 
     // Exchange the k groups' partial sums through LDS: group g keeps fragment rows i in its half
     // and sends the other half. Slot layout: [sender group][fragment row in half][FN][column wave]
     // x 64 lanes x 16 bytes. The group index is made a compile-time constant (one copy of the
     // epilogue per group) so that the accumulators stay in registers.
     __syncthreads();  // every wave is past its last fragment read
+    if (RMAP) {
+        // the gathered residual tile, row pitch STP like the staged output; read after the
+        // exchange barrier inside finish
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            *reinterpret_cast<uint16_t *>(smem + RES_OFF + (rrow0 + r * (512 / BN)) * STP + 2 * rcol) =
+                rgv[r];
+    }
     auto finish = [&](auto G) {
         constexpr int g = decltype(G)::value, other = 1 - g;
         int4 *xch = reinterpret_cast<int4 *>(smem);
@@ -1391,6 +1440,13 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                     if (RES_EARLY) {
                         rl[j][0] = rsd[RES_EARLY ? ih : 0][RES_EARLY ? j : 0][0];
                         rl[j][1] = rsd[RES_EARLY ? ih : 0][RES_EARLY ? j : 0][1];
+                        continue;
+                    }
+                    if (RMAP) {
+                        const int rloc = (g * FMH + ih) * 16 + fr, cloc = wc * WTN + j * 16 + 4 * fg;
+                        const uint2 v = *reinterpret_cast<const uint2 *>(smem + RES_OFF + rloc * STP +
+                                                                         2 * cloc);
+                        rl[j][0] = v.x; rl[j][1] = v.y;
                         continue;
                     }
                     const int n = ncol + j * 16;
@@ -1448,12 +1504,40 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
         __syncthreads();  // every wave's part of the tile is in LDS
         constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
         const int rows_here = min(BM, M - m0), cols_here = min(BN, N - n0);
+        uint8_t *sq = smem + XCH_BYTES + BM * STP;  // RQN: the tile's codes
+        if (RQN && rq_tile) {
+            // x' = y R_rb on the staged fp16 tile with the streaming rotate-quantize's arithmetic
+            // and order: lane inputs are 8 consecutive columns 8 (4 kk + fg) of row 16 mf + fr
+            v4f racc[BM / 16][1];
+            rotate_acc<BM / 16, 1, 4>(rqh, rql, [&](int mf, int kk) {
+                return *reinterpret_cast<const v8h *>(smem + XCH_BYTES + (mf * 16 + fr) * STP +
+                                                      16 * (4 * kk + fg));
+            }, racc);
+            const float rs = rss.rcp * (1.0f / (1 << ROT_LO_SHIFT));
+#pragma unroll
+            for (int mf = 0; mf < BM / 16; ++mf)
+                *reinterpret_cast<uint16_t *>(&sq[(mf * 16 + fr) * 64 + (wave * 16 + 4 * fg) / 2]) =
+                    (uint16_t)quant_pack4(racc[mf][0], rs);
+        }
+        // the fp16 tile, unless it only feeds the next linear and the caller does not need it
+        const bool store_tile = !(RQN && rq_tile && !epi.rq.store_y);
 #pragma unroll 2
         for (int c = tid; c < BM * CPR; c += 512) {
             const int r = c / CPR, cc = c % CPR;
             const uint4 v = *reinterpret_cast<const uint4 *>(smem + XCH_BYTES + r * STP + cc * 16);
-            if (r < rows_here && cc * 8 < cols_here)
+            if (store_tile && r < rows_here && cc * 8 < cols_here)
                 *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+        }
+        if (RQN && rq_tile) {
+            __syncthreads();  // every wave's codes are in LDS
+            const int64_t ldq = epi.rq.kn / 2;
+            for (int c = tid; c < BM * 4; c += 512) {
+                const int r = c >> 2, ch = c & 3;
+                if (r < rows_here)
+                    *reinterpret_cast<uint4 *>(epi.rq.xq + (int64_t)(m0 + r) * ldq + rb * 64 + 16 * ch) =
+                        *reinterpret_cast<const uint4 *>(&sq[r * 64 + 16 * ch]);
+            }
+            if (m0 == 0 && rb == 0 && tid == 0) epi.rq.x_scale[0] = rss.s;
         }
     }
 }
@@ -1827,7 +1911,8 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = fals
     for (int ci = 0; ci < ncand; ++ci) {
         const Cand &c = cands[ci];
         if (c.kind == 4 && !pipe) continue;
-        if (bn128_pipe && c.kind != 3 && c.kind != 4) continue;  // the fused rotate-quantize tiles
+        // the fused rotate-quantize tiles: 128 columns, pipelined or split-group
+        if (bn128_pipe && c.kind != 3 && c.kind != 4 && c.kind != SP_64x128) continue;
         if (c.kind >= SP_128x128 && K % c.gran) continue;  // whole ring slots only
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         // up to 256 splits: K <= 2^24 then always fits pieces of at most MAX_K_SPLIT k, the most
@@ -1978,17 +2063,54 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
 
 // ---- software-pipelined GEMM launch (plan kinds SP_*)
 
-template <int BM, int BN, int NS, int KS, int PE, bool VO, bool ST = false>
+// Whether a split-group tile kind has LDS room to gather a mapped residual tile next to its staged
+// output and codes (k_gemm_sp's RMAP form).
+template <int BM, int BN, int NS, int KS>
+constexpr bool sp_rmap_fits()
+{
+    constexpr size_t xch = 2 * (BM / 32) * (BN / 64) * 4 * 64 * 16, stp = BN * 2 + 16;
+    return BN <= 512 && 512 % BN == 0 &&
+           xch + BM * stp + BM * 64 + BM * stp <= (size_t)NS * KS * (BM + BN) * BG_ROWB;
+}
+static bool sp_kind_maps_residual(int kind) { return kind == SP_64x128; }
+
+template <int BM, int BN, int NS, int KS, int PE, bool VO, bool ST = false, bool RQN = false,
+          bool RMAP = false>
 static int launch_sp_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                        int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
-                       int32_t *partial)
+                       int32_t *partial, int band = 0)
 {
     const size_t lds = (size_t)NS * KS * (BM + BN) * BG_ROWB;
-    const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO, ST>;
+    const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO, ST, RQN, RMAP>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
-    hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO, ST>), grid, dim3(512), lds, s, xq, wq, M,
-                       N, K, k_split, tm, tn, tile_band(tm, tn, BM, BN), epi, partial);
+    hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO, ST, RQN, RMAP>), grid, dim3(512), lds, s, xq,
+                       wq, M, N, K, k_split, tm, tn, band > 0 ? band : tile_band(tm, tn, BM, BN),
+                       epi, partial);
     return W4A4_OK;
+}
+
+// The split-group GEMM with the next linear's rotate-quantize in the staged epilogue (no K split;
+// the caller has checked the staged-store conditions). A launch whose rotated columns are only part
+// of N orders its tiles by row band, as the pipelined form does.
+template <int BM, int NS, int KS>
+static int launch_sp_rq(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
+                        int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi)
+{
+    const int band = (epi.rq.col0 > 0 || epi.rq.kn < N) ? tn : 0;
+    if (epi.mode == W4A4_EPI_GELU)
+        return launch_sp_e<BM, 128, NS, KS, PE_GELU, true, true, true>(
+            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
+    if (epi.mode == W4A4_EPI_RESIDUAL && epi.res_cols) {
+        if constexpr (sp_rmap_fits<BM, 128, NS, KS>())
+            return launch_sp_e<BM, 128, NS, KS, PE_RESIDUAL, true, true, true, true>(
+                grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
+        return fail(W4A4_ERR_UNSUPPORTED, "mapped residual needs the staged split-group epilogue");
+    }
+    if (epi.mode == W4A4_EPI_RESIDUAL)
+        return launch_sp_e<BM, 128, NS, KS, PE_RESIDUAL, true, true, true>(
+            grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
+    return launch_sp_e<BM, 128, NS, KS, PE_NONE, true, true, true>(
+        grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
 }
 
 template <int BM, int BN, int NS, int KS>
@@ -2014,6 +2136,15 @@ static int launch_sp_t(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_
               : launch_sp_e<BM, BN, NS, KS, PEV, false>(grid, s, xq, wq, M, N, K, k_split, tm, tn,  \
                                                         epi, partial);
     if (epi.mode == W4A4_EPI_GELU) { W4A4_SP_E(PE_GELU) }
+    if (epi.mode == W4A4_EPI_RESIDUAL && epi.res_cols) {
+        // launch_gemm routes a residual column map here only for such kinds and staged stores
+        if constexpr (sp_rmap_fits<BM, BN, NS, KS>()) {
+            if (st)
+                return launch_sp_e<BM, BN, NS, KS, PE_RESIDUAL, true, true, false, true>(
+                    grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
+        }
+        return fail(W4A4_ERR_UNSUPPORTED, "mapped residual needs the staged split-group epilogue");
+    }
     if (epi.mode == W4A4_EPI_RESIDUAL) { W4A4_SP_E(PE_RESIDUAL) }
     W4A4_SP_E(PE_NONE)
 #undef W4A4_SP_E
@@ -2105,35 +2236,71 @@ static void launch_smallm_wide(SmallmShape sh, bool q8, hipStream_t s, const uin
 
 // q8: int8 operands [rows][K] (W8A8); the caller guarantees K % 64 == 0 and 16-byte aligned
 // operands for them.
-int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
+size_t gemm_mapped_residual_workspace(int M, int N, int K)
+{
+    return align_up(gemm_workspace(M, N, K, false), 256) + align_up((size_t)M * N * 2, 256);
+}
+
+int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi_in,
                 void *ws, size_t ws_bytes, hipStream_t s, bool q8, bool *rq_done)
 {
     if (rq_done) *rq_done = false;
     if (M == 0) return W4A4_OK;
+    GemmEpilogue epi = epi_in;
+    if (epi.mode != W4A4_EPI_RESIDUAL) epi.res_cols = nullptr;
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     const bool pipe = q8 || (vec && K % BG_KS == 0);
     GemmPlan p = plan_gemm(M, N, K, q8 ? BG_ROWB : BG_KS, pipe, pipe && !q8,
                            epi.mode == W4A4_EPI_GELU);
-    // the next linear's rotate-quantize in the epilogue: a 128-column pipelined tile plan without a
-    // K split, the staged (16-byte) epilogue, 128-aligned columns; else the caller runs it
+    // the next linear's rotate-quantize in the epilogue: a 128-column pipelined or split-group tile
+    // plan without a K split, the staged (16-byte) epilogue, 128-aligned columns; else the caller
+    // runs it
     const bool vo_rows = (N % 8 == 0) && (epi.ldy % 8 == 0) && ((uintptr_t)epi.Y % 16 == 0) &&
                          ((uintptr_t)epi.w_scale % 16 == 0) &&
                          (epi.mode != W4A4_EPI_RESIDUAL ||
                           (epi.ldr % 8 == 0 && (uintptr_t)epi.residual % 16 == 0));
-    if (epi.rq.xq && !q8 && pipe && vo_rows && epi.mode != GEMM_OUT_I32 &&
-        epi.rq.col0 % 128 == 0 && epi.rq.kn % 128 == 0 && (uintptr_t)epi.rq.xq % 16 == 0) {
-        const GemmPlan f = plan_gemm(M, N, K, BG_KS, true, false, epi.mode == W4A4_EPI_GELU, true);
-        if ((f.kind == 3 || f.kind == 4) && f.splits == 1) {
-            const int tm = (M + f.bm - 1) / f.bm, tn = (N + f.bn - 1) / f.bn;
-            const dim3 grid(tm * tn, 1);
-            const int rc = f.kind == 4
-                               ? launch_pipe_rq<64, 1, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi)
-                               : launch_pipe_rq<128, 2, 2>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
+    const bool fuse = epi.rq.xq && !q8 && pipe && vo_rows && epi.mode != GEMM_OUT_I32 &&
+                      epi.rq.col0 % 128 == 0 && epi.rq.kn % 128 == 0 &&
+                      (uintptr_t)epi.rq.xq % 16 == 0;
+    GemmPlan f{};
+    const bool fused = fuse && [&] {
+        f = plan_gemm(M, N, K, BG_KS, true, true, epi.mode == W4A4_EPI_GELU, true);
+        return (f.kind == 3 || f.kind == 4 || sp_kind_maps_residual(f.kind)) && f.splits == 1;
+    }();
+    // A residual column map is read in the split-group kernel's staged epilogue; any other plan
+    // gets the residual gathered into the workspace (after the split-K partials) first.
+    if (epi.res_cols) {
+        const bool in_kernel = fused ? sp_kind_maps_residual(f.kind)
+                                     : (!q8 && sp_kind_maps_residual(p.kind) && p.splits == 1 &&
+                                        vo_rows);
+        if (!in_kernel) {
+            const size_t off = align_up(gemm_workspace(M, N, K, q8), 256);
+            if (!ws || ws_bytes < off + align_up((size_t)M * N * 2, 256))
+                return fail(W4A4_ERR_WORKSPACE, "gemm with a residual map needs %zu workspace bytes",
+                            off + align_up((size_t)M * N * 2, 256));
+            uint16_t *gathered = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + off);
+            const int rc = launch_permute_rows(epi.residual, M, N, epi.ldr, epi.res_cols, gathered,
+                                               nullptr, s);
             if (rc != W4A4_OK) return rc;
-            if (rq_done) *rq_done = true;
-            return check_launch("gemm + next rotate-quantize");
+            epi.residual = gathered;
+            epi.ldr = N;
+            epi.res_cols = nullptr;
         }
+    }
+    if (fused) {
+        const int tm = (M + f.bm - 1) / f.bm, tn = (N + f.bn - 1) / f.bn;
+        const dim3 grid(tm * tn, 1);
+        int rc;
+        if (f.kind == SP_64x128)
+            rc = launch_sp_rq<64, 3, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
+        else if (f.kind == 4)
+            rc = launch_pipe_rq<64, 1, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
+        else
+            rc = launch_pipe_rq<128, 2, 2>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
+        if (rc != W4A4_OK) return rc;
+        if (rq_done) *rq_done = true;
+        return check_launch("gemm + next rotate-quantize");
     }
     // the small-M kernels cover at most SMALL_M rows: a plan without a tile kernel beyond that
     // would leave rows unwritten, so it is refused loudly (no such plan exists for K <= 2^24)

@@ -190,6 +190,10 @@ struct GemmEpilogue {
     int64_t ldr;
     int32_t *acc_out;  // GEMM_OUT_I32 destination, dense [M][N]
     RqNext rq;
+    // residual column map (W4A4_EPI_RESIDUAL): output column n adds residual column res_cols[n]
+    // (nullptr: column n). launch_gemm reads it in the split-group kernel's staged epilogue, or
+    // gathers the residual into its workspace first.
+    const int32_t *res_cols;
 };
 constexpr int GEMM_OUT_I32 = 100;
 // q8: int8 operands [rows][K] (W8A8) instead of packed int4 [rows][K/2]
@@ -198,6 +202,9 @@ size_t gemm_workspace(int M, int N, int K, bool q8);
 // (a 128-column tile plan with the staged epilogue); otherwise the caller runs the rotate-quantize.
 int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const GemmEpilogue &epi,
                 void *ws, size_t ws_bytes, hipStream_t s, bool q8, bool *rq_done = nullptr);
+// Workspace of a launch_gemm call with a residual column map: the split-K partials of its plan, or
+// the gathered residual [M][N] fp16 when the plan cannot read the map in its epilogue.
+size_t gemm_mapped_residual_workspace(int M, int N, int K);
 // group-wise activation scales epi.x_scale[K / 128] (int4, K % 128 == 0, 16-byte aligned operands)
 int launch_gemm_grouped(const uint8_t *xq, const uint8_t *wq, int M, int N, int K,
                         const GemmEpilogue &epi, hipStream_t s);

@@ -28,21 +28,32 @@ class DeviceLinear:
     """One linear's device state. row_perm (optional, device int64 [N]) reorders the output
     channels: the packed weights hold rows W[row_perm], so output column j is channel row_perm[j].
     The zigzag permutation and block SVD are computed on W itself (the row order of W does not
-    change them); only the packed rows move."""
+    change them); only the packed rows move, when pack() is called."""
 
-    def __init__(self, W, block: int, steps: int, perm=None, U=None, bits: int = 4, row_perm=None):
+    def __init__(self, W, block: int, steps: int, perm=None, U=None, bits: int = 4):
         torch = _torch()
-        Wd = W if isinstance(W, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(W)).cuda()
-        self.N, self.K = Wd.shape
+        self._W = W if isinstance(W, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(W)).cuda()
+        self.N, self.K = self._W.shape
         self.B = block
-        self.perm = bd.zigzag_perm(Wd, block) if perm is None else perm
-        self.U = bd.block_svd(Wd, self.perm, block) if U is None else U
+        self.perm = bd.zigzag_perm(self._W, block) if perm is None else perm
+        self.U = bd.block_svd(self._W, self.perm, block) if U is None else U
         self.bits = bits
-        Wp = Wd if row_perm is None else Wd.index_select(0, row_perm).contiguous()
-        self.wq, self.w_scale, self.rot = bd.pack_weights(Wp, self.perm, self.U, block, bits=bits)
-        self.row_perm = row_perm
         self.table = torch.empty(steps, dtype=torch.float32, device="cuda")
         self.steps = steps
+
+    def pack(self, row_perm=None):
+        W = self._W if row_perm is None else self._W.index_select(0, row_perm).contiguous()
+        self.wq, self.w_scale, self.rot = bd.pack_weights(W, self.perm, self.U, self.B, bits=self.bits)
+        self.row_perm = row_perm
+        self._W = None
+        return self
+
+
+def _inverse(p):
+    torch = _torch()
+    inv = torch.empty_like(p)
+    inv[p] = torch.arange(p.numel(), device=p.device, dtype=p.dtype)
+    return inv
 
 
 class _Buffers:
@@ -62,22 +73,33 @@ class _Buffers:
                                            bd.lib().w4a4_gemm_w8a8_workspace_bytes)(rows, N, K)),
                                  torch.uint8)
                     for N, K in ((3 * h, h), (h, h), (f, h), (h, f)) for b in (4, 8)}
-        # codes and scale of O's and down's inputs written by the producing GEMM (QKV, up): apart
-        # from xq / xs, which that GEMM is still reading
+        # codes and scale written by a producing GEMM for the next linear: apart from xq / xs,
+        # which that GEMM is still reading
         self.xqn = {K: e((rows, K // 2), torch.uint8) for K in (h, f)}
         self.xsn = e(1, torch.float32)
-        self.fws = {(N, K, Kn): e(max(256, bd.lib().w4a4_gemm_rq_next_workspace_bytes(
-            rows, N, K, Kn, block)), torch.uint8) for N, K, Kn in ((3 * h, h, h), (f, h, f))}
+        # w4a4_gemm_rq_next workspaces, by (N, K, K_next, residual map)
+        self.fws = {key: e(max(256, bd.lib().w4a4_gemm_rq_next_workspace_bytes(
+            rows, key[0], key[1], key[2], block, key[3])), torch.uint8)
+            for key in ((3 * h, h, h, 0), (h, h, h, 1), (f, h, f, 0), (h, f, h, 1), (h, h, 0, 1),
+                        (h, f, 0, 1))}
 
 
 class DeviceStack:
     """weights: list (one per layer) of dicts qkv [3h,h], o [h,h], up [f,h], down [h,f] (fp16).
     calib: optional list of per-layer dicts name -> (perm, U) device tensors to use instead of the
     device calibration kernels. w8: names of the linears run as W8A8 (e.g. ("o", "down")).
-    fold_perms: the V slice of QKV and the up-projection output each feed one linear only (O and
-    down), so their producers store them directly in that consumer's zigzag order (QKV's V rows and
-    up's rows are packed permuted) and O and down quantize contiguous rows with perm = NULL. The
-    arithmetic is unchanged: a permutation is exact."""
+
+    fold_perms: each linear's zigzag permutation is folded into the row order of the linear that
+    produces its input, so that input comes out already in zigzag order and is rotated and quantized
+    from contiguous columns (perm = NULL). The arithmetic is unchanged: a permutation is exact, and
+    every output handed to the test hooks is put back in natural channel order.
+      - With a W8A8 linear in the stack, only the single-consumer activations are folded: QKV's V
+        rows in O's order and up's rows in down's order.
+      - With every linear W4A4, the residual stream is folded as well: O's rows come out in up's
+        order and down's rows in the next layer's QKV order (the last layer's in natural order).
+        The residual that O and down add is then read through a column map (w4a4_gemm_rq_next's
+        res_cols). Outside calibration every rotate-quantize but layer 0's QKV input then runs in
+        the epilogue of the GEMM that produces the activation."""
 
     def __init__(self, weights, block: int, steps: int, calib=None, w8=(), fold_perms: bool = True):
         torch = _torch()
@@ -85,24 +107,40 @@ class DeviceStack:
         self.h = weights[0]["o"].shape[0]
         self.f = weights[0]["up"].shape[0]
         self.fold = fold_perms
+        self.stream = fold_perms and not w8
         h = self.h
-        self.layers = []
+        nl = len(weights)
+        lin = []
         for li, lw in enumerate(weights):
-            layer = {}
             pu = lambda n: calib[li][n] if calib is not None else (None, None)  # noqa: E731
-            bits = lambda n: 8 if n in w8 else 4  # noqa: E731
-            for name in ("o", "down"):
-                layer[name] = DeviceLinear(lw[name], block, steps, *pu(name), bits=bits(name))
-            rp_qkv = rp_up = None
+            lin.append({n: DeviceLinear(lw[n], block, steps, *pu(n), bits=8 if n in w8 else 4)
+                        for n in LINEARS})
+        perm = lambda li, n: lin[li][n].perm.to(torch.int64)  # noqa: E731
+        self.res_map = []
+        for li in range(nl):
+            rp = dict.fromkeys(LINEARS)
             if fold_perms:
-                po = layer["o"].perm.to(torch.int64)
-                rp_qkv = torch.cat([torch.arange(2 * h, device="cuda", dtype=torch.int64), 2 * h + po])
-                rp_up = layer["down"].perm.to(torch.int64)
-            layer["qkv"] = DeviceLinear(lw["qkv"], block, steps, *pu("qkv"), bits=bits("qkv"),
-                                        row_perm=rp_qkv)
-            layer["up"] = DeviceLinear(lw["up"], block, steps, *pu("up"), bits=bits("up"),
-                                       row_perm=rp_up)
-            self.layers.append({n: layer[n] for n in LINEARS})
+                rp["qkv"] = torch.cat([torch.arange(2 * h, device="cuda", dtype=torch.int64),
+                                       2 * h + perm(li, "o")])
+                rp["up"] = perm(li, "down")
+            maps = {}
+            if self.stream:
+                # storage order of the residual stream entering layer li (None: natural) and of
+                # the one leaving it
+                q_in = perm(li, "qkv") if li > 0 else None
+                q_out = perm(li + 1, "qkv") if li + 1 < nl else None
+                rp["o"] = perm(li, "up")
+                rp["down"] = q_out
+                # O's column j adds channel rp["o"][j] of the stream, stored at inv(q_in)[...];
+                # down's column j adds channel rp["down"][j] of O's output, stored in up's order
+                m_o = rp["o"] if q_in is None else _inverse(q_in)[rp["o"]]
+                inv_u = _inverse(rp["o"])
+                m_d = inv_u if q_out is None else inv_u[q_out]
+                maps = {"o": m_o.to(torch.int32).contiguous(), "down": m_d.to(torch.int32).contiguous()}
+            for n in LINEARS:
+                lin[li][n].pack(rp[n])
+            self.res_map.append(maps)
+        self.layers = lin
         self._bufs = {}
 
     def bufs(self, rows: int) -> _Buffers:
@@ -117,73 +155,114 @@ class DeviceStack:
             for name in LINEARS:
                 layer[name].table.copy_(torch.from_numpy(np.asarray(tl[name], np.float32)))
 
-    def _linear(self, lin, X, Y, step, calib, bufs, epi=bd.EPI_NONE, res=None, in_order=False,
-                record=None, pre=False, nxt=None, col0=0, keep=False):
-        """Rotate-quantize X (unless pre: the producing GEMM already wrote this linear's codes into
-        bufs.xqn / bufs.xsn), then the GEMM; with nxt (the next linear, whose input is Y[:, col0:]
-        in its zigzag order), the GEMM also writes nxt's codes (w4a4_gemm_rq_next) and, unless keep
-        (the test hooks read them), does not store those fp16 columns, whose only consumer is nxt."""
-        b = lin.bits
-        perm = None if in_order else lin.perm  # in_order: X already holds the zigzag order
-        if pre:
-            xq, xs = bufs.xqn[lin.K], bufs.xsn
-        else:
-            if calib:
-                bd.calibrate_act_scale(X, perm, lin.rot, self.block, out=lin.table[step:step + 1],
-                                       ws=bufs.cws[lin.K], bits=b)
-            xq, xs = bufs.xq[(lin.K, b)], bufs.xs
-            bd.rotate_quant_act(X, perm, lin.rot, self.block, None if calib else lin.table,
-                                self.steps, step, xq=xq, x_scale=xs, ws=bufs.ws[lin.K], bits=b)
-        if record is not None:
-            record(xq, xs[:X.shape[0] if calib else 1])
-        if nxt is not None:
-            bd.gemm_rq_next(xq, xs, False, lin.wq, lin.w_scale, lin.K, col0, nxt.K, self.block,
-                            nxt.rot, nxt.table, self.steps, step, Y=Y, epilogue=epi, residual=res,
-                            xq_next=bufs.xqn[nxt.K], x_scale_next=bufs.xsn,
-                            ws=bufs.fws[(lin.N, lin.K, nxt.K)], store_next_cols=keep)
+    def layer_plan(self, li: int, cur, out, calib: bool, bufs: _Buffers, keep: bool = False):
+        """How the four linears of layer li run: one dict per linear with its input X (None when
+        the producing GEMM already wrote its codes), the perm relative to X's column order, its
+        codes buffers cin, output Y, epilogue, residual and residual map, and the next linear whose
+        codes the GEMM writes (nxt, col0, into cout; store: whether those fp16 columns are stored
+        too). keep: the test hooks read every output."""
+        h, f = self.h, self.f
+        L = self.layers[li]
+        qkv, o, up, down = (L[n] for n in LINEARS)
+        cq = lambda lin: (bufs.xq[(lin.K, lin.bits)], bufs.xs)  # noqa: E731
+        plan = [dict(name=n, lin=L[n]) for n in LINEARS]
+        P = {d["name"]: d for d in plan}
+        if self.stream:
+            maps = self.res_map[li]
+            last = li + 1 == len(self.layers)
+            fuse = not calib
+            A, B, F = (bufs.xq[(h, 4)], bufs.xs), (bufs.xqn[h], bufs.xsn), (bufs.xqn[f], bufs.xsn)
+            first = li == 0 or calib
+            P["qkv"].update(X=cur if first else None, perm=qkv.perm if li == 0 else None, cin=A,
+                            Y=bufs.qkv, epi=bd.EPI_NONE, nxt=o if fuse else None, col0=2 * h,
+                            cout=B, store=keep)
+            P["o"].update(X=None if fuse else bufs.qkv[:, 2 * h:3 * h], perm=None,
+                          cin=B if fuse else A, Y=bufs.h2, epi=bd.EPI_RESIDUAL, res=cur,
+                          res_map=maps["o"], nxt=up if fuse else None, cout=A, store=True)
+            P["up"].update(X=None if fuse else bufs.h2, perm=None, cin=A, Y=bufs.g, epi=bd.EPI_GELU,
+                           nxt=down if fuse else None, cout=F, store=keep)
+            P["down"].update(X=None if fuse else bufs.g, perm=None, cin=F if fuse else cq(down),
+                             Y=out, epi=bd.EPI_RESIDUAL, res=bufs.h2, res_map=maps["down"],
+                             nxt=None if (last or not fuse) else self.layers[li + 1]["qkv"],
+                             cout=A, store=True)
+            return plan
+        # single-consumer folds only (or none): O and down quantize in their own launches unless
+        # the producer and consumer are both W4A4
+        fo = self.fold and not calib and qkv.bits == 4 and o.bits == 4
+        fd = self.fold and not calib and up.bits == 4 and down.bits == 4
+        P["qkv"].update(X=cur, perm=qkv.perm, cin=cq(qkv), Y=bufs.qkv, epi=bd.EPI_NONE,
+                        nxt=o if fo else None, col0=2 * h, cout=(bufs.xqn[h], bufs.xsn), store=keep)
+        P["o"].update(X=None if fo else bufs.qkv[:, 2 * h:3 * h], perm=None if self.fold else o.perm,
+                      cin=(bufs.xqn[h], bufs.xsn) if fo else cq(o), Y=bufs.h2, epi=bd.EPI_RESIDUAL,
+                      res=cur)
+        P["up"].update(X=bufs.h2, perm=up.perm, cin=cq(up), Y=bufs.g, epi=bd.EPI_GELU,
+                       nxt=down if fd else None, cout=(bufs.xqn[f], bufs.xsn), store=keep)
+        P["down"].update(X=None if fd else bufs.g, perm=None if self.fold else down.perm,
+                         cin=(bufs.xqn[f], bufs.xsn) if fd else cq(down), Y=out,
+                         epi=bd.EPI_RESIDUAL, res=bufs.h2)
+        return plan
+
+    def rotate_quant_call(self, e, step: int, calib: bool, bufs: _Buffers):
+        """The linear's own rotate-quantize (none when e["X"] is None)."""
+        lin, X = e["lin"], e.get("X")
+        if X is None:
             return
-        bd.gemm(xq, xs, calib, lin.wq, lin.w_scale, lin.K, Y=Y, epilogue=epi, residual=res,
-                ws=bufs.gws[(lin.N, lin.K, b)], bits=b)
+        xq, xs = e["cin"]
+        if calib:
+            bd.calibrate_act_scale(X, e.get("perm"), lin.rot, self.block,
+                                   out=lin.table[step:step + 1], ws=bufs.cws[lin.K], bits=lin.bits)
+        bd.rotate_quant_act(X, e.get("perm"), lin.rot, self.block, None if calib else lin.table,
+                            self.steps, step, xq=xq, x_scale=xs, ws=bufs.ws[lin.K], bits=lin.bits)
+
+    def gemm_call(self, e, step: int, calib: bool, bufs: _Buffers):
+        """The linear's GEMM with its epilogue (and, with e["nxt"], the next linear's codes)."""
+        lin, nxt, rmap = e["lin"], e.get("nxt"), e.get("res_map")
+        xq, xs = e["cin"]
+        if nxt is not None or rmap is not None:
+            kn = nxt.K if nxt is not None else 0
+            cout = e.get("cout") or (None, None)
+            bd.gemm_rq_next(xq, xs, calib, lin.wq, lin.w_scale, lin.K, e.get("col0", 0) if kn else 0,
+                            kn, self.block, nxt.rot if kn else None, nxt.table if kn else None,
+                            self.steps, step, Y=e["Y"], epilogue=e["epi"], residual=e.get("res"),
+                            xq_next=cout[0] if kn else None, x_scale_next=cout[1] if kn else None,
+                            ws=bufs.fws[(lin.N, lin.K, kn, 0 if rmap is None else 1)],
+                            store_next_cols=e.get("store", True), res_cols=rmap)
+            return
+        bd.gemm(xq, xs, calib, lin.wq, lin.w_scale, lin.K, Y=e["Y"], epilogue=e["epi"],
+                residual=e.get("res"), ws=bufs.gws[(lin.N, lin.K, lin.bits)], bits=lin.bits)
 
     def run(self, X, step: int, calib: bool = False, outputs=None, codes=None, rows=None):
-        """One pass of the stack for denoising step `step` on X fp16 [rows, h] (device). In calib
-        mode the linears quantize per token and record their table entry for `step`. Test hooks:
-        if `outputs` is a list, each linear's output (columns in natural channel order) and its
-        input are appended as (output, input, residual or None); if `codes` is a list, each linear's
-        activation codes and scale are appended as (codes, x_scale). `rows` (device int64 index)
-        keeps only those token rows in what the hooks record."""
+        """One pass of the stack for denoising step `step` on X fp16 [rows, h] (device); returns the
+        last layer's output in natural channel order. In calib mode the linears quantize per token
+        and record their table entry for `step`. Test hooks: if `outputs` is a list, each linear's
+        output (columns in natural channel order) and its input are appended as (output, input,
+        residual or None); if `codes` is a list, each linear's activation codes and scale are
+        appended as (codes, x_scale). `rows` (device int64 index) keeps only those token rows in
+        what the hooks record."""
         bufs = self.bufs(X.shape[0])
         h = self.h
         cur = X
         pick = (lambda t: t.clone()) if rows is None else (lambda t: t.index_select(0, rows))
-        cr = None
-        if codes is not None:
-            def cr(xq, xs):
-                codes.append((pick(xq), xs.clone() if xs.numel() == 1 else pick(xs)))
-        for li, layer in enumerate(self.layers):
-            nxt = bufs.hs[li % 2]
-            x_in = pick(cur) if outputs is not None else None
-            # O's and down's inputs are quantized by the GEMM that produces them when both sides
-            # are W4A4 and their channels come out in the consumer's zigzag order
-            fo = self.fold and not calib and layer["qkv"].bits == 4 and layer["o"].bits == 4
-            fd = self.fold and not calib and layer["up"].bits == 4 and layer["down"].bits == 4
-            keep = outputs is not None
-            self._linear(layer["qkv"], cur, bufs.qkv, step, calib, bufs, record=cr,
-                         nxt=layer["o"] if fo else None, col0=2 * h, keep=keep)
-            self._linear(layer["o"], bufs.qkv[:, 2 * h:3 * h], bufs.h2, step, calib, bufs,
-                         bd.EPI_RESIDUAL, cur, in_order=self.fold, record=cr, pre=fo)
-            self._linear(layer["up"], bufs.h2, bufs.g, step, calib, bufs, bd.EPI_GELU, record=cr,
-                         nxt=layer["down"] if fd else None, keep=keep)
-            self._linear(layer["down"], bufs.g, nxt, step, calib, bufs, bd.EPI_RESIDUAL, bufs.h2,
-                         in_order=self.fold, record=cr, pre=fd)
-            if outputs is not None:
-                qkv = pick(self._natural(layer["qkv"], bufs.qkv))
-                h2 = pick(bufs.h2)
-                g = pick(self._natural(layer["up"], bufs.g))
-                out = pick(nxt)
-                outputs.extend([(qkv, x_in, None), (h2, qkv[:, 2 * h:3 * h], x_in), (g, h2, None),
-                                (out, g, h2)])
-            cur = nxt
+        keep = outputs is not None
+        x_nat = pick(X) if keep else None
+        for li in range(len(self.layers)):
+            out = bufs.hs[li % 2]
+            for e in self.layer_plan(li, cur, out, calib, bufs, keep):
+                self.rotate_quant_call(e, step, calib, bufs)
+                if codes is not None:
+                    xq, xs = e["cin"]
+                    codes.append((pick(xq), pick(xs[:xq.shape[0]]) if calib else xs[:1].clone()))
+                self.gemm_call(e, step, calib, bufs)
+            if keep:
+                L = self.layers[li]
+                qkv = pick(self._natural(L["qkv"], bufs.qkv))
+                h2 = pick(self._natural(L["o"], bufs.h2))
+                g = pick(self._natural(L["up"], bufs.g))
+                y = pick(self._natural(L["down"], out))
+                outputs.extend([(qkv, x_nat, None), (h2, qkv[:, 2 * h:3 * h], x_nat), (g, h2, None),
+                                (y, g, h2)])
+                x_nat = y
+            cur = out
         return cur
 
     @staticmethod
