@@ -28,7 +28,11 @@ class DeviceLinear:
     """One linear's device state. row_perm (optional, device int64 [N]) reorders the output
     channels: the packed weights hold rows W[row_perm], so output column j is channel row_perm[j].
     The zigzag permutation and block SVD are computed on W itself (the row order of W does not
-    change them); only the packed rows move, when pack() is called."""
+    change them); only the packed rows move, when pack() is called.
+    perm / U are the zigzag permutation and SVD factor; gperm / gU the order in which the
+    activation's channels are gathered within each block (the same blocks, see _regroup) and the
+    factor with its rows in that order, from which the activation-side rotation operand rot is
+    built. The weights are always packed from perm / U."""
 
     def __init__(self, W, block: int, steps: int, perm=None, U=None, bits: int = 4):
         torch = _torch()
@@ -38,15 +42,38 @@ class DeviceLinear:
         self.perm = bd.zigzag_perm(self._W, block) if perm is None else perm
         self.U = bd.block_svd(self._W, self.perm, block) if U is None else U
         self.bits = bits
+        self.gperm, self.gU = self.perm, self.U
         self.table = torch.empty(steps, dtype=torch.float32, device="cuda")
         self.steps = steps
 
     def pack(self, row_perm=None):
+        torch = _torch()
         W = self._W if row_perm is None else self._W.index_select(0, row_perm).contiguous()
         self.wq, self.w_scale, self.rot = bd.pack_weights(W, self.perm, self.U, self.B, bits=self.bits)
+        if self.gperm is not self.perm:
+            # the rotation operand for the regrouped gather order (R'_b = U'_b H_B: R_b's rows in
+            # the new order); the one-row weight pack beside it is discarded
+            one = torch.zeros((1, self.K), dtype=W.dtype, device=W.device)
+            self.rot = bd.pack_weights(one, self.gperm, self.gU, self.B, bits=self.bits)[2]
         self.row_perm = row_perm
         self._W = None
         return self
+
+
+def _regroup(perm, U, key, B: int):
+    """Reorder the channels inside each rotation block of perm by key[channel] (stable), and U's
+    rows with them. A block is the same set of channels, so x_b R_b is the same rotation (R'_b =
+    U'_b H_B holds R_b's rows in the new order): only the order of the products in its sums
+    changes. Used to make the channels one output tile reads from a residual stream stored in this
+    order sit in runs of adjacent columns."""
+    torch = _torch()
+    nb = perm.numel() // B
+    p = perm.to(torch.int64).view(nb, B)
+    comp = key[p] * B + torch.arange(B, device=p.device, dtype=torch.int64).view(1, B)
+    idx = torch.argsort(comp, dim=1)
+    p2 = torch.gather(p, 1, idx).reshape(-1).to(torch.int32).contiguous()
+    U2 = torch.gather(U, 1, idx.unsqueeze(-1).expand(nb, B, B)).contiguous()
+    return p2, U2
 
 
 def _inverse(p):
@@ -115,7 +142,19 @@ class DeviceStack:
             pu = lambda n: calib[li][n] if calib is not None else (None, None)  # noqa: E731
             lin.append({n: DeviceLinear(lw[n], block, steps, *pu(n), bits=8 if n in w8 else 4)
                         for n in LINEARS})
-        perm = lambda li, n: lin[li][n].perm.to(torch.int64)  # noqa: E731
+        # Gather orders: QKV's input channels grouped, inside each of its blocks, by the up block
+        # they belong to, and up's by the block of the next layer's QKV (the last layer's by
+        # 64-channel line of the natural order): the residual O adds (stream stored in QKV's order)
+        # and the one down adds (O's output, stored in up's order) are then read in runs.
+        for li in range(nl):
+            q, u = lin[li]["qkv"], lin[li]["up"]
+            q.gperm, q.gU = _regroup(q.perm, q.U, _inverse(u.perm.to(torch.int64)) // block, block)
+            if li + 1 < nl:
+                key = _inverse(lin[li + 1]["qkv"].perm.to(torch.int64)) // block
+            else:
+                key = torch.arange(u.K, device="cuda", dtype=torch.int64) // 64
+            u.gperm, u.gU = _regroup(u.perm, u.U, key, block)
+        perm = lambda li, n: lin[li][n].gperm.to(torch.int64)  # noqa: E731
         self.res_map = []
         for li in range(nl):
             rp = dict.fromkeys(LINEARS)
@@ -173,7 +212,7 @@ class DeviceStack:
             fuse = not calib
             A, B, F = (bufs.xq[(h, 4)], bufs.xs), (bufs.xqn[h], bufs.xsn), (bufs.xqn[f], bufs.xsn)
             first = li == 0 or calib
-            P["qkv"].update(X=cur if first else None, perm=qkv.perm if li == 0 else None, cin=A,
+            P["qkv"].update(X=cur if first else None, perm=qkv.gperm if li == 0 else None, cin=A,
                             Y=bufs.qkv, epi=bd.EPI_NONE, nxt=o if fuse else None, col0=2 * h,
                             cout=B, store=keep)
             P["o"].update(X=None if fuse else bufs.qkv[:, 2 * h:3 * h], perm=None,
@@ -190,14 +229,14 @@ class DeviceStack:
         # the producer and consumer are both W4A4
         fo = self.fold and not calib and qkv.bits == 4 and o.bits == 4
         fd = self.fold and not calib and up.bits == 4 and down.bits == 4
-        P["qkv"].update(X=cur, perm=qkv.perm, cin=cq(qkv), Y=bufs.qkv, epi=bd.EPI_NONE,
+        P["qkv"].update(X=cur, perm=qkv.gperm, cin=cq(qkv), Y=bufs.qkv, epi=bd.EPI_NONE,
                         nxt=o if fo else None, col0=2 * h, cout=(bufs.xqn[h], bufs.xsn), store=keep)
-        P["o"].update(X=None if fo else bufs.qkv[:, 2 * h:3 * h], perm=None if self.fold else o.perm,
+        P["o"].update(X=None if fo else bufs.qkv[:, 2 * h:3 * h], perm=None if self.fold else o.gperm,
                       cin=(bufs.xqn[h], bufs.xsn) if fo else cq(o), Y=bufs.h2, epi=bd.EPI_RESIDUAL,
                       res=cur)
-        P["up"].update(X=bufs.h2, perm=up.perm, cin=cq(up), Y=bufs.g, epi=bd.EPI_GELU,
+        P["up"].update(X=bufs.h2, perm=up.gperm, cin=cq(up), Y=bufs.g, epi=bd.EPI_GELU,
                        nxt=down if fd else None, cout=(bufs.xqn[f], bufs.xsn), store=keep)
-        P["down"].update(X=None if fd else bufs.g, perm=None if self.fold else down.perm,
+        P["down"].update(X=None if fd else bufs.g, perm=None if self.fold else down.gperm,
                          cin=(bufs.xqn[f], bufs.xsn) if fd else cq(down), Y=out,
                          epi=bd.EPI_RESIDUAL, res=bufs.h2)
         return plan
