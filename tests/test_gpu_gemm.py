@@ -35,8 +35,9 @@ def test_gemm_i32_bit_exact(M, N, K):
     assert np.array_equal(acc.astype(np.int64), ref)
 
 
+# (1590, 3072, 1024): the 80-row tile plan with a ragged last row band
 @pytest.mark.parametrize("M,N,K", [(1024, 16384, 2048), (1024, 2048, 16384), (1600, 3072, 1024),
-                                   (1600, 1024, 4096), (50, 4096, 1024)])
+                                   (1600, 1024, 4096), (50, 4096, 1024), (1590, 3072, 1024)])
 def test_gemm_i32_full_size_sampled(M, N, K):
     xq, wq = _operands(M, N, K, seed=7)
     acc = host(bd.gemm_i32(dev(xq), dev(wq), K)).astype(np.int64)
@@ -129,7 +130,7 @@ def test_gemm_i32_extremes(K):
 @pytest.mark.parametrize("per_token", [True, False])
 @pytest.mark.parametrize("epi", [EPI_NONE, EPI_RESIDUAL, EPI_GELU])
 @pytest.mark.parametrize("M,N,K", [(50, 4096, 1024), (40, 16400, 1024), (200, 300, 512),
-                                   (1024, 2048, 16384)])
+                                   (1024, 2048, 16384), (1590, 3072, 1024)])
 def test_gemm_dequant_epilogue(per_token, epi, M, N, K):
     xq, wq = _operands(M, N, K, seed=3)
     sx = inputs.random_scales(M if per_token else 1, seed=M, lo=1e-3, hi=5e-2)
@@ -138,7 +139,7 @@ def test_gemm_dequant_epilogue(per_token, epi, M, N, K):
     Y = host(bd.gemm(dev(xq), dev(sx), per_token, dev(wq), dev(sw), K, epilogue=epi,
                      residual=dev(res) if epi == EPI_RESIDUAL else None))
     if M * N * K > 2 ** 32:
-        rows = np.arange(0, M, 97)
+        rows = np.unique(np.r_[np.arange(0, M, 97), M - 1])
         q = oracle.unpack_int4(xq[rows], K)
         acc = oracle.int_gemm(q, oracle.unpack_int4(wq, K))
         ref, _ = oracle.dequant(acc, sx[rows] if per_token else sx, per_token, sw, epi,

@@ -73,6 +73,9 @@ CASES = {
     "down_shape_split_group": (1600, 1024, 4096, 0, 1024, 128, EPI_RESIDUAL),
     "split_group_ragged_part": (700, 512, 2048, 128, 256, 128, EPI_NONE),
     "split_group_gelu": (1000, 1024, 4096, 256, 512, 128, EPI_GELU),
+    # the 80-row pipelined tiles (the stack's QKV plan) with a ragged last row band
+    "rows_80_tiles_ragged": (1590, 3072, 1024, 2048, 1024, 128, EPI_NONE),
+    "rows_80_tiles_residual": (1590, 3072, 1024, 0, 1024, 128, EPI_RESIDUAL),
 }
 
 

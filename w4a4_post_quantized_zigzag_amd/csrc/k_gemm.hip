@@ -796,10 +796,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int A_BYTES = BM * BG_ROWB, B_BYTES = BN * BG_ROWB, STAGE = A_BYTES + B_BYTES;
-    constexpr int QA = A_BYTES / 1024 / NW, QB = B_BYTES / 1024 / NW;  // DMA instrs per wave
+    // DMA instructions (1 KB chunks of 16 rows) per wave and stage. When the A tile's chunks do not
+    // divide among the waves (80-row tiles), chunk q of wave w is chunk q * NW + w and the first
+    // waves take one more; each wave then waits for its own count.
+    constexpr int NCA = A_BYTES / 1024;
+    constexpr bool AWHOLE = NCA % NW == 0;
+    constexpr int QA = (NCA + NW - 1) / NW, QB = B_BYTES / 1024 / NW;
     constexpr int L = QA + QB;
     constexpr int SHIFT = Q8 ? 0 : 8;  // int4 operands enter the MFMA as 16 * code
-    static_assert(QA * 1024 * NW == A_BYTES && QB * 1024 * NW == B_BYTES, "whole KB per wave");
+    static_assert(NCA * 1024 == A_BYTES && QB * 1024 * NW == B_BYTES, "whole KB chunks");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     int tm, tn;
@@ -814,13 +819,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
     const int kb_end = min(kb_begin + split_bytes, ldp);
     const int stages = (kb_end - kb_begin) / BG_ROWB;
 
-    // per-lane DMA sources: instruction q of this wave covers staged rows (wave*Q + q)*16 + lane/4,
+    // per-lane DMA sources: instruction q of this wave covers staged rows achunk(q)*16 + lane/4,
     // physical chunk lane%4, which holds logical chunk (lane%4) ^ swizzle(row)
+    auto achunk = [&](int q) { return AWHOLE ? wave * QA + q : q * NW + wave; };
+    const int uwave_a = __builtin_amdgcn_readfirstlane(wave);
+    const int qa_w = AWHOLE ? QA : (NCA - uwave_a + NW - 1) / NW;  // A chunks this wave loads
+    const int lw = AWHOLE ? L : qa_w + QB;
     const uint8_t *srcA[QA];
     const uint8_t *srcB[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-        const int row = (wave * QA + q) * 16 + (lane >> 2);
+        const int row = min(achunk(q), NCA - 1) * 16 + (lane >> 2);
         const int c = (lane & 3) ^ ((row >> 1) & 3);
         srcA[q] = xq + (int64_t)min(m0 + row, M - 1) * ldp + kb_begin + 16 * c;
     }
@@ -837,7 +846,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         const int koff = st * BG_ROWB;
 #pragma unroll
         for (int q = 0; q < QA; ++q)
-            dma_to_lds16(srcA[q] + koff, base + (uint32_t)((uwave * QA + q) * 1024));
+            if (AWHOLE || q < qa_w)
+                dma_to_lds16(srcA[q] + koff,
+                             base + (uint32_t)((AWHOLE ? uwave * QA + q : q * NW + uwave) * 1024));
 #pragma unroll
         for (int q = 0; q < QB; ++q)
             dma_to_lds16(srcB[q] + koff, base + (uint32_t)(A_BYTES + (uwave * QB + q) * 1024));
@@ -869,7 +880,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         // stages st+1 .. st+NSTAGE-2 may still be in flight; stage st must have landed
         const int ahead = min(stages - 1 - st, NSTAGE - 2);
         asm volatile("" ::: "memory");
-        wait_vmcnt(ahead * L);
+        wait_vmcnt(ahead * lw);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (st + NSTAGE - 1 < stages) issue(st + NSTAGE - 1);
@@ -1870,7 +1881,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_f6(
 }
 
 struct GemmPlan {
-    // 0 small-M; 1 = 256x256, 2 = 128x256, 3 = 128x128, 4 = 64x128 (k_gemm_pipe / k_gemm_big);
+    // 0 small-M; 1 = 256x256, 2 = 128x256, 3 = 128x128, 4 = 64x128, 5 = 80x128 (k_gemm_pipe /
+    // k_gemm_big);
     // SP_* (k_gemm_sp, packed int4 with K % 128 == 0 and aligned operands)
     int kind;
     int bm, bn, splits, k_split;
@@ -1894,6 +1906,8 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = fals
     //   e     each further round of workgroups on a CU
     //   occ   workgroups one CU holds at once (LDS and registers)
     //   gran  k granularity of the ring (a k split is a whole number of it)
+    // (The 80-row tile takes the 64-row tile's f and beta and s scaled by its area; on the stack's
+    // QKV projection this predicts 11.6 us against 11.5 us measured.)
     // Per CU: w = ceil(tiles * splits / 256) workgroups, co = min(w, occ) of them at once:
     //   t = f + stages * s * (1 + beta (co - 1)) * w / co + (ceil(w / occ) - 1) e
     // plus, for the GELU epilogue, its VALU time per output a thread owns (exposed once per
@@ -1904,21 +1918,23 @@ static GemmPlan plan_gemm(int M, int N, int K, int kg, bool pipe, bool sp = fals
                           {2, 128, 256, 512, 1, 6.0, 1.01, 0.0, 3.0, kg},
                           {3, 128, 128, 256, 2, 4.6, 0.61, 0.68, 3.0, kg},
                           {4, 64, 128, 256, 3, 3.9, 0.49, 0.57, 3.0, kg},
+                          {5, 80, 128, 256, 3, 3.9, 0.61, 0.57, 3.0, kg},
                           {SP_128x128, 128, 128, 512, 1, 6.96, 0.58, 0.0, 2.95, 256},
                           {SP_64x128, 64, 128, 512, 1, 5.3, 0.2875, 0.0, 3.05, 512}};
-    const int ncand = sp ? 6 : 4;
+    const int ncand = sp ? 7 : 5;
     double best_t = 1e30;
     for (int ci = 0; ci < ncand; ++ci) {
         const Cand &c = cands[ci];
-        if (c.kind == 4 && !pipe) continue;
+        if ((c.kind == 4 || c.kind == 5) && !pipe) continue;
         // the fused rotate-quantize tiles: 128 columns, pipelined or split-group
-        if (bn128_pipe && c.kind != 3 && c.kind != 4 && c.kind != SP_64x128) continue;
+        if (bn128_pipe && c.kind != 3 && c.kind != 4 && c.kind != 5 && c.kind != SP_64x128)
+            continue;
         if (c.kind >= SP_128x128 && K % c.gran) continue;  // whole ring slots only
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         // up to 256 splits: K <= 2^24 then always fits pieces of at most MAX_K_SPLIT k, the most
         // one int32 accumulator of the tile kernels holds
         for (int splits = 1; splits <= 256; splits *= 2) {
-            if (c.kind == 4 && splits > 1) continue;
+            if ((c.kind == 4 || c.kind == 5) && splits > 1) continue;
             int k_split = ((K + splits - 1) / splits + c.gran - 1) / c.gran * c.gran;
             if (k_split > MAX_K_SPLIT) continue;
             const int real_splits = (K + k_split - 1) / k_split;
@@ -2057,6 +2073,9 @@ static int launch_pipe(int kind, dim3 grid, hipStream_t s, const uint8_t *xq, co
                                                  partial);
     if (kind == 4)
         return launch_pipe_t<64, 128, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
+                                                partial);
+    if (kind == 5)
+        return launch_pipe_t<80, 128, 1, 4, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi,
                                                 partial);
     return launch_pipe_t<128, 128, 2, 2, Q8>(grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, partial);
 }
@@ -2266,7 +2285,8 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     GemmPlan f{};
     const bool fused = fuse && [&] {
         f = plan_gemm(M, N, K, BG_KS, true, true, epi.mode == W4A4_EPI_GELU, true);
-        return (f.kind == 3 || f.kind == 4 || sp_kind_maps_residual(f.kind)) && f.splits == 1;
+        return (f.kind == 3 || f.kind == 4 || f.kind == 5 || sp_kind_maps_residual(f.kind)) &&
+               f.splits == 1;
     }();
     // A residual column map is read in the split-group kernel's staged epilogue; any other plan
     // gets the residual gathered into the workspace (after the split-K partials) first.
@@ -2296,6 +2316,8 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
             rc = launch_sp_rq<64, 3, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
         else if (f.kind == 4)
             rc = launch_pipe_rq<64, 1, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
+        else if (f.kind == 5)
+            rc = launch_pipe_rq<80, 1, 4>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
         else
             rc = launch_pipe_rq<128, 2, 2>(grid, s, xq, wq, M, N, K, f.k_split, tm, tn, epi);
         if (rc != W4A4_OK) return rc;
