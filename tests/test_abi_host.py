@@ -307,3 +307,44 @@ def test_f6_empty_batches_are_valid(L):
                                       NULL, NULL, NULL, 0, NULL) == bd.W4A4_OK
     assert L.w4a4_gemm_f6(NULL, NULL, 1, FAKE, FAKE, 0, 64, 256, NULL, 64, 0, NULL, 0, NULL, 0,
                           NULL) == bd.W4A4_OK
+
+
+def _rqn(L, *, M=16, N=256, K=256, epi=2, res=FAKE, ldr=256, rmap=NULL, col0=0, kn=128,
+         block=128, rot=FAKE, table=FAKE, steps=2, step=0, xqn=FAKE, xsn=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = L.w4a4_gemm_rq_next_workspace_bytes(M, N, K, kn, block, 0 if rmap is None else 1)
+    return L.w4a4_gemm_rq_next(FAKE, FAKE, 0, FAKE, FAKE, M, N, K, FAKE, N, epi, res, ldr, rmap,
+                               col0, kn, block, rot, table, steps, step, xqn, xsn, 1, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(epi=0, res=NULL, rmap=FAKE), bd.W4A4_ERR_ARG),         # a map needs the residual epilogue
+    (dict(rmap=ctypes.c_void_p(0x10002)), bd.W4A4_ERR_ALIGN),    # int32 map, 4-byte aligned
+    (dict(N=70000, ldr=70000, kn=0, rmap=FAKE), bd.W4A4_ERR_UNSUPPORTED),
+    (dict(kn=0, col0=128), bd.W4A4_ERR_SHAPE),                   # no next linear: col0 must be 0
+    (dict(kn=-128), bd.W4A4_ERR_SHAPE),
+    (dict(col0=192, kn=128), bd.W4A4_ERR_SHAPE),                 # past N
+    (dict(kn=200), bd.W4A4_ERR_SHAPE),                           # not a multiple of the block
+    (dict(table=NULL), bd.W4A4_ERR_ARG),                         # per-step scale required
+    (dict(step=2), bd.W4A4_ERR_STEP_RANGE),
+    (dict(xqn=NULL), bd.W4A4_ERR_ARG),
+    (dict(M=1024, N=2048, K=16384, ldr=2048, ws=NULL), bd.W4A4_ERR_WORKSPACE),  # split-K plan
+])
+def test_gemm_rq_next_rejects(L, kw, code):
+    assert _rqn(L, **kw) == code
+
+
+def test_gemm_rq_next_without_next_linear_ignores_its_arguments(L):
+    # K_next = 0: the rotate-quantize arguments may be NULL; only the GEMM's are checked (here an
+    # empty batch, which launches nothing)
+    assert _rqn(L, M=0, kn=0, rot=NULL, table=NULL, xqn=NULL, xsn=NULL, rmap=FAKE) == bd.W4A4_OK
+
+
+def test_gemm_rq_next_workspace_covers_the_mapped_residual(L):
+    # a residual map needs room for the gathered residual (M x N fp16) beyond the GEMM's own
+    # workspace, for the tile plans that gather it before the GEMM
+    M, N, K = 333, 768, 512
+    plain = L.w4a4_gemm_rq_next_workspace_bytes(M, N, K, 0, 128, 0)
+    mapped = L.w4a4_gemm_rq_next_workspace_bytes(M, N, K, 0, 128, 1)
+    assert mapped >= plain + M * N * 2
+    assert L.w4a4_gemm_rq_next_workspace_bytes(0, N, K, 0, 128, 1) == 0
