@@ -212,7 +212,12 @@ int w4a4_gemm(const uint8_t *xq, const float *x_scale, int x_scale_per_token, co
  * linear's output comes out in another's. Entries must lie in [0, N); the kernels clamp any other
  * entry into that range (no out-of-bounds access, but the sum is then meaningless). The tile plan
  * of the stack's 64 x 128 split-group GEMM gathers the mapped residual in its epilogue; other plans
- * gather it into the workspace first.
+ * gather it into the workspace first. res_order (optional, with res_cols; device int32 [N], 4-byte
+ * aligned) is a gather-order hint for that epilogue: for each tile of 128 output columns starting
+ * at column n0, res_order[n0 + j] is the output column (in [n0, n0 + 128)) whose residual the
+ * tile's j-th lane fetches. Sorting each tile's columns by res_cols makes adjacent lanes read
+ * adjacent residual columns. It must permute each tile's columns (unchecked: a column left out
+ * gets an unspecified residual); NULL means column order. Other tile plans ignore it.
  * Arguments and errors as w4a4_gemm and w4a4_rotate_quant_act (per-step scale only: table_next is
  * required when K_next > 0); every argument is checked before anything is launched. ws:
  * w4a4_gemm_rq_next_workspace_bytes(M, N, K, K_next, block_next, res_cols != NULL) bytes, 256-byte
@@ -222,10 +227,10 @@ size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int bl
 int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr,
-                      const int32_t *res_cols, int col0, int K_next, int block_next,
-                      const void *rot_next, const float *table_next, int num_steps, int step,
-                      uint8_t *xq_next, float *x_scale_next, int store_next_cols, void *ws,
-                      size_t ws_bytes, hipStream_t stream);
+                      const int32_t *res_cols, const int32_t *res_order, int col0, int K_next,
+                      int block_next, const void *rot_next, const float *table_next,
+                      int num_steps, int step, uint8_t *xq_next, float *x_scale_next,
+                      int store_next_cols, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Test hook: the raw int32 accumulators acc [M][N] (row-major, dense) of the same integer GEMM. */
 int w4a4_gemm_i32(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, int32_t *acc,

@@ -309,17 +309,20 @@ def test_f6_empty_batches_are_valid(L):
                           NULL) == bd.W4A4_OK
 
 
-def _rqn(L, *, M=16, N=256, K=256, epi=2, res=FAKE, ldr=256, rmap=NULL, col0=0, kn=128,
+def _rqn(L, *, M=16, N=256, K=256, epi=2, res=FAKE, ldr=256, rmap=NULL, rord=NULL, col0=0, kn=128,
          block=128, rot=FAKE, table=FAKE, steps=2, step=0, xqn=FAKE, xsn=FAKE, ws=FAKE, wsb=None):
     if wsb is None:
         wsb = L.w4a4_gemm_rq_next_workspace_bytes(M, N, K, kn, block, 0 if rmap is None else 1)
     return L.w4a4_gemm_rq_next(FAKE, FAKE, 0, FAKE, FAKE, M, N, K, FAKE, N, epi, res, ldr, rmap,
-                               col0, kn, block, rot, table, steps, step, xqn, xsn, 1, ws, wsb, NULL)
+                               rord, col0, kn, block, rot, table, steps, step, xqn, xsn, 1, ws, wsb,
+                               NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(epi=0, res=NULL, rmap=FAKE), bd.W4A4_ERR_ARG),         # a map needs the residual epilogue
     (dict(rmap=ctypes.c_void_p(0x10002)), bd.W4A4_ERR_ALIGN),    # int32 map, 4-byte aligned
+    (dict(rord=FAKE), bd.W4A4_ERR_ARG),                          # a gather order needs a map
+    (dict(rmap=FAKE, rord=ctypes.c_void_p(0x10002)), bd.W4A4_ERR_ALIGN),
     (dict(N=70000, ldr=70000, kn=0, rmap=FAKE), bd.W4A4_ERR_UNSUPPORTED),
     (dict(kn=0, col0=128), bd.W4A4_ERR_SHAPE),                   # no next linear: col0 must be 0
     (dict(kn=-128), bd.W4A4_ERR_SHAPE),

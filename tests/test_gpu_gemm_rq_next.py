@@ -187,11 +187,23 @@ MAP_CASES = {
     "few_tokens": (50, 1024, 1024, 0, 0, False),            # small-M kernel, gathered first
     "per_token_calibration": (300, 1024, 1024, 0, 0, True),
     "k_split": (260, 256, 16384, 0, 0, False),               # split-K partials and the gather
+    "partial_last_tile": (700, 1000, 2048, 0, 0, False),     # a last tile of 104 columns
 }
 
 
+def _gather_order(cols):
+    # each 128-column tile's columns sorted by the residual column they read
+    N = len(cols)
+    order = np.empty(N, np.int64)
+    for t0 in range(0, N, 128):
+        seg = cols[t0:t0 + 128]
+        order[t0:t0 + len(seg)] = t0 + np.argsort(seg, kind="stable")
+    return order
+
+
+@pytest.mark.parametrize("with_order", [False, True])
 @pytest.mark.parametrize("name", list(MAP_CASES))
-def test_gemm_residual_column_map(name):
+def test_gemm_residual_column_map(name, with_order):
     torch = __import__("torch")
     M, N, K, col0, K_next, per_tok = MAP_CASES[name]
     B = 128
@@ -209,8 +221,11 @@ def test_gemm_residual_column_map(name):
     table = dev(np.array([0.05, 0.02], np.float32))
     if K_next:
         table = _table_for(dict(d, Y0=Y_ref), col0, K_next, B)
+    # the gather order only changes which lane fetches which column: same results
+    rord = dev(_gather_order(cols).astype(np.int32)) if with_order else None
     Y, q, s = bd.gemm_rq_next(d["xq"], xs, per_tok, d["wq"], d["ws"], K, col0, K_next, B, d["rot"],
-                              table, 2, 1, epilogue=EPI_RESIDUAL, residual=d["res"], res_cols=rmap)
+                              table, 2, 1, epilogue=EPI_RESIDUAL, residual=d["res"], res_cols=rmap,
+                              res_order=rord)
     assert _same(Y, Y_ref), name
     if K_next:
         q_ref, s_ref = bd.rotate_quant_act(Y_ref[:, col0:col0 + K_next], None, d["rot"], B, table,

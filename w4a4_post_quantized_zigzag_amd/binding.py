@@ -35,7 +35,7 @@ SIGNATURES = {
                                             _vp, _vp]),
     "w4a4_gemm_rq_next_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "w4a4_gemm_rq_next": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i64, _i, _vp, _i64, _vp,
-                               _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+                               _vp, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "w4a4_noalloc_scratch_bytes": (_sz, []),
     "w4a4_rotate_quant_act_noalloc": (_i, [_vp, _i, _i, _i, _i64, _i, _vp, _vp, _vp, _i, _i, _vp,
                                            _vp, _vp, _vp]),
@@ -282,12 +282,12 @@ def gemm(xq, x_scale, per_token: bool, wq, w_scale, K: int, Y=None, epilogue: in
 def gemm_rq_next(xq, x_scale, per_token: bool, wq, w_scale, K: int, col0: int, K_next: int,
                  block_next: int, rot_next, table_next, num_steps: int, step: int, Y=None,
                  epilogue: int = EPI_NONE, residual=None, xq_next=None, x_scale_next=None, ws=None,
-                 store_next_cols: bool = True, res_cols=None):
+                 store_next_cols: bool = True, res_cols=None, res_order=None):
     """W4A4 GEMM, then the next linear's per-step rotate-quantize of Y[:, col0:col0+K_next]
     (fused into the GEMM epilogue where the tile plan allows). store_next_cols=False lets the
     library leave those columns of Y unwritten. K_next = 0: no next linear. res_cols (device int32
-    [N]): residual column map, output column n adds residual[:, res_cols[n]]. Returns
-    (Y, xq_next, x_scale_next)."""
+    [N]): residual column map, output column n adds residual[:, res_cols[n]]; res_order: optional
+    per-tile gather order for it (see w4a4_gemm_rq_next). Returns (Y, xq_next, x_scale_next)."""
     torch = _torch()
     M, N = xq.shape[0], wq.shape[0]
     _code_cols(K, 4)
@@ -310,6 +310,7 @@ def gemm_rq_next(xq, x_scale, per_token: bool, wq, w_scale, K: int, col0: int, K
     ldr = _row_stride(residual) if residual is not None else 0
     check(L.w4a4_gemm_rq_next(_p(xq), _p(x_scale), 1 if per_token else 0, _p(wq), _p(w_scale), M, N,
                               K, _p(Y), _row_stride(Y), epilogue, _p(residual), ldr, _p(res_cols),
+                              _p(res_order),
                               col0, K_next, block_next, _p(rot_next), _p(table_next), num_steps,
                               step, _p(xq_next), _p(x_scale_next), 1 if store_next_cols else 0,
                               _p(ws), nb, _stream()))

@@ -597,7 +597,8 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr, void *ws,
                       size_t ws_bytes, hipStream_t stream, int fmt, const RqNext *rq = nullptr,
-                      bool *rq_done = nullptr, const int32_t *res_cols = nullptr)
+                      bool *rq_done = nullptr, const int32_t *res_cols = nullptr,
+                      const int32_t *res_order = nullptr)
 {
     int rc;
     if ((rc = check_gemm_common(xq, wq, M, N, K, fmt))) return rc;
@@ -625,6 +626,7 @@ static int gemm_entry(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     epi.residual = residual;
     epi.ldr = ldr;
     epi.res_cols = res_cols;
+    epi.res_order = res_order;
     if (rq) epi.rq = *rq;
     if ((rc = fmt == OPF_F6 ? launch_gemm_f6(xq, wq, M, N, K, epi, ws, ws_bytes, stream)
                          : launch_gemm(xq, wq, M, N, K, epi, ws, ws_bytes, stream, fmt == OPF_I8,
@@ -675,7 +677,8 @@ size_t w4a4_gemm_rq_next_workspace_bytes(int M, int N, int K, int K_next, int bl
 int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_token,
                       const uint8_t *wq, const float *w_scale, int M, int N, int K, uint16_t *Y,
                       int64_t ldy, int epilogue, const uint16_t *residual, int64_t ldr,
-                      const int32_t *res_cols, int col0, int K_next, int block_next,
+                      const int32_t *res_cols, const int32_t *res_order, int col0, int K_next,
+                      int block_next,
                       const void *rot_next, const float *table_next, int num_steps, int step,
                       uint8_t *xq_next, float *x_scale_next, int store_next_cols, void *ws,
                       size_t ws_bytes, hipStream_t stream)
@@ -688,6 +691,10 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
             return fail(W4A4_ERR_ARG, "res_cols needs the residual epilogue");
         if (!aligned(res_cols, 4)) return fail(W4A4_ERR_ALIGN, "res_cols misaligned");
         if (N > 65536) return fail(W4A4_ERR_UNSUPPORTED, "res_cols with N = %d > 65536", N);
+    }
+    if (res_order) {
+        if (!res_cols) return fail(W4A4_ERR_ARG, "res_order without res_cols");
+        if (!aligned(res_order, 4)) return fail(W4A4_ERR_ALIGN, "res_order misaligned");
     }
     if (K_next < 0 || col0 < 0 || (int64_t)col0 + K_next > N || (K_next == 0 && col0 != 0))
         return fail(W4A4_ERR_SHAPE, "columns [%d, %d + %d) outside the N = %d outputs", col0, col0,
@@ -715,7 +722,8 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
         return rc;
     if (K_next == 0)
         return gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
-                          residual, ldr, ws, ws_bytes, stream, OPF_I4, nullptr, nullptr, res_cols);
+                          residual, ldr, ws, ws_bytes, stream, OPF_I4, nullptr, nullptr, res_cols,
+                          res_order);
     const RotLayout L = rot_layout(K_next, block_next);
     const char *rb = reinterpret_cast<const char *>(rot_next);
     const RqNext rq{reinterpret_cast<const _Float16 *>(rb + L.r32),
@@ -724,7 +732,7 @@ int w4a4_gemm_rq_next(const uint8_t *xq, const float *x_scale, int x_scale_per_t
     bool done = false;
     if ((rc = gemm_entry(xq, x_scale, x_scale_per_token, wq, w_scale, M, N, K, Y, ldy, epilogue,
                          residual, ldr, ws, ws_bytes, stream, OPF_I4,
-                         block_next == 128 ? &rq : nullptr, &done, res_cols)))
+                         block_next == 128 ? &rq : nullptr, &done, res_cols, res_order)))
         return rc;
     if (done || M == 0) return ok();
     // no fused tile plan for this shape: the rotate-quantize of the columns, after the GEMM on

@@ -748,6 +748,15 @@ __device__ __forceinline__ void dma_to_lds16(const void *gptr, uint32_t lds_addr
                  : "memory", "m0");
 }
 
+// 4 bytes per lane from global memory into LDS at lds_addr + 4 * lane (same counter as the above)
+__device__ __forceinline__ void dma_to_lds4(const void *gptr, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const uint8_t *p)
 {
     return (uint32_t)(uintptr_t)(const lds_u8_t *)p;
@@ -1195,7 +1204,8 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
                            (size_t)XCH_BYTES + (size_t)BM * (STP + 64) <= (size_t)NS * SLOT),
                   "fused rotate-quantize: staged 128-column tiles");
     // RMAP (residual column map epi.res_cols): the tile's residual is gathered row by row into LDS
-    // after the codes area, and the epilogue reads it from there in the fragment layout
+    // after the codes area, and the epilogue reads it from there in the fragment layout. The tile's
+    // map entries and gather order sit in LDS past the ring (2 x BN ints).
     constexpr int RES_OFF = XCH_BYTES + BM * STP + (RQN ? BM * 64 : 0);
     constexpr int RPT = BM * BN / 512;  // residual elements each thread gathers
     static_assert(!RMAP || (ST && PE == PE_RESIDUAL && BN <= 512 && 512 % BN == 0 &&
@@ -1260,12 +1270,12 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
         }
     }
 
-    // RMAP: thread -> tile column tid % BN and rows tid / BN + r (512 / BN) of the residual gather.
-    // Its source column is read now; the gather itself is issued in the last main-loop iteration,
-    // under that iteration's matrix work. Columns and map entries are clamped into [0, N).
-    const int rcol = tid % BN, rrow0 = tid / BN;
-    int rsrc = 0;
-    if (RMAP) rsrc = min(max(epi.res_cols[min(n0 + rcol, N - 1)], 0), N - 1);
+    // RMAP: thread -> tile column rcol and rows tid / BN + r (512 / BN) of the residual gather,
+    // issued in the last main-loop iteration under that iteration's matrix work. rcol is the
+    // tile's gather order at tid % BN (the identity without epi.res_order): lanes that gather
+    // adjacent source columns share cache lines. Columns and map entries are clamped into range.
+    int rcol = tid % BN;
+    const int rrow0 = tid / BN;
     uint16_t rgv[RMAP ? RPT : 1];
 
     const uint8_t *srcA[QA];
@@ -1284,6 +1294,18 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
     }
     const int uwc = __builtin_amdgcn_readfirstlane(wc);
     const uint32_t lds0 = lds_address(smem);
+    if (RMAP && __builtin_amdgcn_readfirstlane(wave) == 0) {
+        // the tile's map entries and gather order into LDS past the ring, loaded by wave 0 ahead of
+        // its first stages (so the first stage's wait and barrier cover them); columns past N
+        // repeat column N - 1
+#pragma unroll
+        for (int q = 0; q < BN / 64; ++q) {
+            const int n = min(n0 + q * 64 + lane, N - 1);
+            dma_to_lds4(epi.res_cols + n, lds0 + (uint32_t)(NS * SLOT + q * 256));
+            if (epi.res_order)
+                dma_to_lds4(epi.res_order + n, lds0 + (uint32_t)(NS * SLOT + BN * 4 + q * 256));
+        }
+    }
     auto issue = [&](int st) {
         if (ugrp != 0) return;
 #pragma unroll
@@ -1361,6 +1383,9 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
         asm volatile("" ::: "memory");
         if (s + NS - 1 < stages) issue(s + NS - 1);
         if (RMAP && s == stages - 1) {
+            const int *sig = reinterpret_cast<const int *>(smem + NS * SLOT);
+            if (epi.res_order) rcol = min(max(sig[BN + tid % BN] - n0, 0), BN - 1);
+            const int rsrc = min(max(sig[rcol], 0), N - 1);
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
                 const int m = min(m0 + rrow0 + r * (512 / BN), M - 1);
@@ -2099,7 +2124,8 @@ static int launch_sp_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_
                        int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi,
                        int32_t *partial, int band = 0)
 {
-    const size_t lds = (size_t)NS * KS * (BM + BN) * BG_ROWB;
+    // RMAP: the tile's map entries and gather order (2 x BN ints) past the ring
+    const size_t lds = (size_t)NS * KS * (BM + BN) * BG_ROWB + (RMAP ? 2 * BN * sizeof(int) : 0);
     const void *fn = (const void *)k_gemm_sp<BM, BN, NS, KS, PE, VO, ST, RQN, RMAP>;
     if (int rc = ensure_dynamic_lds(fn, lds, "gemm")) return rc;
     hipLaunchKernelGGL((k_gemm_sp<BM, BN, NS, KS, PE, VO, ST, RQN, RMAP>), grid, dim3(512), lds, s, xq,
@@ -2266,7 +2292,7 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
     if (rq_done) *rq_done = false;
     if (M == 0) return W4A4_OK;
     GemmEpilogue epi = epi_in;
-    if (epi.mode != W4A4_EPI_RESIDUAL) epi.res_cols = nullptr;
+    if (epi.mode != W4A4_EPI_RESIDUAL || !epi.res_cols) epi.res_cols = epi.res_order = nullptr;
     const int row_bytes = q8 ? K : K / 2;
     const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)xq % 16 == 0) && ((uintptr_t)wq % 16 == 0);
     const bool pipe = q8 || (vec && K % BG_KS == 0);
@@ -2305,7 +2331,7 @@ int launch_gemm(const uint8_t *xq, const uint8_t *wq, int M, int N, int K, const
             if (rc != W4A4_OK) return rc;
             epi.residual = gathered;
             epi.ldr = N;
-            epi.res_cols = nullptr;
+            epi.res_cols = epi.res_order = nullptr;
         }
     }
     if (fused) {

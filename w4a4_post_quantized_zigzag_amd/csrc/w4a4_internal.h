@@ -192,8 +192,10 @@ struct GemmEpilogue {
     RqNext rq;
     // residual column map (W4A4_EPI_RESIDUAL): output column n adds residual column res_cols[n]
     // (nullptr: column n). launch_gemm reads it in the split-group kernel's staged epilogue, or
-    // gathers the residual into its workspace first.
+    // gathers the residual into its workspace first. res_order (optional, with res_cols): for each
+    // 128-column tile, the order in which that kernel's lanes gather the tile's columns.
     const int32_t *res_cols;
+    const int32_t *res_order;
 };
 constexpr int GEMM_OUT_I32 = 100;
 // q8: int8 operands [rows][K] (W8A8) instead of packed int4 [rows][K/2]

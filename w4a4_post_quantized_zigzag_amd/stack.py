@@ -60,6 +60,16 @@ class DeviceLinear:
         return self
 
 
+def _gather_order(cols):
+    """w4a4_gemm_rq_next's res_order for the residual map cols (int32 [N], N % 128 == 0): each
+    128-column tile's columns sorted by the residual column they read (ties by column)."""
+    torch = _torch()
+    t = cols.to(torch.int64).view(-1, 128)
+    idx = torch.argsort(t * 128 + torch.arange(128, device=t.device).view(1, 128), dim=1)
+    base = torch.arange(0, cols.numel(), 128, device=t.device).view(-1, 1)
+    return (idx + base).reshape(-1).to(torch.int32).contiguous()
+
+
 def _regroup(perm, U, key, B: int):
     """Reorder the channels inside each rotation block of perm by key[channel] (stable), and U's
     rows with them. A block is the same set of channels, so x_b R_b is the same rotation (R'_b =
@@ -176,6 +186,8 @@ class DeviceStack:
                 inv_u = _inverse(rp["o"])
                 m_d = inv_u if q_out is None else inv_u[q_out]
                 maps = {"o": m_o.to(torch.int32).contiguous(), "down": m_d.to(torch.int32).contiguous()}
+                if h % 128 == 0:
+                    maps.update(o_order=_gather_order(maps["o"]), down_order=_gather_order(maps["down"]))
             for n in LINEARS:
                 lin[li][n].pack(rp[n])
             self.res_map.append(maps)
@@ -217,11 +229,13 @@ class DeviceStack:
                             cout=B, store=keep)
             P["o"].update(X=None if fuse else bufs.qkv[:, 2 * h:3 * h], perm=None,
                           cin=B if fuse else A, Y=bufs.h2, epi=bd.EPI_RESIDUAL, res=cur,
-                          res_map=maps["o"], nxt=up if fuse else None, cout=A, store=True)
+                          res_map=maps["o"], res_order=maps.get("o_order"), nxt=up if fuse else None,
+                          cout=A, store=True)
             P["up"].update(X=None if fuse else bufs.h2, perm=None, cin=A, Y=bufs.g, epi=bd.EPI_GELU,
                            nxt=down if fuse else None, cout=F, store=keep)
             P["down"].update(X=None if fuse else bufs.g, perm=None, cin=F if fuse else cq(down),
                              Y=out, epi=bd.EPI_RESIDUAL, res=bufs.h2, res_map=maps["down"],
+                             res_order=maps.get("down_order"),
                              nxt=None if (last or not fuse) else self.layers[li + 1]["qkv"],
                              cout=A, store=True)
             return plan
@@ -265,7 +279,8 @@ class DeviceStack:
                             self.steps, step, Y=e["Y"], epilogue=e["epi"], residual=e.get("res"),
                             xq_next=cout[0] if kn else None, x_scale_next=cout[1] if kn else None,
                             ws=bufs.fws[(lin.N, lin.K, kn, 0 if rmap is None else 1)],
-                            store_next_cols=e.get("store", True), res_cols=rmap)
+                            store_next_cols=e.get("store", True), res_cols=rmap,
+                            res_order=e.get("res_order"))
             return
         bd.gemm(xq, xs, calib, lin.wq, lin.w_scale, lin.K, Y=e["Y"], epilogue=e["epi"],
                 residual=e.get("res"), ws=bufs.gws[(lin.N, lin.K, lin.bits)], bits=lin.bits)
