@@ -142,11 +142,14 @@ def time_graph(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_kernel_calls(calls, reps):
+def time_kernel_calls(calls, reps, replays=5):
     """Average duration (ms) of one launch of `calls` (each call enqueues one kernel): a HIP graph
-    holding `reps` back-to-back rounds of the calls is replayed between two HIP events recorded on
-    the launch stream, and the elapsed time is divided by the number of launches. The graph keeps
-    host launch overhead out of the figure; the gap between consecutive graph nodes stays in."""
+    holding `reps` back-to-back rounds of the calls is replayed `replays` times in a row between two
+    HIP events recorded on the launch stream (after two untimed replays), and the elapsed time is
+    divided by the number of launches. The graph keeps host launch overhead out of the figure, and
+    the back-to-back replays keep the queue ahead of the GPU (a single replay left about 1 us idle
+    between its launches while the host was still submitting them); the gap between consecutive
+    graph nodes stays in."""
     torch = _torch()
 
     def body():
@@ -164,14 +167,16 @@ def time_kernel_calls(calls, reps):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         body()
-    g.replay()
+    for _ in range(2):
+        g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    g.replay()
+    for _ in range(replays):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * len(calls))
+    return e0.elapsed_time(e1) / (replays * reps * len(calls))
 
 
 def source_hash(name):
