@@ -2015,7 +2015,10 @@ static void launch_big(bool vec, dim3 grid, hipStream_t s, const uint8_t *xq, co
                            K, k_split, tm, tn, epi, partial);
 }
 
-constexpr int PIPE_STAGES = 4;
+// Operand stages in the pipelined kernel's LDS ring. Three measured faster than four on the
+// 1600-token shapes (1600x3072x1024 GEMM 10.6 -> 10.3 us; mixed W4A4/W8A8 stack 11.04 -> 10.93 ms
+// per pass) and two slower on the int8-operand ones; the 256x256 tile takes two (see launch_pipe).
+constexpr int PIPE_STAGES = 3;
 
 template <int BM, int BN, int WM, int WN, int PE, bool VO, bool Q8, bool GS = false,
           bool RQN = false, int NS = PIPE_STAGES>
@@ -2041,7 +2044,8 @@ static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
 // XCDs in row bands (every XCD gets all column tiles of its rows), so that extra epilogue work is
 // spread evenly instead of landing on the XCDs that own those columns.
 // These launches use a three-stage ring: on the 1600-token stack shapes (K = 1024) it measured
-// faster than four or five stages (up GEMM 18.8 -> 18.1 us, pass about 1 % shorter).
+// faster than four or five stages (up GEMM 18.8 -> 18.1 us, pass about 1 % shorter) and as fast as
+// two.
 template <int BM, int WM, int WN>
 static int launch_pipe_rq(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                           int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi)
