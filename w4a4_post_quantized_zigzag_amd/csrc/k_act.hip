@@ -382,11 +382,12 @@ __global__ __launch_bounds__(64 * NW) void k_rq_mfma(
 //
 // Same arithmetic as k_rq_mfma for rows already in zigzag order (a permuted copy, or the caller's
 // own layout), with the activation tiles streamed by global_load_lds_dwordx4 into a ring of
-// RQ_STAGES LDS tiles so several tiles of loads are in flight while one is multiplied. The ring is
+// RQ_STAGES LDS tiles so the next tile's loads are in flight while one is multiplied (two tiles:
+// measured faster than three or four on the long-K per-token pass, 42.8 -> 41.1 us). The ring is
 // synchronized with explicit vmcnt waits and plain s_barrier (a fenced barrier would drain every
 // in-flight tile). Staged rows are XOR-swizzled by 16-byte chunk (chunk ^ (row % chunks_per_row)),
 // which makes the 16 rows a fragment read touches hit 16 different bank groups.
-constexpr int RQ_STAGES = 4;
+constexpr int RQ_STAGES = 2;
 constexpr int RQ_RING_MAX_ROWS = 1024;  // rows per workgroup (per-token scales staged in LDS)
 constexpr int RQ_SMALL_M = 256;         // batches up to this many tokens use k_rq_small
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
