@@ -104,7 +104,8 @@ __device__ __forceinline__ uint4 zero_unless(const uint4 &v, bool valid)
 // operations, several times less than a library erf with range branches.
 __device__ __forceinline__ float gelu_erf(float v)
 {
-    const float w = fminf(fabsf(v), 6.0f);
+    // min(|v|, 6) in one v_med3_f32 (for NaN v the result is NaN through the exponential below)
+    const float w = __builtin_amdgcn_fmed3f(fabsf(v), 0.0f, 6.0f);
     const float t = __builtin_amdgcn_rcpf(fmaf(0.3f, w, 1.0f));
     float p = 0.0311708786f;
     p = fmaf(p, t, -0.220824048f);
@@ -139,7 +140,10 @@ __device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi)
 // register keeps every rounding where it is written.
 __device__ __forceinline__ float fp32_value(float x)
 {
-    asm volatile("" : "+v"(x));
+    // not volatile: the value stays opaque to instruction selection, but the scheduler may still
+    // interleave the epilogue's per-element chains (volatile statements keep their program order,
+    // which serialized every element's GELU behind the previous one's)
+    asm("" : "+v"(x));
     return x;
 }
 
@@ -796,7 +800,10 @@ enum { PE_NONE = W4A4_EPI_NONE, PE_GELU = W4A4_EPI_GELU, PE_RESIDUAL = W4A4_EPI_
 // not scaled by 256.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int PE, bool VEC_OUT, bool Q8,
           bool GS = false, bool RQN = false>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
+// the fused rotate-quantize tiles run two workgroups per CU: keep their registers within two waves
+// per SIMD (the up projection's GELU form otherwise takes 260 with the interleaved epilogue)
+__attribute__((amdgpu_waves_per_eu(RQN ? 2 : 1))) void k_gemm_pipe(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, int M, int N, int K,
     int k_split, int tiles_m, int tiles_n, int band, GemmEpilogue epi,
     int32_t *__restrict__ partial)
@@ -1092,12 +1099,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_pipe(
         // the fp16 tile, unless it only feeds the next linear (its codes are written below) and the
         // caller does not need it
         const bool store_tile = !(RQN && rq_tile && !epi.rq.store_y);
+        if (store_tile) {
 #pragma unroll 4
-        for (int c = tid; c < BM * CPR; c += NT) {
-            const int r = c / CPR, cc = c % CPR;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
-            if (store_tile && r < rows_here && cc * 8 < cols_here)
-                *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+            for (int c = tid; c < BM * CPR; c += NT) {
+                const int r = c / CPR, cc = c % CPR;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&smem[r * TP + cc * 16]);
+                if (r < rows_here && cc * 8 < cols_here)
+                    *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+            }
         }
         if (RQN && rq_tile) {
             __syncthreads();  // every wave's codes are in LDS
@@ -1557,12 +1566,14 @@ __global__ __launch_bounds__(512) void k_gemm_sp(const uint8_t *__restrict__ xq,
         }
         // the fp16 tile, unless it only feeds the next linear and the caller does not need it
         const bool store_tile = !(RQN && rq_tile && !epi.rq.store_y);
+        if (store_tile) {
 #pragma unroll 2
-        for (int c = tid; c < BM * CPR; c += 512) {
-            const int r = c / CPR, cc = c % CPR;
-            const uint4 v = *reinterpret_cast<const uint4 *>(smem + XCH_BYTES + r * STP + cc * 16);
-            if (store_tile && r < rows_here && cc * 8 < cols_here)
-                *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+            for (int c = tid; c < BM * CPR; c += 512) {
+                const int r = c / CPR, cc = c % CPR;
+                const uint4 v = *reinterpret_cast<const uint4 *>(smem + XCH_BYTES + r * STP + cc * 16);
+                if (r < rows_here && cc * 8 < cols_here)
+                    *reinterpret_cast<uint4 *>(epi.Y + (int64_t)(m0 + r) * epi.ldy + n0 + cc * 8) = v;
+            }
         }
         if (RQN && rq_tile) {
             __syncthreads();  // every wave's codes are in LDS
