@@ -2054,22 +2054,21 @@ static int launch_pipe_e(dim3 grid, hipStream_t s, const uint8_t *xq, const uint
 // some column tiles carry it (the next linear's input is part of the output), the tiles go to the
 // XCDs in row bands (every XCD gets all column tiles of its rows), so that extra epilogue work is
 // spread evenly instead of landing on the XCDs that own those columns.
-// These launches use a three-stage ring: on the 1600-token stack shapes (K = 1024) it measured
-// faster than four or five stages (up GEMM 18.8 -> 18.1 us, pass about 1 % shorter) and as fast as
-// two.
+// Ring depths measured on the 1600-token stack shapes (K = 1024): three stages for the GELU and
+// residual epilogues (up GEMM 18.8 -> 18.1 us against four; two stages no faster), two for the plain
+// one (the QKV projection, pass about 0.7 % shorter than with three).
 template <int BM, int WM, int WN>
 static int launch_pipe_rq(dim3 grid, hipStream_t s, const uint8_t *xq, const uint8_t *wq, int M,
                           int N, int K, int k_split, int tm, int tn, const GemmEpilogue &epi)
 {
-    constexpr int NS = 3;
     const int band = (epi.rq.col0 > 0 || epi.rq.kn < N) ? tn : 0;
     if (epi.mode == W4A4_EPI_GELU)
-        return launch_pipe_e<BM, 128, WM, WN, PE_GELU, true, false, false, true, NS>(
+        return launch_pipe_e<BM, 128, WM, WN, PE_GELU, true, false, false, true, 3>(
             grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
     if (epi.mode == W4A4_EPI_RESIDUAL)
-        return launch_pipe_e<BM, 128, WM, WN, PE_RESIDUAL, true, false, false, true, NS>(
+        return launch_pipe_e<BM, 128, WM, WN, PE_RESIDUAL, true, false, false, true, 3>(
             grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
-    return launch_pipe_e<BM, 128, WM, WN, PE_NONE, true, false, false, true, NS>(
+    return launch_pipe_e<BM, 128, WM, WN, PE_NONE, true, false, false, true, 2>(
         grid, s, xq, wq, M, N, K, k_split, tm, tn, epi, nullptr, band);
 }
 
