@@ -159,6 +159,45 @@ def test_gemm_dequant_epilogue(per_token, epi, M, N, K):
         assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
 
 
+def _near_boundary_scales(n, mode, seed):
+    """fp32 scales with full random mantissas just below (tiny) or just above (edge) 2^-118, or
+    alternating per row (mixed): around the smallest scale whose 2^-8 multiple is still a normal
+    fp32 number, so that a dequantization that folded the accumulator's 2^8 factor into the scale
+    instead of shifting the accumulator would round differently below it."""
+    m = inputs.random_scales(n, seed=seed, lo=1.0, hi=2.0).astype(np.float64)
+    lo, hi = np.ldexp(m, -120), np.ldexp(m, -117)
+    out = {"tiny": lo, "edge": hi, "mixed": np.where(np.arange(n) % 2 == 0, lo, hi)}[mode]
+    return out.astype(np.float32)
+
+
+@pytest.mark.parametrize("mode,per_token", [("tiny", False), ("edge", False), ("tiny", True),
+                                             ("edge", True), ("mixed", True)])
+@pytest.mark.parametrize("epi", [EPI_NONE, EPI_RESIDUAL, EPI_GELU])
+@pytest.mark.parametrize("M,N,K", [(1600, 4096, 1024), (1590, 3072, 1024), (1024, 2048, 2048)])
+def test_gemm_dequant_scales_near_the_fp32_normal_limit(mode, per_token, epi, M, N, K):
+    # the activation scales sit around 2^-118 and the weight scales near 2^108, so that the
+    # outputs are ordinary fp16 values and every fp32 rounding of the dequantization shows in them
+    xq, wq = _operands(M, N, K, seed=9)
+    sx = _near_boundary_scales(M if per_token else 1, mode, seed=M + 1)
+    sw = (inputs.random_scales(N, seed=N + 2, lo=0.5, hi=1.0).astype(np.float64) * 2.0 ** 108)
+    sw = sw.astype(np.float32)
+    res = (np.random.Generator(np.random.PCG64(6)).standard_normal((M, N)) * 4).astype(np.float16)
+    Y = host(bd.gemm(dev(xq), dev(sx), per_token, dev(wq), dev(sw), K, epilogue=epi,
+                     residual=dev(res) if epi == EPI_RESIDUAL else None))
+    rows = np.unique(np.r_[np.arange(0, M, 61), np.arange(M - 4, M)])
+    q = oracle.unpack_int4(xq[rows], K)
+    acc = oracle.int_gemm(q, oracle.unpack_int4(wq, K))
+    ref, _ = oracle.dequant(acc, sx[rows] if per_token else sx, per_token, sw, epi,
+                            res[rows] if epi == EPI_RESIDUAL else None)
+    got = Y[rows].view(np.float16)
+    assert np.all(np.isfinite(ref.astype(np.float32)))
+    if epi == EPI_GELU:
+        d = np.abs(got.view(np.int16).astype(np.int32) - ref.view(np.int16).astype(np.int32))
+        assert np.max(d) <= 1
+    else:
+        assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
 def test_gemm_row_stride_and_empty():
     M, N, K = 33, 96, 256
     xq, wq = _operands(M, N, K)

@@ -108,6 +108,27 @@ def test_gemm_rq_next_matches_gemm_then_rotate_quantize(name):
                                  f"bytes differ, e.g. {bad.tolist()}")
 
 
+@pytest.mark.parametrize("mode", ["tiny", "edge"])
+def test_gemm_rq_next_scales_near_the_fp32_normal_limit(mode):
+    # the fused up-projection tile (GELU, next linear's codes) with its activation scale just
+    # below or just above 2^-118 and weight scales near 2^108: the fp16 output and the codes equal
+    # those of the plain GEMM followed by the stand-alone rotate-quantize, bit for bit
+    M, N, K, K_next, B = 1600, 4096, 1024, 4096, 128
+    d = _case(M, N, K, K_next, B, EPI_GELU, 31)
+    rng = np.random.Generator(np.random.PCG64(32))
+    xs = np.float32(np.ldexp(rng.uniform(1.0, 2.0), -120 if mode == "tiny" else -117))
+    ws = (rng.uniform(0.5, 1.0, N) * 2.0 ** 100).astype(np.float32)
+    d["xs"], d["ws"] = dev(np.array([xs], np.float32)), dev(ws)
+    d["Y0"] = bd.gemm(d["xq"], d["xs"], False, d["wq"], d["ws"], K, epilogue=EPI_GELU)
+    assert np.all(np.isfinite(host(d["Y0"]).astype(np.float32)))
+    table = _table_for(d, 0, K_next, B)
+    Y, q, s = bd.gemm_rq_next(d["xq"], d["xs"], False, d["wq"], d["ws"], K, 0, K_next, B,
+                              d["rot"], table, 2, 0, epilogue=EPI_GELU, store_next_cols=True)
+    assert _same(Y, d["Y0"])
+    q_ref, s_ref = bd.rotate_quant_act(d["Y0"], None, d["rot"], B, table, 2, 0)
+    assert _same(s, s_ref) and _same(q, q_ref)
+
+
 def test_gemm_rq_next_codes_against_the_oracle():
     M, N, K, col0, K_next, B, epi = 200, 1024, 512, 512, 512, 128, EPI_NONE
     d = _case(M, N, K, K_next, B, epi, 7)
